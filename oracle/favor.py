@@ -1,0 +1,174 @@
+"""FAVOR+ attention, oracle side: fp64 NumPy, plain definitions, no stabiliser.
+
+Shapes: q, k [B, H, L, d]; v [B, H, L, dv]; omega [H, m, d] (fp32 values).
+Inputs may be fp32 or bf16 tensors/arrays; they are widened exactly to fp64.
+
+Definitions followed (Performer paper, "Rethinking Attention with Performers",
+unless stated otherwise):
+  * scaling (section 2.3, under equation 6; also the Performer tutorial page,
+    section 1): x = q * d^(-1/4), y = k * d^(-1/4), so x.y = q.k / sqrt(d);
+  * positive random features (Lemma 1, equation 7, with the general form of
+    equation 5, h(x) = exp(-|x|^2/2), f = exp):
+        phi_r(x) = exp(omega_r . x - |x|^2 / 2) / sqrt(m);
+  * ReLU features (equation 5 with h = 1, f = ReLU; the generalised-attention
+    defaults of appendix A.4 add a small kernel epsilon to every feature):
+        phi_r(x) = max(omega_r . x, 0) / sqrt(m) + eps;
+  * bidirectional estimator (equation 4; Algorithm 1 with C = [V 1]):
+        S = Phi_K^T V,  z = Phi_K^T 1,  out_i = (Phi_Q,i . S) / (Phi_Q,i . z);
+  * causal estimator (appendix B.1, equation 11, prefix sums that include the
+    diagonal; the same recurrence as the linear-attention blog's
+    "Autoregressive Generation" section):
+        S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i),
+        out_i = (phi(q_i) . S_i) / (phi(q_i) . z_i);
+  * decode step (the same recurrence applied to one new token; RFA's
+    recurrent form, appendix A.3 of the RFA summary page): the state is
+    updated with token t first, and token t's output reads the updated state;
+  * exact softmax attention (equations 1 and 2) for accuracy reports.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (possibly bf16): widen exactly
+        import torch
+        return x.detach().to("cpu").to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
+    """phi(x) for raw queries or keys x [B,H,L,d] and omega [H,m,d] -> [B,H,L,m] (fp64)."""
+    x = _f64(x)
+    om = _f64(omega)
+    d = x.shape[-1]
+    m = om.shape[-2]
+    xs = x * (float(d) ** -0.25)
+    a = np.einsum("bhld,hmd->bhlm", xs, om)
+    if kind == "prf":
+        half_norm = 0.5 * np.sum(xs * xs, axis=-1, keepdims=True)
+        return np.exp(a - half_norm) / math.sqrt(m)
+    if kind == "relu":
+        return np.maximum(a, 0.0) / math.sqrt(m) + eps
+    raise ValueError(f"unknown feature kind {kind!r}")
+
+
+def bidir_from_features(phi_q, phi_k, v):
+    """Equation 4 from given features: returns (out, S, z)."""
+    phi_q, phi_k, v = _f64(phi_q), _f64(phi_k), _f64(v)
+    S = np.einsum("...lm,...le->...me", phi_k, v)
+    z = np.sum(phi_k, axis=-2)
+    num = np.einsum("...lm,...me->...le", phi_q, S)
+    den = np.einsum("...lm,...m->...l", phi_q, z)
+    return num / den[..., None], S, z
+
+
+def bidir(q, k, v, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
+    out, _, _ = bidir_from_features(features(q, omega, kind, eps), features(k, omega, kind, eps), v)
+    return out
+
+
+def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bool = False):
+    """Causal estimator as the plain recurrence over positions (one token at a time)."""
+    pq = features(q, omega, kind, eps)
+    pk = features(k, omega, kind, eps)
+    v = _f64(v)
+    B, H, L, m = pq.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, m, dv))
+    z = np.zeros((B, H, m))
+    out = np.empty((B, H, L, dv))
+    for i in range(L):
+        S += pk[:, :, i, :, None] * v[:, :, i, None, :]
+        z += pk[:, :, i, :]
+        num = np.einsum("bhm,bhme->bhe", pq[:, :, i, :], S)
+        den = np.einsum("bhm,bhm->bh", pq[:, :, i, :], z)
+        out[:, :, i, :] = num / den[..., None]
+    if return_state:
+        return out, S, z
+    return out
+
+
+def causal_bruteforce_from_features(phi_q, phi_k, v, rows: int | None = None):
+    """Equation 2 applied to the explicit matrix A_hat = Phi_Q Phi_K^T, masked by tril."""
+    phi_q, phi_k, v = _f64(phi_q), _f64(phi_k), _f64(v)
+    L = phi_q.shape[-2]
+    n = L if rows is None else min(rows, L)
+    A = np.einsum("...im,...jm->...ij", phi_q[..., :n, :], phi_k)
+    mask = np.tril(np.ones((n, L), dtype=bool))
+    A = np.where(mask, A, 0.0)
+    num = np.einsum("...ij,...je->...ie", A, v)
+    den = np.sum(A, axis=-1)
+    return num / den[..., None]
+
+
+def causal_bruteforce(q, k, v, omega, kind: str = "prf", eps: float = 0.0, rows: int | None = None):
+    return causal_bruteforce_from_features(features(q, omega, kind, eps), features(k, omega, kind, eps), v, rows)
+
+
+def attention_matrix(q, k, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
+    """The explicit normalised matrix D_hat^{-1} A_hat, A_hat = Phi_Q Phi_K^T ([B,H,L,L])."""
+    A = np.einsum("bhim,bhjm->bhij", features(q, omega, kind, eps), features(k, omega, kind, eps))
+    return A / np.sum(A, axis=-1, keepdims=True)
+
+
+def decode_step(S, z, q, k, v, omega, kind: str = "prf", eps: float = 0.0):
+    """One token for every (sequence, head): S [N,H,m,dv], z [N,H,m], q,k [N,H,d], v [N,H,dv].
+
+    Returns (S', z', out) with the state updated first and out read from it.
+    """
+    S = _f64(S)
+    z = _f64(z)
+    pq = features(_f64(q)[:, :, None, :], omega, kind, eps)[:, :, 0, :]
+    pk = features(_f64(k)[:, :, None, :], omega, kind, eps)[:, :, 0, :]
+    v = _f64(v)
+    S2 = S + pk[..., :, None] * v[..., None, :]
+    z2 = z + pk
+    num = np.einsum("nhm,nhme->nhe", pq, S2)
+    den = np.einsum("nhm,nhm->nh", pq, z2)
+    return S2, z2, num / den[..., None]
+
+
+def decode_run(S, z, q_steps, k_steps, v_steps, omega, kind: str = "prf", eps: float = 0.0):
+    """Several decode steps; q_steps [T,N,H,d] etc. Returns (S_T, z_T, outs [T,N,H,dv])."""
+    q_steps, k_steps, v_steps = _f64(q_steps), _f64(k_steps), _f64(v_steps)
+    S = _f64(S)
+    z = _f64(z)
+    outs = np.empty(q_steps.shape[:3] + (v_steps.shape[-1],))
+    for t in range(q_steps.shape[0]):
+        S, z, outs[t] = decode_step(S, z, q_steps[t], k_steps[t], v_steps[t], omega, kind, eps)
+    return S, z, outs
+
+
+def state_from_prior(k_prior, v_prior, omega, kind: str = "prf", eps: float = 0.0):
+    """The canonical state after a prefix of tokens: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j).
+
+    k_prior [N,H,P,d], v_prior [N,H,P,dv] -> S [N,H,m,dv], z [N,H,m] (fp64).
+    """
+    pk = features(k_prior, omega, kind, eps)
+    v = _f64(v_prior)
+    return np.einsum("nhpm,nhpe->nhme", pk, v), np.sum(pk, axis=-2)
+
+
+def softmax_attention(q, k, v, causal_mask: bool = False) -> np.ndarray:
+    """Exact attention, equations 1 (bidirectional) and 2 (unidirectional)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    d = q.shape[-1]
+    logits = np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(d)
+    if causal_mask:
+        L = logits.shape[-1]
+        logits = np.where(np.tril(np.ones((L, L), dtype=bool)), logits, -np.inf)
+    logits = logits - np.max(logits, axis=-1, keepdims=True)  # exact: cancels in the ratio
+    A = np.exp(logits)
+    return np.einsum("bhij,bhje->bhie", A, v) / np.sum(A, axis=-1)[..., None]
+
+
+def row_norm_rel_err(out, ref) -> float:
+    """max over rows of ||out_i - ref_i||_inf / ||ref_i||_inf (rows = last axis)."""
+    out = _f64(out)
+    ref = _f64(ref)
+    num = np.max(np.abs(out - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    return float(np.max(num / den))

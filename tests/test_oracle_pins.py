@@ -1,0 +1,268 @@
+"""Pins for the oracle: facts fixed by the pages or by mathematics, not by the oracle itself.
+
+Each test names the passage it follows. A plausible slip in the oracle (a
+dropped norm term, a missing d^(-1/4), a transposed contraction, an exclusive
+instead of inclusive prefix, a wrong Gram-Schmidt step) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import features, bidir, bidir_from_features, causal, causal_bruteforce, decode_run, make_omega
+
+RNG = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------- contraction
+
+def test_worked_example_from_features(golden_dir):
+    """Performer tutorial page, section 2 worked example: S=(3,10), z=(1,2), output 13/3."""
+    g = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    phi_k = np.array(g["key_features"])
+    v = np.array(g["values"])[:, None]
+    phi_q = np.array([g["query_feature"]])
+    out, S, z = bidir_from_features(phi_q, phi_k, v)
+    assert np.array_equal(S[:, 0], np.array(g["S"]))
+    assert np.array_equal(z, np.array(g["z"]))
+    assert out[0, 0] == pytest.approx(g["output_numerator"] / g["output_denominator"], rel=1e-15)
+    # the same number as a kernel-weighted average of the values
+    w = phi_q @ phi_k.T
+    assert np.allclose(w[0], g["kernel_weights"])
+
+
+@pytest.mark.parametrize("d", [2, 16])
+def test_worked_example_through_relu_feature_map(golden_dir, d):
+    """Same example through the full path: ReLU features (Performer appendix A.4), Omega = I, eps = 0.
+
+    With omega = identity, ReLU features are the positive parts of the scaled
+    inputs; any common positive factor cancels in the ratio. Negative
+    coordinates check that the ReLU clips them.
+    """
+    g = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    om = np.eye(d, dtype=np.float32)[None]
+    t = 0.7
+    k = np.zeros((1, 1, 2, d))
+    k[0, 0, 0, :2] = np.array([1.0, -3.0]) * t        # ReLU -> (1, 0)
+    k[0, 0, 1, :2] = np.array([0.0, 2.0]) * t         # -> (0, 2)
+    k[0, 0, :, 2:] = -1.5                             # clipped away
+    q = np.zeros((1, 1, 1, d))
+    q[0, 0, 0, :2] = t
+    v = np.zeros((1, 1, 2, 4))
+    v[0, 0, :, 0] = g["values"]
+    pq = features(q, om, "relu", 0.0)
+    pk = features(k, om, "relu", 0.0)
+    out, _, _ = bidir_from_features(pq, pk, v)
+    assert out[0, 0, 0, 0] == pytest.approx(13.0 / 3.0, rel=1e-14)
+    assert np.all(out[0, 0, 0, 1:] == 0.0)
+
+
+def test_four_token_toy_reassociation():
+    """Tutorial page section 2: 4 tokens, feature width 3, value width 2: (Q'K'^T)V equals Q'(K'^T V)."""
+    pq = RNG.random((4, 3)) + 0.1
+    pk = RNG.random((4, 3)) + 0.1
+    v = RNG.normal(size=(4, 2))
+    explicit = pq @ pk.T                      # the 4 x 4 matrix the linear form avoids
+    ref = (explicit @ v) / explicit.sum(axis=1, keepdims=True)
+    out, S, z = bidir_from_features(pq, pk, v)
+    assert S.shape == (3, 2) and z.shape == (3,)
+    assert np.allclose(out, ref, rtol=1e-13, atol=0)
+
+
+def test_bidir_equals_explicit_attention_matrix():
+    """Equation 4 versus the explicit L x L matrix A_hat = Phi_Q Phi_K^T (equation 1 applied to A_hat)."""
+    B, H, L, d, dv, m = 1, 2, 37, 16, 8, 32
+    q = RNG.normal(size=(B, H, L, d)) * 0.5
+    k = RNG.normal(size=(B, H, L, d)) * 0.5
+    v = RNG.normal(size=(B, H, L, dv))
+    om = make_omega(7, H, m, d)
+    pq, pk = features(q, om), features(k, om)
+    for h in range(H):
+        A = pq[0, h] @ pk[0, h].T
+        ref = np.diag(1.0 / A.sum(axis=1)) @ A @ v[0, h]
+        assert np.max(np.abs(bidir(q, k, v, om)[0, h] - ref)) < 1e-12
+
+
+def test_one_hot_values_extract_the_normalised_matrix():
+    """Performer appendix C.4: with V = I_L the output is D_hat^-1 A_hat; rows sum to one."""
+    L, d, m = 24, 16, 32
+    q = RNG.normal(size=(1, 1, L, d)) * 0.5
+    k = RNG.normal(size=(1, 1, L, d)) * 0.5
+    om = make_omega(3, 1, m, d)
+    out = bidir(q, k, np.eye(L)[None, None], om)
+    assert np.allclose(out.sum(axis=-1), 1.0, atol=1e-13)
+    assert np.all(out > 0)
+    assert np.allclose(out, oracle.attention_matrix(q, k, om), atol=1e-14)
+
+
+# ---------------------------------------------------------------- causal
+
+def test_causal_three_forms_agree():
+    """Equation 11 (prefix sums, diagonal included) == masked brute force (equation 2 on A_hat) == decode recurrence."""
+    B, H, L, d, dv, m = 2, 2, 29, 16, 8, 48
+    q = RNG.normal(size=(B, H, L, d)) * 0.5
+    k = RNG.normal(size=(B, H, L, d)) * 0.5
+    v = RNG.normal(size=(B, H, L, dv))
+    om = make_omega(11, H, m, d)
+    rec = causal(q, k, v, om)
+    brute = causal_bruteforce(q, k, v, om)
+    assert np.max(np.abs(rec - brute)) < 1e-12
+    # decode from the zero state: token t's output reads the state after adding token t
+    S0 = np.zeros((B, H, m, dv))
+    z0 = np.zeros((B, H, m))
+    _, _, outs = decode_run(S0, z0, np.moveaxis(q, 2, 0), np.moveaxis(k, 2, 0), np.moveaxis(v, 2, 0), om)
+    assert np.max(np.abs(np.moveaxis(outs, 0, 2) - rec)) < 1e-12
+    # row 0 sees only token 0; the last row equals the bidirectional output
+    assert np.allclose(rec[:, :, 0], v[:, :, 0], atol=1e-14)
+    assert np.allclose(rec[:, :, -1], bidir(q, k, v, om)[:, :, -1], atol=1e-12)
+
+
+def test_causal_state_matches_prior_state():
+    B, H, L, d, dv, m = 1, 2, 40, 16, 16, 32
+    k = RNG.normal(size=(B, H, L, d)) * 0.5
+    v = RNG.normal(size=(B, H, L, dv))
+    om = make_omega(5, H, m, d)
+    _, S, z = causal(k, k, v, om, return_state=True)
+    S2, z2 = oracle.state_from_prior(k, v, om)
+    assert np.allclose(S, S2, rtol=1e-12) and np.allclose(z, z2, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- feature map
+
+def _prf_single_estimates(x, y, om):
+    """m * phi_r(x) phi_r(y) for every feature r: single-feature estimates of SM(x, y) (scaled inputs)."""
+    d = x.shape[-1]
+    s = float(d) ** 0.25  # undo the library-side scaling so that x, y are the scaled vectors
+    m = om.shape[1]
+    fx = features((x * s)[None, None, None], om)[0, 0, 0]
+    fy = features((y * s)[None, None, None], om)[0, 0, 0]
+    return m * fx * fy
+
+
+def test_positive_features_unbiased_lemma1_with_lemma2_variance():
+    """Lemma 1: E[phi(x).phi(y)] = exp(x.y); the iid estimator's MSE is Lemma 2's closed form.
+
+    Lemma 2 (positive features): MSE = (1/m) exp(|z|^2) SM(x,y)^2 (1 - exp(-|z|^2)), z = x + y.
+    """
+    d, m = 16, 32768
+    om = make_omega(2024, 1, m, d, "iid")
+    for trial in range(3):
+        x = RNG.normal(size=d) * 0.1
+        y = RNG.normal(size=d) * 0.1
+        sm = math.exp(float(x @ y))
+        z2 = float((x + y) @ (x + y))
+        mse1 = math.exp(z2) * sm ** 2 * (1.0 - math.exp(-z2))   # one feature
+        est = _prf_single_estimates(x, y, om)
+        mean = float(est.mean())
+        assert abs(mean - sm) < 4.0 * math.sqrt(mse1 / m), (mean, sm)
+        var = float(est.var())
+        assert var == pytest.approx(mse1, rel=0.12), (var, mse1)
+        # a feature map without the -|x|^2/2 term would be biased by exp((|x|^2+|y|^2)/2)
+        bias = sm * (math.exp(0.5 * (float(x @ x) + float(y @ y))) - 1.0)
+        assert bias > 8.0 * math.sqrt(mse1 / m)
+
+
+def test_features_apply_the_sqrt_d_temperature():
+    """Section 2.3 under equation 6: raw q, k are scaled so that the kernel is exp(q.k / sqrt(d))."""
+    d, m = 16, 16384
+    om = make_omega(99, 1, m, d, "iid")
+    q = RNG.normal(size=d) * 0.3
+    k = RNG.normal(size=d) * 0.3
+    est = float((features(q[None, None, None], om) * features(k[None, None, None], om)).sum())
+    assert est == pytest.approx(math.exp(float(q @ k) / math.sqrt(d)), rel=0.02)
+    assert abs(est - math.exp(float(q @ k))) > 0.05 * math.exp(float(q @ k) / math.sqrt(d)) or abs(q @ k) < 0.1
+
+
+def test_orthogonal_features_reduce_mse_theorem2():
+    """Theorem 2 (m <= d): MSE_ort <= MSE_iid - (1 - 1/m) * 2/(d+2) * (SM - Lambda)^2.
+
+    The extracted statement lost its squares; the gap is read from appendix
+    F.4 (equation 42 and its proof), with Lambda = exp(-(|x|^2 + |y|^2)/2).
+    Monte Carlo over many independent Omega draws, small inputs.
+    """
+    d = m = 8
+    R = 6000
+    x = np.array([0.31, -0.12, 0.05, 0.22, -0.18, 0.09, 0.14, -0.07])
+    y = np.array([0.11, 0.25, -0.16, 0.04, 0.13, -0.21, 0.08, 0.19])
+    sm = math.exp(float(x @ y))
+    z2 = float((x + y) @ (x + y))
+    mse_iid = (1.0 / m) * math.exp(z2) * sm ** 2 * (1.0 - math.exp(-z2))
+    lam = math.exp(-0.5 * (float(x @ x) + float(y @ y)))
+    gap = (1.0 - 1.0 / m) * 2.0 / (d + 2) * (sm - lam) ** 2
+    e_ort = np.array([_prf_single_estimates(x, y, make_omega(50000 + s, 1, m, d)).mean() for s in range(R)])
+    e_iid = np.array([_prf_single_estimates(x, y, make_omega(50000 + s, 1, m, d, "iid")).mean() for s in range(R)])
+    se = lambda e: float(np.std((e - sm) ** 2)) / math.sqrt(R)
+    mse_ort = float(np.mean((e_ort - sm) ** 2))
+    mse_iid_mc = float(np.mean((e_iid - sm) ** 2))
+    assert abs(mse_iid_mc - mse_iid) < 4 * se(e_iid)          # Lemma 2 again, iid
+    assert mse_ort < mse_iid - 3 * se(e_ort)                   # orthogonality helps
+    assert mse_ort <= mse_iid - gap + 3 * se(e_ort)            # by at least the gap
+
+
+def test_favor_converges_to_softmax_attention():
+    """The estimator approximates equation 1 (exact softmax attention) and improves with m (section 4.2)."""
+    B, H, L, d, dv = 1, 2, 64, 16, 16
+    q = RNG.normal(size=(B, H, L, d)) * 0.6
+    k = RNG.normal(size=(B, H, L, d)) * 0.6
+    v = RNG.normal(size=(B, H, L, dv))
+    exact = oracle.softmax_attention(q, k, v)
+    errs = []
+    for m in (16, 256, 4096):
+        approx = bidir(q, k, v, make_omega(1, H, m, d))
+        errs.append(float(np.sqrt(np.mean((approx - exact) ** 2))))
+    assert errs[2] < errs[1] < errs[0]
+    assert errs[2] < 0.02
+    ex_c = oracle.softmax_attention(q, k, v, causal_mask=True)
+    ap_c = causal(q, k, v, make_omega(1, H, 4096, d))
+    assert float(np.sqrt(np.mean((ap_c - ex_c) ** 2))) < 0.03
+
+
+def test_relu_features():
+    """Equation 5 with f = ReLU: features are positive parts of omega.x scaled by 1/sqrt(m), plus eps."""
+    d, m = 16, 32
+    om = make_omega(4, 1, m, d)
+    x = RNG.normal(size=(1, 1, 5, d))
+    f0 = features(x, om, "relu", 0.0)
+    f1 = features(x, om, "relu", 1e-3)
+    assert np.all(f0 >= 0) and np.any(f0 == 0)
+    assert np.allclose(f1 - f0, 1e-3, atol=1e-15)
+    # positive rescaling of q (or k) cancels when eps = 0
+    k = RNG.normal(size=(1, 1, 9, d))
+    v = RNG.normal(size=(1, 1, 9, 4))
+    a = bidir(x, k, v, om, "relu", 0.0)
+    b = bidir(3.7 * x, 0.2 * k, v, om, "relu", 0.0)
+    assert np.allclose(a, b, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_invariants():
+    B, H, L, d, dv, m = 1, 1, 31, 16, 8, 64
+    q = RNG.normal(size=(B, H, L, d))
+    k = RNG.normal(size=(B, H, L, d))
+    v = RNG.normal(size=(B, H, L, dv))
+    om = make_omega(21, H, m, d)
+    out = bidir(q, k, v, om)
+    # L = 1: the output is the single value
+    assert np.allclose(bidir(q[:, :, :1], k[:, :, :1], v[:, :, :1], om), v[:, :, :1], atol=1e-15)
+    # constant V gives that constant
+    c = np.broadcast_to(RNG.normal(size=dv), v.shape)
+    assert np.allclose(bidir(q, k, c, om), c, atol=1e-13)
+    # identical keys: the mean of V
+    kk = np.broadcast_to(k[:, :, :1], k.shape)
+    assert np.allclose(bidir(q, kk, v, om), np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape), atol=1e-13)
+    # linear in V
+    v2 = RNG.normal(size=v.shape)
+    assert np.allclose(bidir(q, k, 2.0 * v - v2, om), 2.0 * out - bidir(q, k, v2, om), atol=1e-12)
+    # joint permutation of (K, V) rows leaves the bidirectional output unchanged
+    p = RNG.permutation(L)
+    assert np.allclose(bidir(q, k[:, :, p], v[:, :, p], om), out, atol=1e-13)
+    # permuting the rows of Omega changes nothing
+    pr = RNG.permutation(m)
+    assert np.allclose(bidir(q, k, v, om[:, pr]), out, atol=1e-13)
+    # outputs are convex combinations of values
+    assert np.all(out <= v.max(axis=2, keepdims=True) + 1e-12)
+    assert np.all(out >= v.min(axis=2, keepdims=True) - 1e-12)

@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the benchmark.
+
+This module only draws random numbers and names shapes. It holds none of the
+attention arithmetic: neither the oracle nor the HIP library is imported here,
+and neither of them imports this module. Tests draw one set of inputs here and
+hand identical copies to both sides.
+
+Workloads (all Gaussian, the shapes used by the Performer and RFA pages for
+bidirectional attention, causal attention and recurrent decoding):
+
+  bidir_small  fp32  B1 H1  L256  d16 dv16 m32   Q,K,V ~ N(0, 0.5^2)        seed 0
+  bidir_fp32   fp32  B1 H8  L4096 d16 dv16 m128  Q,K,V ~ N(0, 1)            seed 1
+  bidir_bf16   bf16  B8 H12 L4096 d64 dv64 m256  Q,K ~ N(0,1)/sqrt2, V~N(0,1) seed 2
+  causal_bf16  bf16  B4 H8  L8192 d64 dv64 m256  Q,K,V ~ 0.5 N(0, 1)        seed 3
+  decode_bf16  bf16  256 sequences, H16 d64 dv64 m256; 2048 prior tokens
+               build the state, then 1000 steps of q,k,v ~ N(0,1)         seed 4
+
+Draw order for one workload: Q, then K, then V, each one `torch.randn` call on
+a CPU generator seeded with the workload's seed, scaled, then rounded to the
+workload's dtype with round-to-nearest-even.  Decode step inputs are large
+(1.57 GB), so they are drawn on the device with torch's counter-based CUDA
+generator; tests copy the slices they check back to the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "bidir" | "causal" | "decode"
+    dtype: str           # "f32" | "bf16"
+    B: int
+    H: int
+    L: int
+    d: int
+    dv: int
+    m: int
+    seed: int
+    q_scale: float
+    k_scale: float
+    v_scale: float
+    steps: int = 0       # decode only
+    prior: int = 0       # decode only: tokens folded into the initial state
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "bidir_small": Workload("bidir_small", "bidir", "f32", 1, 1, 256, 16, 16, 32, 0, 0.5, 0.5, 0.5),
+    "bidir_fp32": Workload("bidir_fp32", "bidir", "f32", 1, 8, 4096, 16, 16, 128, 1, 1.0, 1.0, 1.0),
+    "bidir_bf16": Workload("bidir_bf16", "bidir", "bf16", 8, 12, 4096, 64, 64, 256, 2,
+                           1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
+    "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
+    "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
+                            steps=1000, prior=2048),
+}
+
+
+def _randn(gen: torch.Generator, shape, scale: float, dtype: torch.dtype, device="cpu") -> torch.Tensor:
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
+    if scale != 1.0:
+        x = x * scale
+    return x.to(dtype)
+
+
+def make_qkv(w: Workload, device: str = "cpu"):
+    """Q, K in [B,H,L,d] and V in [B,H,L,dv], contiguous, in the workload dtype.
+
+    Drawn on a CPU generator (so the values do not depend on the GPU) and then
+    moved to `device`.
+    """
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    q = _randn(gen, (w.B, w.H, w.L, w.d), w.q_scale, w.torch_dtype)
+    k = _randn(gen, (w.B, w.H, w.L, w.d), w.k_scale, w.torch_dtype)
+    v = _randn(gen, (w.B, w.H, w.L, w.dv), w.v_scale, w.torch_dtype)
+    if device != "cpu":
+        q, k, v = q.to(device), k.to(device), v.to(device)
+    return q, k, v
+
+
+def make_decode_prior(w: Workload, n_seq: Optional[int] = None, device: str = "cpu"):
+    """The `prior` tokens that build the initial decode state.
+
+    Returns k [S,H,prior,d] and v [S,H,prior,dv] for the first `n_seq`
+    sequences (all of them by default), drawn on a CPU generator in the
+    workload dtype. Only K and V enter the state.
+    """
+    n = w.B if n_seq is None else n_seq
+    gen = torch.Generator("cpu").manual_seed(w.seed * 1000003 + 17)
+    k = _randn(gen, (n, w.H, w.prior, w.d), w.k_scale, w.torch_dtype)
+    v = _randn(gen, (n, w.H, w.prior, w.dv), w.v_scale, w.torch_dtype)
+    if device != "cpu":
+        k, v = k.to(device), v.to(device)
+    return k, v
+
+
+def make_decode_steps(w: Workload, device: str, steps: Optional[int] = None):
+    """All decode-step inputs, pre-drawn so that no RNG runs inside a timed loop.
+
+    q, k: [steps, S, H, d]; v: [steps, S, H, dv], in the workload dtype, drawn
+    with a generator on `device` (torch's Philox generator on a GPU).
+    """
+    n_steps = w.steps if steps is None else steps
+    gen = torch.Generator(device).manual_seed(w.seed)
+    q = _randn(gen, (n_steps, w.B, w.H, w.d), w.q_scale, w.torch_dtype, device)
+    k = _randn(gen, (n_steps, w.B, w.H, w.d), w.k_scale, w.torch_dtype, device)
+    v = _randn(gen, (n_steps, w.B, w.H, w.dv), w.v_scale, w.torch_dtype, device)
+    return q, k, v
+
+
+def make_tensor(shape, seed: int, scale: float = 1.0, dtype=torch.float32, device="cpu") -> torch.Tensor:
+    """One seeded Gaussian tensor, for ad-hoc test cases."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    t = _randn(gen, shape, scale, dtype)
+    return t.to(device) if device != "cpu" else t
