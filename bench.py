@@ -1,0 +1,265 @@
+"""FAVOR+ forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one full pass of the selected path over one batch of synthetic,
+seeded inputs already resident in device memory:
+  bidir_bf16  (default, the headline workload) favor_bidir, B8 H12 L4096 d64 dv64 m256, bf16 in/out
+  causal_bf16 favor_causal, B4 H8 L8192 d64 dv64 m256
+  decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
+  bidir_fp32 / bidir_small  the fp32 parity workloads
+Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
+decode, head-tokens/s), the dominant kernel's roofline fraction (per-launch
+durations from HIP events recorded on the launch stream during the timed
+region), and the fp64 oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "FAVOR+ fwd tokens/sec (B*H*L/s) + % MFMA/HBM roofline, L=4096 m=256 bf16"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+
+
+def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
+    """Algorithmic (flops, bytes) of one launch of kernel `name` for workload w.
+
+    Per token-head: projection 2*m*d flops, contraction with [V 1] or [S z]
+    2*m*(dv+1) flops; bytes are the inputs the step must read and the outputs it
+    must write (q/k/v at the input width, out at the output width)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.L
+    proj = 2 * w.m * w.d
+    contr = 2 * w.m * (w.dv + 1)
+    if name == "reduce":
+        return th * (proj + contr), th * (w.d + w.dv) * eb
+    if name == "output":
+        return th * (proj + contr), th * (w.d * eb + w.dv * out_bytes)
+    if name == "sweep":       # queries and keys projected, inter+intra contractions, outputs
+        return th * (2 * proj + 2 * contr), th * ((2 * w.d + w.dv) * eb + w.dv * out_bytes)
+    if name == "decode":      # per (sequence, head): q,k projections, state read+write, out
+        sb = (w.m * w.dv + w.m) * 4
+        return th * (2 * proj + 2 * contr), th * (2 * sb + (2 * w.d + w.dv) * eb + w.dv * 4)
+    return None, None
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "random_feature_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if taken on the current sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("src_hash") != _src_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
+    """The fp64 oracle on the host, single-threaded, on as many (b,h) pairs (decode: sequences) as fit
+    in about `budget_s` seconds; returns tokens/s in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    om = oracle.make_omega(w.seed, w.H, w.m, w.d)
+    with threadpool_limits(1):
+        if w.kind in ("bidir", "causal"):
+            q, k, v = workloads.make_qkv(w)
+            fn = oracle.bidir if w.kind == "bidir" else oracle.causal
+            done, t0 = 0, time.perf_counter()
+            for b in range(w.B):
+                for h in range(w.H):
+                    sl = (slice(b, b + 1), slice(h, h + 1))
+                    fn(q[sl], k[sl], v[sl], om[h:h + 1])
+                    done += 1
+                    if time.perf_counter() - t0 > budget_s:
+                        break
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return dict(value=done * w.L / dt, unit="tokens/s", cores=1, kind="oracle",
+                        sample=f"{done} of {w.B * w.H} (b,h) pairs x {w.L} tokens, fp64 NumPy, 1 thread, "
+                               f"{dt:.1f} s")
+        # decode: steps of the fp64 recurrence for all heads of a few sequences
+        gen = torch.Generator().manual_seed(w.seed)
+        n_seq = 8
+        S = np.zeros((n_seq, w.H, w.m, w.dv))
+        z = np.ones((n_seq, w.H, w.m))
+        steps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            qq = torch.randn(n_seq, w.H, w.d, generator=gen).bfloat16()
+            kk = torch.randn(n_seq, w.H, w.d, generator=gen).bfloat16()
+            vv = torch.randn(n_seq, w.H, w.dv, generator=gen).bfloat16()
+            S, z, _ = oracle.decode_step(S, z, qq, kk, vv, om)
+            steps += 1
+        dt = time.perf_counter() - t0
+        return dict(value=steps * n_seq * w.H / dt, unit="head-tokens/s", cores=1, kind="oracle",
+                    sample=f"{steps} decode steps x {n_seq} sequences x {w.H} heads, fp64 NumPy, 1 thread, "
+                           f"{dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="also time with this many input sets in rotation (> the 256 MB MALL); 0 to skip")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
+              f"(the path shards over (b,h) pairs with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import random_feature_amd as rf
+    w = workloads.WORKLOADS[a.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dt = w.torch_dtype
+    om = rf.make_omega(w.seed, w.H, w.m, w.d, device=dev)
+
+    if w.kind == "decode":
+        S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
+        z = torch.empty((w.B, w.H, w.m), dtype=torch.float32, device=dev)
+        # initial state: the canonical final state of a causal pass over `prior` tokens per sequence
+        gen = torch.Generator(dev).manual_seed(w.seed + 1)
+        for s0 in range(0, w.B, 64):
+            n = min(64, w.B - s0)
+            kp = (torch.randn(n, w.H, w.prior, w.d, generator=gen, device=dev) * w.k_scale).to(dt)
+            vp = (torch.randn(n, w.H, w.prior, w.dv, generator=gen, device=dev) * w.v_scale).to(dt)
+            _, S_, z_ = rf.causal(kp, kp, vp, om, return_state=True)
+            S[s0:s0 + n] = S_
+            z[s0:s0 + n] = z_
+            del kp, vp
+        n_steps = a.warmup + a.steps
+        qs, ks, vs = workloads.make_decode_steps(w, dev, steps=n_steps)
+        out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+        it = iter(range(10 ** 9))
+
+        def step(i=None):
+            t = next(it) % n_steps
+            rf.decode(qs[t], ks[t], vs[t], om, S, z, out=out)
+        tokens_per_step = w.B * w.H
+        unit = "head-tokens/s"
+        out_bytes = 4
+        sets = None
+    else:
+        sets = []
+        nset = 1 + (max(0, a.rotate - 1) if a.rotate else 0)
+        for r in range(nset):
+            q, k, v = workloads.make_qkv(w.with_(seed=w.seed + 1000 * r) if r else w, device=dev)
+            sets.append((q, k, v))
+        q, k, v = sets[0]
+        ws = rf.workspace(w.kind == "causal", q, v, om)
+        out = torch.empty((w.B, w.H, w.L, w.dv), dtype=dt, device=dev)
+        fn = rf.bidir if w.kind == "bidir" else rf.causal
+        cur = [0]
+
+        def step(i=None):
+            qq, kk, vv = sets[cur[0]]
+            fn(qq, kk, vv, om, ws=ws, out=out)
+        tokens_per_step = w.B * w.H * w.L
+        unit = "tokens/s"
+        out_bytes = 2 if dt == torch.bfloat16 else 4
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    rf.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    recs = rf.timing_read()
+    rf.timing_enable(False)
+
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    avg = {n: sum(v) / len(v) for n, v in per.items()}
+    dominant = max(avg, key=lambda n: avg[n] * len(per[n]))
+    flops, nbytes = _kernel_work(w, dominant, out_bytes)
+    roofline = None
+    if flops is not None:
+        t_s = avg[dominant] * 1e-3
+        gbs = nbytes / t_s / 1e9
+        peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        tfl = flops / t_s / 1e12
+        hbm_time, mfma_time = nbytes / (PEAK_HBM_GBS * 1e9), flops / (peak_f * 1e12)
+        if hbm_time >= mfma_time:
+            roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                            frac=round(gbs / PEAK_HBM_GBS, 4), traffic=_traffic(dominant, w.name))
+        else:
+            roofline = dict(bound="mfma", achieved=round(tfl, 2), peak=peak_f, unit="TFLOP/s",
+                            frac=round(tfl / peak_f, 4), traffic=_traffic(dominant, w.name))
+        roofline.update(kernel=dominant, avg_launch_us=round(avg[dominant] * 1e3, 2),
+                        mfma_tflops=round(tfl, 2), mfma_frac=round(tfl / peak_f, 4),
+                        hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+                        algorithmic_flops=flops, algorithmic_bytes=nbytes)
+
+    cold = None
+    if sets is not None and len(sets) > 1:
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(a.steps):
+            cur[0] = i % len(sets)
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold = tokens_per_step * a.steps / (e0.elapsed_time(e1) * 1e-3)
+        cur[0] = 0
+
+    value = tokens_per_step * a.steps / (total_ms * 1e-3)
+    res = {
+        "metric": METRIC if w.name == "bidir_bf16" else f"FAVOR+ {w.kind} {unit}, workload {w.name}",
+        "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "dv": w.dv,
+                   "m": w.m, "feature_map": "prf", "out_dtype": "fp32" if w.kind == "decode" else w.dtype},
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
+        "roofline": roofline,
+    }
+    if cold is not None:
+        res["value_rotating_inputs"] = cold
+        res["rotating_input_sets"] = len(sets)
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

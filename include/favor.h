@@ -1,0 +1,149 @@
+/*
+ * favor.h — C ABI of libfavor, FAVOR+ random-feature attention on MI355X (gfx950).
+ *
+ * The method (Performer paper, "Rethinking Attention with Performers"):
+ *   x = q * d^(-1/4), y = k * d^(-1/4)                      (section 2.3, under eq. 6)
+ *   phi_r(x) = exp(omega_r . x - |x|^2 / 2) / sqrt(m)        (Lemma 1, eq. 7; eq. 5)
+ *   bidirectional: out_i = phi(q_i) . S / phi(q_i) . z,      (eq. 4; Algorithm 1)
+ *                  S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j)
+ *   causal:        the same with the sums over j <= i        (appendix B.1, eq. 11)
+ *   decode:        S += phi(k) v^T, z += phi(k), then out = phi(q).S / phi(q).z
+ *                  (the recurrent form of the causal sums; linear-attention blog,
+ *                  "Autoregressive Generation"; RFA summary page, appendix A.3)
+ * A ReLU feature map phi_r(x) = max(omega_r . x, 0) / sqrt(m) + eps (eq. 5 with
+ * f = ReLU; appendix A.4) is selectable.
+ *
+ * Conventions shared by every entry point
+ *   - Layouts are dense row-major: q, k [B,H,L,d]; v [B,H,L,dv]; out [B,H,L,dv];
+ *     omega [H,m,d] fp32 (one random-feature matrix per head).
+ *   - Device pointers must be 16-byte aligned. The caller owns every buffer;
+ *     the library allocates no device memory and keeps no state between calls.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and the call returns without waiting. FAVOR_ERR_HIP reports a launch
+ *     error; errors inside kernels surface at the caller's next synchronisation.
+ *   - Arguments are checked before anything is launched. Bad arguments return
+ *     FAVOR_ERR_INVALID_ARG, a valid but unbuilt shape FAVOR_ERR_UNSUPPORTED,
+ *     a short workspace FAVOR_ERR_WORKSPACE; nothing is launched in those cases
+ *     and output buffers are untouched. There is no fallback path.
+ *   - Non-finite inputs are not checked; they propagate.
+ *   - q and k are raw: the d^(-1/4) scaling happens inside the library.
+ *   - The max-subtraction stabilisers (per query row; one constant per (b,h)
+ *     for keys, or per segment prefix in the causal form) cancel exactly in the
+ *     ratio, so results equal the unstabilised definitions up to rounding.
+ */
+#ifndef FAVOR_H
+#define FAVOR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FAVOR_OK = 0,
+  FAVOR_ERR_INVALID_ARG = 1,
+  FAVOR_ERR_UNSUPPORTED = 2,
+  FAVOR_ERR_WORKSPACE = 3,
+  FAVOR_ERR_HIP = 4
+} favor_status;
+
+/* Element type of q, k, v (and of out for favor_bidir / favor_causal unless out_f32).
+ * Arithmetic: FAVOR_F32 projects and contracts in fp32 (fp32 MFMA);
+ * FAVOR_BF16 projects and contracts on bf16 MFMA with fp32 accumulation. */
+typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
+
+/* Feature map: positive softmax features (Lemma 1) or ReLU features (appendix A.4). */
+typedef enum { FAVOR_PRF = 0, FAVOR_RELU = 1 } favor_kind;
+
+/* Omega rows: orthogonal blocks with chi(d) lengths (section 2.4, appendix B.2/F.4),
+ * independent Gaussian rows, or orthogonal rows of length sqrt(d) (SMREG, section 2.3). */
+typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2 } favor_omega_mode;
+
+/* favor_make_omega — random features omega [H,m,d] fp32 into device memory.
+ * Section 2.4 and appendix B.2 of the Performer paper: for each head, ceil(m/d)
+ * independent d x d Gaussian blocks, rows orthogonalised by Gram-Schmidt, row r
+ * rescaled by an independent chi(d) length (marginally N(0, I_d), appendix F.4);
+ * rows past m are dropped. Computed on the host in fp64 from a counter-based
+ * SplitMix64 stream keyed by (seed, head, block) and rounded to fp32, so the
+ * bits depend only on (seed, H, m, d, mode): head h's rows do not depend on H.
+ * Then copied with hipMemcpyAsync on `stream` (the host buffer stays alive
+ * until the copy completes: the call synchronises `stream` before returning).
+ * Requires 1 <= d <= 256, 1 <= m <= 4096, 1 <= H <= 65536. */
+favor_status favor_make_omega(uint64_t seed, int H, int m, int d, favor_omega_mode mode,
+                              float* omega_dev, hipStream_t stream);
+
+/* favor_make_omega_host — the same bits into caller-owned host memory [H,m,d]. No GPU needed. */
+favor_status favor_make_omega_host(uint64_t seed, int H, int m, int d, favor_omega_mode mode,
+                                   float* omega_host);
+
+/* favor_features — the feature map alone (Lemma 1 / eq. 5) for x [B,H,L,d] (raw q or k).
+ * Writes phi [B,H,L,m] fp32 and logscale [B,H,L] fp32 with the true feature
+ *   phi_true[b,h,l,r] = phi[b,h,l,r] * exp(logscale[b,h,l]).
+ * PRF: phi is exp(omega_r.x - max_r' omega_r'.x) / sqrt(m) (each row's largest
+ * entry is 1/sqrt(m)) and logscale = max_r omega_r.x - |x|^2/2, so no row over- or
+ * underflows. RELU: phi = max(omega_r.x, 0)/sqrt(m) + eps and logscale = 0.
+ * Supported (d, m): see favor_bidir. */
+favor_status favor_features(const void* x, const float* omega, int B, int H, int L, int d, int m,
+                            favor_dtype dtype, favor_kind kind, float eps,
+                            float* phi, float* logscale, hipStream_t stream);
+
+/* favor_bidir — bidirectional FAVOR+ (eq. 4, Algorithm 1 with C = [V 1]).
+ * out [B,H,L,dv] in the input dtype (bf16 rounded to nearest even), or fp32
+ * when out_f32 != 0. ws: device scratch of at least
+ * favor_workspace_size(0, B, H, L, d, dv, m, dtype) bytes; its contents on
+ * entry do not matter and are garbage on exit.
+ * Built shapes (d, dv, m): (16,16,16) (16,16,32) (16,16,64) (16,16,128) (16,16,256)
+ * (32,32,64) (32,32,128) (64,64,64) (64,64,128) (64,64,256), both dtypes. */
+favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega,
+                         int B, int H, int L, int d, int dv, int m,
+                         favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* favor_causal — unidirectional FAVOR+ (appendix B.1 eq. 11: prefix sums including
+ * the diagonal) as a chunked scan. Same arguments and shapes as favor_bidir
+ * (workspace from favor_workspace_size(1, ...)). If S_final [B,H,m,dv] and
+ * z_final [B,H,m] (fp32, both or neither) are non-NULL, the state after the last
+ * token is written in canonical (unstabilised) scale: exactly what
+ * favor_decode continues from. Canonical state needs PRF with d <= 64
+ * (exp(omega.x - |x|^2/2) <= exp(|omega|^2/2) stays inside fp32). */
+favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega,
+                          int B, int H, int L, int d, int dv, int m,
+                          favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                          void* out, float* S_final, float* z_final,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* favor_decode — one recurrent step for N sequences x H heads (the causal sums
+ * advanced by one token; token t's output reads the state that includes t).
+ * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical
+ * scale, updated in place; out [N,H,dv] fp32.
+ * Requires d in {16, 32, 64}, dv a multiple of 4 with dv <= 256, m a multiple of 64
+ * with m <= 1024. */
+favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega,
+                          float* S, float* z, int N, int H, int d, int dv, int m,
+                          favor_dtype dtype, favor_kind kind, float eps,
+                          float* out, hipStream_t stream);
+
+/* Bytes of device workspace favor_bidir (causal = 0) or favor_causal (causal = 1)
+ * needs for these sizes; 0 if the arguments are invalid. */
+size_t favor_workspace_size(int causal, int B, int H, int L, int d, int dv, int m, favor_dtype dtype);
+
+/* Opt-in launch timing for profiling. favor_timing_enable(1) clears the record list
+ * and, from then on, brackets every kernel the library launches with two HIP events
+ * recorded on that launch's stream; favor_timing_enable(0) clears and stops.
+ * favor_timing_read synchronises the recorded events and fills up to `cap`
+ * (kernel name, milliseconds) pairs in launch order (names are static strings);
+ * it returns the total number of records. Either output pointer may be NULL.
+ * The record list is process-wide and guarded by a mutex. */
+favor_status favor_timing_enable(int on);
+int favor_timing_read(const char** names, float* ms, int cap);
+
+/* Static description of a status code. */
+const char* favor_status_string(favor_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FAVOR_H */

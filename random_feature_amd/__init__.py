@@ -1,0 +1,226 @@
+"""random_feature_amd — FAVOR+ random-feature attention on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of `libfavor.so` (declared in
+include/favor.h). Every step of the computation runs in the library's HIP
+kernels; this module only checks tensors, passes device pointers, sizes and
+the current HIP stream, and allocates outputs/workspace with torch.
+
+The library must be built first (`python random_feature_amd/build.py`, or
+`__graft_entry__.build()`); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfavor.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libfavor.so not found at {LIB_PATH}: build it with `python random_feature_amd/build.py` "
+        "(there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16 = 0, 1
+PRF, RELU = 0, 1
+OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2}
+KINDS = {"prf": PRF, "relu": RELU}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "hip error"}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_lib.favor_make_omega.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
+_lib.favor_make_omega_host.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp]
+_lib.favor_features.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]
+_lib.favor_bidir.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
+                              _sz, _vp]
+_lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
+_lib.favor_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+_lib.favor_workspace_size.restype = _sz
+_lib.favor_timing_enable.argtypes = [_i]
+_lib.favor_timing_enable.restype = _i
+_lib.favor_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), _i]
+_lib.favor_timing_read.restype = _i
+_lib.favor_status_string.argtypes = [_i]
+_lib.favor_status_string.restype = ctypes.c_char_p
+for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
+            "favor_decode"):
+    getattr(_lib, _fn).restype = _i
+
+EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
+            "favor_decode", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
+            "favor_status_string"]
+
+
+class FavorError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.favor_status_string(status).decode()} (status {status})")
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise FavorError(fn, st)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, ndim: int):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+
+
+def _kind(kind) -> int:
+    return KINDS[kind] if isinstance(kind, str) else int(kind)
+
+
+def make_omega_host(seed: int, H: int, m: int, d: int, mode: str = "ortho_chi"):
+    """Omega [H,m,d] fp32 in host memory (numpy), computed by the library's host code."""
+    import numpy as np
+    out = np.empty((H, m, d), dtype=np.float32)
+    _check("favor_make_omega_host",
+           _lib.favor_make_omega_host(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, m, d, OMEGA_MODES[mode],
+                                      out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def make_omega(seed: int, H: int, m: int, d: int, mode: str = "ortho_chi", device="cuda") -> torch.Tensor:
+    """Omega [H,m,d] fp32 on the device (built on the host, copied on the current stream)."""
+    out = torch.empty((H, m, d), dtype=torch.float32, device=device)
+    _check("favor_make_omega",
+           _lib.favor_make_omega(ctypes.c_uint64(seed & (2 ** 64 - 1)), H, m, d, OMEGA_MODES[mode], _ptr(out),
+                                 ctypes.c_void_p(_stream(out.device))))
+    return out
+
+
+def workspace_size(causal: bool, B, H, L, d, dv, m, dtype: torch.dtype) -> int:
+    code = F32 if dtype == torch.float32 else BF16
+    return int(_lib.favor_workspace_size(1 if causal else 0, B, H, L, d, dv, m, code))
+
+
+def workspace(causal: bool, q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) -> torch.Tensor:
+    B, H, L, d = q.shape
+    n = workspace_size(causal, B, H, L, d, v.shape[-1], omega.shape[1], q.dtype)
+    if n == 0:
+        raise FavorError("favor_workspace_size", 1)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0):
+    """phi [B,H,L,m] and logscale [B,H,L] with phi_true = phi * exp(logscale)."""
+    _need(x, "x", 4)
+    _need(omega, "omega", 3)
+    B, H, L, d = x.shape
+    m = omega.shape[1]
+    phi = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
+    ls = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
+    _check("favor_features",
+           _lib.favor_features(_ptr(x), _ptr(omega), B, H, L, d, m, _dtype_code(x), _kind(kind), float(eps),
+                               _ptr(phi), _ptr(ls), ctypes.c_void_p(_stream(x.device))))
+    return phi, ls
+
+
+def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, ws=None, out=None):
+    """Bidirectional FAVOR+ (Performer equation 4). Returns out [B,H,L,dv]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    _need(omega, "omega", 3)
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if ws is None:
+        ws = workspace(False, q, v, omega)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    _check("favor_bidir",
+           _lib.favor_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
+                            float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(ws), ws.numel(),
+                            ctypes.c_void_p(_stream(q.device))))
+    return out
+
+
+def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,
+           ws=None, out=None):
+    """Causal FAVOR+ (Performer appendix B.1). Returns out, or (out, S_final, z_final) in canonical scale."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    _need(omega, "omega", 3)
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if ws is None:
+        ws = workspace(True, q, v, omega)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    S = z = None
+    if return_state:
+        S = torch.empty((B, H, m, dv), dtype=torch.float32, device=q.device)
+        z = torch.empty((B, H, m), dtype=torch.float32, device=q.device)
+    _check("favor_causal",
+           _lib.favor_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
+                             float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(S), _ptr(z), _ptr(ws), ws.numel(),
+                             ctypes.c_void_p(_stream(q.device))))
+    return (out, S, z) if return_state else out
+
+
+def decode(q, k, v, omega, S, z, kind="prf", eps: float = 0.0, out=None):
+    """One decode step: q,k [N,H,d], v [N,H,dv]; S [N,H,m,dv], z [N,H,m] updated in place. Returns out [N,H,dv]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 3)
+    _need(S, "S", 4)
+    _need(z, "z", 3)
+    _need(omega, "omega", 3)
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    _check("favor_decode",
+           _lib.favor_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(S), _ptr(z), N, H, d, dv, m,
+                             _dtype_code(q), _kind(kind), float(eps), _ptr(out), ctypes.c_void_p(_stream(q.device))))
+    return out
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop) recording per-launch kernel durations with HIP events; clears earlier records."""
+    _check("favor_timing_enable", _lib.favor_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """[(kernel name, ms), ...] for every launch recorded since timing_enable(True), in launch order."""
+    n = _lib.favor_timing_read(None, None, 0)
+    names = (ctypes.c_char_p * max(n, 1))()
+    ms = (ctypes.c_float * max(n, 1))()
+    n = _lib.favor_timing_read(names, ms, n)
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments and return its status (for error-path tests)."""
+    return int(getattr(_lib, name)(*args))

@@ -1,0 +1,135 @@
+// C ABI of libfavor: argument checks, workspace sizing and dispatch to the HIP kernels.
+// Every check runs before any launch; a failed check launches nothing.
+#include "../../include/favor.h"
+#include "favor_plan.hpp"
+
+#include <cstdint>
+#include <vector>
+
+namespace favor_host {
+void make_omega(uint64_t seed, int H, int m, int d, int mode, float* out);
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(favor_dtype t) { return t == FAVOR_F32 || t == FAVOR_BF16; }
+bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+favor_status hip_status(hipError_t e) { return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP; }
+
+// Shared checks for the sequence entry points (features / bidir / causal).
+favor_status check_seq(const favor::Shape& s, favor_dtype dt, favor_kind kind, float eps) {
+  if (s.B < 1 || s.H < 1 || s.L < 1 || s.d < 1 || s.dv < 1 || s.m < 1) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !valid_kind(kind)) return FAVOR_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps != eps) return FAVOR_ERR_INVALID_ARG;
+  if ((long long)s.B * s.H > (1LL << 24) || s.L > (1 << 28)) return FAVOR_ERR_INVALID_ARG;
+  if ((long long)s.B * s.H * s.L * (s.d > s.dv ? s.d : s.dv) >= (1LL << 40)) return FAVOR_ERR_INVALID_ARG;
+  return FAVOR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* favor_status_string(favor_status st) {
+  switch (st) {
+    case FAVOR_OK: return "ok";
+    case FAVOR_ERR_INVALID_ARG: return "invalid argument";
+    case FAVOR_ERR_UNSUPPORTED: return "unsupported shape (no kernel built for it)";
+    case FAVOR_ERR_WORKSPACE: return "workspace too small";
+    case FAVOR_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+favor_status favor_make_omega_host(uint64_t seed, int H, int m, int d, favor_omega_mode mode, float* omega_host) {
+  if (!omega_host || H < 1 || H > 65536 || m < 1 || m > 4096 || d < 1 || d > 256) return FAVOR_ERR_INVALID_ARG;
+  if (mode != FAVOR_ORTHO_CHI && mode != FAVOR_IID && mode != FAVOR_ORTHO_SQRTD) return FAVOR_ERR_INVALID_ARG;
+  favor_host::make_omega(seed, H, m, d, static_cast<int>(mode), omega_host);
+  return FAVOR_OK;
+}
+
+favor_status favor_make_omega(uint64_t seed, int H, int m, int d, favor_omega_mode mode, float* omega_dev,
+                              hipStream_t stream) {
+  if (!omega_dev || !aligned16(omega_dev)) return FAVOR_ERR_INVALID_ARG;
+  if (H < 1 || H > 65536 || m < 1 || m > 4096 || d < 1 || d > 256) return FAVOR_ERR_INVALID_ARG;
+  if (mode != FAVOR_ORTHO_CHI && mode != FAVOR_IID && mode != FAVOR_ORTHO_SQRTD) return FAVOR_ERR_INVALID_ARG;
+  std::vector<float> host((size_t)H * m * d);
+  favor_host::make_omega(seed, H, m, d, static_cast<int>(mode), host.data());
+  hipError_t e = hipMemcpyAsync(omega_dev, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return FAVOR_ERR_HIP;
+  return hip_status(hipStreamSynchronize(stream));
+}
+
+size_t favor_workspace_size(int causal, int B, int H, int L, int d, int dv, int m, favor_dtype dtype) {
+  const favor::Shape s{B, H, L, d, dv, m};
+  if (check_seq(s, dtype, FAVOR_PRF, 0.0f) != FAVOR_OK) return 0;
+  if (!favor::shape_built(dtype, d, dv, m)) return 0;
+  return causal ? favor::plan_causal(s, dtype).total : favor::plan_bidir(s, dtype).total;
+}
+
+favor_status favor_features(const void* x, const float* omega, int B, int H, int L, int d, int m, favor_dtype dtype,
+                            favor_kind kind, float eps, float* phi, float* logscale, hipStream_t stream) {
+  const favor::Shape s{B, H, L, d, 16, m};
+  favor_status st = check_seq(s, dtype, kind, eps);
+  if (st != FAVOR_OK) return st;
+  if (!x || !omega || !phi || !logscale) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(omega) || !aligned16(phi) || !aligned16(logscale)) return FAVOR_ERR_INVALID_ARG;
+  bool built = false;
+  for (int dv : {16, 32, 64})
+    if (favor::shape_built(dtype, d, dv, m)) built = true;
+  if (!built) return FAVOR_ERR_UNSUPPORTED;
+  return hip_status(favor::launch_features(x, omega, s, dtype, kind, eps, phi, logscale, stream));
+}
+
+favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
+                         int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  const favor::Shape s{B, H, L, d, dv, m};
+  favor_status st = check_seq(s, dtype, kind, eps);
+  if (st != FAVOR_OK) return st;
+  if (!q || !k || !v || !omega || !out || !ws) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out) || !aligned16(ws))
+    return FAVOR_ERR_INVALID_ARG;
+  if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
+  if (ws_bytes < favor::plan_bidir(s, dtype).total) return FAVOR_ERR_WORKSPACE;
+  return hip_status(favor::launch_bidir(q, k, v, omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out, ws, stream));
+}
+
+favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
+                          int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
+                          float* S_final, float* z_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const favor::Shape s{B, H, L, d, dv, m};
+  favor_status st = check_seq(s, dtype, kind, eps);
+  if (st != FAVOR_OK) return st;
+  if (!q || !k || !v || !omega || !out || !ws) return FAVOR_ERR_INVALID_ARG;
+  if ((S_final == nullptr) != (z_final == nullptr)) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out) || !aligned16(ws))
+    return FAVOR_ERR_INVALID_ARG;
+  if (S_final && (!aligned16(S_final) || !aligned16(z_final))) return FAVOR_ERR_INVALID_ARG;
+  if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
+  if (S_final && (kind != FAVOR_PRF || d > 64)) return FAVOR_ERR_UNSUPPORTED;
+  if (ws_bytes < favor::plan_causal(s, dtype).total) return FAVOR_ERR_WORKSPACE;
+  return hip_status(
+      favor::launch_causal(q, k, v, omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out, S_final, z_final, ws, stream));
+}
+
+favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z, int N,
+                          int H, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps, float* out,
+                          hipStream_t stream) {
+  if (N < 1 || H < 1 || (long long)N * H > (1LL << 24)) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype) || !valid_kind(kind) || !(eps >= 0.0f)) return FAVOR_ERR_INVALID_ARG;
+  if (d < 1 || dv < 1 || m < 1) return FAVOR_ERR_INVALID_ARG;
+  if (!q || !k || !v || !omega || !S || !z || !out) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(S) || !aligned16(z) ||
+      !aligned16(out))
+    return FAVOR_ERR_INVALID_ARG;
+  if (!(d == 16 || d == 32 || d == 64)) return FAVOR_ERR_UNSUPPORTED;
+  if (!pow2(dv) || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
+  if (m % 16 != 0 || m > 1024) return FAVOR_ERR_UNSUPPORTED;
+  return hip_status(favor::launch_decode(q, k, v, omega, S, z, N, H, d, dv, m, dtype, kind, eps, out, stream));
+}
+
+}  // extern "C"

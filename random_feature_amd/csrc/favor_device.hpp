@@ -1,0 +1,188 @@
+// Device-side building blocks for the FAVOR+ kernels on gfx950 (CDNA4, wave64).
+//
+// MFMA fragment convention used by every kernel (lane l of a wave, c = l & 15, g = l >> 4):
+//   * an A fragment of a 16 x 32 tile holds A[row c][k-slot (g, j)], j = 0..7;
+//   * a B fragment of a 32 x 16 tile holds B[k-slot (g, j)][col c];
+//   * a 16 x 16 fp32 accumulator (f32x4) holds C[row 4g + i][col c], i = 0..3.
+// A product sums over all 32 k-slots; which logical index a slot stands for is
+// chosen by the loader, and A and B only have to agree. Two slot maps are used:
+//   * linear:  slot (g, j) <-> k = 8g + j       (contiguous loads along k from memory)
+//   * paired:  slot (g, j) <-> k = 16(j >> 2) + 4g + (j & 3)
+//     which is exactly what a lane already holds in two stacked accumulators
+//     (rows 0..15 and 16..31 of a 32-row C tile), so an accumulator pair turns
+//     into an operand without any data movement.
+// bf16: one v_mfma_f32_16x16x32_bf16 per 16x16x32 step. fp32: eight
+// v_mfma_f32_16x16x4_f32, the j-th one taking slot j of every lane.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace favor {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct VecT;
+template <> struct VecT<bf16> { using v8 = bf16x8; using v4 = bf16x4; using v2 = bf16x2; };
+template <> struct VecT<float> { using v8 = f32x8; using v4 = f32x4; using v2 = f32x2; };
+template <> struct VecT<f16> { using v8 = f16x8; using v4 = f16x4; using v2 = f16x2; };
+template <typename T> using vec8 = typename VecT<T>::v8;
+template <typename T> using vec4 = typename VecT<T>::v4;
+template <typename T> using vec2 = typename VecT<T>::v2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ void mma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const f16x8& a, const f16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return static_cast<bf16>(x); }
+template <> __device__ __forceinline__ f16 to_t<f16>(float x) { return static_cast<f16>(x); }
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f(f16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ vec8<T> zero8() {
+  vec8<T> z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = to_t<T>(0.f);
+  return z;
+}
+
+// Operand types per input type: the projection runs in fp16 for bf16 inputs (a bf16 value
+// inside fp16's range converts exactly, and fp16's 11-bit significand keeps the rounding of
+// the scaled Omega small enough for the exponent), the contraction with values in bf16;
+// fp32 inputs use fp32 for both.
+template <typename T> struct Ops;
+template <> struct Ops<float> { using P = float; using C = float; };
+template <> struct Ops<bf16> { using P = f16; using C = bf16; };
+
+// 8 contiguous elements (16 B for 16-bit types, 32 B for fp32), 16-byte aligned.
+template <typename T> __device__ __forceinline__ vec8<T> ld8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const vec8<T>*>(p);
+  } else {
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { r[j] = a[j]; r[j + 4] = b[j]; }
+    return r;
+  }
+}
+template <typename T> __device__ __forceinline__ void st8(T* p, const vec8<T>& x) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<vec8<T>*>(p) = x;
+  } else {
+    f32x4 a, b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[j] = x[j]; b[j] = x[j + 4]; }
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+// Reduce over the four lanes that share c (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+// Flattened work split: the B*H*ceil(L/32) token tiles, in (b,h)-major order, are cut
+// into G contiguous pieces of nearly equal length. Piece i covers tiles
+// [piece_start(i), piece_start(i+1)). A piece may span several (b,h); the part of
+// piece i that lies in (b,h) bh is stored under index i + bh, which is unique because
+// both indices only grow along the flattened order.
+__host__ __device__ __forceinline__ long long piece_start(long long i, long long total, long long G) {
+  return (i * total) / G;
+}
+__host__ __device__ __forceinline__ long long piece_of(long long t, long long total, long long G) {
+  long long i = (t * G) / total;
+  while (i + 1 < G && piece_start(i + 1, total, G) <= t) ++i;
+  while (i > 0 && piece_start(i, total, G) > t) --i;
+  return i;
+}
+
+// ---- asynchronous global -> LDS copies (gfx950 global_load_lds_dwordx4)
+// Each active lane copies 16 bytes from its own global address to LDS byte address
+// lds_base + 16 * lane (lds_base must be wave-uniform). The copy completes
+// asynchronously and is counted by vmcnt like any vector memory load; the compiler
+// does not track it, so the waits are placed explicitly with wait_vmcnt().
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+// Wait until at most n vector memory operations of this wave are outstanding (n < 64).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+// Workgroup barrier that waits only for this wave's LDS traffic (no vector-memory drain),
+// so asynchronous copies stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// gfx950 transposing LDS read: within each 16-lane group, lane r supplies the address of 4
+// consecutive 16-bit elements M[r][0..3]; lane i receives M[i/4 + 4k][i%4] for k = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Map a launch-order block index so that consecutive logical indices land on
+// the same XCD (the hardware deals workgroups to the 8 XCDs round robin), which
+// keeps work that shares inputs inside one L2. Identity when n is not a
+// multiple of 8.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  if ((n & 7) != 0) return bid;
+  return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+}  // namespace favor

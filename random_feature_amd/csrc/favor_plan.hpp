@@ -1,0 +1,61 @@
+// Host-side launch plans and workspace layouts (shared by the size query and the launchers).
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// (d, dv, m) combinations with compiled kernels for the sequence entry points.
+#define FAVOR_SHAPES(X) \
+  X(16, 16, 16)         \
+  X(16, 16, 32)         \
+  X(16, 16, 64)         \
+  X(16, 16, 128)        \
+  X(16, 16, 256)        \
+  X(32, 32, 64)         \
+  X(32, 32, 128)        \
+  X(64, 64, 64)         \
+  X(64, 64, 128)        \
+  X(64, 64, 256)
+
+
+namespace favor {
+
+struct Shape {
+  int B, H, L, d, dv, m;
+  long long bh() const { return (long long)B * H; }
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bidirectional path: omega fragments, per-segment partial (S, z) sums with their
+// stabiliser maxima, and the combined S fragments.
+// Both passes walk the B*H*ceil(L/32) token tiles split into G contiguous pieces (one
+// workgroup each); partials are stored per (piece, b*h) intersection.
+struct BidirPlan {
+  int tpb = 0, G = 0, nw_reduce = 0;
+  long long T_all = 0;
+  size_t off_omf = 0, off_part = 0, off_pmax = 0, off_sfr = 0, total = 0;
+};
+
+// Causal path: the bidirectional pieces for segment totals plus carried states.
+struct CausalPlan {
+  int nseg = 0, seg_len = 0, nw_reduce = 0;
+  size_t off_omf = 0, off_part = 0, off_pmax = 0, off_carry = 0, off_cmax = 0, total = 0;
+};
+
+bool shape_built(int dtype, int d, int dv, int m);
+BidirPlan plan_bidir(const Shape& s, int dtype);
+CausalPlan plan_causal(const Shape& s, int dtype);
+
+hipError_t launch_features(const void* x, const float* omega, const Shape& s, int dtype, int kind, float eps,
+                           float* phi, float* logscale, hipStream_t st);
+hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
+                        int dtype, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st);
+hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
+                         int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
+                         void* ws, hipStream_t st);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
+                         int N, int H, int d, int dv, int m, int dtype, int kind, float eps, float* out,
+                         hipStream_t st);
+
+}  // namespace favor

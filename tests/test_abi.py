@@ -1,0 +1,132 @@
+"""Host-side checks of libfavor that need no GPU.
+
+* The library loads and exports every entry point declared in include/favor.h.
+* Argument checks return their documented status before anything is launched
+  (the pointers passed here are never dereferenced: each call fails its checks).
+* The host Omega generator reproduces the oracle's Omega bit for bit (two
+  independent implementations of one recipe; Performer section 2.4, appendix B.2).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import random_feature_amd as rf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "favor.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced by the checks under test
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:favor_status|size_t|int|const char\*)\s+(favor_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 10
+    lib = ctypes.CDLL(rf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(rf.EXPORTED) == names
+
+
+def test_status_strings():
+    for code in range(5):
+        assert rf._lib.favor_status_string(code)
+    assert rf._lib.favor_status_string(99) == b"unknown status"
+
+
+def _bidir(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, om=FAKE, B=1, H=1, L=64, d=64, dv=64, m=256, dt=1, kind=0, eps=0.0, of=0,
+             out=FAKE, ws=FAKE, wsb=1 << 30, st=None)
+    a.update(kw)
+    return rf.raw_call("favor_bidir", a["q"], a["k"], a["v"], a["om"], a["B"], a["H"], a["L"], a["d"], a["dv"],
+                       a["m"], a["dt"], a["kind"], ctypes.c_float(a["eps"]), a["of"], a["out"], a["ws"],
+                       ctypes.c_size_t(a["wsb"]), a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(v=MISALIGNED), INVALID),
+    (dict(L=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(dt=7), INVALID),
+    (dict(kind=5), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(d=48), UNSUPPORTED),
+    (dict(m=200), UNSUPPORTED),
+    (dict(dv=24), UNSUPPORTED),
+    (dict(wsb=16), WORKSPACE),
+])
+def test_bidir_argument_checks(kw, status):
+    assert _bidir(**kw) == status
+
+
+def test_causal_argument_checks():
+    def call(S=None, z=None, wsb=1 << 30, d=64, kind=0):
+        return rf.raw_call("favor_causal", FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, d, 256, 1, kind, ctypes.c_float(0.0),
+                           0, FAKE, S, z, FAKE, ctypes.c_size_t(wsb), None)
+    assert call(S=FAKE, z=None) == INVALID          # both or neither
+    assert call(wsb=8) == WORKSPACE
+    assert call(d=48) == UNSUPPORTED
+
+
+def test_decode_argument_checks():
+    def call(N=4, H=2, d=64, dv=64, m=256, q=FAKE, S=FAKE):
+        return rf.raw_call("favor_decode", q, FAKE, FAKE, FAKE, S, FAKE, N, H, d, dv, m, 1, 0, ctypes.c_float(0.0),
+                           FAKE, None)
+    assert call(q=None) == INVALID
+    assert call(S=MISALIGNED) == INVALID
+    assert call(N=0) == INVALID
+    assert call(d=128) == UNSUPPORTED
+    assert call(dv=48) == UNSUPPORTED
+    assert call(m=100) == UNSUPPORTED
+
+
+def test_features_and_omega_argument_checks():
+    st = rf.raw_call("favor_features", FAKE, FAKE, 1, 1, 8, 48, 64, 1, 0, ctypes.c_float(0.0), FAKE, FAKE, None)
+    assert st == UNSUPPORTED
+    assert rf.raw_call("favor_make_omega", ctypes.c_uint64(0), 1, 16, 16, 0, None, None) == INVALID
+    assert rf.raw_call("favor_make_omega", ctypes.c_uint64(0), 1, 16, 16, 9, FAKE, None) == INVALID
+    assert rf.raw_call("favor_make_omega_host", ctypes.c_uint64(0), 0, 16, 16, 0, FAKE) == INVALID
+
+
+def test_workspace_size_query():
+    assert rf.workspace_size(False, 8, 12, 4096, 64, 64, 256, __import__("torch").bfloat16) > 0
+    assert rf.workspace_size(True, 4, 8, 8192, 64, 64, 256, __import__("torch").bfloat16) > 0
+    assert rf._lib.favor_workspace_size(0, 1, 1, 16, 48, 48, 64, 1) == 0      # unsupported -> 0
+    assert rf._lib.favor_workspace_size(0, 0, 1, 16, 64, 64, 64, 1) == 0      # invalid -> 0
+
+
+@pytest.mark.parametrize("seed,H,m,d,mode", [
+    (0, 1, 32, 16, "ortho_chi"),
+    (1, 8, 128, 16, "ortho_chi"),
+    (2, 3, 256, 64, "ortho_chi"),
+    (3, 2, 40, 16, "ortho_chi"),
+    (4, 2, 96, 32, "ortho_sqrtd"),
+    (5, 2, 48, 16, "iid"),
+    (2 ** 64 - 1, 1, 64, 64, "ortho_chi"),
+    (12345678901234, 1, 20, 7, "ortho_chi"),
+])
+def test_host_omega_bit_exact_against_oracle(seed, H, m, d, mode):
+    lib_om = rf.make_omega_host(seed, H, m, d, mode)
+    ref = oracle.make_omega(seed, H, m, d, mode)
+    assert lib_om.dtype == np.float32 and lib_om.shape == (H, m, d)
+    assert np.array_equal(lib_om.view(np.uint32), ref.view(np.uint32))
+
+
+def test_host_omega_head_rows_independent_of_H():
+    a = rf.make_omega_host(9, 2, 64, 16)
+    b = rf.make_omega_host(9, 5, 64, 16)
+    assert np.array_equal(a, b[:2])
