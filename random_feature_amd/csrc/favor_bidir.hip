@@ -33,6 +33,18 @@ template <int M> struct FeatSplit {
   static constexpr int NW = (M / 16) < 4 ? (M / 16) : 4;
   static constexpr int FB = M / (16 * NW);
 };
+// Waves of the key/value reduction (RW_MAX at most, 32 features per wave or more). Two
+// workgroups per CU: NW/2 waves per SIMD (the second launch bound is waves per EU).
+#ifndef FAVOR_REDUCE_WAVES
+#define FAVOR_REDUCE_WAVES 4
+#endif
+template <int M> struct RedSplit {
+  static constexpr int RW_MAX = FAVOR_REDUCE_WAVES;
+  static constexpr int NW = M < 32 ? 1 : ((M / 32) < RW_MAX ? (M / 32) : RW_MAX);
+  static constexpr int FB = M / (16 * NW);
+};
+
+constexpr int kNormNone = 0, kNormSq = 1, kNormAbs = 2;
 
 // ---------------------------------------------------------------- tile ring
 // 32-token tiles of X (keys or queries) and V arrive in an R-slot LDS ring through
@@ -85,16 +97,19 @@ struct Ring {
   }
 
   // this thread's X chunks of a landed slot -> projection type in `conv` (row stride KROW),
-  // and (NORMS) the scaled squared row norms into kn
-  template <typename P, int KROW, bool NORMS>
-  static __device__ __forceinline__ void convert(const unsigned char* slot, P* conv, float* kn, float nscale) {
+  // and per row into `nrm`: NORM == kNormSq: |x|^2 * nscale (+inf for rows at or past
+  // nvalid); NORM == kNormAbs: |x| * nscale
+  template <typename P, int KROW, int NORM>
+  static __device__ __forceinline__ void convert(const unsigned char* slot, P* conv, float* nrm, float nscale,
+                                                 int nvalid) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int q = u * NT + threadIdx.x;
       if (u * NT >= XC) break;  // no X chunks left (known at compile time)
       const int row = q / CPR_X, cc = q % CPR_X;
       float s2 = 0.f;
-      if (q < XC) {
+      const bool has = (XC % NT == 0) || q < XC;  // every thread has a chunk when XC % NT == 0
+      if (has) {
         if constexpr (sizeof(T) == 2) {
           const vec8<T> x = *reinterpret_cast<const vec8<T>*>(slot + q * 16);
           vec8<P> y;
@@ -116,10 +131,14 @@ struct Ring {
           *reinterpret_cast<vec4<P>*>(conv + row * KROW + cc * 4) = y;
         }
       }
-      if constexpr (NORMS) {
-#pragma unroll
-        for (int o = 1; o < CPR_X; o <<= 1) s2 += __shfl_xor(s2, o, 64);
-        if (q < XC && cc == 0) kn[row] = s2 * nscale;
+      if constexpr (NORM != kNormNone) {
+        s2 = lanes_sum<CPR_X>(s2);  // the CPR_X chunks of a row sit on consecutive lanes
+        if (has) {  // every lane of the row holds the sum and stores the same value
+          if constexpr (NORM == kNormSq)
+            nrm[row] = row < nvalid ? s2 * nscale : INFINITY;
+          else
+            nrm[row] = __builtin_sqrtf(s2) * nscale;
+        }
       }
     }
   }
@@ -182,23 +201,29 @@ __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<type
 //   maps        Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps), rounded to the contraction type
 //   contracts   S_aug += Phi^T [V 1]: A = Phi^T (paired token slots, the accumulators as
 //               they are), B = the value fragments
-// Tiles stream through the asynchronous ring R-1 ahead; one barrier per tile.
-template <typename T, int D, int DV, int M, int R>
-__global__ void __launch_bounds__(64 * FeatSplit<M>::NW, 2)
+// The contraction of a tile is deferred by one iteration so that, in each wave, matrix and
+// vector work overlap: the projection MFMAs of tile t run beside the conversion of the K
+// rows of tile t+2, and the contraction MFMAs of tile t-1 beside the exponentials of tile t.
+// Tiles stream through an R-slot asynchronous ring R-2 ahead; three K buffers; one
+// barrier per tile.
+template <typename T, int D, int DV, int M, int R, int KIND>
+__global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
-                 int H, int L, int tpb, long long T_all, int G, int kind, float eps, float inv_sqrt_m, float nscale,
+                 int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
                  float* __restrict__ part, float* __restrict__ pmax) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
-  constexpr int NW = FeatSplit<M>::NW, FB = FeatSplit<M>::FB;
+  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NB = DV / 16 + 1;
+  constexpr int NB = DV / 16 + 1;  // value-column blocks + the ones column (z = Phi^T 1)
   constexpr int KROW = D + 8;
+  static_assert(R >= 5, "ring: the tile contracted late, the one projected, two converted ahead, one in flight");
   using Rg = Ring<T, D, DV, NT, true>;
+  constexpr int WAIT_NEXT = Rg::CPT * (R - 4);  // copies newer than tile t+2 at iteration t
   __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
-  __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
-  __shared__ __attribute__((aligned(16))) float kn[2][32];
+  __shared__ __attribute__((aligned(16))) P ks[3][32 * KROW];
+  __shared__ __attribute__((aligned(16))) float kn[3][32];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -213,8 +238,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   vec8<P> om[FB][DC];
   int cur_bh = -1;
 
-  auto flush = [&]() {
-    float* Pp = part + ((size_t)pc + cur_bh) * M * (DV + 1);
+  auto flush = [&](int fbh, float fmax) {
+    float* Pp = part + ((size_t)pc + fbh) * M * (DV + 1);
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -224,131 +249,183 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         for (int nb = 0; nb < NB - 1; ++nb) Pp[(size_t)r * (DV + 1) + nb * 16 + c] = sacc[fb][nb][i];
         if (c == 0) Pp[(size_t)r * (DV + 1) + DV] = sacc[fb][NB - 1][i];
       }
-    if (lane == 0) pmax[((size_t)pc + cur_bh) * NW + w] = runmax;
+    if (lane == 0) pmax[((size_t)pc + fbh) * NW + w] = fmax;
+  };
+  auto load_om = [&](int bh) {
+    const int h = bh % H;
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+    wait_vmcnt<0>();  // settle the fragment (and any partial) traffic here, off the per-tile path
+  };
+  // S_aug += Phi^T [V 1] for a tile whose features are in af and whose V rows are in `slot`
+  auto contract = [&](const vec8<C> (&af)[FB], const unsigned char* slot) {
+    vec8<C> vf[NB];
+    value_frags<T, D, DV, NT>(slot, vf, c, g);
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af[fb], vf[nb]);
+  };
+  auto zero_sums = [&]() {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
   const int n_tiles = (int)(t_end - t_beg);
-  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb);
+  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), cv(t_beg, tpb);
 #pragma unroll
-  for (int s = 0; s < R - 1; ++s) {
+  for (int s = 0; s < R - 2; ++s) {
     Rg::issue(K, V, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
     if (s < n_tiles) ahead.next();
   }
-  wait_vmcnt<Rg::CPT * (R - 2)>();
-  Rg::template convert<P, KROW, true>(ring[0], ks[0], kn[0], nscale);
+  // tiles 0 and 1 converted up front; iteration t converts tile t+2
+  wait_vmcnt<Rg::CPT * (R - 3)>();
+  Rg::template convert<P, KROW, kNormSq>(ring[0], ks[0], kn[0], nscale, L - cv.tok0());
+  cv.next();
+  wait_vmcnt<Rg::CPT * (R - 4)>();
+  if (n_tiles > 1) Rg::template convert<P, KROW, kNormSq>(ring[1], ks[1], kn[1], nscale, L - cv.tok0());
+  cv.next();
   lds_barrier();
 
-  for (int it = 0; it < n_tiles; ++it, cur.next()) {
-    const int buf = it & 1;
+  zero_sums();
+  vec8<C> afp[FB];     // features of the previous tile, contracted during this one
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb) afp[fb] = zero8<C>();
+  int s_iss = R - 2;   // ring slot of the next copy:             (t + R - 2) mod R
+  int s_cv = 2;        // ring slot of the tile converted now:     (t + 2) mod R
+  int s_prev = R - 1;  // ring slot of the tile contracted late:   (t - 1) mod R
+  int k_cur = 0;       // K buffer of tile t:                      t mod 3
+  int flush_bh = -1;   // (b,h) whose partial is written at the top of the next iteration
+  float flush_max = 0.f;
+  for (int it = 0; it < n_tiles; ++it) {
     const int bh = cur.bh, tok0 = cur.tok0();
+    const int k_cv = k_cur == 0 ? 2 : k_cur - 1;  // (t + 2) mod 3
     {
-      const bool live = it + R - 1 < n_tiles;
-      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + ((it + R - 1) % R) * Rg::SLOT);
+      const bool live = it + R - 2 < n_tiles;
+      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT);
       if (live) ahead.next();
     }
+    if (flush_bh >= 0) {
+      // the previous tile opened a new (b,h); the old one's sums closed with the contraction
+      // of its last tile during that iteration
+      flush(flush_bh, flush_max);
+      zero_sums();
+      flush_bh = -1;
+      wait_vmcnt<0>();  // no stores may stay in flight under the partial waits of the ring
+    }
+    // a new (b,h): its Omega' now; its sums start after the deferred contraction of the
+    // old one's last tile, which happens in this iteration
     if (bh != cur_bh) {
       if (cur_bh >= 0) {
-        flush();
-        wait_vmcnt<0>();
+        flush_bh = cur_bh;
+        flush_max = runmax;
       }
-      const int h = bh % H;
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      runmax = 0.f;
+      load_om(bh);
       first = true;
       cur_bh = bh;
     }
+    wait_vmcnt<WAIT_NEXT>();
 
-    // accumulator start values: the negated key bias of rows 4g+i (-inf for rows past L)
-    f32x4 bias[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = tok0 + tb * 16 + 4 * g + i < L;
-        bias[tb][i] = (kind == kPrf) ? (ok ? -(n4[i] + runmax) : -INFINITY) : 0.f;
-      }
-    }
+    // projection of tile t beside the conversion of tile t+2
     f32x4 pacc[2][FB];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
+      f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KIND == kPrf) {
+        const float rm = first ? 0.f : runmax;
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[k_cur][tb * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bias[i] = -(n4[i] + rm);
+      }
       vec8<P> kf[DC];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const int col = dc * 32 + 8 * g;
-        kf[dc] = (col < D) ? ld8<P>(&ks[buf][(tb * 16 + c) * KROW + col]) : zero8<P>();
+        kf[dc] = (col < D) ? ld8<P>(&ks[k_cur][(tb * 16 + c) * KROW + col]) : zero8<P>();
       }
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        pacc[tb][fb] = bias[tb];
+        pacc[tb][fb] = bias;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) mma16(pacc[tb][fb], kf[dc], om[fb][dc]);
       }
     }
-    if (kind == kPrf) {
-      float tmax = -INFINITY;
+    // (past the end of the piece this converts a filler slot into an unused buffer)
+    Rg::template convert<P, KROW, kNormSq>(ring[s_cv], ks[k_cv], kn[k_cv], nscale, L - cv.tok0());
+    cv.next();
+
+    if constexpr (KIND == kPrf) {
+      float lmax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, pacc[tb][fb][i]);
-      tmax = wave_max(tmax);
-      if (first || tmax > 0.f) {
-        if (!first) {
-          const float sc = fast_exp2(-tmax);
+          for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, pacc[tb][fb][i]);
+      // the running maximum moves only if some exponent is positive (or on a new (b,h))
+      if (first || __builtin_amdgcn_ballot_w64(lmax > 0.f) != 0) {
+        const float tmax = wave_max(lmax);
+        float shift = tmax;
+        if (first) {
+          runmax = tmax;
+        } else {
+          // an integral shift keeps the rescaling of the rounded deferred features exact
+          shift = ceilf(tmax);
+          const float sc = fast_exp2(-shift);
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb)
+          for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] *= sc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) afp[fb][j] = to_t<C>(to_f(afp[fb][j]) * sc);
+          }
+          runmax += shift;
         }
-        runmax += tmax;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb) pacc[tb][fb] -= tmax;
+          for (int fb = 0; fb < FB; ++fb) pacc[tb][fb] -= shift;
         first = false;
       }
+    }
+
+    // contraction of tile t-1 beside the feature map of tile t (on the first iteration the
+    // features are zero and the V rows those of tile 0, so it adds exactly nothing)
+    contract(afp, ring[it == 0 ? 0 : s_prev]);
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pacc[tb][fb][i] = fast_exp2(pacc[tb][fb][i]);
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = tok0 + tb * 16 + 4 * g + i < L;
-#pragma unroll
-          for (int fb = 0; fb < FB; ++fb)
-            pacc[tb][fb][i] = ok ? fmaxf(pacc[tb][fb][i], 0.f) * inv_sqrt_m + eps : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        const float a = pacc[j >> 2][fb][j & 3];
+        float f;
+        if constexpr (KIND == kPrf) {
+          f = fast_exp2(a);  // rows past L carry an infinite norm: exp2(-inf) = 0
+        } else {
+          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L;
+          f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
-    }
-    vec8<C> vf[NB];
-    value_frags<T, D, DV, NT>(ring[it % R], vf, c, g);
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb) {
-      vec8<C> af;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) af[j] = to_t<C>(pacc[j >> 2][fb][j & 3]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af, vf[nb]);
-    }
-    wait_vmcnt<Rg::CPT * (R - 2)>();
-    if (it + 1 < n_tiles) Rg::template convert<P, KROW, true>(ring[(it + 1) % R], ks[buf ^ 1], kn[buf ^ 1], nscale);
+        afp[fb][j] = to_t<C>(f);
+      }
     lds_barrier();
+
+    cur.next();
+    s_prev = s_prev + 1 == R ? 0 : s_prev + 1;
+    s_cv = s_cv + 1 == R ? 0 : s_cv + 1;
+    s_iss = s_iss + 1 == R ? 0 : s_iss + 1;
+    k_cur = k_cur == 2 ? 0 : k_cur + 1;
   }
-  flush();
+  // the last tile's contraction, then the partials still open
+  if (flush_bh >= 0) {
+    flush(flush_bh, flush_max);
+    zero_sums();
+  }
+  contract(afp, ring[s_prev]);
+  flush(cur_bh, runmax);
 }
 
 // ---------------------------------------------------------------- combine
@@ -361,7 +438,7 @@ template <typename C, int DV, int M>
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int tpb, long long T_all, int G,
                int kind, C* __restrict__ sfr) {
-  constexpr int NW = FeatSplit<M>::NW;
+  constexpr int NW = RedSplit<M>::NW;
   constexpr int FPW = M / NW;
   constexpr int NB = DV / 16 + 1;
   constexpr int NFC = (M + 31) / 32;
@@ -392,70 +469,128 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ pmax, i
 }
 
 // ---------------------------------------------------------------- query side
-// Workgroup = NW waves over one piece of the flattened tile space; wave w owns FB*16
-// features and keeps their Omega' and S_aug^T fragments in registers (reloaded when the
-// piece moves to the next (b,h)). Per 32-token tile:
-//   projection   A = Omega' (rows = features), B = Q^T (linear d slots) -> [feature][token]
-//   row maximum  over the wave's features, then across waves through LDS (PRF)
-//   feature map  Phi = exp2(a' - max) (the |q|^2 term is constant per row and cancels)
-//   contraction  out^T partial = S_aug^T Phi^T over the wave's features (paired slots)
-//   combination  partial tiles summed across waves through LDS; the z row gives the
-//                denominator; each wave divides and stores its share of the tile.
-template <typename T, int D, int DV, int M, int R>
+// Largest row norm of the scaled Omega' as the projection sees it (rounded to the
+// projection type), per head: |a'_r| <= omax * |q| bounds every query exponent.
+template <typename P>
+__global__ void __launch_bounds__(256)
+omega_bound_kernel(const float* __restrict__ omega, int m, int d, float scale, float* __restrict__ omax) {
+  __shared__ float wmax[4];
+  const int h = blockIdx.x;
+  float mx = 0.f;
+  for (int r = threadIdx.x; r < m; r += blockDim.x) {
+    const float* row = omega + ((size_t)h * m + r) * d;
+    float s2 = 0.f;
+    for (int j = 0; j < d; ++j) {
+      const float x = to_f(to_t<P>(row[j] * scale));
+      s2 += x * x;
+    }
+    mx = fmaxf(mx, __builtin_sqrtf(s2));
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = wmax[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, wmax[i]);
+    omax[h] = r;
+  }
+}
+
+// Exponent bound (log2 units) under which the bound stabiliser keeps every query feature
+// a normal float: the features lie in [2^(-2 bound), 1].
+constexpr float kQueryBoundLimit = 60.f;
+
+// Workgroup = NW waves over one piece of the flattened tile space. Per 32-token tile:
+//   phase 1 (wave w, its FB*16 features, Omega' fragments in registers)
+//     projection  A = Omega' (rows = features), B = Q^T (linear d slots) -> [feature][token];
+//                 the accumulators start at -b_t, b_t = omax |q_t| >= max_r a'_r, so the
+//                 output is already a non-positive exponent (the |q|^2 term of the map and
+//                 any constant per row cancel in the ratio). If some row of the tile has
+//                 b_t > kQueryBoundLimit, the tile takes the exact row maximum across the
+//                 waves instead (one more barrier).
+//     feature map Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps); the accumulator pairs are
+//                 B operands of the contraction as they stand (paired feature slots) and go
+//                 to LDS; the wave's share of the denominator z^T Phi^T goes with them
+//   barrier
+//   phase 2 (wave w, value-column blocks w, w+NW, ...)
+//     contraction out^T block = S^T block (A, registers) x Phi^T (B, all features from LDS)
+//     division by the summed denominators and the store
+// Wave 0 alone copies Q tiles into the ring and converts them, one tile ahead; so that its
+// memory counter sees nothing but ring copies it stores nothing: it leaves its normalised
+// block in LDS and wave 1 stores it during the next tile.
+template <typename T, int D, int DV, int M, int R, int KIND>
 __global__ void __launch_bounds__(64 * FeatSplit<M>::NW, 2)
 q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ omf,
-                const typename Ops<T>::C* __restrict__ sfr, int H, int L, int tpb, long long T_all, int G, int kind,
-                float eps, float inv_sqrt_m, int out_f32, void* __restrict__ out) {
+                const typename Ops<T>::C* __restrict__ sfr, const float* __restrict__ omax, int H, int L, int tpb,
+                long long T_all, int G, float eps, float inv_sqrt_m, int out_f32, void* __restrict__ out) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = FeatSplit<M>::NW, FB = FeatSplit<M>::FB;
-  constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NB = DV / 16 + 1;
-  constexpr int NFCW = (FB + 1) / 2;       // 32-feature chunks a wave touches (one half of one when FB = 1)
+  constexpr int NB = DV / 16 + 1;           // blocks of S_aug^T in sfr: values, then z
+  constexpr int NVB = DV / 16;              // value-column blocks
+  constexpr int NCB = (NVB + NW - 1) / NW;  // value-column blocks per wave
+  constexpr int NFCW = (FB + 1) / 2;        // 32-feature chunks a wave fills (half of one when FB = 1)
   constexpr int NFC = (M + 31) / 32;
   constexpr int KROW = D + 8;
-  // Only wave 0 copies and converts Q tiles, and it issues no stores, so its vmcnt counts
-  // nothing but the ring copies; the other waves store the outputs. (With a single wave
-  // the wave does both, and its waits drain the stores as well.)
+  constexpr bool HANDOFF = NW > 1;          // wave 0's block is stored by wave 1
   using Rg = Ring<T, D, DV, 64, false>;
-  constexpr int WAIT_N = NW > 1 ? Rg::CPT * (R - 2) : 0;
+  constexpr int WAIT_N = HANDOFF ? Rg::CPT * (R - 2) : 0;
   __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) P qs[2][32 * KROW];
+  __shared__ __attribute__((aligned(16))) float qb[2][32];
+  __shared__ __attribute__((aligned(16))) C phib[2][NFC][2][64 * 8];
+  __shared__ __attribute__((aligned(16))) float dpart[2][2][16][NW];
   __shared__ __attribute__((aligned(16))) float qmx[NW][32];
-  __shared__ __attribute__((aligned(16))) float xch[NW][2][NB][64 * 4];
+  __shared__ __attribute__((aligned(16))) float obuf[HANDOFF ? 2 : 1][NCB][2][64 * 4];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const long long pc = xcd_remap(blockIdx.x, gridDim.x);
   const long long t_beg = piece_start(pc, T_all, G), t_end = piece_start(pc + 1, T_all, G);
   if (t_beg >= t_end) return;
-
-  vec8<P> om[FB][DC];
-  vec8<C> sf[NFCW][NB];
-  int cur_bh = -1;
+  const int n_tiles = (int)(t_end - t_beg);
   const int fc0 = (w * FB) / 2;
+  constexpr float kMargin = 1.f + 1.f / 512.f;  // rounding of q to the projection type and of the MFMA sums
+
+  auto store4 = [&](int bh, int tok, int col, const f32x4& val) {
+    if (tok >= L) return;
+    const size_t o = ((size_t)bh * L + tok) * DV + col;
+    if (out_f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = val;
+    } else {
+      vec4<T> r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = to_t<T>(val[i]);
+      *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(out) + o) = r;
+    }
+  };
 
   const uint32_t ring0 = lds_addr(&ring[0][0]);
-  const int n_tiles = (int)(t_end - t_beg);
-  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb);
-#pragma unroll
-  for (int s = 0; s < R - 1; ++s) {
-    if (w == 0) Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
-    if (s < n_tiles) ahead.next();
-  }
+  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), prev(t_beg, tpb);
   if (w == 0) {
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) {
+      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
+      if (s < n_tiles) ahead.next();
+    }
     wait_vmcnt<Rg::CPT * (R - 2)>();
-    Rg::template convert<P, KROW, false>(ring[0], qs[0], nullptr, 0.f);
+    const float ob = (KIND == kPrf) ? omax[cur.bh % H] * kMargin : 0.f;
+    Rg::template convert<P, KROW, kNormAbs>(ring[0], qs[0], qb[0], ob, L);
   }
   lds_barrier();
 
-  for (int it = 0; it < n_tiles; ++it, cur.next()) {
+  vec8<P> om[FB][DC];
+  vec8<C> zf[NFCW];
+  vec8<C> sf[NCB][NFC];
+  int cur_bh = -1;
+
+  for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
     const int bh = cur.bh, tok0 = cur.tok0();
-    {
+    if (w == 0) {
       const bool live = it + R - 1 < n_tiles;
-      if (w == 0) Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), live, ring0 + ((it + R - 1) % R) * Rg::SLOT);
+      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), live, ring0 + ((it + R - 1) % R) * Rg::SLOT);
       if (live) ahead.next();
     }
     if (bh != cur_bh) {
@@ -466,15 +601,29 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
         for (int dc = 0; dc < DC; ++dc)
           om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
 #pragma unroll
-      for (int fcw = 0; fcw < NFCW; ++fcw) {
-        const int fc = fc0 + fcw;
+      for (int fcw = 0; fcw < NFCW; ++fcw)
+        zf[fcw] = ld8<C>(sfr + ((((size_t)bh * NFC + fc0 + fcw) * NB + (NB - 1)) * 64 + lane) * 8);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sf[fcw][nb] = ld8<C>(sfr + ((((size_t)bh * NFC + fc) * NB + nb) * 64 + lane) * 8);
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int nb = w + cb * NW;
+#pragma unroll
+        for (int fc = 0; fc < NFC; ++fc)
+          sf[cb][fc] = nb < NVB ? ld8<C>(sfr + ((((size_t)bh * NFC + fc) * NB + nb) * 64 + lane) * 8) : zero8<C>();
       }
       cur_bh = bh;
+      wait_vmcnt<0>();  // settle the fragment loads here, off the per-tile path
     }
 
+    // ---- phase 1: this wave's features of the tile
+    f32x4 bias[2];
+    bool exact = false;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const float b = (KIND == kPrf) ? qb[buf][tb * 16 + c] : 0.f;
+      bias[tb] = f32x4{-b, -b, -b, -b};
+      if constexpr (KIND == kPrf) exact |= b > kQueryBoundLimit;
+    }
+    if constexpr (KIND == kPrf) exact = __builtin_amdgcn_ballot_w64(exact) != 0;  // same in every wave
     f32x4 pacc[2][FB];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -486,35 +635,40 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       }
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        pacc[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[tb][fb] = bias[tb];
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) mma16(pacc[tb][fb], om[fb][dc], qf[dc]);
       }
     }
-    if (kind == kPrf) {
+    if constexpr (KIND == kPrf) {
+      if (exact) {
+        // rare: shift every row by its exact maximum, taken across the waves
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float mx = -INFINITY;
+        for (int tb = 0; tb < 2; ++tb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pacc[tb][fb][i]);
+          mx = group_max(mx);
+          if (g == 0) qmx[w][tb * 16 + c] = mx;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          float mx = qmx[0][tb * 16 + c];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb) pacc[tb][fb] -= mx;
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pacc[tb][fb][i]);
-        mx = group_max(mx);
-        if (g == 0) qmx[w][tb * 16 + c] = mx;
-      }
-    }
-    lds_barrier();
-    if (kind == kPrf) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float mx = qmx[0][tb * 16 + c];
-#pragma unroll
-        for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pacc[tb][fb][i] = fast_exp2(pacc[tb][fb][i] - mx);
-      }
+          for (int i = 0; i < 4; ++i) pacc[tb][fb][i] = fast_exp2(pacc[tb][fb][i]);
     } else {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -525,59 +679,104 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
     }
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      f32x4 oacc[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int fcw = 0; fcw < NFCW; ++fcw) {
         vec8<C> bf;
         if constexpr (FB % 2 == 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) bf[j] = to_t<C>(pacc[tb][2 * fcw + (j >> 2)][j & 3]);
+          *reinterpret_cast<vec8<C>*>(&phib[buf][fc0 + fcw][tb][lane * 8]) = bf;
         } else {
           // one 16-feature block per wave: it fills half (w & 1) of its 32-feature chunk
           const int half = w & 1;
+          vec4<C> hv;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) bf[j] = to_t<C>((j >> 2) == half ? pacc[tb][0][j & 3] : 0.f);
+          for (int i = 0; i < 4; ++i) hv[i] = to_t<C>(pacc[tb][0][i]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bf[j] = (j >> 2) == half ? hv[j & 3] : to_t<C>(0.f);
+          if constexpr (M % 32 != 0)
+            *reinterpret_cast<vec8<C>*>(&phib[buf][fc0][tb][lane * 8]) = bf;  // no wave owns the other half
+          else
+            *reinterpret_cast<vec4<C>*>(&phib[buf][fc0][tb][lane * 8 + half * 4]) = hv;
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) mma16(oacc[nb], sf[fcw][nb], bf);
+        mma16(dacc, zf[fcw], bf);
       }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<f32x4*>(&xch[w][tb][nb][lane * 4]) = oacc[nb];
+      if (g == 0) dpart[buf][tb][c][w] = dacc[0];
     }
-    lds_barrier();
-    // tiles (tb, nb) of value columns, shared out over the waves other than the copying one
-    constexpr int NSW = NW > 1 ? NW - 1 : 1;
-    for (int u = (NW > 1 ? w - 1 : 0); u < 2 * (NB - 1); u += NSW) {
-      if (NW > 1 && w == 0) break;
-      const int tb = u / (NB - 1), nb = u % (NB - 1);
-      f32x4 num = *reinterpret_cast<const f32x4*>(&xch[0][tb][nb][lane * 4]);
-      float den = xch[0][tb][NB - 1][c * 4];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) {
-        num += *reinterpret_cast<const f32x4*>(&xch[ww][tb][nb][lane * 4]);
-        den += xch[ww][tb][NB - 1][c * 4];
-      }
-      const int tok = tok0 + tb * 16 + c;
-      if (tok < L) {
-        const float rden = 1.0f / den;
-        const size_t o = ((size_t)bh * L + tok) * DV + nb * 16 + 4 * g;
-        if (out_f32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = num * rden;
-        } else {
-          vec4<T> r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = to_t<T>(num[i] * rden);
-          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(out) + o) = r;
-        }
-      }
-    }
+    // wave 0: land and convert the next tile
     if (w == 0) {
       wait_vmcnt<WAIT_N>();
-      if (it + 1 < n_tiles) Rg::template convert<P, KROW, false>(ring[(it + 1) % R], qs[buf ^ 1], nullptr, 0.f);
+      if (it + 1 < n_tiles) {
+        TileCursor nx = cur;
+        nx.next();
+        const float ob = (KIND == kPrf) ? omax[nx.bh % H] * kMargin : 0.f;
+        Rg::template convert<P, KROW, kNormAbs>(ring[(it + 1) % R], qs[buf ^ 1], qb[buf ^ 1], ob, L);
+      }
     }
     lds_barrier();
+
+    // ---- phase 2: this wave's value columns over all features
+    float rden[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) den += dpart[buf][tb][c][ww];
+      rden[tb] = 1.0f / den;
+    }
+    f32x4 acc[NCB][2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) acc[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fc = 0; fc < NFC; ++fc)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const vec8<C> phi = *reinterpret_cast<const vec8<C>*>(&phib[buf][fc][tb][lane * 8]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) mma16(acc[cb][tb], sf[cb][fc], phi);
+      }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int nb = w + cb * NW;
+      if (nb < NVB) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const f32x4 o = acc[cb][tb] * rden[tb];
+          if (HANDOFF && w == 0)
+            *reinterpret_cast<f32x4*>(&obuf[buf][cb][tb][lane * 4]) = o;
+          else
+            store4(bh, tok0 + tb * 16 + c, nb * 16 + 4 * g, o);
+        }
+      }
+    }
+    if (HANDOFF && w == 1 && it > 0) {
+      // wave 0's block of the previous tile
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        if (cb * NW < NVB)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            store4(prev.bh, prev.tok0() + tb * 16 + c, cb * NW * 16 + 4 * g,
+                   *reinterpret_cast<const f32x4*>(&obuf[buf ^ 1][cb][tb][lane * 4]));
+    }
+    if (it > 0) prev.next();
+    cur.next();
+  }
+  if (HANDOFF) {
+    lds_barrier();
+    if (w == 1) {
+      const int lb = (n_tiles - 1) & 1;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        if (cb * NW < NVB)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            store4(prev.bh, prev.tok0() + tb * 16 + c, cb * NW * 16 + 4 * g,
+                   *reinterpret_cast<const f32x4*>(&obuf[lb][cb][tb][lane * 4]));
+    }
   }
 }
 
@@ -678,10 +877,11 @@ bool shape_built(int dtype, int d, int dv, int m) {
 
 static inline int fb_for(int m) { return std::min(4, m / 16); }
 static inline int nw_for(int m) { return m / (16 * fb_for(m)); }
-static inline int nw_split(int m) { return std::min(4, m / 16); }
+static inline int nw_split(int m) { return m < 32 ? 1 : std::min(FAVOR_REDUCE_WAVES, m / 32); }  // RedSplit<M>::NW
 static inline size_t elt(int dtype) { return dtype == 0 ? 4 : 2; }
 constexpr int kMaxPieces = 512;  // two resident 4-wave workgroups on each of 256 CUs
-constexpr int kRing = 4;         // LDS ring slots: tiles in flight = kRing - 1
+constexpr int kRing = 6;         // LDS ring slots of the key/value reduction
+constexpr int kRingQ = 4;        // LDS ring slots of the query side
 
 static void segmenting(const Shape& s, int& nseg, int& seg_len) {
   // enough segments for ~512 workgroups, but at least 256 tokens each
@@ -705,6 +905,8 @@ BidirPlan plan_bidir(const Shape& s, int dtype) {
   size_t off = 0;
   p.off_omf = off;
   off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
+  p.off_omax = off;
+  off = align256(off + (size_t)s.H * 4);
   p.off_part = off;
   off = align256(off + slots * s.m * (s.dv + 1) * 4);
   p.off_pmax = off;
@@ -748,6 +950,7 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   C* sfr = reinterpret_cast<C*>(base + p.off_sfr);
+  float* omax = reinterpret_cast<float*>(base + p.off_omax);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
@@ -758,22 +961,33 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
     FAVOR_TIMED("omega_frag", st);
     omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
         omega, s.H, M, D, wscale, omf);
+    if (kind == kPrf) omega_bound_kernel<P><<<s.H, 256, 0, st>>>(omega, M, D, wscale, omax);
   }
   {
     FAVOR_TIMED("reduce", st);
-    kv_reduce_kernel<T, D, DV, M, kRing><<<p.G, 64 * NW, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, kind, eps,
-                                                           inv_sqrt_m, nscale, part, pmax);
+    constexpr int NWR = RedSplit<M>::NW;
+    if (kind == kPrf)
+      kv_reduce_kernel<T, D, DV, M, kRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps,
+                                                                        inv_sqrt_m, nscale, part, pmax);
+    else
+      kv_reduce_kernel<T, D, DV, M, kRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
+                                                                         eps, inv_sqrt_m, nscale, part, pmax);
   }
   {
     const int max_pieces = (int)(p.G / s.bh()) + 3;
     FAVOR_TIMED("combine", st);
-    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, (size_t)max_pieces * NW * sizeof(float),
+    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256,
+                               (size_t)max_pieces * RedSplit<M>::NW * sizeof(float),
                                st>>>(part, pmax, p.tpb, p.T_all, p.G, kind, sfr);
   }
   {
     FAVOR_TIMED("output", st);
-    q_output_kernel<T, D, DV, M, kRing><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, s.H, s.L, p.tpb, p.T_all, p.G, kind, eps,
-                                                          inv_sqrt_m, out_f32, out);
+    if (kind == kPrf)
+      q_output_kernel<T, D, DV, M, kRingQ, kPrf><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, omax, s.H, s.L, p.tpb, p.T_all,
+                                                                       p.G, eps, inv_sqrt_m, out_f32, out);
+    else
+      q_output_kernel<T, D, DV, M, kRingQ, kRelu><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, omax, s.H, s.L, p.tpb,
+                                                                        p.T_all, p.G, eps, inv_sqrt_m, out_f32, out);
   }
   return hipGetLastError();
 }

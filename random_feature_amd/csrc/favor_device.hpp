@@ -104,10 +104,41 @@ template <typename T> __device__ __forceinline__ void st8(T* p, const vec8<T>& x
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cross-lane exchanges on the VALU (no LDS round trip).
+// permlane32_swap / permlane16_swap applied to (x, x) leave, in every lane, x and its
+// partner across the 32-lane / 16-lane boundary in the two results (in some order), so a
+// symmetric reduction of the pair is the xor-32 / xor-16 butterfly step.
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// DPP moves within a 16-lane row: row_ror:n rotates, quad_perm permutes inside quads.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRor4 = 0x124, kDppRor8 = 0x128;
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, dpp<kDppRor8>(x));
+  x = fmaxf(x, dpp<kDppRor4>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  return pair_max32(pair_max16(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -115,14 +146,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 // Reduce over the four lanes that share c (lanes c, c+16, c+32, c+48).
-__device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
-__device__ __forceinline__ float group_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
+__device__ __forceinline__ float group_sum(float x) { return pair_sum32(pair_sum16(x)); }
+__device__ __forceinline__ float group_max(float x) { return pair_max32(pair_max16(x)); }
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16).
+template <int N> __device__ __forceinline__ float lanes_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRor8>(x);
+  static_assert(N <= 16, "lanes_sum covers at most 16 lanes");
   return x;
 }
 
@@ -148,7 +180,8 @@ __host__ __device__ __forceinline__ long long piece_of(long long t, long long to
 // does not track it, so the waits are placed explicitly with wait_vmcnt().
 __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
+  // an LDS DMA reading M0 right after an SALU write of M0 needs one wait state
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
