@@ -201,29 +201,34 @@ __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<type
 //   maps        Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps), rounded to the contraction type
 //   contracts   S_aug += Phi^T [V 1]: A = Phi^T (paired token slots, the accumulators as
 //               they are), B = the value fragments
-// The contraction of a tile is deferred by one iteration so that, in each wave, matrix and
-// vector work overlap: the projection MFMAs of tile t run beside the conversion of the K
-// rows of tile t+2, and the contraction MFMAs of tile t-1 beside the exponentials of tile t.
-// Tiles stream through an R-slot asynchronous ring R-2 ahead; three K buffers; one
-// barrier per tile.
+// The projection runs one tile ahead, and each iteration is two stretches in which matrix
+// and vector work of different tiles are independent: the projection MFMAs of tile t+1 run
+// beside the exponentials of tile t, the contraction MFMAs of tile t beside the conversion
+// of the K rows of tile t+2 and the next copies. The stabiliser of tile t (whose projection
+// is complete) comes first, so tile t+1 is projected against the current maximum. Tiles
+// stream through an R-slot asynchronous ring R-1 ahead; two K buffers; one barrier per tile.
 template <typename T, int D, int DV, int M, int R, int KIND>
 __global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
                  int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
-                 float* __restrict__ part, float* __restrict__ pmax) {
+                 float* __restrict__ part, float* __restrict__ zpart, float* __restrict__ pmax) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NFC = (M + 31) / 32;
+  static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
   constexpr int NB = DV / 16 + 1;  // value-column blocks + the ones column (z = Phi^T 1)
   constexpr int KROW = D + 8;
-  static_assert(R >= 5, "ring: the tile contracted late, the one projected, two converted ahead, one in flight");
+  static_assert(R >= 4, "ring: the tile contracted, one converted ahead, one being converted, one in flight");
   using Rg = Ring<T, D, DV, NT, true>;
-  constexpr int WAIT_NEXT = Rg::CPT * (R - 4);  // copies newer than tile t+2 at iteration t
+  // at the wait of iteration t the copies issued so far reach tile t+R-2 (each iteration
+  // issues at its end): R-4 tiles are newer than tile t+2
+  constexpr int WAIT_NEXT = Rg::CPT * (R - 4);
   __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
-  __shared__ __attribute__((aligned(16))) P ks[3][32 * KROW];
-  __shared__ __attribute__((aligned(16))) float kn[3][32];
+  __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
+  __shared__ __attribute__((aligned(16))) float kn[2][32];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -236,20 +241,36 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   float runmax = 0.f;
   bool first = true;
   vec8<P> om[FB][DC];
-  int cur_bh = -1;
 
+  // one (b,h)'s sums of this piece, as fp32 A fragments of S^T (the layout of sfr):
+  // part[slot][fc][nb][lane][j], the z column compacted to zpart[slot][fc][g][j] (lanes c = 0)
   auto flush = [&](int fbh, float fmax) {
-    float* Pp = part + ((size_t)pc + fbh) * M * (DV + 1);
+    const size_t slot = (size_t)pc + fbh;
+#pragma unroll
+    for (int p = 0; p < (FB + 1) / 2; ++p) {
+      const int fc = (w * FB) / 2 + p;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 lo = sacc[2 * p][nb], hi = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FB % 2 == 0) hi = sacc[2 * p + 1][nb];
+        float* dst;
+        if (nb < NB - 1)
+          dst = part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8;
+        else
+          dst = zpart + ((slot * NFC + fc) * 4 + g) * 8;
+        if (nb < NB - 1 || c == 0) {
+          reinterpret_cast<f32x4*>(dst)[0] = lo;
+          reinterpret_cast<f32x4*>(dst)[1] = hi;
+        }
+      }
+    }
+    if (lane == 0) pmax[slot * NW + w] = fmax;
+  };
+  auto zero_sums = [&]() {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = (w * FB + fb) * 16 + 4 * g + i;
-#pragma unroll
-        for (int nb = 0; nb < NB - 1; ++nb) Pp[(size_t)r * (DV + 1) + nb * 16 + c] = sacc[fb][nb][i];
-        if (c == 0) Pp[(size_t)r * (DV + 1) + DV] = sacc[fb][NB - 1][i];
-      }
-    if (lane == 0) pmax[((size_t)pc + fbh) * NW + w] = fmax;
+      for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   auto load_om = [&](int bh) {
     const int h = bh % H;
@@ -260,85 +281,13 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
     wait_vmcnt<0>();  // settle the fragment (and any partial) traffic here, off the per-tile path
   };
-  // S_aug += Phi^T [V 1] for a tile whose features are in af and whose V rows are in `slot`
-  auto contract = [&](const vec8<C> (&af)[FB], const unsigned char* slot) {
-    vec8<C> vf[NB];
-    value_frags<T, D, DV, NT>(slot, vf, c, g);
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af[fb], vf[nb]);
-  };
-  auto zero_sums = [&]() {
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-
-  const int n_tiles = (int)(t_end - t_beg);
-  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), cv(t_beg, tpb);
-#pragma unroll
-  for (int s = 0; s < R - 2; ++s) {
-    Rg::issue(K, V, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
-    if (s < n_tiles) ahead.next();
-  }
-  // tiles 0 and 1 converted up front; iteration t converts tile t+2
-  wait_vmcnt<Rg::CPT * (R - 3)>();
-  Rg::template convert<P, KROW, kNormSq>(ring[0], ks[0], kn[0], nscale, L - cv.tok0());
-  cv.next();
-  wait_vmcnt<Rg::CPT * (R - 4)>();
-  if (n_tiles > 1) Rg::template convert<P, KROW, kNormSq>(ring[1], ks[1], kn[1], nscale, L - cv.tok0());
-  cv.next();
-  lds_barrier();
-
-  zero_sums();
-  vec8<C> afp[FB];     // features of the previous tile, contracted during this one
-#pragma unroll
-  for (int fb = 0; fb < FB; ++fb) afp[fb] = zero8<C>();
-  int s_iss = R - 2;   // ring slot of the next copy:             (t + R - 2) mod R
-  int s_cv = 2;        // ring slot of the tile converted now:     (t + 2) mod R
-  int s_prev = R - 1;  // ring slot of the tile contracted late:   (t - 1) mod R
-  int k_cur = 0;       // K buffer of tile t:                      t mod 3
-  int flush_bh = -1;   // (b,h) whose partial is written at the top of the next iteration
-  float flush_max = 0.f;
-  for (int it = 0; it < n_tiles; ++it) {
-    const int bh = cur.bh, tok0 = cur.tok0();
-    const int k_cv = k_cur == 0 ? 2 : k_cur - 1;  // (t + 2) mod 3
-    {
-      const bool live = it + R - 2 < n_tiles;
-      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT);
-      if (live) ahead.next();
-    }
-    if (flush_bh >= 0) {
-      // the previous tile opened a new (b,h); the old one's sums closed with the contraction
-      // of its last tile during that iteration
-      flush(flush_bh, flush_max);
-      zero_sums();
-      flush_bh = -1;
-      wait_vmcnt<0>();  // no stores may stay in flight under the partial waits of the ring
-    }
-    // a new (b,h): its Omega' now; its sums start after the deferred contraction of the
-    // old one's last tile, which happens in this iteration
-    if (bh != cur_bh) {
-      if (cur_bh >= 0) {
-        flush_bh = cur_bh;
-        flush_max = runmax;
-      }
-      load_om(bh);
-      first = true;
-      cur_bh = bh;
-    }
-    wait_vmcnt<WAIT_NEXT>();
-
-    // projection of tile t beside the conversion of tile t+2
-    f32x4 pacc[2][FB];
+  // projection of the converted tile in ks[kb], exponents relative to the running maximum rm
+  auto project = [&](f32x4 (&pa)[2][FB], int kb, float rm) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x4 bias = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KIND == kPrf) {
-        const float rm = first ? 0.f : runmax;
-        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[k_cur][tb * 16 + 4 * g]);
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[kb][tb * 16 + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) bias[i] = -(n4[i] + rm);
       }
@@ -346,19 +295,57 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const int col = dc * 32 + 8 * g;
-        kf[dc] = (col < D) ? ld8<P>(&ks[k_cur][(tb * 16 + c) * KROW + col]) : zero8<P>();
+        kf[dc] = (col < D) ? ld8<P>(&ks[kb][(tb * 16 + c) * KROW + col]) : zero8<P>();
       }
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        pacc[tb][fb] = bias;
+        pa[tb][fb] = bias;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) mma16(pacc[tb][fb], kf[dc], om[fb][dc]);
+        for (int dc = 0; dc < DC; ++dc) mma16(pa[tb][fb], kf[dc], om[fb][dc]);
       }
     }
-    // (past the end of the piece this converts a filler slot into an unused buffer)
-    Rg::template convert<P, KROW, kNormSq>(ring[s_cv], ks[k_cv], kn[k_cv], nscale, L - cv.tok0());
-    cv.next();
+  };
 
+  const int n_tiles = (int)(t_end - t_beg);
+  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), cv(t_beg, tpb);
+#pragma unroll
+  for (int s = 0; s < R - 1; ++s) {
+    Rg::issue(K, V, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
+    if (s < n_tiles) ahead.next();
+  }
+  // tiles 0 and 1 converted up front; iteration t converts tile t+2
+  wait_vmcnt<Rg::CPT * (R - 2)>();
+  Rg::template convert<P, KROW, kNormSq>(ring[0], ks[0], kn[0], nscale, L - cv.tok0());
+  cv.next();
+  wait_vmcnt<Rg::CPT * (R - 3)>();
+  Rg::template convert<P, KROW, kNormSq>(ring[1], ks[1], kn[1], nscale, L - cv.tok0());
+  cv.next();
+  int cur_bh = cur.bh;
+  load_om(cur_bh);
+  lds_barrier();
+  zero_sums();
+  f32x4 pa0[2][FB], pa1[2][FB];  // projections of tile t and t+1, alternating roles
+  project(pa0, 0, 0.f);
+  lds_barrier();  // every wave has read ks[0] before iteration 0 converts tile 2 into it
+
+  int s_iss = R - 1;  // ring slot of the next copy:  (t + R - 1) mod R
+  int s_cur = 0;      // ring slot of tile t
+  int s_cv = 2 % R;   // ring slot of tile t + 2
+  int flush_bh = -1;  // (b,h) whose partial is written at the top of the next iteration
+  float flush_max = 0.f;
+  int it = 0;
+
+  auto step = [&](f32x4 (&pcur)[2][FB], f32x4 (&pnext)[2][FB]) {
+    const int buf = it & 1;
+    const int tok0 = cur.tok0();
+    if (flush_bh >= 0) {
+      // tile t opened a new (b,h); the old one's sums closed with the previous contraction
+      flush(flush_bh, flush_max);
+      zero_sums();
+      flush_bh = -1;
+      wait_vmcnt<0>();  // no stores may stay in flight under the partial waits of the ring
+    }
+    // stabiliser of tile t (its projection is complete)
     if constexpr (KIND == kPrf) {
       float lmax = -INFINITY;
 #pragma unroll
@@ -366,42 +353,40 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, pacc[tb][fb][i]);
+          for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, pcur[tb][fb][i]);
       // the running maximum moves only if some exponent is positive (or on a new (b,h))
       if (first || __builtin_amdgcn_ballot_w64(lmax > 0.f) != 0) {
         const float tmax = wave_max(lmax);
-        float shift = tmax;
-        if (first) {
-          runmax = tmax;
-        } else {
-          // an integral shift keeps the rescaling of the rounded deferred features exact
-          shift = ceilf(tmax);
-          const float sc = fast_exp2(-shift);
+        if (!first) {
+          const float sc = fast_exp2(-tmax);
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb) {
+          for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] *= sc;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) afp[fb][j] = to_t<C>(to_f(afp[fb][j]) * sc);
-          }
-          runmax += shift;
         }
+        runmax = first ? tmax : runmax + tmax;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb) pacc[tb][fb] -= shift;
+          for (int fb = 0; fb < FB; ++fb) pcur[tb][fb] -= tmax;
         first = false;
       }
     }
+    TileCursor nx = cur;
+    nx.next();
+    const bool more = it + 1 < n_tiles;
+    const bool next_new = more && nx.bh != cur_bh;
+    if (next_new) load_om(nx.bh);  // Omega' of tile t+1's head (tile t's projection is done)
+    wait_vmcnt<WAIT_NEXT>();
 
-    // contraction of tile t-1 beside the feature map of tile t (on the first iteration the
-    // features are zero and the V rows those of tile 0, so it adds exactly nothing)
-    contract(afp, ring[it == 0 ? 0 : s_prev]);
+    // stretch 1: projection of tile t+1 beside the feature map of tile t
+    project(pnext, buf ^ 1, next_new ? 0.f : runmax);
+    vec8<C> af[FB];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float a = pacc[j >> 2][fb][j & 3];
+        const float a = pcur[j >> 2][fb][j & 3];
         float f;
         if constexpr (KIND == kPrf) {
           f = fast_exp2(a);  // rows past L carry an infinite norm: exp2(-inf) = 0
@@ -409,93 +394,91 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
           const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L;
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
-        afp[fb][j] = to_t<C>(f);
+        af[fb][j] = to_t<C>(f);
       }
+    // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
+    // the piece: a filler slot into an unused buffer) and the next copies
+    vec8<C> vf[NB];
+    value_frags<T, D, DV, NT>(ring[s_cur], vf, c, g);
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af[fb], vf[nb]);
+    Rg::template convert<P, KROW, kNormSq>(ring[s_cv], ks[buf], kn[buf], nscale, L - cv.tok0());
+    cv.next();
+    {
+      const bool live = it + R - 1 < n_tiles;
+      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT);
+      if (live) ahead.next();
+    }
     lds_barrier();
 
-    cur.next();
-    s_prev = s_prev + 1 == R ? 0 : s_prev + 1;
-    s_cv = s_cv + 1 == R ? 0 : s_cv + 1;
+    if (next_new) {
+      flush_bh = cur_bh;
+      flush_max = runmax;
+      cur_bh = nx.bh;
+      first = true;
+    }
+    cur = nx;
     s_iss = s_iss + 1 == R ? 0 : s_iss + 1;
-    k_cur = k_cur == 2 ? 0 : k_cur + 1;
+    s_cur = s_cur + 1 == R ? 0 : s_cur + 1;
+    s_cv = s_cv + 1 == R ? 0 : s_cv + 1;
+    ++it;
+  };
+  while (it + 1 < n_tiles) {
+    step(pa0, pa1);
+    step(pa1, pa0);
   }
-  // the last tile's contraction, then the partials still open
-  if (flush_bh >= 0) {
-    flush(flush_bh, flush_max);
-    zero_sums();
-  }
-  contract(afp, ring[s_prev]);
+  if (it < n_tiles) step(pa0, pa1);
   flush(cur_bh, runmax);
 }
 
 // ---------------------------------------------------------------- combine
-// One workgroup per (b*h, 32-feature chunk): S_aug rows of the chunk summed over the
-// pieces of that (b,h), each partial scaled by 2^(M_piece,wave - M_max), written as A
-// fragments of S_aug^T (row = value column, paired feature slots):
+// One workgroup per (b*h, 32-feature chunk), one thread per (value block, lane): the
+// partials of the pieces of that (b,h), already in fragment layout, scaled by
+// 2^(M_piece,wave - M_max) and summed, give the A fragments of S_aug^T:
 // sfr[bh][fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c]; in the last
 // block only row c == 0 (the z column) is nonzero.
 template <typename C, int DV, int M>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int tpb, long long T_all, int G,
-               int kind, C* __restrict__ sfr) {
-  constexpr int NW = RedSplit<M>::NW;
-  constexpr int FPW = M / NW;
+combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
+               int tpb, long long T_all, int G, int kind, C* __restrict__ sfr) {
+  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
   constexpr int NB = DV / 16 + 1;
   constexpr int NFC = (M + 31) / 32;
-  extern __shared__ float scl[];  // [pieces of this bh][NW]
   const int bh = blockIdx.x / NFC, fc = blockIdx.x % NFC;
   const long long i_lo = piece_of((long long)bh * tpb, T_all, G);
   const long long i_hi = piece_of((long long)(bh + 1) * tpb - 1, T_all, G);
   const int np = (int)(i_hi - i_lo + 1);
+  const int wv = (fc * 32) / (FB * 16);  // the reducing wave that owned this chunk
   float gmax = -INFINITY;
-  for (int k = 0; k < np * NW; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW]);
-  for (int k = threadIdx.x; k < np * NW; k += blockDim.x)
-    scl[k] = (kind == kPrf) ? fast_exp2(pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW] - gmax) : 1.f;
-  __syncthreads();
-  C* out = sfr + ((size_t)bh * NFC + fc) * NB * 512;
-  for (int e = threadIdx.x; e < NB * 512; e += blockDim.x) {
-    const int j = e & 7, l = (e >> 3) & 63, nb = e >> 9;
-    const int c = l & 15, g = l >> 4;
-    const int r = fc * 32 + 16 * (j >> 2) + 4 * g + (j & 3);
-    const int n = (nb < NB - 1) ? nb * 16 + c : (c == 0 ? DV : -1);
-    float acc = 0.f;
-    if (n >= 0 && r < M) {
-      const int wv = r / FPW;
-      for (int k = 0; k < np; ++k)
-        acc += part[((size_t)(i_lo + k) + bh) * M * (DV + 1) + (size_t)r * (DV + 1) + n] * scl[k * NW + wv];
+  if (kind == kPrf)
+    for (int k = 0; k < np * NW; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW]);
+  for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {
+    const int nb = e >> 6, lane = e & 63;
+    const int c = lane & 15, g = lane >> 4;
+    f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (nb < NB - 1 || c == 0) {
+      for (int k = 0; k < np; ++k) {
+        const size_t slot = (size_t)(i_lo + k) + bh;
+        const float sc = (kind == kPrf) ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f;
+        const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
+                                         : zpart + ((slot * NFC + fc) * 4 + g) * 8;
+        lo += reinterpret_cast<const f32x4*>(src)[0] * sc;
+        hi += reinterpret_cast<const f32x4*>(src)[1] * sc;
+      }
     }
-    out[e] = to_t<C>(acc);
+    vec8<C> o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = to_t<C>(lo[i]);
+      o[i + 4] = to_t<C>(hi[i]);
+    }
+    st8<C>(sfr + (((size_t)bh * NFC + fc) * NB + nb) * 512 + lane * 8, o);
   }
 }
 
 // ---------------------------------------------------------------- query side
-// Largest row norm of the scaled Omega' as the projection sees it (rounded to the
-// projection type), per head: |a'_r| <= omax * |q| bounds every query exponent.
-template <typename P>
-__global__ void __launch_bounds__(256)
-omega_bound_kernel(const float* __restrict__ omega, int m, int d, float scale, float* __restrict__ omax) {
-  __shared__ float wmax[4];
-  const int h = blockIdx.x;
-  float mx = 0.f;
-  for (int r = threadIdx.x; r < m; r += blockDim.x) {
-    const float* row = omega + ((size_t)h * m + r) * d;
-    float s2 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      const float x = to_f(to_t<P>(row[j] * scale));
-      s2 += x * x;
-    }
-    mx = fmaxf(mx, __builtin_sqrtf(s2));
-  }
-  mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = wmax[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = fmaxf(r, wmax[i]);
-    omax[h] = r;
-  }
-}
-
 // Exponent bound (log2 units) under which the bound stabiliser keeps every query feature
 // a normal float: the features lie in [2^(-2 bound), 1].
 constexpr float kQueryBoundLimit = 60.f;
@@ -503,46 +486,53 @@ constexpr float kQueryBoundLimit = 60.f;
 // Workgroup = NW waves over one piece of the flattened tile space. Per 32-token tile:
 //   phase 1 (wave w, its FB*16 features, Omega' fragments in registers)
 //     projection  A = Omega' (rows = features), B = Q^T (linear d slots) -> [feature][token];
-//                 the accumulators start at -b_t, b_t = omax |q_t| >= max_r a'_r, so the
-//                 output is already a non-positive exponent (the |q|^2 term of the map and
-//                 any constant per row cancel in the ratio). If some row of the tile has
+//                 the accumulators start at -b_t, b_t = omax |q_t| >= max_r a'_r (omax the
+//                 largest row norm of the rounded Omega' of the head), so the output is
+//                 already a non-positive exponent (the |q|^2 term of the map and any
+//                 constant per row cancel in the ratio). If some row of the tile has
 //                 b_t > kQueryBoundLimit, the tile takes the exact row maximum across the
 //                 waves instead (one more barrier).
 //     feature map Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps); the accumulator pairs are
 //                 B operands of the contraction as they stand (paired feature slots) and go
 //                 to LDS; the wave's share of the denominator z^T Phi^T goes with them
+//   every thread then lands, converts and norms its own chunk of tile t+1 and copies its
+//   chunk of tile t+2 into the two-slot ring (all its memory traffic, stores included, has
+//   settled at that point, so one full wait covers it)
 //   barrier
-//   phase 2 (wave w, value-column blocks w, w+NW, ...)
+//   phase 2 (wave w: a token half and value-column blocks, or both halves and fewer blocks)
 //     contraction out^T block = S^T block (A, registers) x Phi^T (B, all features from LDS)
 //     division by the summed denominators and the store
-// Wave 0 alone copies Q tiles into the ring and converts them, one tile ahead; so that its
-// memory counter sees nothing but ring copies it stores nothing: it leaves its normalised
-// block in LDS and wave 1 stores it during the next tile.
-template <typename T, int D, int DV, int M, int R, int KIND>
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * FeatSplit<M>::NW, 2)
 q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ omf,
-                const typename Ops<T>::C* __restrict__ sfr, const float* __restrict__ omax, int H, int L, int tpb,
-                long long T_all, int G, float eps, float inv_sqrt_m, int out_f32, void* __restrict__ out) {
+                const typename Ops<T>::C* __restrict__ sfr, int H, int L, int tpb, long long T_all, int G,
+                float eps, float inv_sqrt_m, int out_f32, void* __restrict__ out) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = FeatSplit<M>::NW, FB = FeatSplit<M>::FB;
+  constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
   constexpr int NB = DV / 16 + 1;           // blocks of S_aug^T in sfr: values, then z
   constexpr int NVB = DV / 16;              // value-column blocks
-  constexpr int NCB = (NVB + NW - 1) / NW;  // value-column blocks per wave
+  // phase 2 split: with TBS wave w takes token half w & 1 and value blocks (w >> 1) + j*NW/2
+  // (half the LDS reads of the features, twice the S fragments); else both halves and
+  // blocks w + j*NW
+  constexpr int SF_REGS = sizeof(typename Ops<T>::C) == 2 ? 4 : 8;
+  constexpr int NWH = NW / 2 > 0 ? NW / 2 : 1;
+  constexpr bool TBS = NW >= 2 && ((NVB + NWH - 1) / NWH) * ((M + 31) / 32) * SF_REGS <= 64;
+  constexpr int NW2 = TBS ? NWH : NW;
+  constexpr int NCB = (NVB + NW2 - 1) / NW2;  // value-column blocks per wave
+  constexpr int NTB = TBS ? 1 : 2;             // token halves per wave in phase 2
   constexpr int NFCW = (FB + 1) / 2;        // 32-feature chunks a wave fills (half of one when FB = 1)
   constexpr int NFC = (M + 31) / 32;
   constexpr int KROW = D + 8;
-  constexpr bool HANDOFF = NW > 1;          // wave 0's block is stored by wave 1
-  using Rg = Ring<T, D, DV, 64, false>;
-  constexpr int WAIT_N = HANDOFF ? Rg::CPT * (R - 2) : 0;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
+  using Rg = Ring<T, D, DV, NT, false>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) P qs[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) float qb[2][32];
   __shared__ __attribute__((aligned(16))) C phib[2][NFC][2][64 * 8];
   __shared__ __attribute__((aligned(16))) float dpart[2][2][16][NW];
   __shared__ __attribute__((aligned(16))) float qmx[NW][32];
-  __shared__ __attribute__((aligned(16))) float obuf[HANDOFF ? 2 : 1][NCB][2][64 * 4];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -551,48 +541,29 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
   if (t_beg >= t_end) return;
   const int n_tiles = (int)(t_end - t_beg);
   const int fc0 = (w * FB) / 2;
+  const int cb0 = TBS ? (w >> 1) : w, tb0 = TBS ? (w & 1) : 0;
   constexpr float kMargin = 1.f + 1.f / 512.f;  // rounding of q to the projection type and of the MFMA sums
 
-  auto store4 = [&](int bh, int tok, int col, const f32x4& val) {
-    if (tok >= L) return;
-    const size_t o = ((size_t)bh * L + tok) * DV + col;
-    if (out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = val;
-    } else {
-      vec4<T> r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = to_t<T>(val[i]);
-      *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(out) + o) = r;
-    }
-  };
-
   const uint32_t ring0 = lds_addr(&ring[0][0]);
-  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), prev(t_beg, tpb);
-  if (w == 0) {
-#pragma unroll
-    for (int s = 0; s < R - 1; ++s) {
-      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
-      if (s < n_tiles) ahead.next();
-    }
-    wait_vmcnt<Rg::CPT * (R - 2)>();
-    const float ob = (KIND == kPrf) ? omax[cur.bh % H] * kMargin : 0.f;
-    Rg::template convert<P, KROW, kNormAbs>(ring[0], qs[0], qb[0], ob, L);
-  }
+  TileCursor ahead(t_beg, tpb), cur(t_beg, tpb);
+  // prologue: tiles 0 and 1 in flight, tile 0 converted
+  Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), true, ring0);
+  ahead.next();
+  Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), n_tiles > 1, ring0 + Rg::SLOT);
+  if (n_tiles > 1) ahead.next();
+  wait_vmcnt<Rg::CPT>();
+  Rg::template convert<P, KROW, kNormAbs>(ring[0], qs[0], qb[0], kMargin, L);
   lds_barrier();
 
   vec8<P> om[FB][DC];
   vec8<C> zf[NFCW];
   vec8<C> sf[NCB][NFC];
+  float omax = 0.f;
   int cur_bh = -1;
 
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
     const int bh = cur.bh, tok0 = cur.tok0();
-    if (w == 0) {
-      const bool live = it + R - 1 < n_tiles;
-      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), live, ring0 + ((it + R - 1) % R) * Rg::SLOT);
-      if (live) ahead.next();
-    }
     if (bh != cur_bh) {
       const int h = bh % H;
 #pragma unroll
@@ -605,13 +576,38 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
         zf[fcw] = ld8<C>(sfr + ((((size_t)bh * NFC + fc0 + fcw) * NB + (NB - 1)) * 64 + lane) * 8);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int nb = w + cb * NW;
+        const int nb = cb0 + cb * NW2;
 #pragma unroll
         for (int fc = 0; fc < NFC; ++fc)
           sf[cb][fc] = nb < NVB ? ld8<C>(sfr + ((((size_t)bh * NFC + fc) * NB + nb) * 64 + lane) * 8) : zero8<C>();
       }
       cur_bh = bh;
-      wait_vmcnt<0>();  // settle the fragment loads here, off the per-tile path
+      if constexpr (KIND == kPrf) {
+        // largest row norm of this head's rounded Omega': the wave's rows, then across waves
+        float n2 = 0.f;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+          float s2 = 0.f;
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float x = to_f(om[fb][dc][j]);
+              s2 += x * x;
+            }
+          n2 = fmaxf(n2, group_sum(s2));
+        }
+        n2 = wave_max(n2);
+        if (lane == 0) qmx[w][0] = n2;
+        lds_barrier();
+        float m2 = qmx[0][0];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) m2 = fmaxf(m2, qmx[ww][0]);
+        omax = __builtin_sqrtf(m2);
+        lds_barrier();  // qmx is reused by the exact-maximum path
+      } else {
+        wait_vmcnt<0>();
+      }
     }
 
     // ---- phase 1: this wave's features of the tile
@@ -619,7 +615,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
     bool exact = false;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const float b = (KIND == kPrf) ? qb[buf][tb * 16 + c] : 0.f;
+      const float b = (KIND == kPrf) ? qb[buf][tb * 16 + c] * omax : 0.f;
       bias[tb] = f32x4{-b, -b, -b, -b};
       if constexpr (KIND == kPrf) exact |= b > kQueryBoundLimit;
     }
@@ -704,79 +700,62 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       }
       if (g == 0) dpart[buf][tb][c][w] = dacc[0];
     }
-    // wave 0: land and convert the next tile
-    if (w == 0) {
-      wait_vmcnt<WAIT_N>();
-      if (it + 1 < n_tiles) {
-        TileCursor nx = cur;
-        nx.next();
-        const float ob = (KIND == kPrf) ? omax[nx.bh % H] * kMargin : 0.f;
-        Rg::template convert<P, KROW, kNormAbs>(ring[(it + 1) % R], qs[buf ^ 1], qb[buf ^ 1], ob, L);
-      }
+
+    // land, convert and norm this thread's chunk of tile t+1; copy its chunk of tile t+2
+    wait_vmcnt<0>();
+    Rg::template convert<P, KROW, kNormAbs>(ring[buf ^ 1], qs[buf ^ 1], qb[buf ^ 1], kMargin, L);
+    {
+      const bool live = it + 2 < n_tiles;
+      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), live, ring0 + buf * Rg::SLOT);
+      if (live) ahead.next();
     }
     lds_barrier();
 
     // ---- phase 2: this wave's value columns over all features
-    float rden[2];
+    float rden[NTB];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tt = 0; tt < NTB; ++tt) {
       float den = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) den += dpart[buf][tb][c][ww];
-      rden[tb] = 1.0f / den;
+      for (int ww = 0; ww < NW; ++ww) den += dpart[buf][tb0 + tt][c][ww];
+      rden[tt] = 1.0f / den;
     }
-    f32x4 acc[NCB][2];
+    f32x4 acc[NCB][NTB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) acc[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < NTB; ++tt) acc[cb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int fc = 0; fc < NFC; ++fc)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const vec8<C> phi = *reinterpret_cast<const vec8<C>*>(&phib[buf][fc][tb][lane * 8]);
+      for (int tt = 0; tt < NTB; ++tt) {
+        const vec8<C> phi = *reinterpret_cast<const vec8<C>*>(&phib[buf][fc][tb0 + tt][lane * 8]);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) mma16(acc[cb][tb], sf[cb][fc], phi);
+        for (int cb = 0; cb < NCB; ++cb) mma16(acc[cb][tt], sf[cb][fc], phi);
       }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int nb = w + cb * NW;
+      const int nb = cb0 + cb * NW2;
       if (nb < NVB) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const f32x4 o = acc[cb][tb] * rden[tb];
-          if (HANDOFF && w == 0)
-            *reinterpret_cast<f32x4*>(&obuf[buf][cb][tb][lane * 4]) = o;
-          else
-            store4(bh, tok0 + tb * 16 + c, nb * 16 + 4 * g, o);
+        for (int tt = 0; tt < NTB; ++tt) {
+          const int tok = tok0 + (tb0 + tt) * 16 + c;
+          if (tok < L) {
+            const f32x4 o = acc[cb][tt] * rden[tt];
+            const size_t off = ((size_t)bh * L + tok) * DV + nb * 16 + 4 * g;
+            if (out_f32) {
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
+            } else {
+              vec4<T> r;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) r[i] = to_t<T>(o[i]);
+              *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(out) + off) = r;
+            }
+          }
         }
       }
     }
-    if (HANDOFF && w == 1 && it > 0) {
-      // wave 0's block of the previous tile
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        if (cb * NW < NVB)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            store4(prev.bh, prev.tok0() + tb * 16 + c, cb * NW * 16 + 4 * g,
-                   *reinterpret_cast<const f32x4*>(&obuf[buf ^ 1][cb][tb][lane * 4]));
-    }
-    if (it > 0) prev.next();
     cur.next();
-  }
-  if (HANDOFF) {
-    lds_barrier();
-    if (w == 1) {
-      const int lb = (n_tiles - 1) & 1;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        if (cb * NW < NVB)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            store4(prev.bh, prev.tok0() + tb * 16 + c, cb * NW * 16 + 4 * g,
-                   *reinterpret_cast<const f32x4*>(&obuf[lb][cb][tb][lane * 4]));
-    }
   }
 }
 
@@ -880,8 +859,7 @@ static inline int nw_for(int m) { return m / (16 * fb_for(m)); }
 static inline int nw_split(int m) { return m < 32 ? 1 : std::min(FAVOR_REDUCE_WAVES, m / 32); }  // RedSplit<M>::NW
 static inline size_t elt(int dtype) { return dtype == 0 ? 4 : 2; }
 constexpr int kMaxPieces = 512;  // two resident 4-wave workgroups on each of 256 CUs
-constexpr int kRing = 6;         // LDS ring slots of the key/value reduction
-constexpr int kRingQ = 4;        // LDS ring slots of the query side
+constexpr int kRing = 5;         // LDS ring slots of the key/value reduction
 
 static void segmenting(const Shape& s, int& nseg, int& seg_len) {
   // enough segments for ~512 workgroups, but at least 256 tokens each
@@ -905,10 +883,11 @@ BidirPlan plan_bidir(const Shape& s, int dtype) {
   size_t off = 0;
   p.off_omf = off;
   off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
-  p.off_omax = off;
-  off = align256(off + (size_t)s.H * 4);
+  const size_t nfc = (s.m + 31) / 32;
   p.off_part = off;
-  off = align256(off + slots * s.m * (s.dv + 1) * 4);
+  off = align256(off + slots * nfc * (s.dv / 16) * 512 * 4);
+  p.off_zpart = off;
+  off = align256(off + slots * nfc * 32 * 4);
   p.off_pmax = off;
   off = align256(off + slots * p.nw_reduce * 4);
   p.off_sfr = off;
@@ -948,9 +927,9 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + p.off_omf);
   float* part = reinterpret_cast<float*>(base + p.off_part);
+  float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   C* sfr = reinterpret_cast<C*>(base + p.off_sfr);
-  float* omax = reinterpret_cast<float*>(base + p.off_omax);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
@@ -961,33 +940,30 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
     FAVOR_TIMED("omega_frag", st);
     omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
         omega, s.H, M, D, wscale, omf);
-    if (kind == kPrf) omega_bound_kernel<P><<<s.H, 256, 0, st>>>(omega, M, D, wscale, omax);
   }
   {
     FAVOR_TIMED("reduce", st);
     constexpr int NWR = RedSplit<M>::NW;
     if (kind == kPrf)
       kv_reduce_kernel<T, D, DV, M, kRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps,
-                                                                        inv_sqrt_m, nscale, part, pmax);
+                                                                        inv_sqrt_m, nscale, part, zpart, pmax);
     else
       kv_reduce_kernel<T, D, DV, M, kRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
-                                                                         eps, inv_sqrt_m, nscale, part, pmax);
+                                                                         eps, inv_sqrt_m, nscale, part, zpart, pmax);
   }
   {
-    const int max_pieces = (int)(p.G / s.bh()) + 3;
     FAVOR_TIMED("combine", st);
-    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256,
-                               (size_t)max_pieces * RedSplit<M>::NW * sizeof(float),
-                               st>>>(part, pmax, p.tpb, p.T_all, p.G, kind, sfr);
+    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
+        part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr);
   }
   {
     FAVOR_TIMED("output", st);
     if (kind == kPrf)
-      q_output_kernel<T, D, DV, M, kRingQ, kPrf><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, omax, s.H, s.L, p.tpb, p.T_all,
-                                                                       p.G, eps, inv_sqrt_m, out_f32, out);
+      q_output_kernel<T, D, DV, M, kPrf><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, s.H, s.L, p.tpb, p.T_all, p.G, eps,
+                                                                inv_sqrt_m, out_f32, out);
     else
-      q_output_kernel<T, D, DV, M, kRingQ, kRelu><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, omax, s.H, s.L, p.tpb,
-                                                                        p.T_all, p.G, eps, inv_sqrt_m, out_f32, out);
+      q_output_kernel<T, D, DV, M, kRelu><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, s.H, s.L, p.tpb, p.T_all, p.G, eps,
+                                                                 inv_sqrt_m, out_f32, out);
   }
   return hipGetLastError();
 }

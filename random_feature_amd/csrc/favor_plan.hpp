@@ -34,7 +34,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct BidirPlan {
   int tpb = 0, G = 0, nw_reduce = 0;
   long long T_all = 0;
-  size_t off_omf = 0, off_omax = 0, off_part = 0, off_pmax = 0, off_sfr = 0, total = 0;
+  size_t off_omf = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_sfr = 0, total = 0;
 };
 
 // Causal path: the bidirectional pieces for segment totals plus carried states.
