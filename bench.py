@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="launch one elementwise copy of this many MiB first (counter calibration)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="also time with this many input sets in rotation (> the 256 MB MALL); 0 to skip")
     a = ap.parse_args()
@@ -191,6 +193,15 @@ def main():
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4
 
+    if a.copy_calib:
+        # a plain elementwise copy of known size: hardware counters of the same run are
+        # calibrated against it (see random_feature_amd.profiling)
+        n = a.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(a.warmup):
         step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

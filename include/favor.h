@@ -27,9 +27,12 @@
  *     and output buffers are untouched. There is no fallback path.
  *   - Non-finite inputs are not checked; they propagate.
  *   - q and k are raw: the d^(-1/4) scaling happens inside the library.
- *   - The max-subtraction stabilisers (per query row; one constant per (b,h)
- *     for keys, or per segment prefix in the causal form) cancel exactly in the
- *     ratio, so results equal the unstabilised definitions up to rounding.
+ *   - The stabilisers (a constant per query row: a norm bound max_r|omega_r||x|
+ *     or the exact row maximum; one constant per (b,h) for keys, or per segment
+ *     prefix in the causal form) cancel exactly in the ratio, so results equal
+ *     the unstabilised definitions up to rounding.
+ *   - bf16 inputs are projected in fp16 (exact for 2^-14 <= |x| < 65504); values
+ *     of magnitude 65504 or more are outside the supported domain.
  */
 #ifndef FAVOR_H
 #define FAVOR_H
@@ -119,8 +122,8 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
  * advanced by one token; token t's output reads the state that includes t).
  * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical
  * scale, updated in place; out [N,H,dv] fp32.
- * Requires d in {16, 32, 64}, dv a multiple of 4 with dv <= 256, m a multiple of 64
- * with m <= 1024. */
+ * Requires d in {16, 32, 64}, dv a power of two in [16, 256], m a multiple of 16
+ * with m <= 1024 (other values: FAVOR_ERR_UNSUPPORTED). */
 favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega,
                           float* S, float* z, int N, int H, int d, int dv, int m,
                           favor_dtype dtype, favor_kind kind, float eps,
