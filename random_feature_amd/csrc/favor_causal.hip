@@ -34,6 +34,8 @@
 namespace favor {
 
 // ---------------------------------------------------------------- scan over segments
+// Grid (element chunks of 256, b*h): every thread scans one element of S_aug over the
+// segments; the prefix maxima (a few values per segment) are recomputed per workgroup.
 template <int DV, int M, int NW>
 __global__ void __launch_bounds__(256)
 scan_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int nseg, int kind, float log2_sqrt_m,
@@ -42,7 +44,7 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int 
   constexpr int FPW = M / NW;
   constexpr int W = DV + 1;
   extern __shared__ float pre[];  // [nseg] prefix maxima
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   if (threadIdx.x == 0) {
     float run = -INFINITY;
     for (int p = 0; p < nseg; ++p) {
@@ -50,30 +52,30 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int 
       for (int w = 0; w < NW; ++w) mx = fmaxf(mx, pmax[((size_t)bh * nseg + p) * NW + w]);
       run = fmaxf(run, mx);
       pre[p] = (kind == kPrf) ? run : 0.f;
-      cmax[(size_t)bh * nseg + p] = pre[p];
+      if (blockIdx.x == 0) cmax[(size_t)bh * nseg + p] = pre[p];
     }
   }
   __syncthreads();
   const size_t base = (size_t)bh * nseg * M * W;
-  for (int e = threadIdx.x; e < M * W; e += blockDim.x) {
-    const int wv = (e / W) / FPW;
-    float acc = 0.f, prev = 0.f;
-    for (int p = 0; p < nseg; ++p) {
-      const float mp = pre[p];
-      if (p > 0) acc *= fast_exp2(prev - mp);
-      carry[base + (size_t)p * M * W + e] = acc;
-      const float sc = (kind == kPrf) ? fast_exp2(pmax[((size_t)bh * nseg + p) * NW + wv] - mp) : 1.f;
-      acc += part[base + (size_t)p * M * W + e] * sc;
-      prev = mp;
-    }
-    if (S_final) {
-      const float canon = (kind == kPrf) ? acc * fast_exp2(prev - log2_sqrt_m) : acc;
-      const int r = e / W, n = e % W;
-      if (n < DV)
-        S_final[((size_t)bh * M + r) * DV + n] = canon;
-      else
-        z_final[(size_t)bh * M + r] = canon;
-    }
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * W) return;
+  const int wv = (e / W) / FPW;
+  float acc = 0.f, prev = 0.f;
+  for (int p = 0; p < nseg; ++p) {
+    const float mp = pre[p];
+    if (p > 0) acc *= fast_exp2(prev - mp);
+    carry[base + (size_t)p * M * W + e] = acc;
+    const float sc = (kind == kPrf) ? fast_exp2(pmax[((size_t)bh * nseg + p) * NW + wv] - mp) : 1.f;
+    acc += part[base + (size_t)p * M * W + e] * sc;
+    prev = mp;
+  }
+  if (S_final) {
+    const float canon = (kind == kPrf) ? acc * fast_exp2(prev - log2_sqrt_m) : acc;
+    const int r = e / W, n = e % W;
+    if (n < DV)
+      S_final[((size_t)bh * M + r) * DV + n] = canon;
+    else
+      z_final[(size_t)bh * M + r] = canon;
   }
 }
 
@@ -404,7 +406,8 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   }
   {
     FAVOR_TIMED("scan", st);
-    scan_kernel<DV, M, NW><<<(unsigned)s.bh(), 256, p.nseg * sizeof(float), st>>>(
+    scan_kernel<DV, M, NW><<<dim3((unsigned)((M * (DV + 1) + 255) / 256), (unsigned)s.bh()), 256,
+                             p.nseg * sizeof(float), st>>>(
         part, pmax, p.nseg, kind, log2_sqrt_m, carry, cmax, S_final, z_final);
   }
   constexpr int KROW = D + 8, VROW = 40, NT = 4 + 2 * NB, OROW = DV + 4;
