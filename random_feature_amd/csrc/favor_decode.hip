@@ -6,17 +6,15 @@
 // with the updated state (token t's output includes token t).
 //
 // The state S [N,H,m,dv] fp32 dominates the traffic: each step reads and writes it
-// once, so the kernel is an HBM stream. Work split: one workgroup per (head, group
-// of G sequences).
-//   phase 1  thread r holds omega_r of its head in registers and computes
-//            a = omega_r . x for the group's q and k (fp32 FMA). Keys use the
-//            canonical feature exp(a - |x|^2/2)/sqrt(m) because the state is kept
-//            unstabilised; queries use exp(a - max_r a), a per-row constant that
-//            cancels in the ratio. phi is staged in LDS.
-//   phase 2  per sequence, the state block is streamed with 16-byte loads and
-//            stores: consecutive threads cover consecutive columns of one row, so
-//            a wave touches whole rows; the numerator is accumulated on the fly
-//            from the updated rows and reduced across row groups through LDS.
+// once, so the kernel is an HBM stream. Work split: one workgroup per (sequence, head).
+//   every thread first requests the loads the features need (q, k, its v columns, the
+//   Omega row of its feature), then its state rows (16-byte loads, consecutive threads
+//   on consecutive columns of a row), so the state streams in during the projections;
+//   thread r computes a = omega_r . x for q and k (fp32 FMA). Keys use the canonical
+//   feature exp(a - |x|^2/2)/sqrt(m) because the state is kept unstabilised; queries
+//   use exp(a - max_r a), a per-row constant that cancels in the ratio.
+//   Each thread then updates its rows in place, accumulates its share of the numerator
+//   and the workgroup reduces the shares through LDS.
 #include "favor_device.hpp"
 #include "favor_plan.hpp"
 #include "favor_timing.hpp"
@@ -26,208 +24,246 @@
 
 namespace favor {
 
-constexpr int kDecodeThreads = 256;
+#ifndef FAVOR_DECODE_THREADS
+#define FAVOR_DECODE_THREADS 256
+#endif
+#ifndef FAVOR_DECODE_ROWS
+#define FAVOR_DECODE_ROWS 8
+#endif
+constexpr int kDecodeThreads = FAVOR_DECODE_THREADS;
+constexpr int kDecodeRows = FAVOR_DECODE_ROWS;  // state rows (16 bytes each) a thread moves per sequence and batch
+constexpr int kDecodeSeqs = 1;                  // sequences of one head per workgroup (they share Omega's rows)
 
-constexpr int kDecodeGroup = 4;  // sequences per workgroup
-constexpr int kDecodeRows = 8;   // state rows per thread per batch (loads in flight)
-
+// One workgroup per (head, group of kDecodeSeqs sequences); every thread owns 4 columns of
+// runs of kDecodeRows consecutive state rows of each sequence. The first batch of state
+// rows is requested right after the (older) loads the features need, so the state streams
+// in while the projections are computed. Two threads share each feature's projection (one
+// half of d each). Measured on the 256-sequence, 16-head, m = 256, dv = 64 step: 256
+// threads with 8 rows each (two batches) beat larger workgroups and longer runs.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
               const float* __restrict__ omega, float* __restrict__ S, float* __restrict__ z, int N, int H,
-              int dv, int m, int n_groups, int kind, float eps, float inv_sqrt_m, float wscale,
-              float nscale, float log2_sqrt_m, float* __restrict__ out) {
-  constexpr int G = kDecodeGroup, U = kDecodeRows;
+              int dv, int m, int kind, float eps, float inv_sqrt_m, float wscale, float nscale, float log2_sqrt_m,
+              float* __restrict__ out) {
+  constexpr int U = kDecodeRows, G = kDecodeSeqs;
+  constexpr int NWV = kDecodeThreads / 64;
+  constexpr int DH = D / 2;  // the d-half of a feature this thread projects
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  // layout: aq[G][m], ak[G][m] (features after phase 1), xs[2][G][D] (q, k as fp32),
-  //         red[G][256][4] (numerator partials), scal[G][4]
-  float* aq = sm;
-  float* ak = aq + G * m;
-  float* xs = ak + G * m;
-  float* red = xs + 2 * G * D;
-  float* scal = red + G * kDecodeThreads * 4;
-  __shared__ float dsum[G][kDecodeThreads / 64];
+  // layout: fq[G][m], fk[G][m] (features), xs[G][2][D] (q, k as fp32), red[G][threads][4]
+  float* fq = sm;
+  float* fk = fq + G * m;
+  float* xs = fk + G * m;
+  float* red = xs + G * 2 * D;
+  __shared__ float wred[G][2][NWV];
 
+  const int n_grp = (N + G - 1) / G;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = logical / n_groups, grp = logical % n_groups;
-  const int s0 = grp * G;
+  const int h = logical / n_grp, s0 = (logical % n_grp) * G;
   const int ng = min(G, N - s0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-
-  // the state stream: batch i covers rows [b*U*rpp, (b+1)*U*rpp) of sequence i / nbat;
-  // thread (row0, col4) moves U rows, 16 bytes each. The first batch is requested now,
-  // so its loads are in flight while the features are computed.
-  const int tpr = dv / 4;                 // threads per row (power of two, <= 64)
-  const int rpp = kDecodeThreads / tpr;   // rows per pass
-  const int col4 = tid % tpr, row0 = tid / tpr;
-  const int rows_per_batch = U * rpp;
+  const int tpr = dv / 4;                 // threads per row (power of two, 4..64)
+  const int rgs = kDecodeThreads / tpr;   // row groups of U consecutive rows per batch
+  const int col4 = tid % tpr, rg0 = tid / tpr;
+  const int rows_per_batch = U * rgs;
   const int nbat = (m + rows_per_batch - 1) / rows_per_batch;
-  const int total = ng * nbat;
-  auto load_batch = [&](int i, f32x4 (&buf)[U]) {
-    const int sq = i / nbat, b = i % nbat;
-    const float* Sp = S + ((size_t)(s0 + sq) * H + h) * m * dv;
+  // this thread's rows in batch b: b*rows_per_batch + rg0*U + u, u < U (consecutive rows,
+  // so one base address and immediate offsets); a wave covers whole rows
+  // the pair (sequence, head) of slot g; a missing sequence of the last group reuses
+  // the first one's data for its loads and writes nothing
+  auto pair_of = [&](int g) -> size_t { return (size_t)(s0 + (g < ng ? g : 0)) * H + h; };
+
+  // loads the features wait for: q, k, this thread's v columns, its Omega half-row
+  for (int i = tid; i < G * 2 * D; i += kDecodeThreads) {
+    const int g = i / (2 * D), w2 = (i / D) & 1, dd = i % D;
+    xs[i] = to_f((w2 == 0 ? q : k)[pair_of(g) * D + dd]);
+  }
+  f32x4 vv[G];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = b * rows_per_batch + u * rpp + row0;
-      if (r < m) buf[u] = *reinterpret_cast<const f32x4*>(Sp + (size_t)r * dv + col4 * 4);
-    }
+  for (int g = 0; g < G; ++g) {
+    const T* vs = v + pair_of(g) * dv + col4 * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[g][j] = to_f(vs[j]);
+  }
+  const int half = tid & 1, f0 = tid >> 1;
+  // (loads are unconditional, from clamped rows, so they issue back to back with no
+  // waits in between; results for rows past m are never used)
+  f32x4 w0[DH / 4];
+  {
+    const f32x4* wr =
+        reinterpret_cast<const f32x4*>(omega + ((size_t)h * m + (f0 < m ? f0 : m - 1)) * D + half * DH);
+#pragma unroll
+    for (int i = 0; i < DH / 4; ++i) w0[i] = wr[i];
+  }
+  // then the first state batch of every sequence; a row past m is read as row m-1 and its
+  // value never used
+  auto row_ptr = [&](int g, int r) -> float* {
+    return S + pair_of(g) * m * dv + (size_t)(r < m ? r : m - 1) * dv + col4 * 4;
   };
-  // stage q and k of the group as fp32
-  for (int i = tid; i < 2 * G * D; i += kDecodeThreads) {
-    const int which = i / (G * D), rem = i % (G * D), s = rem / D, dd = rem % D;
-    float x = 0.f;
-    if (s < ng) {
-      const T* src = which == 0 ? q : k;
-      x = to_f(src[((size_t)(s0 + s) * H + h) * D + dd]);
-    }
-    xs[i] = x;
-  }
-  // this thread's first Omega row, then the first state batch: every load the features
-  // wait for is older than the state loads, so those stay in flight meanwhile
-  f32x4 w0[D / 4];
-  if (tid < m) {
-    const f32x4* wr = reinterpret_cast<const f32x4*>(omega + ((size_t)h * m + tid) * D);
+  f32x4 buf[G][U];
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) w0[i] = wr[i];
+  for (int g = 0; g < G; ++g) {
+    const int r0 = rg0 * U;
+    if (r0 + U <= m) {
+      const float* p0 = row_ptr(g, r0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(p0 + u * dv);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(row_ptr(g, r0 + u));
+    }
   }
-  f32x4 bufA[U], bufB[U];
-  if (total > 0) load_batch(0, bufA);
   __syncthreads();
 
-  // phase 1: projections a = omega' . x
-  for (int r = tid; r < m; r += kDecodeThreads) {
-    float w[D];
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const f32x4 t = (r == tid) ? w0[i] : reinterpret_cast<const f32x4*>(omega + ((size_t)h * m + r) * D)[i];
-      w[4 * i] = t[0] * wscale;
-      w[4 * i + 1] = t[1] * wscale;
-      w[4 * i + 2] = t[2] * wscale;
-      w[4 * i + 3] = t[3] * wscale;
-    }
-    for (int s = 0; s < G; ++s) {
-      const float* xq = xs + s * D;
-      const float* xk = xs + (G + s) * D;
+  // projections a = omega' . x of q and k, stored raw; the key norms meanwhile
+  if (wv < G) {
+    float k2 = 0.f;
+    for (int dd = lane; dd < D; dd += 64) k2 += xs[(wv * 2 + 1) * D + dd] * xs[(wv * 2 + 1) * D + dd];
+    k2 = wave_sum(k2);
+    if (lane == 0) wred[wv][1][0] = k2 * nscale + log2_sqrt_m;  // log2 of the key's normaliser
+  }
+  // feature r's projection from this thread's half of omega_r (w), completed across the
+  // lane pair by DPP; every thread runs the same iterations
+  auto feature = [&](int r, const f32x4 (&w)[DH / 4]) {
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+      const f32x4* xq = reinterpret_cast<const f32x4*>(xs + (g * 2) * D + half * DH);
+      const f32x4* xk = reinterpret_cast<const f32x4*>(xs + (g * 2 + 1) * D + half * DH);
       float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int dd = 0; dd < D; ++dd) {
-        a0 += w[dd] * xq[dd];
-        a1 += w[dd] * xk[dd];
-      }
-      aq[s * m + r] = a0;
-      ak[s * m + r] = a1;
-    }
-  }
-  __syncthreads();
-
-  // per-sequence scalars: query row max (PRF) and the key's log2 normaliser
-  if (kind == 0) {
-    for (int s = wv; s < G; s += kDecodeThreads / 64) {
-      float mx = -INFINITY;
-      for (int r = lane; r < m; r += 64) mx = fmaxf(mx, aq[s * m + r]);
-      mx = wave_max(mx);
-      float k2 = 0.f;
-      for (int dd = lane; dd < D; dd += 64) {
-        const float x = xs[(G + s) * D + dd];
-        k2 += x * x;
-      }
-      k2 = wave_sum(k2);
-      if (lane == 0) {
-        scal[s * 4 + 0] = mx;
-        scal[s * 4 + 1] = k2 * nscale + log2_sqrt_m;
-      }
-    }
-    __syncthreads();
-  }
-  for (int i = tid; i < G * m; i += kDecodeThreads) {
-    const int s = i / m;
-    if (kind == 0) {
-      aq[i] = fast_exp2(aq[i] - scal[s * 4 + 0]);
-      ak[i] = fast_exp2(ak[i] - scal[s * 4 + 1]);
-    } else {
-      aq[i] = fmaxf(aq[i], 0.f) * inv_sqrt_m + eps;
-      ak[i] = fmaxf(ak[i], 0.f) * inv_sqrt_m + eps;
-    }
-  }
-  __syncthreads();
-
-  // z rows and the denominators (small: m floats per sequence)
-  for (int sq = 0; sq < ng; ++sq) {
-    const size_t pair = (size_t)(s0 + sq) * H + h;
-    float* zp = z + pair * m;
-    float dpart = 0.f;
-    for (int r = tid; r < m; r += kDecodeThreads) {
-      const float zn = zp[r] + ak[sq * m + r];
-      zp[r] = zn;
-      dpart += aq[sq * m + r] * zn;
-    }
-    dpart = wave_sum(dpart);
-    if (lane == 0) dsum[sq][wv] = dpart;
-  }
-
-  // phase 2: stream the state, two batches in flight
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto process = [&](int i, const f32x4 (&buf)[U]) {
-    const int sq = i / nbat, b = i % nbat;
-    const size_t pair = (size_t)(s0 + sq) * H + h;
-    float* Sp = S + pair * m * dv;
-    const float* pq = aq + sq * m;
-    const float* pk = ak + sq * m;
-    f32x4 vv;
-    const T* vs = v + pair * dv + col4 * 4;
+      for (int i = 0; i < DH / 4; ++i) {
+        const f32x4 tq = xq[i], tk = xk[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = to_f(vs[j]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = b * rows_per_batch + u * rpp + row0;
-      if (r < m) {
-        const f32x4 st = buf[u] + pk[r] * vv;
-        acc += pq[r] * st;
-        *reinterpret_cast<f32x4*>(Sp + (size_t)r * dv + col4 * 4) = st;
+        for (int j = 0; j < 4; ++j) {
+          a0 += w[i][j] * tq[j];
+          a1 += w[i][j] * tk[j];
+        }
       }
-    }
-    if (b == nbat - 1) {  // the sequence is complete: park its numerator partial
-      *reinterpret_cast<f32x4*>(red + ((size_t)sq * kDecodeThreads + tid) * 4) = acc;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      a0 = (a0 + dpp<kDppXor1>(a0)) * wscale;
+      a1 = (a1 + dpp<kDppXor1>(a1)) * wscale;
+      if (r < m && half == 0) {
+        fq[g * m + r] = a0;
+        fk[g * m + r] = a1;
+      }
     }
   };
-  int i = 0;
-  for (; i + 1 < total; i += 2) {
-    load_batch(i + 1, bufB);
-    process(i, bufA);
-    if (i + 2 < total) load_batch(i + 2, bufA);
-    process(i + 1, bufB);
+  feature(f0, w0);
+  for (int r = f0 + kDecodeThreads / 2; r - f0 < m; r += kDecodeThreads / 2) {  // m > 256 only
+    f32x4 w[DH / 4];
+    const int rr = r < m ? r : m - 1;
+#pragma unroll
+    for (int i = 0; i < DH / 4; ++i)
+      w[i] = reinterpret_cast<const f32x4*>(omega + ((size_t)h * m + rr) * D + half * DH)[i];
+    feature(r, w);
   }
-  if (i < total) process(i, bufA);
+  __syncthreads();
+  // feature maps: keys the canonical exp(a - |k|^2/2)/sqrt(m) (the state is kept
+  // unstabilised), queries exp(a - max_r a), a per-row constant that cancels in the ratio
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    if (kind == 0) {
+      float mx = -INFINITY;
+      for (int r = tid; r < m; r += kDecodeThreads) mx = fmaxf(mx, fq[g * m + r]);
+      mx = wave_max(mx);
+      if (lane == 0) wred[g][0][wv] = mx;
+    }
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    float mx = 0.f;
+    if (kind == 0) {
+      mx = wred[g][0][0];
+#pragma unroll
+      for (int i = 1; i < NWV; ++i) mx = fmaxf(mx, wred[g][0][i]);
+    }
+    const float kbg = wred[g][1][0];
+    for (int r = tid; r < m; r += kDecodeThreads) {
+      if (kind == 0) {
+        fq[g * m + r] = fast_exp2(fq[g * m + r] - mx);
+        fk[g * m + r] = fast_exp2(fk[g * m + r] - kbg);
+      } else {
+        fq[g * m + r] = fmaxf(fq[g * m + r], 0.f) * inv_sqrt_m + eps;
+        fk[g * m + r] = fmaxf(fk[g * m + r], 0.f) * inv_sqrt_m + eps;
+      }
+    }
+  }
+  __syncthreads();
+
+  // z and the denominators
+  float dpart[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    dpart[g] = 0.f;
+    float* zp = z + pair_of(g) * m;
+    for (int r = tid; r < m; r += kDecodeThreads) {
+      const float zn = zp[r] + fk[g * m + r];
+      if (g < ng) zp[r] = zn;
+      dpart[g] += fq[g * m + r] * zn;
+    }
+  }
+  // the state: S += phi(k) v^T, numerator += phi(q) . S
+  f32x4 acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < nbat; ++b) {
+    const int r0 = b * rows_per_batch + rg0 * U;
+    if (b > 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(row_ptr(g, r0 + u));
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* const p0 = row_ptr(g, r0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u;
+        if (r < m) {
+          const f32x4 st = buf[g][u] + fk[g * m + r] * vv[g];
+          acc[g] += fq[g * m + r] * st;
+          if (g < ng) *reinterpret_cast<f32x4*>(p0 + u * dv) = st;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    *reinterpret_cast<f32x4*>(red + ((size_t)g * kDecodeThreads + tid) * 4) = acc[g];
+    const float dp = wave_sum(dpart[g]);
+    if (lane == 0) wred[g][1][wv] = dp;
+  }
   __syncthreads();
   for (int o = tid; o < ng * dv; o += kDecodeThreads) {
-    const int sq = o / dv, col = o % dv;
+    const int g = o / dv, col = o % dv;
     const int cc = col / 4, ii = col % 4;
     float num = 0.f;
-    for (int rg = 0; rg < rpp; ++rg) num += red[((size_t)sq * kDecodeThreads + rg * tpr + cc) * 4 + ii];
+    for (int rg = 0; rg < rgs; ++rg) num += red[((size_t)g * kDecodeThreads + rg * tpr + cc) * 4 + ii];
     float den = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeThreads / 64; ++w) den += dsum[sq][w];
-    out[((size_t)(s0 + sq) * H + h) * dv + col] = num / den;
+    for (int i = 0; i < NWV; ++i) den += wred[g][1][i];
+    out[pair_of(g) * dv + col] = num / den;
   }
 }
 
 template <typename T, int D>
 static hipError_t run_decode(const T* q, const T* k, const T* v, const float* omega, float* S, float* z, int N, int H,
                              int dv, int m, int kind, float eps, float* out, hipStream_t st) {
-  const int G = kDecodeGroup;
-  const int n_groups = (N + G - 1) / G;
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == 0) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
   const float log2_sqrt_m = 0.5f * std::log2((float)m);
   const float inv_sqrt_m = 1.0f / std::sqrt((float)m);
-  const size_t lds = (size_t)(2 * G * m + 2 * G * D + G * kDecodeThreads * 4 + G * 4) * sizeof(float);
+  const size_t lds =
+      (size_t)(2 * kDecodeSeqs * m + kDecodeSeqs * 2 * D + kDecodeSeqs * kDecodeThreads * 4) * sizeof(float);
+  if (N == 0) return hipSuccess;
+  const size_t n_grp = ((size_t)N + kDecodeSeqs - 1) / kDecodeSeqs;
   {
     FAVOR_TIMED("decode", st);
-    decode_kernel<T, D><<<(unsigned)(H * n_groups), kDecodeThreads, lds, st>>>(
-        q, k, v, omega, S, z, N, H, dv, m, n_groups, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, out);
+    decode_kernel<T, D><<<(unsigned)(n_grp * H), kDecodeThreads, lds, st>>>(
+        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, out);
   }
   return hipGetLastError();
 }
