@@ -459,13 +459,27 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
     const int c = lane & 15, g = lane >> 4;
     f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
     if (nb < NB - 1 || c == 0) {
-      for (int k = 0; k < np; ++k) {
-        const size_t slot = (size_t)(i_lo + k) + bh;
-        const float sc = (kind == kPrf) ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f;
-        const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
-                                         : zpart + ((slot * NFC + fc) * 4 + g) * 8;
-        lo += reinterpret_cast<const f32x4*>(src)[0] * sc;
-        hi += reinterpret_cast<const f32x4*>(src)[1] * sc;
+      // KP partials at a time, all loads issued before the sums (a slot past the last piece
+      // is read as the last one and weighted 0)
+      constexpr int KP = 8;
+      for (int k0 = 0; k0 < np; k0 += KP) {
+        f32x4 pl[KP], ph[KP];
+        float sc[KP];
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+          const int k = k0 + j < np ? k0 + j : np - 1;
+          const size_t slot = (size_t)(i_lo + k) + bh;
+          sc[j] = k0 + j < np ? ((kind == kPrf) ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f) : 0.f;
+          const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
+                                           : zpart + ((slot * NFC + fc) * 4 + g) * 8;
+          pl[j] = reinterpret_cast<const f32x4*>(src)[0];
+          ph[j] = reinterpret_cast<const f32x4*>(src)[1];
+        }
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+          lo += pl[j] * sc[j];
+          hi += ph[j] * sc[j];
+        }
       }
     }
     vec8<C> o;
