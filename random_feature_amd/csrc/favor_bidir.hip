@@ -197,7 +197,8 @@ __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<type
 //               accumulators start at -(n'_t + M) (n'_t = log2e |x_t|^2/2, M the wave's
 //               running key maximum) so the MFMA output is already the stabilised exponent
 //   stabilises  if the tile maximum exceeds 0 (or on the first tile of a (b,h)), shift M
-//               and rescale the accumulated S_aug by the same power of two
+//               to kKeyMargin above it and rescale the accumulated S_aug by the same
+//               power of two
 //   maps        Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps), rounded to the contraction type
 //   contracts   S_aug += Phi^T [V 1]: A = Phi^T (paired token slots, the accumulators as
 //               they are), B = the value fragments
@@ -207,6 +208,10 @@ __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<type
 // of the K rows of tile t+2 and the next copies. The stabiliser of tile t (whose projection
 // is complete) comes first, so tile t+1 is projected against the current maximum. Tiles
 // stream through an R-slot asynchronous ring R-1 ahead; two K buffers; one barrier per tile.
+// Headroom (log2 units) the key stabiliser leaves below its running maximum: the largest
+// feature after a shift is 2^-8, far above the bottom of the fp32/bf16 range.
+constexpr float kKeyMargin = 8.f;
+
 template <typename T, int D, int DV, int M, int R, int KIND>
 __global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
@@ -355,20 +360,21 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 #pragma unroll
           for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, pcur[tb][fb][i]);
       // the running maximum moves only if some exponent is positive (or on a new (b,h))
+      // it moves kKeyMargin past the tile maximum, so later tiles seldom move it again
       if (first || __builtin_amdgcn_ballot_w64(lmax > 0.f) != 0) {
-        const float tmax = wave_max(lmax);
+        const float shift = wave_max(lmax) + kKeyMargin;
         if (!first) {
-          const float sc = fast_exp2(-tmax);
+          const float sc = fast_exp2(-shift);
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] *= sc;
         }
-        runmax = first ? tmax : runmax + tmax;
+        runmax = first ? shift : runmax + shift;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int fb = 0; fb < FB; ++fb) pcur[tb][fb] -= tmax;
+          for (int fb = 0; fb < FB; ++fb) pcur[tb][fb] -= shift;
         first = false;
       }
     }

@@ -31,7 +31,19 @@ namespace favor {
 #define FAVOR_DECODE_ROWS 8
 #endif
 constexpr int kDecodeThreads = FAVOR_DECODE_THREADS;
+#ifndef FAVOR_DECODE_NT
+#define FAVOR_DECODE_NT 1
+#endif
 constexpr int kDecodeRows = FAVOR_DECODE_ROWS;  // state rows (16 bytes each) a thread moves per sequence and batch
+// the state is streamed once per step: bit 0 marks its loads, bit 1 its stores non-temporal
+__device__ __forceinline__ f32x4 ld_state(const float* p) {
+  if constexpr (FAVOR_DECODE_NT & 1) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void st_state(float* p, const f32x4& x) {
+  if constexpr (FAVOR_DECODE_NT & 2) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+  else *reinterpret_cast<f32x4*>(p) = x;
+}
 constexpr int kDecodeSeqs = 1;                  // sequences of one head per workgroup (they share Omega's rows)
 
 // One workgroup per (head, group of kDecodeSeqs sequences); every thread owns 4 columns of
@@ -108,10 +120,10 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     if (r0 + U <= m) {
       const float* p0 = row_ptr(g, r0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(p0 + u * dv);
+      for (int u = 0; u < U; ++u) buf[g][u] = ld_state(p0 + u * dv);
     } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(row_ptr(g, r0 + u));
+      for (int u = 0; u < U; ++u) buf[g][u] = ld_state(row_ptr(g, r0 + u));
     }
   }
   __syncthreads();
@@ -213,7 +225,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int u = 0; u < U; ++u) buf[g][u] = *reinterpret_cast<const f32x4*>(row_ptr(g, r0 + u));
+        for (int u = 0; u < U; ++u) buf[g][u] = ld_state(row_ptr(g, r0 + u));
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -224,7 +236,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
         if (r < m) {
           const f32x4 st = buf[g][u] + fk[g * m + r] * vv[g];
           acc[g] += fq[g * m + r] * st;
-          if (g < ng) *reinterpret_cast<f32x4*>(p0 + u * dv) = st;
+          if (g < ng) st_state(p0 + u * dv, st);
         }
       }
     }
