@@ -7,26 +7,26 @@
 // This file keeps both properties: L is cut into P segments that run in parallel, the
 // segments are joined by a scan over their totals, and inside a segment the state is
 // carried sequentially from one 32-token chunk to the next, never materialising G^PS.
-//   1. omega_frag_kernel + reduce_kernel (shared with the bidirectional path):
-//      per-segment totals of S_aug = Phi_K^T [V 1] with the segment's key maxima.
+//   1. omega_frag_kernel, then kv_reduce_kernel (the bidirectional reduction) with one
+//      piece per (b*h, segment): the segment totals of S_aug = Phi_K^T [V 1] in MFMA
+//      fragment layout, with the waves' key maxima.
 //   2. scan_kernel: prefix maxima M*_p over segments and the exclusive prefix sums
-//      carry_p = sum_{q<p} total_q * 2^(M_q - M*_p); optionally the final state in
-//      canonical (unstabilised) scale.
-//   3. sweep_kernel, one workgroup per (segment, b*h), wave w owning FB*16 features:
-//      per chunk of 32 tokens
-//        * Q and K projections transposed (lane = token): Phi_Q with the row max
-//          taken across all waves, Phi_K = 2^(a' - n' - M*_p);
-//        * A^T = Phi_K Phi_Q^T over the wave's features (the intra-chunk scores) and
-//          the inter-chunk term out^T = S_carry^T Phi_Q^T over the wave's features;
-//          the partial tiles of all waves are summed through LDS;
-//        * the intra-chunk term out^T += [V 1]^T tril(A)^T (keys <= queries);
-//        * the wave's carried rows: S_carry += Phi_K^T [V 1], where Phi_K^T in the
-//          row = feature layout comes from an exact MFMA product with an identity;
-//        * division by the z row and a coalesced store of the chunk.
+//      carry_p = sum_{q<p} total_q * 2^(M_q - M*_p) in the same layout; optionally the
+//      final state in canonical (unstabilised) scale.
+//   3. sweep_kernel, one workgroup per (b*h, segment), wave w owning a block of features
+//      with its rows of the carried state in registers; per chunk of 32 tokens
+//        * the key and query projections on MFMA (fp16 for bf16 inputs), keys against
+//          the fixed key maximum M*_p of the segment, queries against the per-row bound;
+//        * the carried term out^T = S_carry^T Phi_Q^T over the wave's features;
+//        * the state update S_carry += Phi_K^T [V 1];
+//        * the intra-chunk scores A^T = Phi_K Phi_Q^T over the wave's features (Phi_K
+//          transposed through LDS), masked to keys <= queries, and out^T += [V 1]^T A^T;
+//        * the waves' partial outputs summed through LDS, divided by the z row, stored.
 #include "favor_device.hpp"
 #include "favor_plan.hpp"
-#include "favor_timing.hpp"
 #include "favor_reduce.hpp"
+#include "favor_tiles.hpp"
+#include "favor_timing.hpp"
 
 #include <algorithm>
 #include <cmath>
@@ -34,358 +34,554 @@
 namespace favor {
 
 // ---------------------------------------------------------------- scan over segments
-// Grid (element chunks of 256, b*h): every thread scans one element of S_aug over the
-// segments; the prefix maxima (a few values per segment) are recomputed per workgroup.
-template <int DV, int M, int NW>
+// Grid b*h x (element chunks of 256), flattened: every thread scans one element of a segment partial
+// (fragment layout, see kv_reduce_kernel) over the segments of its (b,h). Element e of a
+// partial: e < NP: part[fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c];
+// e >= NP: zpart[fc][g][j] = z[fc*32 + 16(j>>2) + 4g + (j&3)] (c = lane & 15, g = lane >> 4).
+template <int DV, int M>
 __global__ void __launch_bounds__(256)
-scan_kernel(const float* __restrict__ part, const float* __restrict__ pmax, int nseg, int kind, float log2_sqrt_m,
-            float* __restrict__ carry, float* __restrict__ cmax, float* __restrict__ S_final,
-            float* __restrict__ z_final) {
-  constexpr int FPW = M / NW;
-  constexpr int W = DV + 1;
-  extern __shared__ float pre[];  // [nseg] prefix maxima
-  const int bh = blockIdx.y;
+scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
+            int nseg, int kind, float log2_sqrt_m, float* __restrict__ cpart, float* __restrict__ cz,
+            float* __restrict__ cmax, float* __restrict__ S_final, float* __restrict__ z_final) {
+  constexpr int NWR = RedSplit<M>::NW, FBR = RedSplit<M>::FB;
+  constexpr int NFC = (M + 31) / 32, NVB = DV / 16;
+  constexpr int NP = NFC * NVB * 512, NZ = NFC * 32;
+  constexpr int NBLK = (NP + NZ + 255) / 256;
+  extern __shared__ float pre[];  // [nseg] prefix maxima over segments and waves
+  const int bh = blockIdx.x / NBLK, blk = blockIdx.x % NBLK;
   if (threadIdx.x == 0) {
     float run = -INFINITY;
     for (int p = 0; p < nseg; ++p) {
+      const size_t slot = (size_t)bh * nseg + p;
       float mx = -INFINITY;
-      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, pmax[((size_t)bh * nseg + p) * NW + w]);
+      for (int w = 0; w < NWR; ++w) mx = fmaxf(mx, pmax[slot * NWR + w]);
       run = fmaxf(run, mx);
       pre[p] = (kind == kPrf) ? run : 0.f;
-      if (blockIdx.x == 0) cmax[(size_t)bh * nseg + p] = pre[p];
+      if (blk == 0) cmax[slot] = pre[p];
     }
   }
   __syncthreads();
-  const size_t base = (size_t)bh * nseg * M * W;
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= M * W) return;
-  const int wv = (e / W) / FPW;
+  const int e = blk * 256 + threadIdx.x;
+  if (e >= NP + NZ) return;
+  const bool isz = e >= NP;
+  int fc, col, g, j;
+  if (!isz) {
+    fc = e / (NVB * 512);
+    const int rest = e % (NVB * 512), nb = rest / 512, lane = (rest / 8) % 64;
+    j = rest % 8;
+    g = lane >> 4;
+    col = nb * 16 + (lane & 15);
+  } else {
+    const int ez = e - NP;
+    fc = ez / 32;
+    g = (ez / 8) % 4;
+    j = ez % 8;
+    col = DV;
+  }
+  const int r = fc * 32 + 16 * (j >> 2) + 4 * g + (j & 3);  // feature (row of S_aug)
+  const int wv = (fc * 32) / (FBR * 16);                    // the reducing wave that owned it
+  const float* src = isz ? zpart + (e - NP) : part + e;
+  float* dst = isz ? cz + (e - NP) : cpart + e;
+  const size_t stride = isz ? NZ : NP;
   float acc = 0.f, prev = 0.f;
   for (int p = 0; p < nseg; ++p) {
+    const size_t slot = (size_t)bh * nseg + p;
     const float mp = pre[p];
     if (p > 0) acc *= fast_exp2(prev - mp);
-    carry[base + (size_t)p * M * W + e] = acc;
-    const float sc = (kind == kPrf) ? fast_exp2(pmax[((size_t)bh * nseg + p) * NW + wv] - mp) : 1.f;
-    acc += part[base + (size_t)p * M * W + e] * sc;
+    dst[slot * stride] = acc;
+    const float sc = (kind == kPrf) ? fast_exp2(pmax[slot * NWR + wv] - mp) : 1.f;
+    acc += src[slot * stride] * sc;
     prev = mp;
   }
-  if (S_final) {
+  if (S_final && r < M) {
     const float canon = (kind == kPrf) ? acc * fast_exp2(prev - log2_sqrt_m) : acc;
-    const int r = e / W, n = e % W;
-    if (n < DV)
-      S_final[((size_t)bh * M + r) * DV + n] = canon;
+    if (!isz)
+      S_final[((size_t)bh * M + r) * DV + col] = canon;
     else
       z_final[(size_t)bh * M + r] = canon;
   }
 }
 
-// ---------------------------------------------------------------- chunk sweep
-template <typename T, int D, int DV, int M, int FB>
-__global__ void __launch_bounds__(64 * (M / (16 * FB)))
-sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ omf,
-             const float* __restrict__ carry, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
-             int kind, float eps, float inv_sqrt_m, float nscale, int out_f32, void* __restrict__ out) {
-  constexpr int NW = M / (16 * FB);
+// ---------------------------------------------------------------- sweep ring
+// One slot per 32-token chunk: Q rows, K rows, V rows, in 16-byte chunks copied
+// asynchronously (global_load_lds), chunk q of the slot by thread q mod NT. Q and K chunks
+// are XOR-swizzled by row (chunk cc of row r at position cc ^ (r mod CPR_X)) so that the
+// projection reads of 16 rows spread over the banks, and are converted in place to the
+// projection type by the thread that copied them; V rows are laid out as in Ring (so
+// value_frags reads them from slot + XC*16). Rows past L are copies of row L-1.
+template <typename T, int D, int DV, int NT>
+struct SweepRing {
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int CPR_X = D / EPC;
+  static constexpr int CPR_V = DV / EPC;
+  static constexpr int XC = 32 * CPR_X;
+  static constexpr int VC = 32 * CPR_V;
+  static constexpr int NCH = 2 * XC + VC;
+  static constexpr int CPT = (NCH + NT - 1) / NT;
+  static constexpr int SLOT = CPT * NT * 16;
+  static constexpr bool SWZ_V = sizeof(T) == 2;
+  static_assert((CPR_X & (CPR_X - 1)) == 0 && CPR_X <= 64, "rows of whole, power-of-two chunk counts");
+
+  static __device__ __forceinline__ int x_off(int x, int row, int cc) {
+    return (x * XC + row * CPR_X + (cc ^ (row & (CPR_X - 1)))) * 16;
+  }
+
+  static __device__ __forceinline__ void issue(const T* Q, const T* K, const T* V, int L, size_t rowbase, int tok0,
+                                               uint32_t slot) {
+    const int tid = threadIdx.x, w = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = u * NT + tid;
+      const void* src = Q + rowbase * D;  // filler for positions past the tile: a valid row
+      if (q < 2 * XC) {
+        const int x = q / XC, p = q % XC, row = p / CPR_X;
+        const int cc = (p % CPR_X) ^ (row & (CPR_X - 1));
+        src = (x == 0 ? Q : K) + (rowbase + min(tok0 + row, L - 1)) * D + cc * EPC;
+      } else if (q < NCH) {
+        const int p = q - 2 * XC, row = p / CPR_V, pc = p % CPR_V;
+        const int cc = SWZ_V ? (pc ^ (row & (CPR_V - 1))) : pc;
+        src = V + (rowbase + min(tok0 + row, L - 1)) * DV + cc * EPC;
+      }
+      lds_dma16(src, slot + (uint32_t)(u * NT + w * 64) * 16u);
+    }
+  }
+
+  // this thread's Q and K chunks of a landed slot, converted in place to P; per row
+  // qn = |q| * kQueryMargin and kn = |k|^2 * nscale (+inf for rows at or past nvalid)
+  template <typename P>
+  static __device__ __forceinline__ void convert(unsigned char* slot, float* qn, float* kn, float nscale,
+                                                 int nvalid) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int q = u * NT + threadIdx.x;
+      if (u * NT >= 2 * XC) break;  // no X chunks left (known at compile time)
+      const bool has = ((2 * XC) % NT == 0) || q < 2 * XC;
+      const int x = q / XC, row = (q % XC) / CPR_X;
+      float s2 = 0.f;
+      if (has) {
+        if constexpr (sizeof(T) == 2) {
+          const vec8<T> v8 = *reinterpret_cast<const vec8<T>*>(slot + q * 16);
+          vec8<P> y;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float f = to_f(v8[j]);
+            s2 += f * f;
+            y[j] = to_t<P>(f);
+          }
+          *reinterpret_cast<vec8<P>*>(slot + q * 16) = y;
+        } else {
+          const f32x4 v4 = *reinterpret_cast<const f32x4*>(slot + q * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s2 += v4[j] * v4[j];
+        }
+      }
+      s2 = lanes_sum<CPR_X>(s2);  // the CPR_X chunks of a row sit on consecutive lanes
+      if (has) {
+        if (x == 0)
+          qn[row] = __builtin_sqrtf(s2) * kQueryMargin;
+        else
+          kn[row] = row < nvalid ? s2 * nscale : INFINITY;
+      }
+    }
+  }
+
+  // 8 elements of row r of X (0: Q, 1: K) from column col (a multiple of 8), converted slot
+  template <typename P>
+  static __device__ __forceinline__ vec8<P> ld_x8(const unsigned char* slot, int x, int r, int col) {
+    if constexpr (sizeof(P) == 2) {
+      return *reinterpret_cast<const vec8<P>*>(slot + x_off(x, r, col / 8));
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(slot + x_off(x, r, col / 4));
+      const f32x4 b = *reinterpret_cast<const f32x4*>(slot + x_off(x, r, col / 4 + 1));
+      vec8<P> v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = a[j];
+        v[j + 4] = b[j];
+      }
+      return v;
+    }
+  }
+};
+
+// ---------------------------------------------------------------- sweep
+// Workgroup = NW waves on segment sp of (b,h) (piece pc = bh * nseg + sp); wave w owns the
+// FB*16 features [w*FB*16, (w+1)*FB*16), the same split as the reduction, so its rows of
+// the carried state arrive from the scan in its own fragment layout. The segment's keys
+// use the fixed maximum M*_sp of the scan (every key exponent of the segment is below it),
+// so the carry never needs rescaling. Per chunk t (ring slot t mod 3):
+//   barrier X (chunk t converted by every thread; the partial outputs of chunk t-1 written)
+//   the output of chunk t-1: the NW partials summed, divided by the z row, stored
+//   phase A (all in registers but the Phi_K transpose):
+//     K projection  A = K rows, B = Omega'         -> [token][feature] (start -(n'_k + M*))
+//     Q projection  A = Omega', B = Q rows         -> [feature][token] (start -b_q)
+//     features      Phi_K as A operand (paired token slots), Phi_Q as B operand (paired
+//                   feature slots), straight from the accumulators
+//     carried term  o^T[col][q]  = S^T (A, the state rows as they stand) x Phi_Q^T
+//     update        S_aug       += Phi_K^T (A) x [V 1] (B, transposing reads of V)
+//     scores        A^T[key][q]  = Phi_K (A, through LDS, per 32-feature chunk) x Phi_Q^T
+//     intra term    o^T         += [V 1]^T (A: the value fragments) x masked A^T (B)
+//   chunk t+1 lands and is converted in place by the threads that copied it
+//   barrier Y; the wave's partial o^T goes to LDS; chunk t+2 is copied into slot (t+2) mod 3
+template <typename T, int D, int DV, int M, int KIND>
+__global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
+sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+             const typename Ops<T>::P* __restrict__ omf, const float* __restrict__ cpart,
+             const float* __restrict__ cz, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
+             float eps, float inv_sqrt_m, float nscale, int out_f32, void* __restrict__ out) {
+  using P = typename Ops<T>::P;
+  using C = typename Ops<T>::C;
+  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NB = DV / 16 + 1;
-  constexpr int NFC = (FB + 1) / 2;
-  constexpr int KROW = D + 8, VROW = 40;
-  constexpr int NT = 4 + 2 * NB;
-  constexpr int OROW = DV + 4;
-  constexpr int W = DV + 1;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* qs = reinterpret_cast<T*>(smem);
-  T* ks = qs + 32 * KROW;
-  T* vts = ks + 32 * KROW;
-  constexpr size_t TILE_BYTES = ((2 * 32 * KROW + DV * VROW) * sizeof(T) + 15) & ~(size_t)15;
-  float* qmx = reinterpret_cast<float*>(smem + TILE_BYTES);
-  float* xch = qmx + NW * 32;
-  float* outs = xch + NW * NT * 256;
+  constexpr int NB = DV / 16 + 1;  // value-column blocks + the ones column
+  constexpr int NVB = DV / 16;
+  constexpr int NFC = (M + 31) / 32;
+  constexpr int NFCW = (FB + 1) / 2;  // 32-feature chunks of a wave
+  constexpr int R = 3;
+  constexpr int PROW = 36;              // row stride (elements) of the Phi_K transpose buffer
+  constexpr int XO = 2 * NVB * 256 + 32;  // floats of one wave's partial output
+  static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
+  using Rg = SweepRing<T, D, DV, NT>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) float xo[NW][XO];
+  __shared__ __attribute__((aligned(16))) C phk[NW][32 * PROW];
+  __shared__ __attribute__((aligned(16))) float kn[R][32];
+  __shared__ __attribute__((aligned(16))) float qn[R][32];
+  __shared__ __attribute__((aligned(16))) float qmx[NW][32];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int seg = blockIdx.x, bh = blockIdx.y, h = bh % H;
-  const int tbeg = seg * seg_len, tend = min(L, tbeg + seg_len);
+  const int pc = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = pc / nseg, sp = pc % nseg, h = bh % H;
+  const int t0 = sp * seg_len, tend = min(t0 + seg_len, L);
+  const int n = (tend - t0 + 31) / 32;
   const size_t rowbase = (size_t)bh * L;
-  const T* Qb = Q + rowbase * D;
-  const T* Kb = K + rowbase * D;
-  const T* Vb = V + rowbase * DV;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
 
-  vec8<T> om[FB][DC];
+  // chunks 0 and 1 in flight
+  Rg::issue(Q, K, V, L, rowbase, t0, ring0);
+  if (n > 1) Rg::issue(Q, K, V, L, rowbase, t0 + 32, ring0 + Rg::SLOT);
+
+  vec8<P> om[FB][DC];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<T>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
-
-  // carried state for this wave's rows, C layout: sacc[fb][nb][i] = S_aug[row 4g+i of block][col nb*16+c]
+      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+  // the wave's rows of the carry (fragment layout of the reduction's partials)
   f32x4 sacc[FB][NB];
-  {
-    const float* cp = carry + ((size_t)bh * nseg + seg) * M * W;
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+  for (int p = 0; p < NFCW; ++p) {
+    const int fc = (w * FB) / 2 + p;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = (w * FB + fb) * 16 + 4 * g + i;
-#pragma unroll
-        for (int nb = 0; nb < NB - 1; ++nb) sacc[fb][nb][i] = cp[(size_t)r * W + nb * 16 + c];
-        sacc[fb][NB - 1][i] = (c == 0) ? cp[(size_t)r * W + DV] : 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+      if (nb < NB - 1) {
+        const float* src = cpart + ((((size_t)pc * NFC + fc) * NVB + nb) * 64 + lane) * 8;
+        lo = reinterpret_cast<const f32x4*>(src)[0];
+        hi = reinterpret_cast<const f32x4*>(src)[1];
+      } else if (c == 0) {
+        const float* src = cz + (((size_t)pc * NFC + fc) * 4 + g) * 8;
+        lo = reinterpret_cast<const f32x4*>(src)[0];
+        hi = reinterpret_cast<const f32x4*>(src)[1];
       }
-  }
-  const float mstar = cmax[(size_t)bh * nseg + seg];
-
-  vec8<T> ones, idb[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ones[j] = to_t<T>(c == 0 ? 1.f : 0.f);
-    const int kslot = 16 * (j >> 2) + 4 * g + (j & 3);
-    idb[0][j] = to_t<T>(kslot == c ? 1.f : 0.f);
-    idb[1][j] = to_t<T>(kslot == 16 + c ? 1.f : 0.f);
-  }
-
-  for (int t0 = tbeg; t0 < tend; t0 += 32) {
-    // ---- stage Q, K (row major) and V (transposed, token pairs) in LDS
-    constexpr int XCH8 = 32 * D / 8;
-    for (int q = threadIdx.x; q < 2 * XCH8; q += NW * 64) {
-      const int which = q / XCH8, qq = q % XCH8;
-      const int row = qq / (D / 8), col = (qq % (D / 8)) * 8;
-      const T* src = which == 0 ? Qb : Kb;
-      const vec8<T> x = (t0 + row < tend) ? ld8<T>(src + (size_t)(t0 + row) * D + col) : zero8<T>();
-      st8<T>((which == 0 ? qs : ks) + row * KROW + col, x);
+      sacc[2 * p][nb] = lo;
+      if (2 * p + 1 < FB) sacc[2 * p + 1][nb] = hi;
     }
-    constexpr int VCH = 16 * (DV / 8);
-    for (int q = threadIdx.x; q < VCH; q += NW * 64) {
-      const int tp = q / (DV / 8), col = (q % (DV / 8)) * 8;
-      const int t = t0 + 2 * tp;
-      const vec8<T> a = (t < tend) ? ld8<T>(Vb + (size_t)t * DV + col) : zero8<T>();
-      const vec8<T> b = (t + 1 < tend) ? ld8<T>(Vb + (size_t)(t + 1) * DV + col) : zero8<T>();
+  }
+  const float mk = (KIND == kPrf) ? cmax[pc] : 0.f;
+  float omax = 0.f;
+  if constexpr (KIND == kPrf) omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
+  wait_vmcnt<0>();
+  Rg::template convert<P>(ring[0], qn[0], kn[0], nscale, tend - t0);
+
+  // the summed partial outputs of chunk tc: divided by the z row and stored
+  auto store_chunk = [&](int tc) {
+    constexpr int C8 = DV / 8;
+    const int tok0 = t0 + 32 * tc;
+    for (int e = threadIdx.x; e < 32 * C8; e += NT) {
+      const int qrow = e / C8, c8 = e % C8;
+      const int tok = tok0 + qrow;
+      if (tok >= tend) continue;
+      const int tb = qrow >> 4, cq = qrow & 15;
+      const int cb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+      float den = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        vec2<T> pr;
-        pr[0] = a[e];
-        pr[1] = b[e];
-        *reinterpret_cast<vec2<T>*>(vts + (col + e) * VROW + 2 * tp) = pr;
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* base = &xo[ww][((tb * NVB + cb) * 64 + cq + 16 * g0) * 4];
+        lo += *reinterpret_cast<const f32x4*>(base);
+        hi += *reinterpret_cast<const f32x4*>(base + 64);
+        den += xo[ww][2 * NVB * 256 + tb * 16 + cq];
+      }
+      const float rden = 1.0f / den;
+      const size_t off = (rowbase + tok) * DV + c8 * 8;
+      if (out_f32) {
+        f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off);
+        o4[0] = lo * rden;
+        o4[1] = hi * rden;
+      } else {
+        vec8<T> r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r[i] = to_t<T>(lo[i] * rden);
+          r[i + 4] = to_t<T>(hi[i] * rden);
+        }
+        st8<T>(reinterpret_cast<T*>(out) + off, r);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- projections (transposed: A = Omega' rows, B = X^T) -> [feature 4g+i][token c]
-    f32x4 pq[2][FB], pk[2][FB];
-    float knorm[2];
+  int s_cur = 0;
+  for (int t = 0; t < n; ++t) {
+    const int s_nx = s_cur + 1 == R ? 0 : s_cur + 1;
+    const int s_is = s_nx + 1 == R ? 0 : s_nx + 1;
+    lds_barrier();  // X
+    if (t > 0) store_chunk(t - 1);
+
+    const unsigned char* sl = ring[s_cur];
+    const int tok0 = t0 + 32 * t;
+    // ---- projections
+    f32x4 pk[2][FB], pq[2][FB];
+    bool exact = false;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      vec8<T> qf[DC], kf[DC];
-      float s2 = 0.f;
+      f32x4 kbias = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KIND == kPrf) {
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[s_cur][tb * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kbias[i] = -(n4[i] + mk);
+      }
+      const float b = (KIND == kPrf) ? qn[s_cur][tb * 16 + c] * omax : 0.f;
+      if constexpr (KIND == kPrf) exact |= b > kQueryBoundLimit;
+      vec8<P> kf[DC], qf[DC];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const int col = dc * 32 + 8 * g;
-        qf[dc] = (col < D) ? ld8<T>(qs + (tb * 16 + c) * KROW + col) : zero8<T>();
-        kf[dc] = (col < D) ? ld8<T>(ks + (tb * 16 + c) * KROW + col) : zero8<T>();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = to_f(kf[dc][j]);
-          s2 += x * x;
-        }
+        kf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 1, tb * 16 + c, col) : zero8<P>();
+        qf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 0, tb * 16 + c, col) : zero8<P>();
       }
-      knorm[tb] = group_sum(s2) * nscale;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        pq[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pk[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pk[tb][fb] = kbias;
+        pq[tb][fb] = f32x4{-b, -b, -b, -b};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
+          mma16(pk[tb][fb], kf[dc], om[fb][dc]);
           mma16(pq[tb][fb], om[fb][dc], qf[dc]);
-          mma16(pk[tb][fb], om[fb][dc], kf[dc]);
+        }
+      }
+    }
+    if constexpr (KIND == kPrf) {
+      if (__builtin_amdgcn_ballot_w64(exact) != 0) {  // the same in every wave
+        // rare: shift every query row by its exact maximum, taken across the waves
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
+          mx = group_max(mx);
+          if (g == 0) qmx[w][tb * 16 + c] = mx;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          float mx = qmx[0][tb * 16 + c];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb) pq[tb][fb] -= mx;
         }
       }
     }
     // ---- feature maps
-    if (kind == kPrf) {
+    vec8<C> af[FB];        // Phi_K^T: A operand [feature][token], paired token slots
+    vec8<C> bq[2][NFCW];   // Phi_Q^T: B operand [feature][query], paired feature slots
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float mx = -INFINITY;
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
-        mx = group_max(mx);
-        if (g == 0) qmx[w * 32 + tb * 16 + c] = mx;
-        const bool ok = t0 + tb * 16 + c < tend;
-        const float sub = knorm[tb] + mstar;
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk[tb][fb][i] = ok ? fast_exp2(pk[tb][fb][i] - sub) : 0.f;
+      for (int j = 0; j < 8; ++j) {
+        const float a = pk[j >> 2][fb][j & 3];
+        float f;
+        if constexpr (KIND == kPrf) {
+          f = fast_exp2(a);  // rows past the segment carry an infinite norm: exp2(-inf) = 0
+        } else {
+          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < tend;
+          f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
+        }
+        af[fb][j] = to_t<C>(f);
       }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const bool ok = t0 + tb * 16 + c < tend;
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pk[tb][fb][i] = ok ? fmaxf(pk[tb][fb][i], 0.f) * inv_sqrt_m + eps : 0.f;
-            pq[tb][fb][i] = fmaxf(pq[tb][fb][i], 0.f) * inv_sqrt_m + eps;
-          }
-      }
-    }
-    __syncthreads();
-    if (kind == kPrf) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww * 32 + tb * 16 + c]);
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pq[tb][fb][i] = fast_exp2(pq[tb][fb][i] - mx);
-      }
-    }
-    // operand fragments with paired feature slots: lane = token c
-    vec8<T> fq[2][NFC], fk[2][NFC];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int fc = 0; fc < NFC; ++fc)
+      for (int fcw = 0; fcw < NFCW; ++fcw)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int fb = 2 * fc + (j >> 2);
-          const int fbs = fb < FB ? fb : 0;
-          fq[tb][fc][j] = to_t<T>(fb < FB ? pq[tb][fbs][j & 3] : 0.f);
-          fk[tb][fc][j] = to_t<T>(fb < FB ? pk[tb][fbs][j & 3] : 0.f);
+          const int fb = 2 * fcw + (j >> 2);
+          float f = 0.f;
+          if (fb < FB) {
+            const float a = pq[tb][fb][j & 3];
+            f = (KIND == kPrf) ? fast_exp2(a) : fmaxf(a, 0.f) * inv_sqrt_m + eps;
+          }
+          bq[tb][fcw][j] = to_t<C>(f);
         }
-
-    // ---- partial tiles over this wave's features -> LDS
-    float* xw = xch + (size_t)w * NT * 256;
+    // ---- carried term, before the state takes this chunk
+    f32x4 o[NB][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int cb = 0; cb < NB; ++cb) {
+      o[cb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o[cb][1] = o[cb][0];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int fcw = 0; fcw < NFCW; ++fcw) {
+        vec8<C> sa;
 #pragma unroll
-        for (int fc = 0; fc < NFC; ++fc) mma16(a, fk[kt][fc], fq[qt][fc]);
-        *reinterpret_cast<f32x4*>(xw + (kt * 2 + qt) * 256 + lane * 4) = a;
-      }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      vec8<T> sf[NFC];
-#pragma unroll
-      for (int fc = 0; fc < NFC; ++fc)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int fb = 2 * fc + (j >> 2);
-          sf[fc][j] = to_t<T>(fb < FB ? sacc[fb < FB ? fb : 0][nb][j & 3] : 0.f);
+        for (int j = 0; j < 4; ++j) {
+          sa[j] = to_t<C>(sacc[2 * fcw][cb][j]);
+          sa[j + 4] = (2 * fcw + 1 < FB) ? to_t<C>(sacc[2 * fcw + 1][cb][j]) : to_t<C>(0.f);
         }
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int fc = 0; fc < NFC; ++fc) mma16(o, sf[fc], fq[qt][fc]);
-        *reinterpret_cast<f32x4*>(xw + (4 + qt * NB + nb) * 256 + lane * 4) = o;
+        mma16(o[cb][0], sa, bq[0][fcw]);
+        mma16(o[cb][1], sa, bq[1][fcw]);
       }
     }
-
-    // ---- value fragments (paired token slots), shared by the update and the intra term
-    vec8<T> vf[NB];
+    // ---- state update
+    vec8<C> vf[NB];
+    value_frags<T, D, DV, NT>(sl + Rg::XC * 16, vf, c, g);
 #pragma unroll
-    for (int nb = 0; nb < NB - 1; ++nb) {
-      const T* row = vts + (nb * 16 + c) * VROW;
-      const vec4<T> lo = *reinterpret_cast<const vec4<T>*>(row + 4 * g);
-      const vec4<T> hi = *reinterpret_cast<const vec4<T>*>(row + 16 + 4 * g);
+    for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[nb][j] = lo[j];
-        vf[nb][j + 4] = hi[j];
-      }
-    }
-    vf[NB - 1] = ones;
-
-    // ---- carried rows: S_carry += Phi_K^T [V 1]; Phi_K^T (row = feature) via identity products
+      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af[fb], vf[nb]);
+    // ---- intra-chunk scores A^T[key][query] over this wave's features
+    f32x4 sc[2][2];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) {
-      f32x4 tr[2];
+    for (int kb = 0; kb < 2; ++kb) sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    C* ph = &phk[w][0];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        tr[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma16(tr[tb], fk[tb][fb >> 1], idb[fb & 1]);
-      }
-      vec8<T> afk;
+    for (int fcw = 0; fcw < NFCW; ++fcw) {
+      // Phi_K rows (features) of this 32-feature chunk, [feature][token] (wave-private: the
+      // wave's own LDS operations complete in order)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) afk[j] = to_t<T>(tr[j >> 2][j & 3]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], afk, vf[nb]);
-    }
-    __syncthreads();
-
-    // ---- sum the intra scores over waves, mask keys > query: B fragments (k = key, n = query)
-    vec8<T> atf[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) a += *reinterpret_cast<const f32x4*>(xch + ((size_t)ww * NT + kt * 2 + qt) * 256 + lane * 4);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int fb = 2 * fcw + hh;
+        vec4<C> lo4, hi4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kt * 16 + 4 * g + i, qry = qt * 16 + c;
-          atf[qt][kt * 4 + i] = to_t<T>(key <= qry ? a[i] : 0.f);
+          lo4[i] = fb < FB ? af[fb][i] : to_t<C>(0.f);
+          hi4[i] = fb < FB ? af[fb][i + 4] : to_t<C>(0.f);
         }
+        *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * PROW + 4 * g) = lo4;
+        *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * PROW + 16 + 4 * g) = hi4;
       }
-    }
-    // ---- output tiles owned by this wave: sum of inter partials + intra product
-    for (int t = w; t < 2 * NB; t += NW) {
-      const int qt = t / NB, nb = t % NB;
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) o += *reinterpret_cast<const f32x4*>(xch + ((size_t)ww * NT + 4 + qt * NB + nb) * 256 + lane * 4);
-      mma16(o, vf[nb], atf[qt]);
-      // o[i] = out^T[col nb*16 + 4g + i][query qt*16 + c]
-      if (nb < NB - 1) {
-        *reinterpret_cast<f32x4*>(outs + (qt * 16 + c) * OROW + nb * 16 + 4 * g) = o;
-      } else if (g == 0) {
-        outs[(qt * 16 + c) * OROW + DV] = o[0];
-      }
-    }
-    __syncthreads();
-
-    // ---- normalise and store the chunk (coalesced rows)
-    constexpr int C4 = DV / 4;
-    for (int e = threadIdx.x; e < 32 * C4; e += NW * 64) {
-      const int qrow = e / C4, c4 = e % C4;
-      const int tok = t0 + qrow;
-      if (tok < tend) {
-        const float rden = 1.0f / outs[qrow * OROW + DV];
-        const f32x4 o = *reinterpret_cast<const f32x4*>(outs + qrow * OROW + c4 * 4);
-        const size_t off = (rowbase + tok) * DV + c4 * 4;
-        if (out_f32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o * rden;
+      for (int kb = 0; kb < 2; ++kb) {
+        vec8<C> ka;  // A operand [key][feature]: Phi_K of key kb*16 + c, paired feature slots
+        if constexpr (sizeof(C) == 2) {
+          const bf16x4 lo = lds_read_tr4(reinterpret_cast<const bf16*>(ph + (4 * g + (c >> 2)) * PROW + kb * 16 + 4 * (c & 3)));
+          const bf16x4 hi = lds_read_tr4(reinterpret_cast<const bf16*>(ph + (16 + 4 * g + (c >> 2)) * PROW + kb * 16 + 4 * (c & 3)));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ka[i] = lo[i];
+            ka[i + 4] = hi[i];
+          }
         } else {
-          vec4<T> r;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = to_t<T>(o[i] * rden);
-          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(out) + off) = r;
+          for (int jj = 0; jj < 8; ++jj) ka[jj] = ph[(16 * (jj >> 2) + 4 * g + (jj & 3)) * PROW + kb * 16 + c];
         }
+        mma16(sc[kb][0], ka, bq[0][fcw]);
+        mma16(sc[kb][1], ka, bq[1][fcw]);
       }
     }
+    // ---- masked scores as B [key][query] (paired key slots) and the intra term
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      vec8<C> sb;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int kb = jj >> 2, i = jj & 3;
+        const int key = kb * 16 + 4 * g + i, qry = tb * 16 + c;
+        sb[jj] = to_t<C>(key <= qry ? sc[kb][tb][i] : 0.f);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) mma16(o[cb][tb], vf[cb], sb);
+    }
+
+    // ---- chunk t+1 lands and is converted
+    if (t + 1 < n) {
+      wait_vmcnt<0>();  // its copies, and the stores of chunk t-1
+      Rg::template convert<P>(ring[s_nx], qn[s_nx], kn[s_nx], nscale, tend - tok0 - 32);
+    }
+    lds_barrier();  // Y: slot s_is and the partial outputs of chunk t-1 are no longer read
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+      for (int cb = 0; cb < NVB; ++cb)
+        *reinterpret_cast<f32x4*>(&xo[w][((tb * NVB + cb) * 64 + lane) * 4]) = o[cb][tb];
+      if (g == 0) xo[w][2 * NVB * 256 + tb * 16 + c] = o[NB - 1][tb][0];
+    }
+    if (t + 2 < n) Rg::issue(Q, K, V, L, rowbase, tok0 + 64, ring0 + s_is * Rg::SLOT);
+    s_cur = s_nx;
   }
+  lds_barrier();
+  store_chunk(n - 1);
+}
+
+// ---------------------------------------------------------------- host side
+static void segmenting(const Shape& s, int& nseg, int& seg_len) {
+  // enough segments for ~512 workgroups, but at least 256 tokens each
+  const long long bh = s.bh();
+  const int max_seg = std::max(1, (s.L + 255) / 256);
+  const int want = (int)std::max(1LL, (512 + bh - 1) / bh);
+  nseg = std::min(max_seg, want);
+  seg_len = (s.L + nseg - 1) / nseg;
+  seg_len = (seg_len + 31) / 32 * 32;
+  nseg = (s.L + seg_len - 1) / seg_len;
+}
+
+CausalPlan plan_causal(const Shape& s, int dtype) {
+  CausalPlan p;
+  segmenting(s, p.nseg, p.seg_len);
+  p.tpb = (s.L + 31) / 32;
+  p.T_all = s.bh() * p.tpb;
+  p.G = (int)(s.bh() * p.nseg);
+  p.nw_reduce = reduce_waves(s.m);
+  const int dc = (s.d + 31) / 32;
+  const size_t nfc = (s.m + 31) / 32, G = (size_t)p.G;
+  size_t off = 0;
+  p.off_omf = off;
+  off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
+  p.off_part = off;
+  off = align256(off + G * nfc * (s.dv / 16) * 512 * 4);
+  p.off_zpart = off;
+  off = align256(off + G * nfc * 32 * 4);
+  p.off_pmax = off;
+  off = align256(off + G * p.nw_reduce * 4);
+  p.off_cpart = off;
+  off = align256(off + G * nfc * (s.dv / 16) * 512 * 4);
+  p.off_cz = off;
+  off = align256(off + G * nfc * 32 * 4);
+  p.off_cmax = off;
+  off = align256(off + G * 4);
+  p.total = off;
+  return p;
 }
 
 template <typename T, int D, int DV, int M>
 static hipError_t run_causal(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int kind,
                              float eps, int out_f32, void* out, float* S_final, float* z_final, void* ws,
                              hipStream_t st) {
-  constexpr int FB = (M / 16) < 4 ? (M / 16) : 4;
-  constexpr int NW = M / (16 * FB);
-  constexpr int DC = (D + 31) / 32, NB = DV / 16 + 1;
+  using P = typename Ops<T>::P;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NWR = RedSplit<M>::NW;
   const CausalPlan p = plan_causal(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
-  T* omf = reinterpret_cast<T*>(base + p.off_omf);
+  P* omf = reinterpret_cast<P*>(base + p.off_omf);
   float* part = reinterpret_cast<float*>(base + p.off_part);
+  float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
-  float* carry = reinterpret_cast<float*>(base + p.off_carry);
+  float* cpart = reinterpret_cast<float*>(base + p.off_cpart);
+  float* cz = reinterpret_cast<float*>(base + p.off_cz);
   float* cmax = reinterpret_cast<float*>(base + p.off_cmax);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
@@ -396,34 +592,33 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   {
     FAVOR_TIMED("omega_frag", st);
-    omega_frag_kernel<T><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
         omega, s.H, M, D, wscale, omf);
   }
   {
     FAVOR_TIMED("reduce", st);
-    reduce_kernel<T, D, DV, M, FB><<<dim3(p.nseg, (unsigned)s.bh()), 64 * NW, 0, st>>>(
-        k, v, omf, s.H, s.L, p.seg_len, p.nseg, kind, eps, inv_sqrt_m, nscale, part, pmax);
+    const int seg_tiles = p.seg_len / 32;
+    if (kind == kPrf)
+      kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(
+          k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
+    else
+      kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(
+          k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
   }
   {
     FAVOR_TIMED("scan", st);
-    scan_kernel<DV, M, NW><<<dim3((unsigned)((M * (DV + 1) + 255) / 256), (unsigned)s.bh()), 256,
-                             p.nseg * sizeof(float), st>>>(
-        part, pmax, p.nseg, kind, log2_sqrt_m, carry, cmax, S_final, z_final);
-  }
-  constexpr int KROW = D + 8, VROW = 40, NT = 4 + 2 * NB, OROW = DV + 4;
-  const size_t lds = (((2 * 32 * KROW + DV * VROW) * sizeof(T) + 15) & ~(size_t)15) +
-                     (size_t)(NW * 32 + NW * NT * 256 + 32 * OROW) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel<T, D, DV, M, FB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+    constexpr int NEL = ((M + 31) / 32) * ((DV / 16) * 512 + 32);
+    scan_kernel<DV, M><<<(unsigned)(s.bh() * ((NEL + 255) / 256)), 256, p.nseg * sizeof(float), st>>>(
+        part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final, z_final);
   }
   {
     FAVOR_TIMED("sweep", st);
-    sweep_kernel<T, D, DV, M, FB><<<dim3(p.nseg, (unsigned)s.bh()), 64 * NW, lds, st>>>(
-        q, k, v, omf, carry, cmax, s.H, s.L, p.seg_len, p.nseg, kind, eps, inv_sqrt_m, nscale, out_f32, out);
+    if (kind == kPrf)
+      sweep_kernel<T, D, DV, M, kPrf><<<p.G, 64 * NWR, 0, st>>>(q, k, v, omf, cpart, cz, cmax, s.H, s.L, p.seg_len,
+                                                                p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
+    else
+      sweep_kernel<T, D, DV, M, kRelu><<<p.G, 64 * NWR, 0, st>>>(q, k, v, omf, cpart, cz, cmax, s.H, s.L, p.seg_len,
+                                                                 p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
   }
   return hipGetLastError();
 }

@@ -26,6 +26,16 @@ struct Shape {
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t elt(int dtype) { return dtype == 0 ? 4 : 2; }
+
+// Waves of the key/value reduction for m features (at most FAVOR_REDUCE_WAVES, at least 32
+// features each); the device-side split (RedSplit) follows the same rule.
+#ifndef FAVOR_REDUCE_WAVES
+#define FAVOR_REDUCE_WAVES 4
+#endif
+inline int reduce_waves(int m) {
+  return m < 32 ? 1 : ((m / 32) < FAVOR_REDUCE_WAVES ? (m / 32) : FAVOR_REDUCE_WAVES);
+}
 
 // Bidirectional path: omega fragments, per-segment partial (S, z) sums with their
 // stabiliser maxima, and the combined S fragments.
@@ -37,10 +47,14 @@ struct BidirPlan {
   size_t off_omf = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_sfr = 0, total = 0;
 };
 
-// Causal path: the bidirectional pieces for segment totals plus carried states.
+// Causal path: Omega fragments, one partial (S, z) sum per (b*h, segment) in MFMA fragment
+// layout with its stabiliser maxima, the exclusive prefix over segments (carries) in the same
+// layout, and the carries' common key maxima.
 struct CausalPlan {
-  int nseg = 0, seg_len = 0, nw_reduce = 0;
-  size_t off_omf = 0, off_part = 0, off_pmax = 0, off_carry = 0, off_cmax = 0, total = 0;
+  int nseg = 0, seg_len = 0, tpb = 0, G = 0, nw_reduce = 0;
+  long long T_all = 0;
+  size_t off_omf = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_cpart = 0, off_cz = 0, off_cmax = 0,
+         total = 0;
 };
 
 bool shape_built(int dtype, int d, int dv, int m);
