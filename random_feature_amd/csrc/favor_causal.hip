@@ -34,10 +34,12 @@
 namespace favor {
 
 // ---------------------------------------------------------------- scan over segments
-// Grid b*h x (element chunks of 256), flattened: every thread scans one element of a segment partial
-// (fragment layout, see kv_reduce_kernel) over the segments of its (b,h). Element e of a
-// partial: e < NP: part[fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c];
-// e >= NP: zpart[fc][g][j] = z[fc*32 + 16(j>>2) + 4g + (j&3)] (c = lane & 15, g = lane >> 4).
+// Grid b*h x (chunks of 256 float4 elements), flattened: every thread scans four consecutive
+// elements of a segment partial (fragment layout, see kv_reduce_kernel) over the segments of
+// its (b,h), loading a batch of segments before it sums them. Element e of a partial:
+// e < NP: part[fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c];
+// e >= NP: zpart[fc][g][j] = z[fc*32 + 16(j>>2) + 4g + (j&3)] (c = lane & 15, g = lane >> 4);
+// the four elements of a thread share fc and g and differ in j & 3.
 template <int DV, int M>
 __global__ void __launch_bounds__(256)
 scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
@@ -46,59 +48,84 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
   constexpr int NWR = RedSplit<M>::NW, FBR = RedSplit<M>::FB;
   constexpr int NFC = (M + 31) / 32, NVB = DV / 16;
   constexpr int NP = NFC * NVB * 512, NZ = NFC * 32;
-  constexpr int NBLK = (NP + NZ + 255) / 256;
+  constexpr int NQ = (NP + NZ) / 4;  // float4 elements per partial
+  constexpr int NBLK = (NQ + 255) / 256;
+  constexpr int KB = 8;  // segments loaded per batch
   extern __shared__ float pre[];  // [nseg] prefix maxima over segments and waves
   const int bh = blockIdx.x / NBLK, blk = blockIdx.x % NBLK;
-  if (threadIdx.x == 0) {
+  for (int p = threadIdx.x; p < nseg; p += blockDim.x) {  // the segments' own maxima
+    const size_t slot = (size_t)bh * nseg + p;
+    float mx = -INFINITY;
+    for (int w = 0; w < NWR; ++w) mx = fmaxf(mx, pmax[slot * NWR + w]);
+    pre[p] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // prefix maxima
     float run = -INFINITY;
     for (int p = 0; p < nseg; ++p) {
-      const size_t slot = (size_t)bh * nseg + p;
-      float mx = -INFINITY;
-      for (int w = 0; w < NWR; ++w) mx = fmaxf(mx, pmax[slot * NWR + w]);
-      run = fmaxf(run, mx);
+      run = fmaxf(run, pre[p]);
       pre[p] = (kind == kPrf) ? run : 0.f;
-      if (blk == 0) cmax[slot] = pre[p];
+      if (blk == 0) cmax[(size_t)bh * nseg + p] = pre[p];
     }
   }
   __syncthreads();
-  const int e = blk * 256 + threadIdx.x;
-  if (e >= NP + NZ) return;
+  const int e4 = blk * 256 + threadIdx.x;
+  if (e4 >= NQ) return;
+  const int e = e4 * 4;
   const bool isz = e >= NP;
-  int fc, col, g, j;
+  int fc, col, g, j0;
   if (!isz) {
     fc = e / (NVB * 512);
     const int rest = e % (NVB * 512), nb = rest / 512, lane = (rest / 8) % 64;
-    j = rest % 8;
+    j0 = rest % 8;
     g = lane >> 4;
     col = nb * 16 + (lane & 15);
   } else {
     const int ez = e - NP;
     fc = ez / 32;
     g = (ez / 8) % 4;
-    j = ez % 8;
+    j0 = ez % 8;
     col = DV;
   }
-  const int r = fc * 32 + 16 * (j >> 2) + 4 * g + (j & 3);  // feature (row of S_aug)
-  const int wv = (fc * 32) / (FBR * 16);                    // the reducing wave that owned it
-  const float* src = isz ? zpart + (e - NP) : part + e;
-  float* dst = isz ? cz + (e - NP) : cpart + e;
-  const size_t stride = isz ? NZ : NP;
-  float acc = 0.f, prev = 0.f;
-  for (int p = 0; p < nseg; ++p) {
-    const size_t slot = (size_t)bh * nseg + p;
-    const float mp = pre[p];
-    if (p > 0) acc *= fast_exp2(prev - mp);
-    dst[slot * stride] = acc;
-    const float sc = (kind == kPrf) ? fast_exp2(pmax[slot * NWR + wv] - mp) : 1.f;
-    acc += src[slot * stride] * sc;
-    prev = mp;
+  const int r0 = fc * 32 + 16 * (j0 >> 2) + 4 * g;  // features r0..r0+3 (rows of S_aug)
+  const int wv = (fc * 32) / (FBR * 16);           // the reducing wave that owned them
+  const f32x4* src = reinterpret_cast<const f32x4*>(isz ? zpart + (e - NP) : part + e);
+  f32x4* dst = reinterpret_cast<f32x4*>(isz ? cz + (e - NP) : cpart + e);
+  const size_t stride = (isz ? NZ : NP) / 4;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float prev = 0.f;
+  for (int p0 = 0; p0 < nseg; p0 += KB) {
+    f32x4 x[KB];
+    float sc[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {  // a segment past the last is read as the last, weight 0
+      const int p = p0 + u < nseg ? p0 + u : nseg - 1;
+      const size_t slot = (size_t)bh * nseg + p;
+      x[u] = src[slot * stride];
+      sc[u] = (kind == kPrf) ? pmax[slot * NWR + wv] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int p = p0 + u;
+      if (p < nseg) {
+        const size_t slot = (size_t)bh * nseg + p;
+        const float mp = pre[p];
+        if (p > 0) acc *= fast_exp2(prev - mp);
+        dst[slot * stride] = acc;
+        acc += x[u] * ((kind == kPrf) ? fast_exp2(sc[u] - mp) : 1.f);
+        prev = mp;
+      }
+    }
   }
-  if (S_final && r < M) {
-    const float canon = (kind == kPrf) ? acc * fast_exp2(prev - log2_sqrt_m) : acc;
-    if (!isz)
-      S_final[((size_t)bh * M + r) * DV + col] = canon;
-    else
-      z_final[(size_t)bh * M + r] = canon;
+  if (S_final && r0 < M) {
+    const float f = (kind == kPrf) ? fast_exp2(prev - log2_sqrt_m) : 1.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!isz)
+        S_final[((size_t)bh * M + r0 + i) * DV + col] = acc[i] * f;
+      else
+        z_final[(size_t)bh * M + r0 + i] = acc[i] * f;
+    }
   }
 }
 
@@ -607,8 +634,8 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   }
   {
     FAVOR_TIMED("scan", st);
-    constexpr int NEL = ((M + 31) / 32) * ((DV / 16) * 512 + 32);
-    scan_kernel<DV, M><<<(unsigned)(s.bh() * ((NEL + 255) / 256)), 256, p.nseg * sizeof(float), st>>>(
+    constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
+    scan_kernel<DV, M><<<(unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st>>>(
         part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final, z_final);
   }
   {
