@@ -58,16 +58,25 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
     return None, None
 
 
-def _src_hash() -> str:
+# the device sources each path's kernels are built from
+_PATH_SOURCES = {
+    "bidir": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
+    "causal": ["favor_causal.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
+    "decode": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
+}
+
+
+def _src_hash(kind: str) -> str:
+    """Digest of the sources of one path's kernels: a counter summary is valid while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "random_feature_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in _PATH_SOURCES[kind]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, workload: str):
+def _traffic(kernel: str, workload: str, kind: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if taken on the current sources."""
     p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(p):
@@ -76,7 +85,7 @@ def _traffic(kernel: str, workload: str):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("src_hash") != _src_hash():
+    if d.get("src_hash") != _src_hash(kind):
         return None
     return d.get("bytes_per_launch")
 
@@ -196,10 +205,11 @@ def main():
     if a.copy_calib:
         # a plain elementwise copy of known size: hardware counters of the same run are
         # calibrated against it (see random_feature_amd.profiling)
+        # (a bitwise not over int32: no other kernel of any workload's setup has that name)
         n = a.copy_calib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
+        src = torch.ones(n, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
+        torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     for _ in range(a.warmup):
@@ -235,10 +245,10 @@ def main():
         hbm_time, mfma_time = nbytes / (PEAK_HBM_GBS * 1e9), flops / (peak_f * 1e12)
         if hbm_time >= mfma_time:
             roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                            frac=round(gbs / PEAK_HBM_GBS, 4), traffic=_traffic(dominant, w.name))
+                            frac=round(gbs / PEAK_HBM_GBS, 4), traffic=_traffic(dominant, w.name, w.kind))
         else:
             roofline = dict(bound="mfma", achieved=round(tfl, 2), peak=peak_f, unit="TFLOP/s",
-                            frac=round(tfl / peak_f, 4), traffic=_traffic(dominant, w.name))
+                            frac=round(tfl / peak_f, 4), traffic=_traffic(dominant, w.name, w.kind))
         roofline.update(kernel=dominant, avg_launch_us=round(avg[dominant] * 1e3, 2),
                         mfma_tflops=round(tfl, 2), mfma_frac=round(tfl / peak_f, 4),
                         hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),

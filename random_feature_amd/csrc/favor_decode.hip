@@ -28,7 +28,7 @@ namespace favor {
 #define FAVOR_DECODE_THREADS 256
 #endif
 #ifndef FAVOR_DECODE_ROWS
-#define FAVOR_DECODE_ROWS 8
+#define FAVOR_DECODE_ROWS 16
 #endif
 constexpr int kDecodeThreads = FAVOR_DECODE_THREADS;
 #ifndef FAVOR_DECODE_NT

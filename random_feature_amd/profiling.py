@@ -7,8 +7,8 @@ reads it and prints
   the table that ``rocprofv3 --kernel-trace --stats`` summarises;
 * ``traffic``: HBM bytes per launch of one kernel from two counter runs, ``--pmc
   FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (KiB per dispatch), each scaled by what the same
-  counter reads for a plain copy kernel of known size in the same run (the elementwise
-  copy that ``bench.py --copy-calib MiB`` launches before its timed steps).
+  counter reads for a plain copy kernel of known size in the same run (the int32
+  elementwise bitwise-not that ``bench.py --copy-calib MiB`` launches before its timed steps).
 
 Kernels are reported under the names the library's timers use (``reduce``, ``output``...).
 """
@@ -38,6 +38,8 @@ def short_name(kernel: str) -> str:
         for frag, name in _SHORT:
             if frag in kernel:
                 return name
+    if "bitwise_not" in kernel:
+        return "copy:bitwise_not"
     if "elementwise" in kernel or "copy" in kernel.lower():
         return "copy:" + re.sub(r"\W+", "_", kernel)[:48]
     return re.sub(r"\W+", "_", kernel)[:48]
@@ -78,12 +80,11 @@ def counter_per_dispatch(db: str, counter: str):
 
 
 def _copy_factor(vals: dict, copy_bytes: int) -> float:
-    cands = [(n, v) for n, v in vals.items() if n.startswith("copy:")]
-    if not cands:
-        raise SystemExit("no copy kernel in the counter run (bench.py --copy-calib)")
-    # the calibration copy is the largest elementwise kernel of the run
-    n, v = max(cands, key=lambda nv: max(nv[1]))
-    measured_kib = max(v)
+    # the calibration copy is the int32 bitwise-not kernel that bench.py --copy-calib launches
+    cands = [(n, v) for n, v in vals.items() if n.startswith("copy:") and "bitwise_not" in n]
+    if len(cands) != 1 or len(cands[0][1]) != 1:
+        raise SystemExit("expected exactly one calibration copy in the counter run (bench.py --copy-calib)")
+    measured_kib = cands[0][1][0]
     return (copy_bytes / 1024.0) / measured_kib
 
 
