@@ -7,11 +7,13 @@ seeded inputs already resident in device memory:
   bidir_bf16  (default, the headline workload) favor_bidir, B8 H12 L4096 d64 dv64 m256, bf16 in/out
   causal_bf16 favor_causal, B4 H8 L8192 d64 dv64 m256
   decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
+  decode_gated_bf16 the same with favor_decode_gated (gates U[0.9,1), input weight 1 - g)
   bidir_fp32 / bidir_small  the fp32 parity workloads
 Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
 decode, head-tokens/s), the dominant kernel's roofline fraction (per-launch
-durations from HIP events recorded on the launch stream during the timed
-region), and the fp64 oracle timed on the host on a bounded sample.
+durations from HIP events recorded on the launch stream during a second pass of
+the same steps, right after the timed one), and the fp64 oracle timed on the
+host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -52,9 +54,10 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
         return th * (proj + contr), th * (w.d * eb + w.dv * out_bytes)
     if name == "sweep":       # queries and keys projected, inter+intra contractions, outputs
         return th * (2 * proj + 2 * contr), th * ((2 * w.d + w.dv) * eb + w.dv * out_bytes)
-    if name == "decode":      # per (sequence, head): q,k projections, state read+write, out
+    if name == "decode":      # per (sequence, head): q,k projections, state read+write, out (+ gate, weight)
         sb = (w.m * w.dv + w.m) * 4
-        return th * (2 * proj + 2 * contr), th * (2 * sb + (2 * w.d + w.dv) * eb + w.dv * 4)
+        gb = 8 if w.kind == "decode_gated" else 0
+        return th * (2 * proj + 2 * contr), th * (2 * sb + (2 * w.d + w.dv) * eb + w.dv * 4 + gb)
     return None, None
 
 
@@ -63,6 +66,7 @@ _PATH_SOURCES = {
     "bidir": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "causal": ["favor_causal.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "decode": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
+    "decode_gated": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
 }
 
 
@@ -126,7 +130,11 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
             qq = torch.randn(n_seq, w.H, w.d, generator=gen).bfloat16()
             kk = torch.randn(n_seq, w.H, w.d, generator=gen).bfloat16()
             vv = torch.randn(n_seq, w.H, w.dv, generator=gen).bfloat16()
-            S, z, _ = oracle.decode_step(S, z, qq, kk, vv, om)
+            if w.kind == "decode_gated":
+                gg = 0.9 + 0.1 * torch.rand(n_seq, w.H, generator=gen).double().numpy()
+                S, z, _ = oracle.decode_gated_step(S, z, qq, kk, vv, om, gg, 1.0 - gg)
+            else:
+                S, z, _ = oracle.decode_step(S, z, qq, kk, vv, om)
             steps += 1
         dt = time.perf_counter() - t0
         return dict(value=steps * n_seq * w.H / dt, unit="head-tokens/s", cores=1, kind="oracle",
@@ -158,7 +166,7 @@ def main():
     dt = w.torch_dtype
     om = rf.make_omega(w.seed, w.H, w.m, w.d, device=dev)
 
-    if w.kind == "decode":
+    if w.kind in ("decode", "decode_gated"):
         S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
         z = torch.empty((w.B, w.H, w.m), dtype=torch.float32, device=dev)
         # initial state: the canonical final state of a causal pass over `prior` tokens per sequence
@@ -175,10 +183,16 @@ def main():
         qs, ks, vs = workloads.make_decode_steps(w, dev, steps=n_steps)
         out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
         it = iter(range(10 ** 9))
+        if w.kind == "decode_gated":
+            gs = workloads.make_gates((n_steps, w.B, w.H), w.seed, device=dev)
+            wts = 1.0 - gs
 
         def step(i=None):
             t = next(it) % n_steps
-            rf.decode(qs[t], ks[t], vs[t], om, S, z, out=out)
+            if w.kind == "decode_gated":
+                rf.decode_gated(qs[t], ks[t], vs[t], om, S, z, gs[t], wts[t], out=out)
+            else:
+                rf.decode(qs[t], ks[t], vs[t], om, S, z, out=out)
         tokens_per_step = w.B * w.H
         unit = "head-tokens/s"
         out_bytes = 4
@@ -273,7 +287,7 @@ def main():
         "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "dv": w.dv,
-                   "m": w.m, "feature_map": "prf", "out_dtype": "fp32" if w.kind == "decode" else w.dtype},
+                   "m": w.m, "feature_map": "prf", "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
         "roofline": roofline,
     }

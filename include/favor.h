@@ -129,6 +129,21 @@ favor_status favor_decode(const void* q, const void* k, const void* v, const flo
                           favor_dtype dtype, favor_kind kind, float eps,
                           float* out, hipStream_t stream);
 
+/* favor_decode_gated — the decode step with recency gating (RFA page, section 3.2,
+ * RFA-GATE: the historical state decays by a scalar gate computed from the step's
+ * input, in both the value state and the normalisation state). Per (sequence, head)
+ * pair p = n*H + h, with g = gate[p] and w = in_weight[p] (w = 1 if in_weight is NULL):
+ *   S = g*S + w*phi(k) v^T,  z = g*z + w*phi(k),  out = phi(q).S / phi(q).z
+ * (RFA's own form uses w = 1 - g). gate and in_weight are fp32 device arrays [N,H],
+ * 4-byte aligned, read once; the gate network itself is the caller's. Everything else
+ * as favor_decode; gate == NULL is FAVOR_ERR_INVALID_ARG. With every g = w = 1 the
+ * result equals favor_decode's. */
+favor_status favor_decode_gated(const void* q, const void* k, const void* v, const float* omega,
+                                float* S, float* z, const float* gate, const float* in_weight,
+                                int N, int H, int d, int dv, int m,
+                                favor_dtype dtype, favor_kind kind, float eps,
+                                float* out, hipStream_t stream);
+
 /* Bytes of device workspace favor_bidir (causal = 0) or favor_causal (causal = 1)
  * needs for these sizes; 0 if the arguments are invalid. */
 size_t favor_workspace_size(int causal, int B, int H, int L, int d, int dv, int m, favor_dtype dtype);

@@ -16,8 +16,9 @@ Contents
             Algorithm 1), the causal estimator as the prefix-sum recurrence
             (appendix B.1 equation 11; the RNN form in the linear-attention
             blog's "Autoregressive Generation" section), the single-token
-            decode step, and exact softmax attention (equations 1-2) for
-            accuracy reports.
+            decode step, the gated decode step of the RFA page (section 3.2)
+            with its unrolled form, and exact softmax attention (equations
+            1-2) for accuracy reports.
 
 Every floating-point quantity is computed in fp64 from inputs that are
 exactly representable (fp32 or bf16 values widened to fp64). No stabiliser is
@@ -32,12 +33,14 @@ convergence to exact softmax attention as m grows, invariants).
 from .omega import make_omega, splitmix64_mix, stream_key, uniform52, gaussians, OMEGA_MODES
 from .favor import (
     features, bidir, bidir_from_features, causal, causal_bruteforce, causal_bruteforce_from_features,
-    decode_step, decode_run, state_from_prior, softmax_attention, attention_matrix, row_norm_rel_err,
+    decode_step, decode_run, decode_gated_step, decode_gated_run, decode_gated_unrolled, state_from_prior,
+    softmax_attention, attention_matrix, row_norm_rel_err,
 )
 
 __all__ = [
     "make_omega", "splitmix64_mix", "stream_key", "uniform52", "gaussians", "OMEGA_MODES",
     "features", "bidir", "bidir_from_features", "causal", "causal_bruteforce",
-    "causal_bruteforce_from_features", "decode_step", "decode_run", "state_from_prior",
+    "causal_bruteforce_from_features", "decode_step", "decode_run", "decode_gated_step", "decode_gated_run",
+    "decode_gated_unrolled", "state_from_prior",
     "softmax_attention", "attention_matrix", "row_norm_rel_err",
 ]

@@ -142,6 +142,66 @@ def decode_run(S, z, q_steps, k_steps, v_steps, omega, kind: str = "prf", eps: f
     return S, z, outs
 
 
+def decode_gated_step(S, z, q, k, v, omega, gate, in_weight=None, kind: str = "prf", eps: float = 0.0):
+    """One gated step (RFA page, section 3.2, RFA-GATE): the historical state of every (sequence, head)
+    decays by its scalar gate g, in the value state and the normalisation state alike, and the new token
+    enters with weight w (1 unless given; RFA's own choice is w = 1 - g):
+        S' = g S + w phi(k) v^T,  z' = g z + w phi(k);  out = phi(q).S' / phi(q).z'.
+    gate, in_weight: [N,H]. Returns (S', z', out)."""
+    S = _f64(S)
+    z = _f64(z)
+    g = _f64(gate)
+    w = np.ones_like(g) if in_weight is None else _f64(in_weight)
+    pq = features(_f64(q)[:, :, None, :], omega, kind, eps)[:, :, 0, :]
+    pk = features(_f64(k)[:, :, None, :], omega, kind, eps)[:, :, 0, :]
+    v = _f64(v)
+    S2 = g[..., None, None] * S + (w[..., None] * pk)[..., :, None] * v[..., None, :]
+    z2 = g[..., None] * z + w[..., None] * pk
+    num = np.einsum("nhm,nhme->nhe", pq, S2)
+    den = np.einsum("nhm,nhm->nh", pq, z2)
+    return S2, z2, num / den[..., None]
+
+
+def decode_gated_run(S, z, q_steps, k_steps, v_steps, omega, gates, in_weights=None, kind: str = "prf",
+                     eps: float = 0.0):
+    """Several gated steps; gates (and in_weights) [T,N,H]. Returns (S_T, z_T, outs [T,N,H,dv])."""
+    q_steps, k_steps, v_steps = _f64(q_steps), _f64(k_steps), _f64(v_steps)
+    S = _f64(S)
+    z = _f64(z)
+    outs = np.empty(q_steps.shape[:3] + (v_steps.shape[-1],))
+    for t in range(q_steps.shape[0]):
+        w = None if in_weights is None else in_weights[t]
+        S, z, outs[t] = decode_gated_step(S, z, q_steps[t], k_steps[t], v_steps[t], omega, gates[t], w, kind, eps)
+    return S, z, outs
+
+
+def decode_gated_unrolled(S0, z0, q_steps, k_steps, v_steps, omega, gates, in_weights=None, kind: str = "prf",
+                          eps: float = 0.0):
+    """The gated recurrence written out: at step t token j <= t carries the weight
+    c_tj = w_j * prod_{j < l <= t} g_l and the initial state prod_{l <= t} g_l, so
+    out_t = phi(q_t).(c_t0' S0 + sum_j c_tj phi(k_j) v_j^T) / phi(q_t).(c_t0' z0 + sum_j c_tj phi(k_j)).
+    Returns outs [T,N,H,dv]."""
+    S0, z0 = _f64(S0), _f64(z0)
+    g = _f64(gates)
+    T = g.shape[0]
+    w = np.ones_like(g) if in_weights is None else _f64(in_weights)
+    pq = np.stack([features(_f64(q_steps[t])[:, :, None, :], omega, kind, eps)[:, :, 0, :] for t in range(T)])
+    pk = np.stack([features(_f64(k_steps[t])[:, :, None, :], omega, kind, eps)[:, :, 0, :] for t in range(T)])
+    v = _f64(v_steps)
+    outs = np.empty(v.shape)
+    for t in range(T):
+        c0 = np.prod(g[:t + 1], axis=0)                                   # [N,H]
+        num = np.einsum("nhm,nhme->nhe", pq[t], S0) * c0[..., None]
+        den = np.einsum("nhm,nhm->nh", pq[t], z0) * c0
+        for j in range(t + 1):
+            c = w[j] * np.prod(g[j + 1:t + 1], axis=0)                    # [N,H]
+            a = np.einsum("nhm,nhm->nh", pq[t], pk[j]) * c
+            num += a[..., None] * v[j]
+            den += a
+        outs[t] = num / den[..., None]
+    return outs
+
+
 def state_from_prior(k_prior, v_prior, omega, kind: str = "prf", eps: float = 0.0):
     """The canonical state after a prefix of tokens: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j).
 

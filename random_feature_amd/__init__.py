@@ -43,6 +43,7 @@ _lib.favor_bidir.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
 _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
                               _sz, _vp]
 _lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
+_lib.favor_decode_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
 _lib.favor_workspace_size.restype = _sz
 _lib.favor_timing_enable.argtypes = [_i]
@@ -52,11 +53,11 @@ _lib.favor_timing_read.restype = _i
 _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
 for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
-            "favor_decode"):
+            "favor_decode", "favor_decode_gated"):
     getattr(_lib, _fn).restype = _i
 
 EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
-            "favor_decode", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
+            "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
             "favor_status_string"]
 
 
@@ -204,6 +205,32 @@ def decode(q, k, v, omega, S, z, kind="prf", eps: float = 0.0, out=None):
     _check("favor_decode",
            _lib.favor_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(S), _ptr(z), N, H, d, dv, m,
                              _dtype_code(q), _kind(kind), float(eps), _ptr(out), ctypes.c_void_p(_stream(q.device))))
+    return out
+
+
+def decode_gated(q, k, v, omega, S, z, gate, in_weight=None, kind="prf", eps: float = 0.0, out=None):
+    """One gated decode step: S = g S + w phi(k) v^T, z = g z + w phi(k) with gate g and optional input weight w
+    (fp32 [N,H], device); otherwise as decode(). Returns out [N,H,dv]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 3)
+    _need(S, "S", 4)
+    _need(z, "z", 3)
+    _need(omega, "omega", 3)
+    for t, n in ((gate, "gate"), (in_weight, "in_weight")):
+        if t is not None:
+            _need(t, n, 2)
+            if t.dtype != torch.float32:
+                raise ValueError(f"{n} must be float32")
+    N, H, d = q.shape
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    _check("favor_decode_gated",
+           _lib.favor_decode_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(S), _ptr(z), _ptr(gate),
+                                   _ptr(in_weight) if in_weight is not None else None, N, H, d, dv, m,
+                                   _dtype_code(q), _kind(kind), float(eps), _ptr(out),
+                                   ctypes.c_void_p(_stream(q.device))))
     return out
 
 

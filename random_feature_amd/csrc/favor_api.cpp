@@ -13,6 +13,7 @@ void make_omega(uint64_t seed, int H, int m, int d, int mode, float* out);
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_dtype(favor_dtype t) { return t == FAVOR_F32 || t == FAVOR_BF16; }
 bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -116,9 +117,9 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
       favor::launch_causal(q, k, v, omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out, S_final, z_final, ws, stream));
 }
 
-favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z, int N,
-                          int H, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps, float* out,
-                          hipStream_t stream) {
+static favor_status decode_common(const void* q, const void* k, const void* v, const float* omega, float* S,
+                                  float* z, const float* gate, const float* inw, int N, int H, int d, int dv, int m,
+                                  favor_dtype dtype, favor_kind kind, float eps, float* out, hipStream_t stream) {
   if (N < 1 || H < 1 || (long long)N * H > (1LL << 24)) return FAVOR_ERR_INVALID_ARG;
   if (!valid_dtype(dtype) || !valid_kind(kind) || !(eps >= 0.0f)) return FAVOR_ERR_INVALID_ARG;
   if (d < 1 || dv < 1 || m < 1) return FAVOR_ERR_INVALID_ARG;
@@ -129,7 +130,21 @@ favor_status favor_decode(const void* q, const void* k, const void* v, const flo
   if (!(d == 16 || d == 32 || d == 64)) return FAVOR_ERR_UNSUPPORTED;
   if (!pow2(dv) || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
   if (m % 16 != 0 || m > 1024) return FAVOR_ERR_UNSUPPORTED;
-  return hip_status(favor::launch_decode(q, k, v, omega, S, z, N, H, d, dv, m, dtype, kind, eps, out, stream));
+  return hip_status(
+      favor::launch_decode(q, k, v, omega, S, z, N, H, d, dv, m, dtype, kind, eps, gate, inw, out, stream));
+}
+
+favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z, int N,
+                          int H, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps, float* out,
+                          hipStream_t stream) {
+  return decode_common(q, k, v, omega, S, z, nullptr, nullptr, N, H, d, dv, m, dtype, kind, eps, out, stream);
+}
+
+favor_status favor_decode_gated(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
+                                const float* gate, const float* in_weight, int N, int H, int d, int dv, int m,
+                                favor_dtype dtype, favor_kind kind, float eps, float* out, hipStream_t stream) {
+  if (!gate || !aligned4(gate) || (in_weight && !aligned4(in_weight))) return FAVOR_ERR_INVALID_ARG;
+  return decode_common(q, k, v, omega, S, z, gate, in_weight, N, H, d, dv, m, dtype, kind, eps, out, stream);
 }
 
 }  // extern "C"

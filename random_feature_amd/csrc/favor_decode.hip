@@ -51,13 +51,17 @@ constexpr int kDecodeSeqs = 1;                  // sequences of one head per wor
 // rows is requested right after the (older) loads the features need, so the state streams
 // in while the projections are computed. Two threads share each feature's projection (one
 // half of d each). Measured on the 256-sequence, 16-head, m = 256, dv = 64 step: 256
-// threads with 8 rows each (two batches) beat larger workgroups and longer runs.
+// threads with 16 rows each (the whole state in one batch) beat 8 or 4 rows and 512
+// threads.
+// Gated form (RFA page, section 3.2): with `gate` non-null the old state decays by the
+// pair's scalar gate[pair] and the new token enters with weight inw[pair] (1 if inw is
+// null): S = g S + w phi(k) v^T, z = g z + w phi(k); with gate null g = w = 1.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecodeThreads)
 decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
               const float* __restrict__ omega, float* __restrict__ S, float* __restrict__ z, int N, int H,
               int dv, int m, int kind, float eps, float inv_sqrt_m, float wscale, float nscale, float log2_sqrt_m,
-              float* __restrict__ out) {
+              const float* __restrict__ gate, const float* __restrict__ inw, float* __restrict__ out) {
   constexpr int U = kDecodeRows, G = kDecodeSeqs;
   constexpr int NWV = kDecodeThreads / 64;
   constexpr int DH = D / 2;  // the d-half of a feature this thread projects
@@ -97,6 +101,12 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     const T* vs = v + pair_of(g) * dv + col4 * 4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) vv[g][j] = to_f(vs[j]);
+  }
+  float gv[G], iw[G];  // decay of the old state and weight of the new token
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    gv[g] = gate ? gate[pair_of(g)] : 1.f;
+    iw[g] = gate && inw ? inw[pair_of(g)] : 1.f;
   }
   const int half = tid & 1, f0 = tid >> 1;
   // (loads are unconditional, from clamped rows, so they issue back to back with no
@@ -210,7 +220,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     dpart[g] = 0.f;
     float* zp = z + pair_of(g) * m;
     for (int r = tid; r < m; r += kDecodeThreads) {
-      const float zn = zp[r] + fk[g * m + r];
+      const float zn = zp[r] * gv[g] + fk[g * m + r] * iw[g];
       if (g < ng) zp[r] = zn;
       dpart[g] += fq[g * m + r] * zn;
     }
@@ -234,7 +244,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
       for (int u = 0; u < U; ++u) {
         const int r = r0 + u;
         if (r < m) {
-          const f32x4 st = buf[g][u] + fk[g * m + r] * vv[g];
+          const f32x4 st = buf[g][u] * gv[g] + (fk[g * m + r] * iw[g]) * vv[g];
           acc[g] += fq[g * m + r] * st;
           if (g < ng) st_state(p0 + u * dv, st);
         }
@@ -262,7 +272,8 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 
 template <typename T, int D>
 static hipError_t run_decode(const T* q, const T* k, const T* v, const float* omega, float* S, float* z, int N, int H,
-                             int dv, int m, int kind, float eps, float* out, hipStream_t st) {
+                             int dv, int m, int kind, float eps, const float* gate, const float* inw, float* out,
+                             hipStream_t st) {
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == 0) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
@@ -275,21 +286,23 @@ static hipError_t run_decode(const T* q, const T* k, const T* v, const float* om
   {
     FAVOR_TIMED("decode", st);
     decode_kernel<T, D><<<(unsigned)(n_grp * H), kDecodeThreads, lds, st>>>(
-        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, out);
+        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, gate, inw, out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
-                         int N, int H, int d, int dv, int m, int dtype, int kind, float eps, float* out,
-                         hipStream_t st) {
+                         int N, int H, int d, int dv, int m, int dtype, int kind, float eps, const float* gate,
+                         const float* inw, float* out, hipStream_t st) {
 #define DEC(D_)                                                                                                 \
   if (d == D_) {                                                                                                \
     if (dtype == 0)                                                                                             \
       return run_decode<float, D_>(static_cast<const float*>(q), static_cast<const float*>(k),                  \
-                                   static_cast<const float*>(v), omega, S, z, N, H, dv, m, kind, eps, out, st); \
+                                   static_cast<const float*>(v), omega, S, z, N, H, dv, m, kind, eps, gate,     \
+                                   inw, out, st);                                                               \
     return run_decode<bf16, D_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),                       \
-                                static_cast<const bf16*>(v), omega, S, z, N, H, dv, m, kind, eps, out, st);     \
+                                static_cast<const bf16*>(v), omega, S, z, N, H, dv, m, kind, eps, gate, inw,    \
+                                out, st);                                                                       \
   }
   DEC(16)
   DEC(32)

@@ -69,7 +69,7 @@ hipError_t launch_causal(const void* q, const void* k, const void* v, const floa
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
                          void* ws, hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
-                         int N, int H, int d, int dv, int m, int dtype, int kind, float eps, float* out,
-                         hipStream_t st);
+                         int N, int H, int d, int dv, int m, int dtype, int kind, float eps, const float* gate,
+                         const float* inw, float* out, hipStream_t st);
 
 }  // namespace favor

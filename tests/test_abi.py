@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -92,6 +92,17 @@ def test_decode_argument_checks():
     assert call(d=128) == UNSUPPORTED
     assert call(dv=48) == UNSUPPORTED
     assert call(m=100) == UNSUPPORTED
+
+
+def test_decode_gated_argument_checks():
+    def call(gate=FAKE, inw=None, q=FAKE, d=64):
+        return rf.raw_call("favor_decode_gated", q, FAKE, FAKE, FAKE, FAKE, FAKE, gate, inw, 4, 2, d, 64, 256, 1, 0,
+                           ctypes.c_float(0.0), FAKE, None)
+    assert call(gate=None) == INVALID
+    assert call(gate=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(inw=ctypes.c_void_p(0x10001)) == INVALID
+    assert call(q=None) == INVALID
+    assert call(d=128) == UNSUPPORTED
 
 
 def test_features_and_omega_argument_checks():

@@ -330,3 +330,87 @@ def test_decode_workload_sampled():
         assert np.max(np.abs(S[s, h].cpu().double().numpy() - Sp[0, 0])) / np.max(np.abs(Sp)) < 1e-4
     print(f"decode_bf16 sampled rel err {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- gated decode
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d,dv,m,with_w", [(16, 16, 32, False), (32, 32, 64, True), (64, 64, 256, True),
+                                           (64, 32, 128, False)])
+def test_decode_gated_steps(dtype, d, dv, m, with_w):
+    """RFA-GATE steps (RFA page, section 3.2) against the oracle's gated recurrence: outputs and final state."""
+    N, H, T, P = 5, 3, 20, 40
+    om_dev, om = _omega(23, H, m, d)
+    kp = workloads.make_tensor((N, H, P, d), 11, 1.0, dtype)
+    vp = workloads.make_tensor((N, H, P, dv), 12, 1.0, dtype)
+    S0, z0 = oracle.state_from_prior(kp, vp, om)
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    qs = workloads.make_tensor((T, N, H, d), 13, 1.0, dtype)
+    ks = workloads.make_tensor((T, N, H, d), 14, 1.0, dtype)
+    vs = workloads.make_tensor((T, N, H, dv), 15, 1.0, dtype)
+    gates = workloads.make_gates((T, N, H), 16, lo=0.5)
+    wts = (1.0 - gates) if with_w else None
+    S_ref, z_ref, outs_ref = oracle.decode_gated_run(S0, z0, qs, ks, vs, om, gates.numpy(),
+                                                     None if wts is None else wts.numpy())
+    S = torch.from_numpy(S0).to(DEV)
+    z = torch.from_numpy(z0).to(DEV)
+    qd, kd, vd, gd = qs.to(DEV), ks.to(DEV), vs.to(DEV), gates.to(DEV)
+    wd = None if wts is None else wts.to(DEV)
+    outs = torch.stack([rf.decode_gated(qd[t], kd[t], vd[t], om_dev, S, z, gd[t], None if wd is None else wd[t])
+                        for t in range(T)])
+    torch.cuda.synchronize()
+    assert rel_err(outs, outs_ref) < TOL[dtype]
+    assert np.max(np.abs(S.cpu().double().numpy() - S_ref)) / np.max(np.abs(S_ref)) < 1e-5
+    assert rel_err(z, z_ref) < 1e-5
+
+
+def test_decode_gated_unit_gate_is_decode():
+    """With every gate and input weight 1 the gated step is the plain step, bit for bit."""
+    N, H, d, dv, m = 7, 2, 64, 64, 256
+    om_dev, _ = _omega(24, H, m, d)
+    S = workloads.make_tensor((N, H, m, dv), 31, 0.1).abs().to(DEV)
+    z = workloads.make_tensor((N, H, m), 32, 1.0).abs().to(DEV)
+    q = workloads.make_tensor((N, H, d), 33, 1.0, torch.bfloat16).to(DEV)
+    k = workloads.make_tensor((N, H, d), 34, 1.0, torch.bfloat16).to(DEV)
+    v = workloads.make_tensor((N, H, dv), 35, 1.0, torch.bfloat16).to(DEV)
+    S2, z2 = S.clone(), z.clone()
+    one = torch.ones((N, H), dtype=torch.float32, device=DEV)
+    o1 = rf.decode(q, k, v, om_dev, S, z)
+    o2 = rf.decode_gated(q, k, v, om_dev, S2, z2, one, one)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S, S2) and torch.equal(z, z2)
+
+
+def test_decode_gated_workload_sampled():
+    """The gated decode workload (256 sequences x 16 heads, d64 m256, bf16, gates U[0.9,1), input weight 1 - g):
+    200 steps, sampled pairs against the oracle's gated recurrence."""
+    w = workloads.WORKLOADS["decode_gated_bf16"]
+    T, R = 200, 4
+    om_dev, om = _omega(w.seed, w.H, w.m, w.d)
+    kp, vp = workloads.make_decode_prior(w, n_seq=R)
+    S0, z0 = oracle.state_from_prior(kp, vp, om)
+    S0 = torch.from_numpy(S0.astype(np.float32))
+    z0 = torch.from_numpy(z0.astype(np.float32))
+    idx = torch.arange(w.B) % R
+    S = S0[idx].contiguous().to(DEV)
+    z = z0[idx].contiguous().to(DEV)
+    qs, ks, vs = workloads.make_decode_steps(w, DEV, steps=T)
+    gates = workloads.make_gates((T, w.B, w.H), w.seed, device=DEV)
+    wts = 1.0 - gates
+    pairs = [(0, 0), (77, 9), (255, 15)]
+    outs = []
+    for t in range(T):
+        o = rf.decode_gated(qs[t], ks[t], vs[t], om_dev, S, z, gates[t], wts[t])
+        outs.append(torch.stack([o[s, h] for s, h in pairs]).cpu())
+    torch.cuda.synchronize()
+    outs = torch.stack(outs)
+    worst = 0.0
+    for i, (s, h) in enumerate(pairs):
+        sl = (slice(None), slice(s, s + 1), slice(h, h + 1))
+        _, _, ref = oracle.decode_gated_run(S0[s % R, h][None, None].numpy(), z0[s % R, h][None, None].numpy(),
+                                            qs[sl].cpu(), ks[sl].cpu(), vs[sl].cpu(), om[h:h + 1],
+                                            gates[sl].cpu().numpy(), wts[sl].cpu().numpy())
+        worst = max(worst, rel_err(outs[:, i], ref[:, 0, 0]))
+    print(f"decode_gated_bf16 sampled rel err {worst:.3e}")
+    assert worst < TOL[torch.bfloat16]

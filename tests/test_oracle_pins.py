@@ -130,6 +130,32 @@ def test_causal_state_matches_prior_state():
     assert np.allclose(S, S2, rtol=1e-12) and np.allclose(z, z2, rtol=1e-12)
 
 
+def test_gated_decode_recurrence_equals_unrolled_sum():
+    """RFA page, section 3.2 (RFA-GATE): the step-by-step gated recurrence equals its unrolled form, in which
+    token j enters step t with weight w_j * prod_{j<l<=t} g_l and the initial state with prod_{l<=t} g_l;
+    with every g = w = 1 it is the ungated decode, and with g -> 0 a step sees only its own token."""
+    N, H, T, d, dv, m = 2, 3, 9, 16, 8, 32
+    om = make_omega(21, H, m, d)
+    kp = RNG.normal(size=(N, H, 6, d)) * 0.5
+    vp = RNG.normal(size=(N, H, 6, dv))
+    S0, z0 = oracle.state_from_prior(kp, vp, om)
+    q = RNG.normal(size=(T, N, H, d)) * 0.5
+    k = RNG.normal(size=(T, N, H, d)) * 0.5
+    v = RNG.normal(size=(T, N, H, dv))
+    g = RNG.uniform(0.3, 1.0, size=(T, N, H))
+    w = 1.0 - g
+    for wt in (None, w):
+        _, _, rec = oracle.decode_gated_run(S0, z0, q, k, v, om, g, wt)
+        unrolled = oracle.decode_gated_unrolled(S0, z0, q, k, v, om, g, wt)
+        assert np.max(np.abs(rec - unrolled)) < 1e-12
+    ones = np.ones((T, N, H))
+    S1, z1, o1 = oracle.decode_gated_run(S0, z0, q, k, v, om, ones)
+    S2, z2, o2 = decode_run(S0, z0, q, k, v, om)
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.allclose(S1, S2, rtol=1e-14)
+    _, _, tiny = oracle.decode_gated_run(S0, z0, q, k, v, om, np.full((T, N, H), 1e-30))
+    assert np.max(np.abs(tiny - v)) < 1e-12
+
+
 # ---------------------------------------------------------------- feature map
 
 def _prf_single_estimates(x, y, om):

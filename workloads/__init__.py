@@ -14,6 +14,8 @@ bidirectional attention, causal attention and recurrent decoding):
   causal_bf16  bf16  B4 H8  L8192 d64 dv64 m256  Q,K,V ~ 0.5 N(0, 1)        seed 3
   decode_bf16  bf16  256 sequences, H16 d64 dv64 m256; 2048 prior tokens
                build the state, then 1000 steps of q,k,v ~ N(0,1)         seed 4
+  decode_gated_bf16  the same, each step with a gate g ~ U[0.9, 1) per
+               (sequence, head) and input weight 1 - g                   seed 5
 
 Draw order for one workload: Q, then K, then V, each one `torch.randn` call on
 a CPU generator seeded with the workload's seed, scaled, then rounded to the
@@ -33,7 +35,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "bidir" | "causal" | "decode"
+    kind: str            # "bidir" | "causal" | "decode" | "decode_gated"
     dtype: str           # "f32" | "bf16"
     B: int
     H: int
@@ -64,6 +66,8 @@ WORKLOADS = {
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
                             steps=1000, prior=2048),
+    "decode_gated_bf16": Workload("decode_gated_bf16", "decode_gated", "bf16", 256, 16, 1, 64, 64, 256, 5,
+                                  1.0, 1.0, 1.0, steps=1000, prior=2048),
 }
 
 
@@ -117,6 +121,12 @@ def make_decode_steps(w: Workload, device: str, steps: Optional[int] = None):
     k = _randn(gen, (n_steps, w.B, w.H, w.d), w.k_scale, w.torch_dtype, device)
     v = _randn(gen, (n_steps, w.B, w.H, w.dv), w.v_scale, w.torch_dtype, device)
     return q, k, v
+
+
+def make_gates(shape, seed: int, lo: float = 0.9, hi: float = 1.0, device: str = "cpu") -> torch.Tensor:
+    """Gate values ~ U[lo, hi) in fp32 (recency gates of the gated decode), drawn on `device`."""
+    gen = torch.Generator(device).manual_seed(seed)
+    return lo + (hi - lo) * torch.rand(*shape, generator=gen, dtype=torch.float32, device=device)
 
 
 def make_tensor(shape, seed: int, scale: float = 1.0, dtype=torch.float32, device="cpu") -> torch.Tensor:
