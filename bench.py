@@ -94,14 +94,17 @@ def _traffic(kernel: str, workload: str, kind: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
+def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str = "ortho_chi"):
     """The fp64 oracle on the host, single-threaded, on as many (b,h) pairs (decode: sequences) as fit
     in about `budget_s` seconds; returns tokens/s in the metric's unit."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
-    om = oracle.make_omega(w.seed, w.H, w.m, w.d)
+    if omega_mode == "hyperbolic":  # the oracle takes the m/2 vectors and builds the 2 x m/2 features itself
+        om, kind = oracle.make_omega(w.seed, w.H, w.m // 2, w.d), "hyperbolic"
+    else:
+        om, kind = oracle.make_omega(w.seed, w.H, w.m, w.d, omega_mode), "prf"
     with threadpool_limits(1):
         if w.kind in ("bidir", "causal"):
             q, k, v = workloads.make_qkv(w)
@@ -110,7 +113,7 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
             for b in range(w.B):
                 for h in range(w.H):
                     sl = (slice(b, b + 1), slice(h, h + 1))
-                    fn(q[sl], k[sl], v[sl], om[h:h + 1])
+                    fn(q[sl], k[sl], v[sl], om[h:h + 1], kind)
                     done += 1
                     if time.perf_counter() - t0 > budget_s:
                         break
@@ -132,9 +135,9 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
             vv = torch.randn(n_seq, w.H, w.dv, generator=gen).bfloat16()
             if w.kind == "decode_gated":
                 gg = 0.9 + 0.1 * torch.rand(n_seq, w.H, generator=gen).double().numpy()
-                S, z, _ = oracle.decode_gated_step(S, z, qq, kk, vv, om, gg, 1.0 - gg)
+                S, z, _ = oracle.decode_gated_step(S, z, qq, kk, vv, om, gg, 1.0 - gg, kind)
             else:
-                S, z, _ = oracle.decode_step(S, z, qq, kk, vv, om)
+                S, z, _ = oracle.decode_step(S, z, qq, kk, vv, om, kind)
             steps += 1
         dt = time.perf_counter() - t0
         return dict(value=steps * n_seq * w.H / dt, unit="head-tokens/s", cores=1, kind="oracle",
@@ -149,6 +152,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--omega-mode", default="ortho_chi", choices=["ortho_chi", "iid", "ortho_sqrtd", "hyperbolic"],
+                    help="random features: hyperbolic gives Lemma 1's hyperbolic features (m/2 vectors)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="launch one elementwise copy of this many MiB first (counter calibration)")
     ap.add_argument("--rotate", type=int, default=4,
@@ -164,7 +169,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     dt = w.torch_dtype
-    om = rf.make_omega(w.seed, w.H, w.m, w.d, device=dev)
+    om = rf.make_omega(w.seed, w.H, w.m, w.d, a.omega_mode, device=dev)
 
     if w.kind in ("decode", "decode_gated"):
         S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
@@ -287,7 +292,8 @@ def main():
         "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "dv": w.dv,
-                   "m": w.m, "feature_map": "prf", "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
+                   "m": w.m, "feature_map": "prf" if a.omega_mode != "hyperbolic" else "prf_hyperbolic",
+                   "omega": a.omega_mode, "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
         "roofline": roofline,
     }
@@ -295,7 +301,7 @@ def main():
         res["value_rotating_inputs"] = cold
         res["rotating_input_sets"] = len(sets)
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, omega_mode=a.omega_mode)
     print(json.dumps(res), flush=True)
 
 

@@ -62,8 +62,11 @@ typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
 typedef enum { FAVOR_PRF = 0, FAVOR_RELU = 1 } favor_kind;
 
 /* Omega rows: orthogonal blocks with chi(d) lengths (section 2.4, appendix B.2/F.4),
- * independent Gaussian rows, or orthogonal rows of length sqrt(d) (SMREG, section 2.3). */
-typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2 } favor_omega_mode;
+ * independent Gaussian rows, or orthogonal rows of length sqrt(d) (SMREG, section 2.3).
+ * FAVOR_HYPERBOLIC (m even): the m/2 rows of FAVOR_ORTHO_CHI, then their negatives; with
+ * FAVOR_PRF every entry point then computes the hyperbolic positive features of Lemma 1
+ * (second form): exp(-|x|^2/2)/sqrt(m) (exp(w_i.x), exp(-w_i.x)) for the m/2 vectors w_i. */
+typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2, FAVOR_HYPERBOLIC = 3 } favor_omega_mode;
 
 /* favor_make_omega — random features omega [H,m,d] fp32 into device memory.
  * Section 2.4 and appendix B.2 of the Performer paper: for each head, ceil(m/d)
@@ -74,7 +77,7 @@ typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2 } favor
  * bits depend only on (seed, H, m, d, mode): head h's rows do not depend on H.
  * Then copied with hipMemcpyAsync on `stream` (the host buffer stays alive
  * until the copy completes: the call synchronises `stream` before returning).
- * Requires 1 <= d <= 256, 1 <= m <= 4096, 1 <= H <= 65536. */
+ * Requires 1 <= d <= 256, 1 <= m <= 4096, 1 <= H <= 65536 (m even for FAVOR_HYPERBOLIC). */
 favor_status favor_make_omega(uint64_t seed, int H, int m, int d, favor_omega_mode mode,
                               float* omega_dev, hipStream_t stream);
 

@@ -40,7 +40,8 @@ def _f64(x) -> np.ndarray:
 
 
 def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
-    """phi(x) for raw queries or keys x [B,H,L,d] and omega [H,m,d] -> [B,H,L,m] (fp64)."""
+    """phi(x) for raw queries or keys x [B,H,L,d] and omega [H,m,d] -> [B,H,L,m] (fp64);
+    kind "hyperbolic": the 2m hyperbolic features of the m rows (features_hyperbolic)."""
     x = _f64(x)
     om = _f64(omega)
     d = x.shape[-1]
@@ -52,7 +53,24 @@ def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
         return np.exp(a - half_norm) / math.sqrt(m)
     if kind == "relu":
         return np.maximum(a, 0.0) / math.sqrt(m) + eps
+    if kind == "hyperbolic":  # the rows of omega are the random vectors; 2m features
+        return features_hyperbolic(x, omega)
     raise ValueError(f"unknown feature kind {kind!r}")
+
+
+def features_hyperbolic(x, omega) -> np.ndarray:
+    """The hyperbolic positive features (Performer paper, Lemma 1, second form) for raw x [B,H,L,d] and the
+    random vectors w_i = rows of omega [H,m,d]: with x scaled by d^-1/4,
+        phi(x) = exp(-|x|^2/2) / sqrt(2m) * (exp(w_1.x), ..., exp(w_m.x), exp(-w_1.x), ..., exp(-w_m.x)),
+    so phi(x).phi(y) = (1/m) sum_i exp(-(|x|^2+|y|^2)/2) cosh(w_i.(x+y)). Returns [B,H,L,2m] (fp64)."""
+    x = _f64(x)
+    om = _f64(omega)
+    d = x.shape[-1]
+    m = om.shape[-2]
+    xs = x * (float(d) ** -0.25)
+    a = np.einsum("bhld,hmd->bhlm", xs, om)
+    h = np.exp(-0.5 * np.sum(xs * xs, axis=-1, keepdims=True)) / math.sqrt(2.0 * m)
+    return np.concatenate([h * np.exp(a), h * np.exp(-a)], axis=-1)
 
 
 def bidir_from_features(phi_q, phi_k, v):

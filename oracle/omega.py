@@ -49,7 +49,7 @@ import numpy as np
 MASK64 = (1 << 64) - 1
 GAMMA = 0x9E3779B97F4A7C15
 TWO_PI = 6.283185307179586  # the binary64 value nearest to 2*pi (== 2 * math.pi)
-OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2}
+OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2, "hyperbolic": 3}
 
 
 def splitmix64_mix(z: int) -> int:
@@ -128,6 +128,14 @@ def _block_rows(seed: int, head: int, block: int, d: int, mode: int) -> list:
 
 @lru_cache(maxsize=64)
 def _make_omega_cached(seed: int, H: int, m: int, d: int, mode: int) -> bytes:
+    if mode == 3:
+        # hyperbolic positive features (Performer paper, Lemma 1, second form): the m/2 vectors of the
+        # orthogonal chi(d) mode, then their negatives, so that the positive feature map over these m rows
+        # is exp(-|x|^2/2)/sqrt(m) (exp(w_i.x), exp(-w_i.x))
+        if m % 2:
+            raise ValueError("hyperbolic mode needs an even m")
+        half = np.frombuffer(_make_omega_cached(seed, H, m // 2, d, 0), dtype=np.float32).reshape(H, m // 2, d)
+        return np.concatenate([half, -half], axis=1).tobytes()
     out = np.empty((H, m, d), dtype=np.float32)
     nblocks = (m + d - 1) // d
     for h in range(H):

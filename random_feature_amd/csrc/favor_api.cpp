@@ -17,6 +17,10 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool valid_dtype(favor_dtype t) { return t == FAVOR_F32 || t == FAVOR_BF16; }
 bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool valid_omega_mode(favor_omega_mode mode, int m) {
+  if (mode == FAVOR_HYPERBOLIC) return m % 2 == 0;
+  return mode == FAVOR_ORTHO_CHI || mode == FAVOR_IID || mode == FAVOR_ORTHO_SQRTD;
+}
 
 favor_status hip_status(hipError_t e) { return e == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP; }
 
@@ -47,7 +51,7 @@ const char* favor_status_string(favor_status st) {
 
 favor_status favor_make_omega_host(uint64_t seed, int H, int m, int d, favor_omega_mode mode, float* omega_host) {
   if (!omega_host || H < 1 || H > 65536 || m < 1 || m > 4096 || d < 1 || d > 256) return FAVOR_ERR_INVALID_ARG;
-  if (mode != FAVOR_ORTHO_CHI && mode != FAVOR_IID && mode != FAVOR_ORTHO_SQRTD) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_omega_mode(mode, m)) return FAVOR_ERR_INVALID_ARG;
   favor_host::make_omega(seed, H, m, d, static_cast<int>(mode), omega_host);
   return FAVOR_OK;
 }
@@ -56,7 +60,7 @@ favor_status favor_make_omega(uint64_t seed, int H, int m, int d, favor_omega_mo
                               hipStream_t stream) {
   if (!omega_dev || !aligned16(omega_dev)) return FAVOR_ERR_INVALID_ARG;
   if (H < 1 || H > 65536 || m < 1 || m > 4096 || d < 1 || d > 256) return FAVOR_ERR_INVALID_ARG;
-  if (mode != FAVOR_ORTHO_CHI && mode != FAVOR_IID && mode != FAVOR_ORTHO_SQRTD) return FAVOR_ERR_INVALID_ARG;
+  if (!valid_omega_mode(mode, m)) return FAVOR_ERR_INVALID_ARG;
   std::vector<float> host((size_t)H * m * d);
   favor_host::make_omega(seed, H, m, d, static_cast<int>(mode), host.data());
   hipError_t e = hipMemcpyAsync(omega_dev, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice, stream);

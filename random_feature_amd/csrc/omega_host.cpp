@@ -94,6 +94,21 @@ static void block_rows(uint64_t seed, int head, int block, int d, int mode, std:
 }
 
 void make_omega(uint64_t seed, int H, int m, int d, int mode, float* out) {
+  if (mode == 3) {
+    // hyperbolic positive features: the m/2 rows of the orthogonal chi(d) mode, then their
+    // negatives (m is even)
+    const int half = m / 2;
+    std::vector<float> base(static_cast<size_t>(H) * half * d);
+    make_omega(seed, H, half, d, 0, base.data());
+    for (int h = 0; h < H; ++h)
+      for (int r = 0; r < half; ++r)
+        for (int t = 0; t < d; ++t) {
+          const float x = base[(static_cast<size_t>(h) * half + r) * d + t];
+          out[(static_cast<size_t>(h) * m + r) * d + t] = x;
+          out[(static_cast<size_t>(h) * m + half + r) * d + t] = -x;
+        }
+    return;
+  }
   const int nblocks = (m + d - 1) / d;
   std::vector<double> rows;
   for (int h = 0; h < H; ++h) {

@@ -109,6 +109,9 @@ def test_features_and_omega_argument_checks():
     st = rf.raw_call("favor_features", FAKE, FAKE, 1, 1, 8, 48, 64, 1, 0, ctypes.c_float(0.0), FAKE, FAKE, None)
     assert st == UNSUPPORTED
     assert rf.raw_call("favor_make_omega", ctypes.c_uint64(0), 1, 16, 16, 0, None, None) == INVALID
+    # the hyperbolic mode pairs every row with its negative: m must be even
+    assert rf.raw_call("favor_make_omega_host", ctypes.c_uint64(0), 1, 33, 16, 3, FAKE) == INVALID
+    assert rf.raw_call("favor_make_omega", ctypes.c_uint64(0), 1, 33, 16, 3, FAKE, None) == INVALID
     assert rf.raw_call("favor_make_omega", ctypes.c_uint64(0), 1, 16, 16, 9, FAKE, None) == INVALID
     assert rf.raw_call("favor_make_omega_host", ctypes.c_uint64(0), 0, 16, 16, 0, FAKE) == INVALID
 
@@ -126,6 +129,7 @@ def test_workspace_size_query():
     (2, 3, 256, 64, "ortho_chi"),
     (3, 2, 40, 16, "ortho_chi"),
     (4, 2, 96, 32, "ortho_sqrtd"),
+    (6, 3, 128, 64, "hyperbolic"),
     (5, 2, 48, 16, "iid"),
     (2 ** 64 - 1, 1, 64, 64, "ortho_chi"),
     (12345678901234, 1, 20, 7, "ortho_chi"),

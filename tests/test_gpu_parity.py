@@ -414,3 +414,45 @@ def test_decode_gated_workload_sampled():
         worst = max(worst, rel_err(outs[:, i], ref[:, 0, 0]))
     print(f"decode_gated_bf16 sampled rel err {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- hyperbolic features
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("path", ["bidir", "causal"])
+@pytest.mark.parametrize("shape", [(16, 16, 32), (64, 64, 256)])
+def test_hyperbolic_features_bidir_and_causal(dtype, path, shape):
+    """Lemma 1's hyperbolic positive features through the hyperbolic Omega mode, against the oracle's
+    estimator built from the hyperbolic feature map itself (the m/2 vectors, exp(+-w.x))."""
+    d, dv, m = shape
+    B, H, L = 2, 2, 300
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 500 + m)
+    om_dev = rf.make_omega(41, H, m, d, "hyperbolic")
+    om_half = oracle.make_omega(41, H, m // 2, d, "ortho_chi")
+    if path == "bidir":
+        ref = oracle.bidir(q, k, v, om_half, kind="hyperbolic")
+        out = rf.bidir(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, out_f32=True)
+    else:
+        ref = oracle.causal(q, k, v, om_half, kind="hyperbolic")
+        out = rf.causal(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, out_f32=True)
+    torch.cuda.synchronize()
+    assert rel_err(out, ref) < TOL[dtype]
+
+
+def test_hyperbolic_features_decode():
+    """Decode steps with the hyperbolic Omega against the oracle recurrence on the hyperbolic features."""
+    N, H, T, P, d, dv, m = 4, 2, 12, 30, 64, 64, 128
+    om_dev = rf.make_omega(42, H, m, d, "hyperbolic")
+    om_half = oracle.make_omega(42, H, m // 2, d, "ortho_chi")
+    kp = workloads.make_tensor((N, H, P, d), 51, 1.0, torch.bfloat16)
+    vp = workloads.make_tensor((N, H, P, dv), 52, 1.0, torch.bfloat16)
+    S0, z0 = oracle.state_from_prior(kp, vp, om_half, kind="hyperbolic")
+    S0, z0 = S0.astype(np.float32), z0.astype(np.float32)
+    qs = workloads.make_tensor((T, N, H, d), 53, 1.0, torch.bfloat16)
+    ks = workloads.make_tensor((T, N, H, d), 54, 1.0, torch.bfloat16)
+    vs = workloads.make_tensor((T, N, H, dv), 55, 1.0, torch.bfloat16)
+    _, _, refs = oracle.decode_run(S0, z0, qs, ks, vs, om_half, kind="hyperbolic")
+    Sd, zd = torch.from_numpy(S0).to(DEV), torch.from_numpy(z0).to(DEV)
+    outs = torch.stack([rf.decode(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), om_dev, Sd, zd) for t in range(T)])
+    torch.cuda.synchronize()
+    assert rel_err(outs, refs) < TOL[torch.bfloat16]

@@ -191,6 +191,42 @@ def test_positive_features_unbiased_lemma1_with_lemma2_variance():
         assert bias > 8.0 * math.sqrt(mse1 / m)
 
 
+def test_hyperbolic_features_unbiased_with_lemma2_variance():
+    """Lemma 1 (second form): the hyperbolic features are unbiased for exp(x.y), and one random vector's
+    estimate Lambda cosh(w.z) has variance m * MSE^hyp+ = (1/2)(1 - exp(-|z|^2)) exp(|z|^2) SM^2 (1 - exp(-|z|^2))
+    (Lemma 2, equation 8, third line, with the second line for MSE^+)."""
+    d, m = 16, 32768
+    om = make_omega(2025, 1, m, d, "iid")
+    s = float(d) ** 0.25
+    for trial in range(3):
+        x = RNG.normal(size=d) * 0.15
+        y = RNG.normal(size=d) * 0.15
+        sm = math.exp(float(x @ y))
+        z2 = float((x + y) @ (x + y))
+        var1 = 0.5 * (1.0 - math.exp(-z2)) * math.exp(z2) * sm ** 2 * (1.0 - math.exp(-z2))
+        fx = oracle.features_hyperbolic((x * s)[None, None, None], om)[0, 0, 0]
+        fy = oracle.features_hyperbolic((y * s)[None, None, None], om)[0, 0, 0]
+        assert float(fx @ fy) == pytest.approx(sm, abs=4.0 * math.sqrt(var1 / m))
+        est = m * (fx[:m] * fy[:m] + fx[m:] * fy[m:])   # one vector each
+        assert float(est.var()) == pytest.approx(var1, rel=0.12)
+        # the positive features' single-feature variance is larger by 2 / (1 - exp(-|z|^2))
+        var_plus = math.exp(z2) * sm ** 2 * (1.0 - math.exp(-z2))
+        assert float(_prf_single_estimates(x, y, om).var()) > 1.5 * var1 and var_plus > 2.0 * var1
+
+
+def test_hyperbolic_omega_mode_gives_the_hyperbolic_features():
+    """The hyperbolic Omega mode (the m/2 orthogonal chi(d) rows, then their negatives) under the plain
+    positive feature map equals the hyperbolic features of those m/2 rows, in value and normaliser."""
+    H, d, m = 2, 16, 64
+    x = RNG.normal(size=(1, H, 7, d))
+    om_h = make_omega(31, H, m, d, "hyperbolic")
+    om_half = make_omega(31, H, m // 2, d, "ortho_chi")
+    assert np.array_equal(om_h[:, :m // 2], om_half) and np.array_equal(om_h[:, m // 2:], -om_half)
+    a = features(x, om_h)
+    b = oracle.features_hyperbolic(x, om_half)
+    assert np.max(np.abs(a - b) / b) < 1e-13
+
+
 def test_features_apply_the_sqrt_d_temperature():
     """Section 2.3 under equation 6: raw q, k are scaled so that the kernel is exp(q.k / sqrt(d))."""
     d, m = 16, 16384
