@@ -108,6 +108,22 @@ favor_status favor_bidir(const void* q, const void* k, const void* v, const floa
                          favor_dtype dtype, favor_kind kind, float eps, int out_f32,
                          void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* favor_bidir_cross — bidirectional FAVOR+ between Lq queries and Lk keys (the RFA
+ * page's cross-attention procedure; Performer Algorithm 1 with Q' of Lq rows and K' of
+ * Lk rows), with the renormaliser D^-1 optional (Performer appendices A.3 and D.3,
+ * "renormalize"): q [B,H,Lq,d], k [B,H,Lk,d], v [B,H,Lk,dv], out [B,H,Lq,dv].
+ *   renormalize != 0: out_i = phi(q_i).S / phi(q_i).z   (as favor_bidir)
+ *   renormalize == 0: out_i = phi(q_i).S with S = sum_j phi(k_j) v_j^T and the features
+ *     in canonical scale, phi = exp(omega.x - |x|^2/2)/sqrt(m) (PRF) or
+ *     max(omega.x, 0)/sqrt(m) + eps (ReLU); the stabilisers are undone exactly.
+ * Workspace: favor_workspace_size(0, B, H, Lk, d, dv, m, dtype). Built shapes, dtypes,
+ * errors as favor_bidir, and 1 <= Lq <= 2^28. favor_bidir(..., L, ...) is
+ * favor_bidir_cross(..., L, L, ..., renormalize = 1, ...). */
+favor_status favor_bidir_cross(const void* q, const void* k, const void* v, const float* omega,
+                               int B, int H, int Lq, int Lk, int d, int dv, int m,
+                               favor_dtype dtype, favor_kind kind, float eps, int renormalize,
+                               int out_f32, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* favor_causal — unidirectional FAVOR+ (appendix B.1 eq. 11: prefix sums including
  * the diagonal) as a chunked scan. Same arguments and shapes as favor_bidir
  * (workspace from favor_workspace_size(1, ...)). If S_final [B,H,m,dv] and

@@ -83,9 +83,14 @@ def bidir_from_features(phi_q, phi_k, v):
     return num / den[..., None], S, z
 
 
-def bidir(q, k, v, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
-    out, _, _ = bidir_from_features(features(q, omega, kind, eps), features(k, omega, kind, eps), v)
-    return out
+def bidir(q, k, v, omega, kind: str = "prf", eps: float = 0.0, renormalize: bool = True) -> np.ndarray:
+    """Equation 4 (Algorithm 1): q [B,H,Lq,d] against k [B,H,Lk,d], v [B,H,Lk,dv] (Lq and Lk may differ: the
+    RFA page's cross attention). renormalize=False drops D^-1 (Performer appendices A.3, D.3): the output is
+    Phi_Q (Phi_K^T V) with the features in their own scale."""
+    out, S, _ = bidir_from_features(features(q, omega, kind, eps), features(k, omega, kind, eps), v)
+    if renormalize:
+        return out
+    return np.einsum("...lm,...me->...le", features(q, omega, kind, eps), S)
 
 
 def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bool = False):

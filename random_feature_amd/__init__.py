@@ -40,6 +40,8 @@ _lib.favor_make_omega.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 _lib.favor_make_omega_host.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp]
 _lib.favor_features.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]
 _lib.favor_bidir.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.favor_bidir_cross.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _sz,
+                                   _vp]
 _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
                               _sz, _vp]
 _lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
@@ -52,11 +54,12 @@ _lib.favor_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINT
 _lib.favor_timing_read.restype = _i
 _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
-for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
-            "favor_decode", "favor_decode_gated"):
+for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
+            "favor_causal", "favor_decode", "favor_decode_gated"):
     getattr(_lib, _fn).restype = _i
 
-EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_causal",
+EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
+            "favor_causal",
             "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
             "favor_status_string"]
 
@@ -163,6 +166,28 @@ def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, w
            _lib.favor_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
                             float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(ws), ws.numel(),
                             ctypes.c_void_p(_stream(q.device))))
+    return out
+
+
+def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool = True, out_f32: bool = False,
+                ws=None, out=None):
+    """Bidirectional FAVOR+ between q [B,H,Lq,d] and k [B,H,Lk,d], v [B,H,Lk,dv]; without renormalisation the
+    output is phi(q).S in canonical feature scale. Returns out [B,H,Lq,dv]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, 4)
+    _need(omega, "omega", 3)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if ws is None:
+        ws = workspace(False, k, v, omega)
+    if out is None:
+        out = torch.empty((B, H, Lq, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    _check("favor_bidir_cross",
+           _lib.favor_bidir_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, Lq, Lk, d, dv, m, _dtype_code(q),
+                                  _kind(kind), float(eps), 1 if renormalize else 0, 1 if out_f32 else 0, _ptr(out),
+                                  _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
     return out
 
 

@@ -89,18 +89,28 @@ favor_status favor_features(const void* x, const float* omega, int B, int H, int
   return hip_status(favor::launch_features(x, omega, s, dtype, kind, eps, phi, logscale, stream));
 }
 
-favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
-                         int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
-                         void* ws, size_t ws_bytes, hipStream_t stream) {
-  const favor::Shape s{B, H, L, d, dv, m};
+favor_status favor_bidir_cross(const void* q, const void* k, const void* v, const float* omega, int B, int H,
+                               int Lq, int Lk, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps,
+                               int renormalize, int out_f32, void* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  const favor::Shape s{B, H, Lk, d, dv, m};
   favor_status st = check_seq(s, dtype, kind, eps);
   if (st != FAVOR_OK) return st;
+  if (Lq < 1 || Lq > (1 << 28)) return FAVOR_ERR_INVALID_ARG;
   if (!q || !k || !v || !omega || !out || !ws) return FAVOR_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out) || !aligned16(ws))
     return FAVOR_ERR_INVALID_ARG;
   if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_bidir(s, dtype).total) return FAVOR_ERR_WORKSPACE;
-  return hip_status(favor::launch_bidir(q, k, v, omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out, ws, stream));
+  return hip_status(favor::launch_bidir(q, k, v, omega, s, Lq, renormalize ? 1 : 0, dtype, kind, eps,
+                                        out_f32 ? 1 : 0, out, ws, stream));
+}
+
+favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
+                         int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  return favor_bidir_cross(q, k, v, omega, B, H, L, L, d, dv, m, dtype, kind, eps, 1, out_f32, out, ws, ws_bytes,
+                           stream);
 }
 
 favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,

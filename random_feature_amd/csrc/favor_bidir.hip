@@ -38,7 +38,7 @@ namespace favor {
 template <typename C, int DV, int M>
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
-               int tpb, long long T_all, int G, int kind, C* __restrict__ sfr) {
+               int tpb, long long T_all, int G, int kind, C* __restrict__ sfr, float* __restrict__ gmx) {
   constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
   constexpr int NB = DV / 16 + 1;
   constexpr int NFC = (M + 31) / 32;
@@ -50,6 +50,7 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
   float gmax = -INFINITY;
   if (kind == kPrf)
     for (int k = 0; k < np * NW; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW]);
+  if (fc == 0 && threadIdx.x == 0) gmx[bh] = (kind == kPrf) ? gmax : 0.f;  // the keys' common maximum
   for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {
     const int nb = e >> 6, lane = e & 63;
     const int c = lane & 15, g = lane >> 4;
@@ -113,7 +114,8 @@ template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * FeatSplit<M>::NW, 2)
 q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ omf,
                 const typename Ops<T>::C* __restrict__ sfr, int H, int L, int tpb, long long T_all, int G,
-                float eps, float inv_sqrt_m, int out_f32, void* __restrict__ out) {
+                float eps, float inv_sqrt_m, int out_f32, int renorm, const float* __restrict__ gmx, float nscale,
+                float log2_m, void* __restrict__ out) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = FeatSplit<M>::NW, FB = FeatSplit<M>::FB;
@@ -165,6 +167,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
   vec8<C> zf[NFCW];
   vec8<C> sf[NCB][NFC];
   float omax = 0.f;
+  float gm = 0.f;  // key stabiliser of the current (b,h) (renormalisation off)
   int cur_bh = -1;
 
   for (int it = 0; it < n_tiles; ++it) {
@@ -188,6 +191,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
           sf[cb][fc] = nb < NVB ? ld8<C>(sfr + ((((size_t)bh * NFC + fc) * NB + nb) * 64 + lane) * 8) : zero8<C>();
       }
       cur_bh = bh;
+      if constexpr (KIND == kPrf) gm = renorm ? 0.f : gmx[bh];
       if constexpr (KIND == kPrf) {
         omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
       } else {
@@ -197,11 +201,13 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 
     // ---- phase 1: this wave's features of the tile
     f32x4 bias[2];
+    float shf[2];  // the exponent shift of this lane's query row of each token half
     bool exact = false;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const float b = (KIND == kPrf) ? qb[buf][tb * 16 + c] * omax : 0.f;
       bias[tb] = f32x4{-b, -b, -b, -b};
+      shf[tb] = b;
       if constexpr (KIND == kPrf) exact |= b > kQueryBoundLimit;
     }
     if constexpr (KIND == kPrf) exact = __builtin_amdgcn_ballot_w64(exact) != 0;  // same in every wave
@@ -242,6 +248,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
           for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb) pacc[tb][fb] -= mx;
+          shf[tb] += mx;
         }
       }
 #pragma unroll
@@ -304,6 +311,15 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) den += dpart[buf][tb0 + tt][c][ww];
       rden[tt] = 1.0f / den;
+      if (!renorm) {
+        // no D^-1: undo the stabilisers instead, giving phi(q).S in canonical scale
+        // (phi = 2^(a' - n') / sqrt(m) on both sides; the keys' constant is gm)
+        rden[tt] = 1.f;
+        if constexpr (KIND == kPrf) {
+          const float qa = qb[buf][(tb0 + tt) * 16 + c] * (1.f / kQueryMargin);
+          rden[tt] = fast_exp2(shf[tb0 + tt] - qa * qa * nscale + gm - log2_m);
+        }
+      }
     }
     f32x4 acc[NCB][NTB];
 #pragma unroll
@@ -441,11 +457,14 @@ bool shape_built(int dtype, int d, int dv, int m) {
 
 constexpr int kMaxPieces = 512;  // two resident 4-wave workgroups on each of 256 CUs
 
-BidirPlan plan_bidir(const Shape& s, int dtype) {
+BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
   BidirPlan p;
-  p.tpb = (s.L + 31) / 32;
+  p.tpb = (s.L + 31) / 32;  // keys
   p.T_all = s.bh() * p.tpb;
   p.G = (int)std::min<long long>(p.T_all, kMaxPieces);
+  p.tpb_q = ((Lq > 0 ? Lq : s.L) + 31) / 32;  // queries
+  p.T_all_q = s.bh() * p.tpb_q;
+  p.G_q = (int)std::min<long long>(p.T_all_q, kMaxPieces);
   p.nw_reduce = reduce_waves(s.m);
   const int dc = (s.d + 31) / 32, nb = s.dv / 16 + 1;
   const size_t slots = (size_t)p.G + (size_t)s.bh();
@@ -461,25 +480,29 @@ BidirPlan plan_bidir(const Shape& s, int dtype) {
   off = align256(off + slots * p.nw_reduce * 4);
   p.off_sfr = off;
   off = align256(off + (size_t)s.bh() * ((s.m + 31) / 32) * nb * 512 * elt(dtype));
+  p.off_gmax = off;
+  off = align256(off + (size_t)s.bh() * 4);
   p.total = off;
   return p;
 }
 
 
 template <typename T, int D, int DV, int M>
-static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int kind,
-                            float eps, int out_f32, void* out, void* ws, hipStream_t st) {
+static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int Lq,
+                            int renorm, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = FeatSplit<M>::NW;
   constexpr int DC = (D + 31) / 32;
-  const BidirPlan p = plan_bidir(s, sizeof(T) == 4 ? 0 : 1);
+  const BidirPlan p = plan_bidir(s, sizeof(T) == 4 ? 0 : 1, Lq);
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + p.off_omf);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   C* sfr = reinterpret_cast<C*>(base + p.off_sfr);
+  float* gmx = reinterpret_cast<float*>(base + p.off_gmax);
+  const float log2_m = std::log2((float)M);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
@@ -504,30 +527,34 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   {
     FAVOR_TIMED("combine", st);
     combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
-        part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr);
+        part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
   }
   {
     FAVOR_TIMED("output", st);
     if (kind == kPrf)
-      q_output_kernel<T, D, DV, M, kPrf><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, s.H, s.L, p.tpb, p.T_all, p.G, eps,
-                                                                inv_sqrt_m, out_f32, out);
+      q_output_kernel<T, D, DV, M, kPrf><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
+                                                                  eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
+                                                                  log2_m, out);
     else
-      q_output_kernel<T, D, DV, M, kRelu><<<p.G, 64 * NW, 0, st>>>(q, omf, sfr, s.H, s.L, p.tpb, p.T_all, p.G, eps,
-                                                                 inv_sqrt_m, out_f32, out);
+      q_output_kernel<T, D, DV, M, kRelu><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
+                                                                   eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
+                                                                   log2_m, out);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
-                        int dtype, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st) {
+hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s, int Lq,
+                        int renorm, int dtype, int kind, float eps, int out_f32, void* out, void* ws,
+                        hipStream_t st) {
 #define X(D_, DV_, M_)                                                                                         \
   if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                 \
     if (dtype == 0)                                                                                            \
       return run_bidir<float, D_, DV_, M_>(static_cast<const float*>(q), static_cast<const float*>(k),        \
-                                           static_cast<const float*>(v), omega, s, kind, eps, out_f32, out, ws, \
-                                           st);                                                                \
+                                           static_cast<const float*>(v), omega, s, Lq, renorm, kind, eps,      \
+                                           out_f32, out, ws, st);                                              \
     return run_bidir<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),             \
-                                        static_cast<const bf16*>(v), omega, s, kind, eps, out_f32, out, ws, st); \
+                                        static_cast<const bf16*>(v), omega, s, Lq, renorm, kind, eps, out_f32,   \
+                                        out, ws, st);                                                            \
   }
   FAVOR_SHAPES(X)
 #undef X

@@ -42,9 +42,11 @@ inline int reduce_waves(int m) {
 // Both passes walk the B*H*ceil(L/32) token tiles split into G contiguous pieces (one
 // workgroup each); partials are stored per (piece, b*h) intersection.
 struct BidirPlan {
-  int tpb = 0, G = 0, nw_reduce = 0;
+  int tpb = 0, G = 0, nw_reduce = 0;  // key side (the reduction)
   long long T_all = 0;
-  size_t off_omf = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_sfr = 0, total = 0;
+  int tpb_q = 0, G_q = 0;             // query side (the output)
+  long long T_all_q = 0;
+  size_t off_omf = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_sfr = 0, off_gmax = 0, total = 0;
 };
 
 // Causal path: Omega fragments, one partial (S, z) sum per (b*h, segment) in MFMA fragment
@@ -58,13 +60,15 @@ struct CausalPlan {
 };
 
 bool shape_built(int dtype, int d, int dv, int m);
-BidirPlan plan_bidir(const Shape& s, int dtype);
+// s.L is the key length; Lq > 0 sets a different query length (cross attention).
+BidirPlan plan_bidir(const Shape& s, int dtype, int Lq = 0);
 CausalPlan plan_causal(const Shape& s, int dtype);
 
 hipError_t launch_features(const void* x, const float* omega, const Shape& s, int dtype, int kind, float eps,
                            float* phi, float* logscale, hipStream_t st);
-hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
-                        int dtype, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st);
+hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s, int Lq,
+                        int renorm, int dtype, int kind, float eps, int out_f32, void* out, void* ws,
+                        hipStream_t st);
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
                          void* ws, hipStream_t st);

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -456,3 +456,37 @@ def test_hyperbolic_features_decode():
     outs = torch.stack([rf.decode(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), om_dev, Sd, zd) for t in range(T)])
     torch.cuda.synchronize()
     assert rel_err(outs, refs) < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- cross attention, renormalisation off
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("Lq,Lk", [(100, 300), (513, 64), (1, 33), (300, 300)])
+@pytest.mark.parametrize("renormalize", [True, False])
+@pytest.mark.parametrize("kind", ["prf", "relu"])
+def test_bidir_cross(dtype, Lq, Lk, renormalize, kind):
+    """Cross attention (Lq != Lk) with and without D^-1, against the oracle's Algorithm 1."""
+    d, dv, m = 64, 64, 128
+    B, H = 2, 3
+    eps = 1e-3 if kind == "relu" else 0.0
+    q = workloads.make_tensor((B, H, Lq, d), 600 + Lq, 0.5, dtype)
+    k = workloads.make_tensor((B, H, Lk, d), 601 + Lk, 0.5, dtype)
+    v = workloads.make_tensor((B, H, Lk, dv), 602, 1.0, dtype)
+    om_dev, om = _omega(43, H, m, d)
+    ref = oracle.bidir(q, k, v, om, kind, eps, renormalize=renormalize)
+    out = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind=kind, eps=eps, renormalize=renormalize,
+                         out_f32=True)
+    torch.cuda.synchronize()
+    assert out.shape == (B, H, Lq, dv)
+    assert rel_err(out, ref) < TOL[dtype], rel_err(out, ref)
+
+
+def test_bidir_cross_equal_lengths_is_bidir():
+    """favor_bidir_cross with Lq = Lk and renormalisation on is favor_bidir, bit for bit."""
+    w = workloads.WORKLOADS["bidir_small"]
+    q, k, v = workloads.make_qkv(w)
+    om_dev, _ = _omega(w.seed, w.H, w.m, w.d)
+    a = rf.bidir(q.to(DEV), k.to(DEV), v.to(DEV), om_dev)
+    b = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

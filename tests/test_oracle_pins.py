@@ -86,6 +86,38 @@ def test_bidir_equals_explicit_attention_matrix():
         assert np.max(np.abs(bidir(q, k, v, om)[0, h] - ref)) < 1e-12
 
 
+def test_cross_and_unnormalised_bidir_equal_the_explicit_matrix():
+    """Algorithm 1 with Lq != Lk (the RFA page's cross attention): Phi_Q (Phi_K^T V) equals the explicit
+    Lq x Lk matrix A_hat = Phi_Q Phi_K^T applied to V, without D^-1 (renormalize off, appendix D.3) and with it
+    (equation 1's normalisation applied to A_hat)."""
+    B, H, Lq, Lk, d, dv, m = 1, 2, 5, 11, 16, 8, 32
+    q = RNG.normal(size=(B, H, Lq, d)) * 0.5
+    k = RNG.normal(size=(B, H, Lk, d)) * 0.5
+    v = RNG.normal(size=(B, H, Lk, dv))
+    om = make_omega(8, H, m, d)
+    for kind, eps in (("prf", 0.0), ("relu", 1e-3)):
+        A = np.einsum("bhim,bhjm->bhij", features(q, om, kind, eps), features(k, om, kind, eps))
+        un = bidir(q, k, v, om, kind, eps, renormalize=False)
+        assert np.max(np.abs(un - A @ v)) < 1e-12 * np.max(np.abs(A @ v))
+        nrm = bidir(q, k, v, om, kind, eps)
+        assert np.max(np.abs(nrm - (A @ v) / A.sum(-1, keepdims=True))) < 1e-12
+
+
+def test_unnormalised_output_converges_to_the_softmax_numerator():
+    """Lemma 1 under the unnormalised output: phi(q_i).S -> sum_j exp(q_i.k_j / sqrt(d)) v_j as m grows
+    (the feature scale 1/sqrt(m) and the -|x|^2/2 term both matter here, unlike in the ratio)."""
+    B, H, Lq, Lk, d, dv = 1, 1, 4, 9, 16, 3
+    q = RNG.normal(size=(B, H, Lq, d)) * 0.4
+    k = RNG.normal(size=(B, H, Lk, d)) * 0.4
+    v = RNG.normal(size=(B, H, Lk, dv))
+    exact = np.exp(np.einsum("bhid,bhjd->bhij", q, k) / math.sqrt(d)) @ v
+    errs = []
+    for m in (64, 4096, 65536):
+        om = make_omega(90 + m, H, m, d)
+        errs.append(np.max(np.abs(bidir(q, k, v, om, renormalize=False) - exact)) / np.max(np.abs(exact)))
+    assert errs[-1] < 0.02 and errs[-1] < errs[0]
+
+
 def test_one_hot_values_extract_the_normalised_matrix():
     """Performer appendix C.4: with V = I_L the output is D_hat^-1 A_hat; rows sum to one."""
     L, d, m = 24, 16, 32
@@ -231,11 +263,18 @@ def test_features_apply_the_sqrt_d_temperature():
     """Section 2.3 under equation 6: raw q, k are scaled so that the kernel is exp(q.k / sqrt(d))."""
     d, m = 16, 16384
     om = make_omega(99, 1, m, d, "iid")
-    q = RNG.normal(size=d) * 0.3
-    k = RNG.normal(size=d) * 0.3
+    rng = np.random.default_rng(7)  # its own draws: the bound below holds for any inputs, not for lucky ones
+    q = rng.normal(size=d) * 0.3
+    k = rng.normal(size=d) * 0.3
     est = float((features(q[None, None, None], om) * features(k[None, None, None], om)).sum())
-    assert est == pytest.approx(math.exp(float(q @ k) / math.sqrt(d)), rel=0.02)
-    assert abs(est - math.exp(float(q @ k))) > 0.05 * math.exp(float(q @ k) / math.sqrt(d)) or abs(q @ k) < 0.1
+    # Lemma 2 on the scaled vectors x = q d^-1/4, y = k d^-1/4: one feature's MSE is
+    # exp(|x+y|^2) SM^2 (1 - exp(-|x+y|^2)); m iid features divide it by m
+    sm = math.exp(float(q @ k) / math.sqrt(d))
+    z2 = float((q + k) @ (q + k)) / math.sqrt(d)
+    sigma = math.sqrt(math.exp(z2) * sm ** 2 * (1.0 - math.exp(-z2)) / m)
+    assert abs(est - sm) < 4.0 * sigma
+    # without the temperature the estimate would target exp(q.k), many standard deviations away
+    assert abs(math.exp(float(q @ k)) - sm) > 8.0 * sigma
 
 
 def test_orthogonal_features_reduce_mse_theorem2():
