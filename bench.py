@@ -5,6 +5,7 @@
 A step is one full pass of the selected path over one batch of synthetic,
 seeded inputs already resident in device memory:
   bidir_bf16  (default, the headline workload) favor_bidir, B8 H12 L4096 d64 dv64 m256, bf16 in/out
+  cross_bf16  favor_bidir_cross, B8 H12 Lq1024 Lk4096 d64 dv64 m256 (tokens = query tokens)
   causal_bf16 favor_causal, B4 H8 L8192 d64 dv64 m256
   decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
   decode_gated_bf16 the same with favor_decode_gated (gates U[0.9,1), input weight 1 - g)
@@ -45,13 +46,14 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
     2*m*(dv+1) flops; bytes are the inputs the step must read and the outputs it
     must write (q/k/v at the input width, out at the output width)."""
     eb = 2 if w.dtype == "bf16" else 4
-    th = w.B * w.H * w.L
+    th = w.B * w.H * w.L          # keys (and queries unless cross attention)
+    thq = w.B * w.H * w.Lq_eff    # queries
     proj = 2 * w.m * w.d
     contr = 2 * w.m * (w.dv + 1)
     if name == "reduce":
         return th * (proj + contr), th * (w.d + w.dv) * eb
     if name == "output":
-        return th * (proj + contr), th * (w.d * eb + w.dv * out_bytes)
+        return thq * (proj + contr), thq * (w.d * eb + w.dv * out_bytes)
     if name == "sweep":       # queries and keys projected, inter+intra contractions, outputs
         return th * (2 * proj + 2 * contr), th * ((2 * w.d + w.dv) * eb + w.dv * out_bytes)
     if name == "decode":      # per (sequence, head): q,k projections, state read+write, out (+ gate, weight)
@@ -64,6 +66,7 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
 # the device sources each path's kernels are built from
 _PATH_SOURCES = {
     "bidir": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
+    "cross": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "causal": ["favor_causal.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "decode": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
     "decode_gated": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
@@ -106,9 +109,9 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
     else:
         om, kind = oracle.make_omega(w.seed, w.H, w.m, w.d, omega_mode), "prf"
     with threadpool_limits(1):
-        if w.kind in ("bidir", "causal"):
+        if w.kind in ("bidir", "cross", "causal"):
             q, k, v = workloads.make_qkv(w)
-            fn = oracle.bidir if w.kind == "bidir" else oracle.causal
+            fn = oracle.causal if w.kind == "causal" else oracle.bidir
             done, t0 = 0, time.perf_counter()
             for b in range(w.B):
                 for h in range(w.H):
@@ -120,8 +123,8 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
                 if time.perf_counter() - t0 > budget_s:
                     break
             dt = time.perf_counter() - t0
-            return dict(value=done * w.L / dt, unit="tokens/s", cores=1, kind="oracle",
-                        sample=f"{done} of {w.B * w.H} (b,h) pairs x {w.L} tokens, fp64 NumPy, 1 thread, "
+            return dict(value=done * w.Lq_eff / dt, unit="tokens/s", cores=1, kind="oracle",
+                        sample=f"{done} of {w.B * w.H} (b,h) pairs x {w.Lq_eff} tokens, fp64 NumPy, 1 thread, "
                                f"{dt:.1f} s")
         # decode: steps of the fp64 recurrence for all heads of a few sequences
         gen = torch.Generator().manual_seed(w.seed)
@@ -209,15 +212,15 @@ def main():
             q, k, v = workloads.make_qkv(w.with_(seed=w.seed + 1000 * r) if r else w, device=dev)
             sets.append((q, k, v))
         q, k, v = sets[0]
-        ws = rf.workspace(w.kind == "causal", q, v, om)
-        out = torch.empty((w.B, w.H, w.L, w.dv), dtype=dt, device=dev)
-        fn = rf.bidir if w.kind == "bidir" else rf.causal
+        ws = rf.workspace(w.kind == "causal", k, v, om)
+        out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
+        fn = {"bidir": rf.bidir, "cross": rf.bidir_cross, "causal": rf.causal}[w.kind]
         cur = [0]
 
         def step(i=None):
             qq, kk, vv = sets[cur[0]]
             fn(qq, kk, vv, om, ws=ws, out=out)
-        tokens_per_step = w.B * w.H * w.L
+        tokens_per_step = w.B * w.H * w.Lq_eff   # output (query) tokens
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4
 
@@ -291,7 +294,7 @@ def main():
         "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "dv": w.dv,
+        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d, "dv": w.dv,
                    "m": w.m, "feature_map": "prf" if a.omega_mode != "hyperbolic" else "prf_hyperbolic",
                    "omega": a.omega_mode, "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},

@@ -490,3 +490,18 @@ def test_bidir_cross_equal_lengths_is_bidir():
     b = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_cross_bf16_workload_sampled():
+    """The cross-attention workload (B8 H12 Lq1024 Lk4096 d64 m256, bf16) in the benchmark's launch
+    configuration, sampled (b,h) pairs against the oracle."""
+    w = workloads.WORKLOADS["cross_bf16"]
+    q, k, v = workloads.make_qkv(w)
+    om_dev, om = _omega(w.seed, w.H, w.m, w.d)
+    out = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev).cpu()
+    worst = 0.0
+    for b, h in _sample_pairs(w.B, w.H, 3, 2):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        worst = max(worst, rel_err(out[sl], oracle.bidir(q[sl], k[sl], v[sl], om[h:h + 1])))
+    print(f"cross_bf16 sampled rel err {worst:.3e}")
+    assert worst < TOL[torch.bfloat16]

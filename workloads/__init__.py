@@ -11,6 +11,8 @@ bidirectional attention, causal attention and recurrent decoding):
   bidir_small  fp32  B1 H1  L256  d16 dv16 m32   Q,K,V ~ N(0, 0.5^2)        seed 0
   bidir_fp32   fp32  B1 H8  L4096 d16 dv16 m128  Q,K,V ~ N(0, 1)            seed 1
   bidir_bf16   bf16  B8 H12 L4096 d64 dv64 m256  Q,K ~ N(0,1)/sqrt2, V~N(0,1) seed 2
+  cross_bf16   bf16  B8 H12 Lq1024 Lk4096 d64 dv64 m256, as bidir_bf16     seed 6
+               (a synthetic cross-attention shape: the pages fix none)
   causal_bf16  bf16  B4 H8  L8192 d64 dv64 m256  Q,K,V ~ 0.5 N(0, 1)        seed 3
   decode_bf16  bf16  256 sequences, H16 d64 dv64 m256; 2048 prior tokens
                build the state, then 1000 steps of q,k,v ~ N(0,1)         seed 4
@@ -35,7 +37,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "bidir" | "causal" | "decode" | "decode_gated"
+    kind: str            # "bidir" | "cross" | "causal" | "decode" | "decode_gated"
     dtype: str           # "f32" | "bf16"
     B: int
     H: int
@@ -49,6 +51,11 @@ class Workload:
     v_scale: float
     steps: int = 0       # decode only
     prior: int = 0       # decode only: tokens folded into the initial state
+    Lq: int = 0          # cross attention: query length (L is then the key length); 0 = L
+
+    @property
+    def Lq_eff(self) -> int:
+        return self.Lq if self.Lq else self.L
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -63,6 +70,8 @@ WORKLOADS = {
     "bidir_fp32": Workload("bidir_fp32", "bidir", "f32", 1, 8, 4096, 16, 16, 128, 1, 1.0, 1.0, 1.0),
     "bidir_bf16": Workload("bidir_bf16", "bidir", "bf16", 8, 12, 4096, 64, 64, 256, 2,
                            1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
+    "cross_bf16": Workload("cross_bf16", "cross", "bf16", 8, 12, 4096, 64, 64, 256, 6,
+                           1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0, Lq=1024),
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
                             steps=1000, prior=2048),
@@ -79,13 +88,13 @@ def _randn(gen: torch.Generator, shape, scale: float, dtype: torch.dtype, device
 
 
 def make_qkv(w: Workload, device: str = "cpu"):
-    """Q, K in [B,H,L,d] and V in [B,H,L,dv], contiguous, in the workload dtype.
+    """Q [B,H,Lq,d] (Lq = L unless set), K [B,H,L,d] and V [B,H,L,dv], contiguous, in the workload dtype.
 
     Drawn on a CPU generator (so the values do not depend on the GPU) and then
     moved to `device`.
     """
     gen = torch.Generator("cpu").manual_seed(w.seed)
-    q = _randn(gen, (w.B, w.H, w.L, w.d), w.q_scale, w.torch_dtype)
+    q = _randn(gen, (w.B, w.H, w.Lq_eff, w.d), w.q_scale, w.torch_dtype)
     k = _randn(gen, (w.B, w.H, w.L, w.d), w.k_scale, w.torch_dtype)
     v = _randn(gen, (w.B, w.H, w.L, w.dv), w.v_scale, w.torch_dtype)
     if device != "cpu":
