@@ -93,6 +93,57 @@ def bidir(q, k, v, omega, kind: str = "prf", eps: float = 0.0, renormalize: bool
     return np.einsum("...lm,...me->...le", features(q, omega, kind, eps), S)
 
 
+def _feature_backward(x, omega, phi, dphi, kind: str):
+    """d loss / d x (raw x) from d loss / d phi for the feature map of `features`.
+
+    PRF: phi = exp(w.xs - |xs|^2/2)/sqrt(m), xs = d^-1/4 x, so
+        d/dxs = Omega^T (phi * dphi) - xs * sum_r phi_r dphi_r;
+    ReLU: phi = max(w.xs, 0)/sqrt(m) + eps, so d/dxs = Omega^T (1[w.xs > 0]/sqrt(m) * dphi).
+    The chain rule through xs = d^-1/4 x multiplies by d^-1/4."""
+    x = _f64(x)
+    om = _f64(omega)
+    d = x.shape[-1]
+    m = om.shape[-2]
+    s = float(d) ** -0.25
+    xs = x * s
+    if kind == "prf":
+        pd = phi * dphi
+        g = np.einsum("bhlm,hmd->bhld", pd, om) - xs * np.sum(pd, axis=-1, keepdims=True)
+    elif kind == "relu":
+        a = np.einsum("bhld,hmd->bhlm", xs, om)
+        g = np.einsum("bhlm,hmd->bhld", (a > 0) * dphi / math.sqrt(m), om)
+    else:
+        raise ValueError(f"no backward for feature kind {kind!r}")
+    return g * s
+
+
+def bidir_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
+    """Gradients of equation 4's output out = (Phi_Q S) / (Phi_Q z) (S = Phi_K^T V, z = Phi_K^T 1) with respect
+    to the raw q, k and v, for the upstream gradient dout [B,H,L,dv]. By the chain rule, with N = Phi_Q S and
+    D = Phi_Q z:
+        dN = dout / D,  dD = -(dout . out) / D,
+        dPhi_Q = dN S^T + dD z^T,  dS = Phi_Q^T dN,  dz = Phi_Q^T dD,
+        dPhi_K = V dS^T + 1 dz^T,  dV = Phi_K dS,
+    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64."""
+    pq = features(q, omega, kind, eps)
+    pk = features(k, omega, kind, eps)
+    v = _f64(v)
+    g = _f64(dout)
+    S = np.einsum("...lm,...le->...me", pk, v)
+    z = np.sum(pk, axis=-2)
+    N = np.einsum("...lm,...me->...le", pq, S)
+    D = np.einsum("...lm,...m->...l", pq, z)
+    out = N / D[..., None]
+    dN = g / D[..., None]
+    dD = -np.sum(g * out, axis=-1) / D
+    dpq = np.einsum("...le,...me->...lm", dN, S) + dD[..., None] * z[..., None, :]
+    dS = np.einsum("...lm,...le->...me", pq, dN)
+    dz = np.einsum("...lm,...l->...m", pq, dD)
+    dpk = np.einsum("...le,...me->...lm", v, dS) + dz[..., None, :]
+    dv = np.einsum("...lm,...me->...le", pk, dS)
+    return (_feature_backward(q, omega, pq, dpq, kind), _feature_backward(k, omega, pk, dpk, kind), dv)
+
+
 def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bool = False):
     """Causal estimator as the plain recurrence over positions (one token at a time)."""
     pq = features(q, omega, kind, eps)

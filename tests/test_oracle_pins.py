@@ -188,6 +188,58 @@ def test_gated_decode_recurrence_equals_unrolled_sum():
     assert np.max(np.abs(tiny - v)) < 1e-12
 
 
+@pytest.mark.parametrize("kind,eps", [("prf", 0.0), ("relu", 1e-3)])
+def test_bidir_backward_matches_finite_differences(kind, eps):
+    """The chain-rule gradients of equation 4 against central differences of the forward estimator (fp64):
+    every entry of dq, dk and dv for a random linear functional of the output."""
+    B, H, L, d, dv, m = 1, 2, 6, 8, 4, 16
+    rng = np.random.default_rng(3)
+    q = rng.normal(size=(B, H, L, d)) * 0.6
+    k = rng.normal(size=(B, H, L, d)) * 0.6
+    v = rng.normal(size=(B, H, L, dv))
+    g = rng.normal(size=(B, H, L, dv))
+    om = make_omega(13, H, m, d)
+    grads = oracle.bidir_backward(q, k, v, om, g, kind, eps)
+    h = 1e-6
+    for x, gx in zip((q, k, v), grads):
+        num = np.empty_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fp = np.sum(g * bidir(*args_p, om, kind, eps))
+            fm = np.sum(g * bidir(*args_m, om, kind, eps))
+            num[i] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - gx)) < 1e-6 * max(1.0, np.max(np.abs(gx))), (kind, np.max(np.abs(num - gx)))
+
+
+def test_bidir_backward_query_features_gradient_is_orthogonal_to_features():
+    """The output is invariant to a per-row scale of the query features (it cancels in the ratio), so
+    phi(q_i) . dPhi_Q_i = 0 for every row; hence dq has no |q|^2 term. Checked by rescaling q's features:
+    the output and hence the gradients are unchanged."""
+    B, H, L, d, dv, m = 1, 1, 9, 16, 8, 32
+    rng = np.random.default_rng(4)
+    q = rng.normal(size=(B, H, L, d)) * 0.5
+    k = rng.normal(size=(B, H, L, d)) * 0.5
+    v = rng.normal(size=(B, H, L, dv))
+    g = rng.normal(size=(B, H, L, dv))
+    om = make_omega(14, H, m, d)
+    pq = features(q, om)
+    pk = features(k, om)
+    S = np.einsum("...lm,...le->...me", pk, v)
+    z = pk.sum(-2)
+    out, _, _ = bidir_from_features(pq, pk, v)
+    D = np.einsum("...lm,...m->...l", pq, z)
+    dpq = np.einsum("...le,...me->...lm", g / D[..., None], S) - (np.sum(g * out, -1) / D)[..., None] * z[..., None, :]
+    assert np.max(np.abs(np.sum(pq * dpq, -1))) < 1e-12
+    out2, _, _ = bidir_from_features(pq * rng.uniform(0.5, 2.0, size=(B, H, L, 1)), pk, v)
+    assert np.max(np.abs(out2 - out)) < 1e-12
+
+
 # ---------------------------------------------------------------- feature map
 
 def _prf_single_estimates(x, y, om):
