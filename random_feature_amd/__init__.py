@@ -47,6 +47,10 @@ _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i
 _lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_decode_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+_lib.favor_bidir_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]
+_lib.favor_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.favor_backward_workspace_size.restype = _sz
 _lib.favor_workspace_size.restype = _sz
 _lib.favor_timing_enable.argtypes = [_i]
 _lib.favor_timing_enable.restype = _i
@@ -55,11 +59,11 @@ _lib.favor_timing_read.restype = _i
 _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
 for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
-            "favor_causal", "favor_decode", "favor_decode_gated"):
+            "favor_bidir_backward", "favor_causal", "favor_decode", "favor_decode_gated"):
     getattr(_lib, _fn).restype = _i
 
 EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
-            "favor_causal",
+            "favor_bidir_backward", "favor_backward_workspace_size", "favor_causal",
             "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
             "favor_status_string"]
 
@@ -189,6 +193,31 @@ def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool 
                                   _kind(kind), float(eps), 1 if renormalize else 0, 1 if out_f32 else 0, _ptr(out),
                                   _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
     return out
+
+
+def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None):
+    """Gradients (dq, dk, dv) of bidir()'s output for the upstream gradient `dout` (the forward sums are
+    recomputed)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, n, 4)
+    _need(omega, "omega", 3)
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    m = omega.shape[1]
+    if ws is None:
+        n = int(_lib.favor_backward_workspace_size(B, H, L, d, dv, m, _dtype_code(q)))
+        if n == 0:
+            raise FavorError("favor_backward_workspace_size", 1)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    gdt = torch.float32 if grad_f32 else q.dtype
+    dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
+    dk = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
+    dvv = torch.empty((B, H, L, dv), dtype=gdt, device=q.device)
+    _check("favor_bidir_backward",
+           _lib.favor_bidir_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv,
+                                     m, _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk),
+                                     _ptr(dvv), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
+    return dq, dk, dvv
 
 
 def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,

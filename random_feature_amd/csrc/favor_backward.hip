@@ -1,0 +1,971 @@
+// Gradients of bidirectional FAVOR+ on gfx950.
+//
+// Performer paper, equation 4 and Algorithm 1: out_i = N_i / D_i with N = Phi_Q S, D = Phi_Q z,
+// S = Phi_K^T V, z = Phi_K^T 1. For an upstream gradient g = dL/dout the chain rule gives
+//   W_i = [g_i, -(g_i . out_i)] / D_i                       (dv + 1 columns)
+//   dPhi_Q = W S_aug^T,  dS_aug = Phi_Q^T W,   S_aug = [S z], dS_aug = [dS dz]
+//   dPhi_K = [V 1] dS_aug^T,  dV = Phi_K dS
+// and through the positive feature map phi(x) = exp(w.xs - |xs|^2/2)/sqrt(m), xs = d^-1/4 x:
+//   dx = d^-1/4 (Omega^T (phi * dphi) - xs sum_r phi_r dphi_r).
+// For the queries sum_r phi_r dphi_r = g_i . out_i - g_i . out_i = 0, so only the first term
+// remains. Every per-row constant of the query features and the keys' common constant
+// cancel in phi * dphi (query side) or come out as one per-key factor (key side), so the
+// kernels work with stabilised features throughout:
+//   query side: phi' = 2^(a' - max_r a'), features of the row scaled to a largest entry of 1;
+//   key side:   phi' likewise, and the key's true scale F_j = 2^(max_r a'_j - n'_j - M) / sqrt(m)
+//               relative to the stabilised sums (M the keys' common maximum of the forward).
+// Kernels, in launch order:
+//   omega_frag_kernel / omegaT_frag_kernel  Omega' fragments for the projections and for
+//                       Omega'^T (the gradient's back-projection)
+//   kv_reduce_kernel    the forward key/value reduction (recomputed), then
+//   combine_rows_kernel S_aug of every (b,h) as fp32 rows, and the keys' maximum M
+//   bwd_q_kernel        per 32-query tile: Phi_Q, D, W, dPhi_Q = W S_aug^T on MFMA, dq, and
+//                       the piece's partial dS_aug += Phi_Q^T W
+//   combine_rows_kernel dS_aug of every (b,h) as fp32 rows
+//   bwd_k_kernel        per 32-key tile: Phi_K, dPhi_K = [V 1] dS_aug^T, dk and dV
+// The two products that subtract nearly equal terms (dPhi_Q's S g - z (g . out) and dPhi_K's
+// dS v + dz) take fp16 operands (11-bit mantissas) scaled by powers of two: S_aug and dS_aug
+// per (b,h) to a largest magnitude in [8, 16), W and [V 1] per row to one in [1/2, 1); the
+// scales are undone exactly on the results. Products without cancellation use bf16.
+#include "favor_device.hpp"
+#include "favor_plan.hpp"
+#include "favor_reduce.hpp"
+#include "favor_tiles.hpp"
+#include "favor_timing.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+namespace favor {
+
+// operand types of the backward: XS for the scaled products, XB for the range-safe ones
+template <typename T> struct BwdOps;
+template <> struct BwdOps<bf16> { using XS = f16; using XB = bf16; };
+template <> struct BwdOps<float> { using XS = float; using XB = float; };
+
+// Omega'^T fragments, the A operand (rows = d, k = features in the paired slot order of
+// stacked accumulator tiles): frag[h][db][fc][lane][j] = scale * omega[h][f][db*16 + c] with
+// f = fc*32 + 16(j>>2) + 4g + (j&3) (0 past m or d).
+template <typename T>
+__global__ void omegaT_frag_kernel(const float* __restrict__ omega, int H, int m, int d, float scale,
+                                   T* __restrict__ frag) {
+  const int nfc = (m + 31) / 32, ndb = (d + 15) / 16;
+  const long long total = (long long)H * ndb * nfc * 64;
+  for (long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(id & 63);
+    unsigned rest = (unsigned)(id >> 6);
+    const int fc = (int)(rest % (unsigned)nfc);
+    rest /= (unsigned)nfc;
+    const int db = (int)(rest % (unsigned)ndb);
+    const int h = (int)(rest / (unsigned)ndb);
+    const int c = lane & 15, g = lane >> 4;
+    const int dd = db * 16 + c;
+    vec8<T> x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = fc * 32 + 16 * (j >> 2) + 4 * g + (j & 3);
+      x[j] = to_t<T>((f < m && dd < d) ? omega[((size_t)h * m + f) * d + dd] * scale : 0.f);
+    }
+    st8<T>(frag + (size_t)id * 8, x);
+  }
+}
+
+// Row length (floats) of S_aug / dS_aug rows: dv + 1 columns padded to whole 32-column chunks.
+template <int DV> struct Rows {
+  static constexpr int RC = ((DV + 1 + 31) / 32) * 32;
+  static constexpr int KC = RC / 32;
+};
+
+// Per (b*h, 32-feature chunk): the partials of the pieces of that (b,h) (fragment layout of
+// kv_reduce_kernel), scaled by 2^(M_piece,wave - M_max) when `scaled`, summed and written as
+// fp32 rows rows[bh][f][RC] (value columns, the z column at DV, zeros after); the common
+// maximum goes to gmx[bh] (0 when not scaled) unless gmx is null. tpb, T_all and G describe
+// the pieces that wrote the partials (slot = piece + bh); NWP waves per piece wrote maxima.
+template <int DV, int M, int NWP>
+__global__ void __launch_bounds__(256)
+combine_rows_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
+                    int tpb, long long T_all, int G, int scaled, float* __restrict__ rows,
+                    float* __restrict__ gmx) {
+  constexpr int FBP = M / (16 * NWP);
+  constexpr int NB = DV / 16 + 1;
+  constexpr int NFC = (M + 31) / 32;
+  constexpr int RC = Rows<DV>::RC;
+  const int bh = blockIdx.x / NFC, fc = blockIdx.x % NFC;
+  const long long i_lo = piece_of((long long)bh * tpb, T_all, G);
+  const long long i_hi = piece_of((long long)(bh + 1) * tpb - 1, T_all, G);
+  const int np = (int)(i_hi - i_lo + 1);
+  const int wv = (fc * 32) / (FBP * 16);
+  float gmax = -INFINITY;
+  if (scaled)
+    for (int k = 0; k < np * NWP; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NWP + bh) * NWP + k % NWP]);
+  if (gmx && fc == 0 && threadIdx.x == 0) gmx[bh] = scaled ? gmax : 0.f;
+  float* out = rows + (size_t)bh * M * RC;
+  for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {
+    const int nb = e >> 6, lane = e & 63;
+    const int c = lane & 15, g = lane >> 4;
+    f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (nb < NB - 1 || c == 0) {
+      for (int k = 0; k < np; ++k) {
+        const size_t slot = (size_t)(i_lo + k) + bh;
+        const float sc = scaled ? fast_exp2(pmax[slot * NWP + wv] - gmax) : 1.f;
+        const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
+                                         : zpart + ((slot * NFC + fc) * 4 + g) * 8;
+        lo += reinterpret_cast<const f32x4*>(src)[0] * sc;
+        hi += reinterpret_cast<const f32x4*>(src)[1] * sc;
+      }
+    }
+    const int col = nb * 16 + c;  // the z column is DV = (NB - 1) * 16; past it zeros
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f0 = fc * 32 + 4 * g + i, f1 = f0 + 16;
+      if (f0 < M) out[(size_t)f0 * RC + col] = lo[i];
+      if (f1 < M) out[(size_t)f1 * RC + col] = hi[i];
+    }
+  }
+  // columns past the last block
+  constexpr int PAD = RC - NB * 16;
+  if constexpr (PAD > 0)
+    for (int e = threadIdx.x; e < 32 * PAD; e += blockDim.x) {
+      const int f = fc * 32 + e / PAD, col = NB * 16 + e % PAD;
+      if (f < M) out[(size_t)f * RC + col] = 0.f;
+    }
+}
+
+// Largest magnitude across the NW waves of a workgroup (xch: NW floats; two barriers).
+template <int NW>
+__device__ __forceinline__ float wg_absmax(float x, float* xch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  x = wave_max(x);
+  if (lane == 0) xch[w] = x;
+  lds_barrier();
+  float r = xch[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, xch[i]);
+  lds_barrier();
+  return r;
+}
+
+// exponent e with x * 2^-e in [1/2, 1) (0 for x = 0 or not finite)
+__device__ __forceinline__ int scale_exp(float x) {
+  int e = 0;
+  if (x > 0.f && x < INFINITY) (void)frexpf(x, &e);
+  return e;
+}
+
+// ---------------------------------------------------------------- query side
+// Workgroup = NW waves over one piece of the flattened query-tile space; wave w owns the
+// FB*16 features of the reduction's split. Per tile of 32 queries:
+//   projection   A = Omega' (rows = features), B = Q rows -> a'[feature][query]; the exact
+//                row maximum across the waves; phi' = 2^(a' - max) in (0, 1]
+//   g rows       scaled per query to [1/2, 1) (fp16, exponent e_i)
+//   u            A = S rows (fp16, scaled by 2^-eS per (b,h)), B = g rows -> u = S g (scaled)
+//   D', A        D'_i = phi'_i . z and A_i = phi'_i . u_i, fp32 sums over the features, across
+//                the waves through LDS; gamma_i = g_i . out_i = A_i 2^(eS + e_i) / D'_i
+//   dPhi_Q       phi' * (u - z A/D'), the scaled dPhi_Q (phi'.dPhi_Q = 0 by construction)
+//   dq           A = Omega'^T fragments, B = that product (fp16, paired feature slots),
+//                partial over the wave's features, summed through LDS, times 2^(eS + e_i)/D'_i
+//   dS_aug       W_i = [g_i, -gamma_i]/D'_i (rows), A = phi'^T (transposing reads of the phi' rows
+//                in LDS), B = W (transposing reads), both as sums of two bf16 parts;
+//                accumulated over the piece's tiles of one (b,h) and written as a partial in
+//                the reduction's fragment layout
+template <typename T, int D, int DV, int M>
+__global__ void __launch_bounds__(64 * RedSplit<M>::NW, 1)
+bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
+             const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ srow, int H, int L, int tpb,
+             long long T_all, int G, int grad_f32, float* __restrict__ dpart, float* __restrict__ dzpart,
+             void* __restrict__ dq) {
+  using P = typename Ops<T>::P;
+  using XS = typename BwdOps<T>::XS;
+  using XB = typename BwdOps<T>::XB;
+  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
+  constexpr int NT = 64 * NW;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NDB = D / 16;
+  constexpr int NB = DV / 16 + 1;
+  constexpr int NFC = (M + 31) / 32;
+  constexpr int NFCW = (FB + 1) / 2;
+  constexpr int RC = Rows<DV>::RC, KC = Rows<DV>::KC;
+  constexpr int KROW = D + 8;
+  constexpr int EROW = FB * 16 + 8;
+  constexpr int WROW = RC + 8;
+  constexpr int CPR = DV / 8;                     // 8-column chunks of a g row
+  constexpr int IPT = (32 * CPR + NT - 1) / NT;  // (query, chunk) items per thread
+  using Rg = Ring<T, D, DV, NT, false>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) P qs[32 * KROW];
+  constexpr int NSPL = sizeof(XB) == 2 ? 2 : 1;  // bf16 operands of dS_aug as a sum of two (hi + lo)
+  __shared__ __attribute__((aligned(16))) XB erow[NSPL][NW][32 * EROW];
+  __shared__ __attribute__((aligned(16))) XS gsr[32 * WROW];
+  __shared__ __attribute__((aligned(16))) XB wbr[NSPL][32 * WROW];
+  __shared__ __attribute__((aligned(16))) float xq[NW][2 * NDB * 256];
+  __shared__ __attribute__((aligned(16))) float qmx[NW][32];
+  __shared__ __attribute__((aligned(16))) float dsum[NW][32];
+  __shared__ __attribute__((aligned(16))) float asum[NW][32];
+  __shared__ __attribute__((aligned(16))) float gex[32], rsc[32];
+  __shared__ float xch[NW];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const long long pc = xcd_remap(blockIdx.x, gridDim.x);
+  const long long t_beg = piece_start(pc, T_all, G), t_end = piece_start(pc + 1, T_all, G);
+  if (t_beg >= t_end) return;
+  const int n_tiles = (int)(t_end - t_beg);
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+  TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
+
+  vec8<P> om[FB][DC];
+  vec8<P> omt[NDB][NFCW];
+  vec8<XS> sa[FB][KC];
+  float zv[FB][4];  // z of this lane's features (4g + i of each block)
+  f32x4 sacc[FB][NB];
+  int eS = 0;  // S rows were scaled by 2^-eS
+  int cur_bh = -1;
+
+  auto zero_sums = [&]() {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // partial dS_aug of (piece, bh) in the reduction's fragment layout (slot = piece + bh)
+  auto flush = [&](int fbh) {
+    const size_t slot = (size_t)pc + fbh;
+#pragma unroll
+    for (int p = 0; p < NFCW; ++p) {
+      const int fc = (w * FB) / 2 + p;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const f32x4 lo = sacc[2 * p][nb];
+        const f32x4 hi = (2 * p + 1 < FB) ? sacc[2 * p + 1][nb] : f32x4{0.f, 0.f, 0.f, 0.f};
+        float* dst = (nb < NB - 1) ? dpart + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
+                                   : dzpart + ((slot * NFC + fc) * 4 + g) * 8;
+        if (nb < NB - 1 || c == 0) {
+          reinterpret_cast<f32x4*>(dst)[0] = lo;
+          reinterpret_cast<f32x4*>(dst)[1] = hi;
+        }
+      }
+    }
+  };
+
+  Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), true, ring0);
+  ahead.next();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const int bh = cur.bh, tok0 = cur.tok0();
+    // ---- this tile's Q rows land and are converted; the next tile's copies start
+    wait_vmcnt<0>();  // the copies, and every store of the previous tile
+    Rg::template convert<P, KROW, kNormNone>(ring[buf], qs, nullptr, 0.f, L);
+    if (it + 1 < n_tiles) {
+      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), true, ring0 + (buf ^ 1) * Rg::SLOT);
+      ahead.next();
+    }
+    // ---- a new (b,h): close the old one's sums, load this one's operands
+    if (bh != cur_bh) {
+      if (cur_bh >= 0) flush(cur_bh);
+      zero_sums();
+      const int h = bh % H;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw)
+          omt[db][fcw] = ld8<P>(omT + ((((size_t)h * NDB + db) * NFC + (w * FB) / 2 + fcw) * 64 + lane) * 8);
+      const float* rows = srow + (size_t)bh * M * RC;
+      f32x8 sf[FB][KC];
+      float amax = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int f = (w * FB + fb) * 16 + c;
+          const f32x4* src = reinterpret_cast<const f32x4*>(rows + (size_t)f * RC + kc * 32 + 8 * g);
+          const f32x4 a = src[0], b = src[1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sf[fb][kc][j] = a[j];
+            sf[fb][kc][j + 4] = b[j];
+            amax = fmaxf(amax, fmaxf(fabsf(a[j]), fabsf(b[j])));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zv[fb][i] = rows[(size_t)((w * FB + fb) * 16 + 4 * g + i) * RC + DV];
+      }
+      eS = scale_exp(wg_absmax<NW>(amax, xch)) - 4;  // largest |S_aug| * 2^-eS in [8, 16)
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sa[fb][kc][j] = to_t<XS>(ldexpf(sf[fb][kc][j], -eS));
+      cur_bh = bh;
+    }
+    // ---- g rows scaled per query (rows past L: zero)
+    float gv[IPT][8];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int item = threadIdx.x + u * NT;
+      const int row = item / CPR, c8 = item % CPR;
+      const bool ok = item < 32 * CPR && tok0 + row < L;
+      const size_t off = ((size_t)bh * L + min(tok0 + row, L - 1)) * DV + c8 * 8;
+      const vec8<T> g8 = ld8<T>(dOut + off);
+      float mabs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        gv[u][j] = ok ? to_f(g8[j]) : 0.f;
+        mabs = fmaxf(mabs, fabsf(gv[u][j]));
+      }
+      mabs = lanes_max<CPR>(mabs);
+      if (item < 32 * CPR) {
+        const int eg = scale_exp(mabs);
+        vec8<XS> x8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x8[j] = to_t<XS>(ldexpf(gv[u][j], -eg));
+        *reinterpret_cast<vec8<XS>*>(&gsr[row * WROW + c8 * 8]) = x8;
+        if (c8 == 0) {
+          for (int col = DV; col < RC; ++col) gsr[row * WROW + col] = to_t<XS>(0.f);
+          gex[row] = (float)eg;
+        }
+      }
+    }
+    lds_barrier();  // qs of this tile, scaled g rows
+
+    // ---- projection and row maxima
+    f32x4 pq[2][FB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      vec8<P> qf[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int col = dc * 32 + 8 * g;
+        qf[dc] = (col < D) ? ld8<P>(&qs[(tb * 16 + c) * KROW + col]) : zero8<P>();
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        pq[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) mma16(pq[tb][fb], om[fb][dc], qf[dc]);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
+      mx = group_max(mx);
+      if (g == 0) qmx[w][tb * 16 + c] = mx;
+    }
+    // ---- u = S g (scaled), [feature][query]
+    f32x4 uq[2][FB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      vec8<XS> gf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) gf[kc] = ld8<XS>(&gsr[(tb * 16 + c) * WROW + kc * 32 + 8 * g]);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        uq[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma16(uq[tb][fb], sa[fb][kc], gf[kc]);
+      }
+    }
+    lds_barrier();  // B1: row maxima
+
+    // ---- phi' = 2^(a' - max); D' and A partials; phi' rows for the dS transposes
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float mx = qmx[0][tb * 16 + c];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
+      float dz = 0.f, da = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        vec4<XB> e4, e4lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ph = fast_exp2(pq[tb][fb][i] - mx);
+          pq[tb][fb][i] = ph;
+          dz += ph * zv[fb][i];
+          da += ph * uq[tb][fb][i];
+          e4[i] = to_t<XB>(ph);
+          e4lo[i] = to_t<XB>(ph - to_f(e4[i]));
+        }
+        *reinterpret_cast<vec4<XB>*>(&erow[0][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4;
+        if constexpr (NSPL == 2) *reinterpret_cast<vec4<XB>*>(&erow[NSPL - 1][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4lo;
+      }
+      dz = group_sum(dz);
+      da = group_sum(da);
+      if (g == 0) {
+        dsum[w][tb * 16 + c] = dz;
+        asum[w][tb * 16 + c] = da;
+      }
+    }
+    lds_barrier();  // B2: D' and A partials, phi' rows
+
+    // ---- dPhi_Q (scaled) times phi', and the dq^T partial over this wave's features
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float den = 0.f, aa = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        den += dsum[ww][tb * 16 + c];
+        aa += asum[ww][tb * 16 + c];
+      }
+      const float ad = aa / den;
+      vec8<XS> pb[NFCW];
+#pragma unroll
+      for (int fcw = 0; fcw < NFCW; ++fcw)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int fb = 2 * fcw + (j >> 2), i = j & 3;
+          pb[fcw][j] = to_t<XS>(fb < FB ? pq[tb][fb][i] * (uq[tb][fb][i] - zv[fb][i] * ad) : 0.f);
+        }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, omt[db][fcw], pb[fcw]);
+        *reinterpret_cast<f32x4*>(&xq[w][((db * 2 + tb) * 64 + lane) * 4]) = a;
+      }
+    }
+    // ---- W rows (bf16): [g, -gamma] / D'
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int item = threadIdx.x + u * NT;
+      if (item < 32 * CPR) {
+        const int row = item / CPR, c8 = item % CPR;
+        float den = 0.f, aa = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          den += dsum[ww][row];
+          aa += asum[ww][row];
+        }
+        const float rd = 1.f / den;
+        vec8<XB> wb, wl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = gv[u][j] * rd;
+          wb[j] = to_t<XB>(x);
+          wl[j] = to_t<XB>(x - to_f(wb[j]));
+        }
+        *reinterpret_cast<vec8<XB>*>(&wbr[0][row * WROW + c8 * 8]) = wb;
+        if constexpr (NSPL == 2) *reinterpret_cast<vec8<XB>*>(&wbr[NSPL - 1][row * WROW + c8 * 8]) = wl;
+        if (c8 == 0) {
+          const int e = (int)gex[row] + eS;
+          const float gam = ldexpf(aa, e) * rd;  // g . out
+          for (int col = DV; col < RC; ++col) {
+            const float x = col == DV ? -gam * rd : 0.f;
+            const XB xh = to_t<XB>(x);
+            wbr[0][row * WROW + col] = xh;
+            if constexpr (NSPL == 2) wbr[NSPL - 1][row * WROW + col] = to_t<XB>(x - to_f(xh));
+          }
+          rsc[row] = ldexpf(rd * (1.f / kLog2e), e);
+        }
+      }
+    }
+    lds_barrier();  // B3: dq partials, W rows
+
+    // ---- dS_aug += phi'^T W over the tile's queries: with bf16 operands as hi + lo pairs,
+    // hi*hi + hi*lo + lo*hi (the sums over the queries cancel, so 8-bit operands would not do)
+    {
+      auto tr8 = [&](const XB* base, int stride, int col0) {
+        vec8<XB> r;
+        if constexpr (sizeof(XB) == 2) {
+          const bf16x4 lo = lds_read_tr4(reinterpret_cast<const bf16*>(base + (4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
+          const bf16x4 hi = lds_read_tr4(reinterpret_cast<const bf16*>(base + (16 + 4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r[i] = lo[i];
+            r[i + 4] = hi[i];
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) r[jj] = base[(16 * (jj >> 2) + 4 * g + (jj & 3)) * stride + col0 + c];
+        }
+        return r;
+      };
+      vec8<XB> wt[NSPL][NB];
+#pragma unroll
+      for (int sp = 0; sp < NSPL; ++sp)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) wt[sp][nb] = tr8(wbr[sp], WROW, nb * 16);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        const vec8<XB> ea = tr8(&erow[0][w][0], EROW, fb * 16);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], ea, wt[0][nb]);
+        if constexpr (NSPL == 2) {
+          const vec8<XB> el = tr8(&erow[NSPL - 1][w][0], EROW, fb * 16);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            mma16(sacc[fb][nb], ea, wt[NSPL - 1][nb]);
+            mma16(sacc[fb][nb], el, wt[0][nb]);
+          }
+        }
+      }
+    }
+
+    // ---- dq: the waves' partials summed, unscaled, stored (rows past L skipped)
+    constexpr int CD = D / 8;
+    for (int e = threadIdx.x; e < 32 * CD; e += NT) {
+      const int qrow = e / CD, c8 = e % CD;
+      const int tok = tok0 + qrow;
+      if (tok >= L) continue;
+      const int tb = qrow >> 4, cq = qrow & 15;
+      const int db = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* base = &xq[ww][((db * 2 + tb) * 64 + cq + 16 * g0) * 4];
+        lo += *reinterpret_cast<const f32x4*>(base);
+        hi += *reinterpret_cast<const f32x4*>(base + 64);
+      }
+      const float r = rsc[qrow];
+      const size_t off = ((size_t)bh * L + tok) * D + c8 * 8;
+      if (grad_f32) {
+        f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off);
+        o4[0] = lo * r;
+        o4[1] = hi * r;
+      } else {
+        vec8<T> o8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o8[i] = to_t<T>(lo[i] * r);
+          o8[i + 4] = to_t<T>(hi[i] * r);
+        }
+        st8<T>(reinterpret_cast<T*>(dq) + off, o8);
+      }
+    }
+    cur.next();
+  }
+  flush(cur_bh);
+}
+
+// ---------------------------------------------------------------- key side
+// Workgroup = NW waves over one piece of the flattened key-tile space. Per tile of 32 keys:
+//   projection   A = Omega', B = K rows (fp16, converted with |k|^2 n'-norms) -> a'[feature][key];
+//                exact row maximum across the waves; phi' = 2^(a' - max) in (0, 1]; the key's
+//                scale F_j = 2^(max_j - n'_j - M) (0 for keys past L)
+//   [V 1] rows   scaled per key to [1/2, 1), fp16, in LDS
+//   dPhi_K       A = dS_aug rows (fp16, scaled per (b,h)), B = [V 1] rows -> [feature][key]
+//   dk           A = Omega'^T, B = phi' * dPhi_K; minus d^-1/2 k_j sum_r phi'_r dPhi_K,r
+//   dV           A = dS^T (bf16 fragments, paired features), B = phi' (bf16) -> dV^T
+//   partial sums over the waves through LDS, scaled by F_j (and the operand scales), stored.
+template <typename T, int D, int DV, int M>
+__global__ void __launch_bounds__(64 * RedSplit<M>::NW, 1)
+bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
+             const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ dsrow,
+             const float* __restrict__ gmx, int H, int L, int tpb, long long T_all, int G, float nscale,
+             float s2, int grad_f32, void* __restrict__ dk, void* __restrict__ dv) {
+  using P = typename Ops<T>::P;
+  using XS = typename BwdOps<T>::XS;
+  using XB = typename BwdOps<T>::XB;
+  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
+  constexpr int NT = 64 * NW;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NDB = D / 16;
+  constexpr int NVB = DV / 16;
+  constexpr int NFC = (M + 31) / 32;
+  constexpr int NFCW = (FB + 1) / 2;
+  constexpr int RC = Rows<DV>::RC, KC = Rows<DV>::KC;
+  constexpr int KROW = D + 8;
+  constexpr int WROW = RC + 8;
+  constexpr int CPR = DV / 8;
+  constexpr int IPT = (32 * CPR + NT - 1) / NT;
+  using Rg = Ring<T, D, DV, NT, true>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
+  __shared__ __attribute__((aligned(16))) float kn[2][32];
+  __shared__ __attribute__((aligned(16))) XS vsr[32 * WROW];
+  __shared__ __attribute__((aligned(16))) float xk[NW][2 * NDB * 256];
+  __shared__ __attribute__((aligned(16))) float xv[NW][2 * NVB * 256];
+  __shared__ __attribute__((aligned(16))) float qmx[NW][32];
+  __shared__ __attribute__((aligned(16))) float rho[NW][32];
+  __shared__ __attribute__((aligned(16))) float vex[32];
+  __shared__ float xch[NW];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const long long pc = xcd_remap(blockIdx.x, gridDim.x);
+  const long long t_beg = piece_start(pc, T_all, G), t_end = piece_start(pc + 1, T_all, G);
+  if (t_beg >= t_end) return;
+  const int n_tiles = (int)(t_end - t_beg);
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+  TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
+
+  vec8<P> om[FB][DC];
+  vec8<P> omt[NDB][NFCW];
+  vec8<XS> da[FB][KC];
+  vec8<XB> dt[NVB][NFCW];
+  float eD = 0.f, gm = 0.f;
+  int cur_bh = -1;
+
+  Rg::issue(K, V, L, ahead.bh, ahead.tok0(), true, ring0);
+  ahead.next();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int buf = it & 1;
+    const int bh = cur.bh, tok0 = cur.tok0();
+    wait_vmcnt<0>();  // this tile's copies, and every store of the previous tile
+    Rg::template convert<P, KROW, kNormSq>(ring[buf], ks[buf], kn[buf], nscale, L - tok0);
+    if (it + 1 < n_tiles) {
+      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), true, ring0 + (buf ^ 1) * Rg::SLOT);
+      ahead.next();
+    }
+    if (bh != cur_bh) {
+      const int h = bh % H;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw)
+          omt[db][fcw] = ld8<P>(omT + ((((size_t)h * NDB + db) * NFC + (w * FB) / 2 + fcw) * 64 + lane) * 8);
+      const float* rows = dsrow + (size_t)bh * M * RC;
+      f32x8 sf[FB][KC];
+      float amax = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int f = (w * FB + fb) * 16 + c;
+          const f32x4* src = reinterpret_cast<const f32x4*>(rows + (size_t)f * RC + kc * 32 + 8 * g);
+          const f32x4 a = src[0], b = src[1];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sf[fb][kc][j] = a[j];
+            sf[fb][kc][j + 4] = b[j];
+            amax = fmaxf(amax, fmaxf(fabsf(a[j]), fabsf(b[j])));
+          }
+        }
+      // dS^T fragments for dV: A[m = column][k = feature, paired slots], unscaled bf16
+#pragma unroll
+      for (int cb = 0; cb < NVB; ++cb)
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int fb = 2 * fcw + (j >> 2);
+            const int f = (w * FB + fb) * 16 + 4 * g + (j & 3);
+            dt[cb][fcw][j] = to_t<XB>(fb < FB ? rows[(size_t)f * RC + cb * 16 + c] : 0.f);
+          }
+      gm = gmx[bh];
+      eD = (float)(scale_exp(wg_absmax<NW>(amax, xch)) - 4);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) da[fb][kc][j] = to_t<XS>(ldexpf(sf[fb][kc][j], -(int)eD));
+      cur_bh = bh;
+    }
+    lds_barrier();  // ks, kn of this tile
+
+    // ---- projection and row maxima
+    f32x4 pk[2][FB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      vec8<P> kf[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int col = dc * 32 + 8 * g;
+        kf[dc] = (col < D) ? ld8<P>(&ks[buf][(tb * 16 + c) * KROW + col]) : zero8<P>();
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        pk[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) mma16(pk[tb][fb], om[fb][dc], kf[dc]);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pk[tb][fb][i]);
+      mx = group_max(mx);
+      if (g == 0) qmx[w][tb * 16 + c] = mx;
+    }
+    // ---- [V 1] rows scaled per key to [1/2, 1) (fp16)
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int item = threadIdx.x + u * NT;
+      const int row = item / CPR, c8 = item % CPR;
+      float vals[8];
+      float mabs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vals[j] = item < 32 * CPR
+                      ? to_f(*reinterpret_cast<const T*>(ring[buf] + Rg::v_off(row < 32 ? row : 31, c8 * 8 + j)))
+                      : 0.f;
+        mabs = fmaxf(mabs, fabsf(vals[j]));
+      }
+      mabs = lanes_max<CPR>(mabs);
+      if (item < 32 * CPR) {
+        const int ev = scale_exp(fmaxf(mabs, 1.f));
+        vec8<XS> x8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x8[j] = to_t<XS>(ldexpf(vals[j], -ev));
+        *reinterpret_cast<vec8<XS>*>(&vsr[row * WROW + c8 * 8]) = x8;
+        if (c8 == 0) {
+          for (int col = DV; col < RC; ++col) vsr[row * WROW + col] = to_t<XS>(col == DV ? ldexpf(1.f, -ev) : 0.f);
+          vex[row] = (float)ev;
+        }
+      }
+    }
+    lds_barrier();  // B1: row maxima, [V 1] rows
+
+    // ---- phi', dPhi_K, P, rho; dk and dV partials
+    vec8<XS> pb[2][NFCW];
+    vec8<XB> fk[2][NFCW];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float mx = qmx[0][tb * 16 + c];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[tb][fb][i] = fast_exp2(pk[tb][fb][i] - mx);
+      vec8<XS> vf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) vf[kc] = ld8<XS>(&vsr[(tb * 16 + c) * WROW + kc * 32 + 8 * g]);
+      f32x4 dp[FB];
+      float r = 0.f;
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        dp[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) mma16(dp[fb], da[fb][kc], vf[kc]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dp[fb][i] *= pk[tb][fb][i];  // P = phi' * dPhi_K (scaled)
+          r += dp[fb][i];
+        }
+      }
+      r = group_sum(r);
+      if (g == 0) rho[w][tb * 16 + c] = r;
+#pragma unroll
+      for (int fcw = 0; fcw < NFCW; ++fcw)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int fb = 2 * fcw + (j >> 2);
+          pb[tb][fcw][j] = to_t<XS>(fb < FB ? dp[fb][j & 3] : 0.f);
+          fk[tb][fcw][j] = to_t<XB>(fb < FB ? pk[tb][fb][j & 3] : 0.f);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, omt[db][fcw], pb[tb][fcw]);
+        *reinterpret_cast<f32x4*>(&xk[w][((db * 2 + tb) * 64 + lane) * 4]) = a;
+      }
+#pragma unroll
+    for (int cb = 0; cb < NVB; ++cb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, dt[cb][fcw], fk[tb][fcw]);
+        *reinterpret_cast<f32x4*>(&xv[w][((cb * 2 + tb) * 64 + lane) * 4]) = a;
+      }
+    lds_barrier();  // B2: partials
+
+    // ---- dk and dV: sums over the waves, the key's scale, stored (keys past L skipped)
+    constexpr int CD = D / 8;
+    for (int e = threadIdx.x; e < 32 * (CD + CPR); e += NT) {
+      const bool isk = e < 32 * CD;
+      const int e2 = isk ? e : e - 32 * CD;
+      const int ncol8 = isk ? CD : CPR;
+      const int krow = e2 / ncol8, c8 = e2 % ncol8;
+      const int tok = tok0 + krow;
+      if (tok >= L) continue;
+      const int tb = krow >> 4, cq = krow & 15;
+      const int blk = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
+      float mx = qmx[0][krow];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][krow]);
+      const float lf = mx - kn[buf][krow] - gm;  // log2 of the key's scale F_j
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+      if (isk) {
+        float rs = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float* base = &xk[ww][((blk * 2 + tb) * 64 + cq + 16 * g0) * 4];
+          lo += *reinterpret_cast<const f32x4*>(base);
+          hi += *reinterpret_cast<const f32x4*>(base + 64);
+          rs += rho[ww][krow];
+        }
+        const float f = fast_exp2(lf + eD + vex[krow]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] = f * (lo[i] * (1.f / kLog2e) - s2 * to_f(ks[buf][krow * KROW + c8 * 8 + i]) * rs);
+          hi[i] = f * (hi[i] * (1.f / kLog2e) - s2 * to_f(ks[buf][krow * KROW + c8 * 8 + 4 + i]) * rs);
+        }
+      } else {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float* base = &xv[ww][((blk * 2 + tb) * 64 + cq + 16 * g0) * 4];
+          lo += *reinterpret_cast<const f32x4*>(base);
+          hi += *reinterpret_cast<const f32x4*>(base + 64);
+        }
+        const float f = fast_exp2(lf);
+        lo = lo * f;
+        hi = hi * f;
+      }
+      const int ncol = isk ? D : DV;
+      void* dst = isk ? dk : dv;
+      const size_t off = ((size_t)bh * L + tok) * ncol + c8 * 8;
+      if (grad_f32) {
+        f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + off);
+        o4[0] = lo;
+        o4[1] = hi;
+      } else {
+        vec8<T> o8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o8[i] = to_t<T>(lo[i]);
+          o8[i + 4] = to_t<T>(hi[i]);
+        }
+        st8<T>(reinterpret_cast<T*>(dst) + off, o8);
+      }
+    }
+    cur.next();
+  }
+}
+
+// ---------------------------------------------------------------- host side
+bool bwd_shape_built(int d, int dv, int m) {
+#define X(D_, DV_, M_) \
+  if (d == D_ && dv == DV_ && m == M_) return true;
+  FAVOR_BWD_SHAPES(X)
+#undef X
+  return false;
+}
+
+constexpr int kBwdPieces = 256;  // one 4-wave workgroup per CU (one wave per SIMD)
+
+BackwardPlan plan_backward(const Shape& s, int dtype) {
+  BackwardPlan p;
+  const BidirPlan f = plan_bidir(s, dtype);
+  p.tpb = f.tpb;
+  p.T_all = f.T_all;
+  p.G_red = f.G;
+  p.G = (int)std::min<long long>(p.T_all, kBwdPieces);
+  p.nw_reduce = f.nw_reduce;
+  const int dc = (s.d + 31) / 32;
+  const size_t nfc = (s.m + 31) / 32;
+  const size_t rc = ((s.dv + 1 + 31) / 32) * 32;
+  const size_t slots_red = (size_t)p.G_red + (size_t)s.bh(), slots = (size_t)p.G + (size_t)s.bh();
+  size_t off = 0;
+  p.off_omf = off;
+  off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
+  p.off_omt = off;
+  off = align256(off + (size_t)s.H * (s.d / 16) * nfc * 512 * elt(dtype));
+  p.off_part = off;
+  off = align256(off + slots_red * nfc * (s.dv / 16) * 512 * 4);
+  p.off_zpart = off;
+  off = align256(off + slots_red * nfc * 32 * 4);
+  p.off_pmax = off;
+  off = align256(off + slots_red * p.nw_reduce * 4);
+  p.off_srow = off;
+  off = align256(off + (size_t)s.bh() * s.m * rc * 4);
+  p.off_gmax = off;
+  off = align256(off + (size_t)s.bh() * 4);
+  p.off_dpart = off;
+  off = align256(off + slots * nfc * (s.dv / 16) * 512 * 4);
+  p.off_dzpart = off;
+  off = align256(off + slots * nfc * 32 * 4);
+  p.off_dsrow = off;
+  off = align256(off + (size_t)s.bh() * s.m * rc * 4);
+  p.total = off;
+  return p;
+}
+
+template <typename T, int D, int DV, int M>
+static hipError_t run_backward(const T* q, const T* k, const T* v, const float* omega, const T* dout,
+                               const Shape& s, int grad_f32, void* dq, void* dk, void* dv, void* ws,
+                               hipStream_t st) {
+  using P = typename Ops<T>::P;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NWR = RedSplit<M>::NW;
+  const BackwardPlan p = plan_backward(s, sizeof(T) == 4 ? 0 : 1);
+  char* base = static_cast<char*>(ws);
+  P* omf = reinterpret_cast<P*>(base + p.off_omf);
+  P* omt = reinterpret_cast<P*>(base + p.off_omt);
+  float* part = reinterpret_cast<float*>(base + p.off_part);
+  float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
+  float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
+  float* srow = reinterpret_cast<float*>(base + p.off_srow);
+  float* gmx = reinterpret_cast<float*>(base + p.off_gmax);
+  float* dpart = reinterpret_cast<float*>(base + p.off_dpart);
+  float* dzpart = reinterpret_cast<float*>(base + p.off_dzpart);
+  float* dsrow = reinterpret_cast<float*>(base + p.off_dsrow);
+  const float sc = std::pow((float)D, -0.25f);
+  const float wscale = sc * kLog2e;
+  const float nscale = sc * sc * kLog2e * 0.5f;
+  const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
+  const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
+  const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
+  {
+    FAVOR_TIMED("omega_frag", st);
+    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+        omega, s.H, M, D, wscale, omf);
+    omegaT_frag_kernel<P><<<(unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st>>>(
+        omega, s.H, M, D, wscale, omt);
+  }
+  {
+    FAVOR_TIMED("reduce", st);
+    kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true><<<p.G_red, 64 * NWR, 0, st>>>(
+        k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+  }
+  {
+    FAVOR_TIMED("combine", st);
+    combine_rows_kernel<DV, M, NWR><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
+        part, zpart, pmax, p.tpb, p.T_all, p.G_red, 1, srow, gmx);
+  }
+  {
+    FAVOR_TIMED("bwd_q", st);
+    bwd_q_kernel<T, D, DV, M><<<p.G, 64 * NWR, 0, st>>>(q, dout, omf, omt, srow, s.H, s.L, p.tpb, p.T_all, p.G,
+                                                        grad_f32, dpart, dzpart, dq);
+  }
+  {
+    FAVOR_TIMED("combine_d", st);
+    combine_rows_kernel<DV, M, NWR><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
+        dpart, dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
+  }
+  {
+    FAVOR_TIMED("bwd_k", st);
+    bwd_k_kernel<T, D, DV, M><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb, p.T_all, p.G,
+                                                        nscale, sc * sc, grad_f32, dk, dv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout, const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv,
+                           void* ws, hipStream_t st) {
+#define X(D_, DV_, M_)                                                                                          \
+  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
+    if (dtype == 0)                                                                                             \
+      return run_backward<float, D_, DV_, M_>(static_cast<const float*>(q), static_cast<const float*>(k),      \
+                                              static_cast<const float*>(v), omega,                              \
+                                              static_cast<const float*>(dout), s, grad_f32, dq, dk, dv, ws, st); \
+    return run_backward<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),           \
+                                           static_cast<const bf16*>(v), omega, static_cast<const bf16*>(dout),  \
+                                           s, grad_f32, dq, dk, dv, ws, st);                                    \
+  }
+  FAVOR_BWD_SHAPES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace favor

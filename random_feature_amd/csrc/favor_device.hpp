@@ -158,6 +158,15 @@ template <int N> __device__ __forceinline__ float lanes_sum(float x) {
   return x;
 }
 
+template <int N> __device__ __forceinline__ float lanes_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppRor8>(x));
+  static_assert(N <= 16, "lanes_max covers at most 16 lanes");
+  return x;
+}
+
 // Flattened work split: the B*H*ceil(L/32) token tiles, in (b,h)-major order, are cut
 // into G contiguous pieces of nearly equal length. Piece i covers tiles
 // [piece_start(i), piece_start(i+1)). A piece may span several (b,h); the part of

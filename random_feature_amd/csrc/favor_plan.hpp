@@ -17,6 +17,12 @@
   X(64, 64, 128)        \
   X(64, 64, 256)
 
+// (d, dv, m) combinations with compiled kernels for the bidirectional backward.
+#define FAVOR_BWD_SHAPES(X) \
+  X(16, 16, 32)             \
+  X(32, 32, 64)             \
+  X(64, 64, 128)            \
+  X(64, 64, 256)
 
 namespace favor {
 
@@ -59,7 +65,18 @@ struct CausalPlan {
          total = 0;
 };
 
+// Bidirectional backward: the forward reduction's pieces and partials, S_aug rows, the
+// backward's own pieces (G, one workgroup per CU) and their dS_aug partials, dS_aug rows.
+struct BackwardPlan {
+  int tpb = 0, G_red = 0, G = 0, nw_reduce = 0;
+  long long T_all = 0;
+  size_t off_omf = 0, off_omt = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_srow = 0, off_gmax = 0,
+         off_dpart = 0, off_dzpart = 0, off_dsrow = 0, total = 0;
+};
+
 bool shape_built(int dtype, int d, int dv, int m);
+bool bwd_shape_built(int d, int dv, int m);
+BackwardPlan plan_backward(const Shape& s, int dtype);
 // s.L is the key length; Lq > 0 sets a different query length (cross attention).
 BidirPlan plan_bidir(const Shape& s, int dtype, int Lq = 0);
 CausalPlan plan_causal(const Shape& s, int dtype);
@@ -72,6 +89,8 @@ hipError_t launch_bidir(const void* q, const void* k, const void* v, const float
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
                          void* ws, hipStream_t st);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout, const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv,
+                           void* ws, hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
                          int N, int H, int d, int dv, int m, int dtype, int kind, float eps, const float* gate,
                          const float* inw, float* out, hipStream_t st);

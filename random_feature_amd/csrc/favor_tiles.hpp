@@ -196,7 +196,7 @@ constexpr int kReduceRing = 5;
 // feature after a shift is 2^-8, far above the bottom of the fp32/bf16 range.
 constexpr float kKeyMargin = 8.f;
 
-template <typename T, int D, int DV, int M, int R, int KIND>
+template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
                  int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
@@ -381,7 +381,10 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 
     // stretch 1: projection of tile t+1 beside the feature map of tile t
     project(pnext, buf ^ 1, next_new ? 0.f : runmax);
-    vec8<C> af[FB];
+    // SPLIT (16-bit contraction type): each feature as the sum of two values of that type,
+    // both contracted, so S_aug carries the features' fp32 precision
+    constexpr bool LO = SPLIT && sizeof(C) == 2;
+    vec8<C> af[FB], al[LO ? FB : 1];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -395,6 +398,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
         af[fb][j] = to_t<C>(f);
+        if constexpr (LO) al[fb][j] = to_t<C>(f - to_f(af[fb][j]));
       }
     // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
     // the piece: a filler slot into an unused buffer) and the next copies
@@ -403,7 +407,10 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], af[fb], vf[nb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        mma16(sacc[fb][nb], af[fb], vf[nb]);
+        if constexpr (LO) mma16(sacc[fb][nb], al[fb], vf[nb]);
+      }
     Rg::template convert<P, KROW, kNormSq>(ring[s_cv], ks[buf], kn[buf], nscale, L - cv.tok0());
     cv.next();
     {

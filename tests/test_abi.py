@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -103,6 +103,18 @@ def test_decode_gated_argument_checks():
     assert call(inw=ctypes.c_void_p(0x10001)) == INVALID
     assert call(q=None) == INVALID
     assert call(d=128) == UNSUPPORTED
+
+
+def test_backward_argument_checks():
+    def call(kind=0, d=64, dv=64, m=256, wsb=1 << 30, q=FAKE):
+        return rf.raw_call("favor_bidir_backward", q, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, dv, m, 1, kind, 0, FAKE,
+                           FAKE, FAKE, FAKE, ctypes.c_size_t(wsb), None)
+    assert call(q=None) == INVALID
+    assert call(kind=1) == UNSUPPORTED          # ReLU has no backward kernels
+    assert call(d=16, dv=16, m=256) == UNSUPPORTED
+    assert call(wsb=8) == WORKSPACE
+    assert rf._lib.favor_backward_workspace_size(1, 1, 64, 64, 64, 256, 1) > 0
+    assert rf._lib.favor_backward_workspace_size(0, 1, 64, 64, 64, 256, 1) == 0
 
 
 def test_features_and_omega_argument_checks():

@@ -505,3 +505,45 @@ def test_cross_bf16_workload_sampled():
         worst = max(worst, rel_err(out[sl], oracle.bidir(q[sl], k[sl], v[sl], om[h:h + 1])))
     print(f"cross_bf16 sampled rel err {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- backward
+
+BWD_SHAPES = [(16, 16, 32), (32, 32, 64), (64, 64, 128), (64, 64, 256)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("L", [300, 33])
+def test_bidir_backward(dtype, shape, L):
+    """Gradients of the bidirectional estimator (chain rule through equation 4 and Lemma 1's map) against
+    the oracle's: dq, dk, dv row by row."""
+    d, dv, m = shape
+    B, H = 2, 2
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 700 + m + L)
+    g = workloads.make_tensor((B, H, L, dv), 777 + L, 1.0, dtype)
+    om_dev, om = _omega(44, H, m, d)
+    ref = oracle.bidir_backward(q, k, v, om, g)
+    got = rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        e = rel_err(a, b)
+        assert e < TOL[dtype], (name, e)
+
+
+def test_bidir_backward_workload_sampled():
+    """The backward at the headline workload's size (B8 H12 L4096 d64 m256, bf16) in the benchmark's launch
+    configuration, sampled (b,h) pairs against the oracle."""
+    w = workloads.WORKLOADS["bidir_bf16"]
+    q, k, v = workloads.make_qkv(w)
+    g = workloads.make_tensor((w.B, w.H, w.L, w.dv), 888, 1.0, torch.bfloat16)
+    om_dev, om = _omega(w.seed, w.H, w.m, w.d)
+    got = [t.cpu() for t in rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV))]
+    worst = 0.0
+    for b, h in _sample_pairs(w.B, w.H, 3, 3):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.bidir_backward(q[sl], k[sl], v[sl], om[h:h + 1], g[sl])
+        for a, r in zip(got, ref):
+            worst = max(worst, rel_err(a[sl], r))
+    print(f"bidir_bf16 backward sampled rel err {worst:.3e}")
+    assert worst < TOL[torch.bfloat16]
