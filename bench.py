@@ -9,6 +9,7 @@ seeded inputs already resident in device memory:
   causal_bf16 favor_causal, B4 H8 L8192 d64 dv64 m256
   decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
   decode_gated_bf16 the same with favor_decode_gated (gates U[0.9,1), input weight 1 - g)
+  backward_bf16 favor_bidir_backward (dq, dk, dv) at bidir_bf16's shape, bf16 gradients
   bidir_fp32 / bidir_small  the fp32 parity workloads
 Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
 decode, head-tokens/s), the dominant kernel's roofline fraction (per-launch
@@ -56,6 +57,10 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
         return thq * (proj + contr), thq * (w.d * eb + w.dv * out_bytes)
     if name == "sweep":       # queries and keys projected, inter+intra contractions, outputs
         return th * (2 * proj + 2 * contr), th * ((2 * w.d + w.dv) * eb + w.dv * out_bytes)
+    if name == "bwd_q":       # projection, u = S g, dq = Omega^T (phi' . Delta), dS_aug += phi'^T W
+        return thq * (2 * proj + 2 * w.m * w.dv + contr), thq * ((w.d + w.dv) * eb + w.d * out_bytes)
+    if name == "bwd_k":       # projection, dPhi_K = dS_aug [v 1], dk = Omega^T P, dv = dS^T phi
+        return th * (2 * proj + contr + 2 * w.m * w.dv), th * ((w.d + w.dv) * eb + (w.d + w.dv) * out_bytes)
     if name == "decode":      # per (sequence, head): q,k projections, state read+write, out (+ gate, weight)
         sb = (w.m * w.dv + w.m) * 4
         gb = 8 if w.kind == "decode_gated" else 0
@@ -70,6 +75,7 @@ _PATH_SOURCES = {
     "causal": ["favor_causal.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "decode": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
     "decode_gated": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
+    "backward": ["favor_backward.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
 }
 
 
@@ -109,14 +115,19 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
     else:
         om, kind = oracle.make_omega(w.seed, w.H, w.m, w.d, omega_mode), "prf"
     with threadpool_limits(1):
-        if w.kind in ("bidir", "cross", "causal"):
+        if w.kind in ("bidir", "cross", "causal", "backward"):
             q, k, v = workloads.make_qkv(w)
-            fn = oracle.causal if w.kind == "causal" else oracle.bidir
+            if w.kind == "backward":
+                dout = workloads.make_dout(w)
+                fn = lambda q_, k_, v_, o_, kd, sl: oracle.bidir_backward(q_, k_, v_, o_, dout[sl], kd)  # noqa: E731
+            else:
+                f0 = oracle.causal if w.kind == "causal" else oracle.bidir
+                fn = lambda q_, k_, v_, o_, kd, sl: f0(q_, k_, v_, o_, kd)  # noqa: E731
             done, t0 = 0, time.perf_counter()
             for b in range(w.B):
                 for h in range(w.H):
                     sl = (slice(b, b + 1), slice(h, h + 1))
-                    fn(q[sl], k[sl], v[sl], om[h:h + 1], kind)
+                    fn(q[sl], k[sl], v[sl], om[h:h + 1], kind, sl)
                     done += 1
                     if time.perf_counter() - t0 > budget_s:
                         break
@@ -212,14 +223,24 @@ def main():
             q, k, v = workloads.make_qkv(w.with_(seed=w.seed + 1000 * r) if r else w, device=dev)
             sets.append((q, k, v))
         q, k, v = sets[0]
-        ws = rf.workspace(w.kind == "causal", k, v, om)
-        out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
-        fn = {"bidir": rf.bidir, "cross": rf.bidir_cross, "causal": rf.causal}[w.kind]
         cur = [0]
+        if w.kind == "backward":
+            douts = [workloads.make_dout(w.with_(seed=w.seed + 1000 * r) if r else w, device=dev)
+                     for r in range(nset)]
+            ws = rf.backward_workspace(q, v, om)
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
 
-        def step(i=None):
-            qq, kk, vv = sets[cur[0]]
-            fn(qq, kk, vv, om, ws=ws, out=out)
+            def step(i=None):
+                qq, kk, vv = sets[cur[0]]
+                rf.bidir_backward(qq, kk, vv, om, douts[cur[0]], ws=ws, out=grads)
+        else:
+            ws = rf.workspace(w.kind == "causal", k, v, om)
+            out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
+            fn = {"bidir": rf.bidir, "cross": rf.bidir_cross, "causal": rf.causal}[w.kind]
+
+            def step(i=None):
+                qq, kk, vv = sets[cur[0]]
+                fn(qq, kk, vv, om, ws=ws, out=out)
         tokens_per_step = w.B * w.H * w.Lq_eff   # output (query) tokens
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4

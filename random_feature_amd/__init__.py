@@ -140,6 +140,15 @@ def workspace(causal: bool, q: torch.Tensor, v: torch.Tensor, omega: torch.Tenso
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
+def backward_workspace(q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) -> torch.Tensor:
+    """Device scratch for bidir_backward() at q's shape (reusable across calls of that shape)."""
+    B, H, L, d = q.shape
+    n = int(_lib.favor_backward_workspace_size(B, H, L, d, v.shape[-1], omega.shape[1], _dtype_code(q)))
+    if n == 0:
+        raise FavorError("favor_backward_workspace_size", 1)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0):
     """phi [B,H,L,m] and logscale [B,H,L] with phi_true = phi * exp(logscale)."""
     _need(x, "x", 4)
@@ -195,9 +204,9 @@ def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool 
     return out
 
 
-def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None):
+def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None, out=None):
     """Gradients (dq, dk, dv) of bidir()'s output for the upstream gradient `dout` (the forward sums are
-    recomputed)."""
+    recomputed). `out`: optional preallocated (dq, dk, dv)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, n, 4)
     _need(omega, "omega", 3)
@@ -205,14 +214,17 @@ def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=
     dv = v.shape[-1]
     m = omega.shape[1]
     if ws is None:
-        n = int(_lib.favor_backward_workspace_size(B, H, L, d, dv, m, _dtype_code(q)))
-        if n == 0:
-            raise FavorError("favor_backward_workspace_size", 1)
-        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+        ws = backward_workspace(q, v, omega)
     gdt = torch.float32 if grad_f32 else q.dtype
-    dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
-    dk = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
-    dvv = torch.empty((B, H, L, dv), dtype=gdt, device=q.device)
+    if out is None:
+        dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
+        dk = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
+        dvv = torch.empty((B, H, L, dv), dtype=gdt, device=q.device)
+    else:
+        dq, dk, dvv = out
+        for t, n, last in ((dq, "dq", d), (dk, "dk", d), (dvv, "dv", dv)):
+            if tuple(t.shape) != (B, H, L, last) or t.dtype != gdt or not t.is_contiguous():
+                raise ValueError(f"{n}: expected a contiguous {gdt} tensor of shape {(B, H, L, last)}")
     _check("favor_bidir_backward",
            _lib.favor_bidir_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv,
                                      m, _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk),

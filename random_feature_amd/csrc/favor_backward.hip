@@ -43,9 +43,9 @@ template <typename T> struct BwdOps;
 template <> struct BwdOps<bf16> { using XS = f16; using XB = bf16; };
 template <> struct BwdOps<float> { using XS = float; using XB = float; };
 
-// Omega'^T fragments, the A operand (rows = d, k = features in the paired slot order of
-// stacked accumulator tiles): frag[h][db][fc][lane][j] = scale * omega[h][f][db*16 + c] with
-// f = fc*32 + 16(j>>2) + 4g + (j&3) (0 past m or d).
+// Omega'^T fragments, the A operand (rows = d, k = features): frag[h][db][fc][lane][j] =
+// scale * omega[h][f][db*16 + c] with f = fc*32 + 8g + j (0 past m or d), the order in which
+// lane (c, g) reads 8 consecutive features of a row operand.
 template <typename T>
 __global__ void omegaT_frag_kernel(const float* __restrict__ omega, int H, int m, int d, float scale,
                                    T* __restrict__ frag) {
@@ -64,7 +64,7 @@ __global__ void omegaT_frag_kernel(const float* __restrict__ omega, int H, int m
     vec8<T> x;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int f = fc * 32 + 16 * (j >> 2) + 4 * g + (j & 3);
+      const int f = fc * 32 + 8 * g + j;
       x[j] = to_t<T>((f < m && dd < d) ? omega[((size_t)h * m + f) * d + dd] * scale : 0.f);
     }
     st8<T>(frag + (size_t)id * 8, x);
@@ -153,24 +153,37 @@ __device__ __forceinline__ int scale_exp(float x) {
   return e;
 }
 
+// ---------------------------------------------------------------- wave split
+// Waves of the gradient kernels: one per 32 features, at most FAVOR_BWD_WAVES. Eight waves in
+// one workgroup per CU put two waves on every SIMD, so one wave's vector work overlaps
+// another's matrix work.
+#ifndef FAVOR_BWD_WAVES
+#define FAVOR_BWD_WAVES 8
+#endif
+template <int M> struct BwdSplit {
+  static constexpr int NW = M < 32 ? 1 : ((M / 32) < FAVOR_BWD_WAVES ? (M / 32) : FAVOR_BWD_WAVES);
+  static constexpr int FB = M / (16 * NW);
+};
+
 // ---------------------------------------------------------------- query side
-// Workgroup = NW waves over one piece of the flattened query-tile space; wave w owns the
-// FB*16 features of the reduction's split. Per tile of 32 queries:
+// Workgroup = NW waves over one piece of the flattened query-tile space; wave w owns FB*16
+// features. Per tile of 32 queries (Q and dOut rows arrive through a two-slot DMA ring):
+//   g rows       scaled per query to [1/2, 1) (fp16, exponent e_i)
 //   projection   A = Omega' (rows = features), B = Q rows -> a'[feature][query]; the exact
 //                row maximum across the waves; phi' = 2^(a' - max) in (0, 1]
-//   g rows       scaled per query to [1/2, 1) (fp16, exponent e_i)
 //   u            A = S rows (fp16, scaled by 2^-eS per (b,h)), B = g rows -> u = S g (scaled)
 //   D', A        D'_i = phi'_i . z and A_i = phi'_i . u_i, fp32 sums over the features, across
 //                the waves through LDS; gamma_i = g_i . out_i = A_i 2^(eS + e_i) / D'_i
-//   dPhi_Q       phi' * (u - z A/D'), the scaled dPhi_Q (phi'.dPhi_Q = 0 by construction)
-//   dq           A = Omega'^T fragments, B = that product (fp16, paired feature slots),
-//                partial over the wave's features, summed through LDS, times 2^(eS + e_i)/D'_i
+//   dPhi_Q       phi' * (u - z A/D'), the scaled dPhi_Q (phi'.dPhi_Q = 0 by construction),
+//                written as fp16 rows [query][feature] to LDS
+//   dq           per wave BPW blocks of dq^T (16 dims x 16 queries): A = Omega'^T fragments
+//                over all features, B = the rows above; times 2^(eS + e_i)/D'_i, stored
 //   dS_aug       W_i = [g_i, -gamma_i]/D'_i (rows), A = phi'^T (transposing reads of the phi' rows
 //                in LDS), B = W (transposing reads), both as sums of two bf16 parts;
 //                accumulated over the piece's tiles of one (b,h) and written as a partial in
 //                the reduction's fragment layout
 template <typename T, int D, int DV, int M>
-__global__ void __launch_bounds__(64 * RedSplit<M>::NW, 1)
+__global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ srow, int H, int L, int tpb,
              long long T_all, int G, int grad_f32, float* __restrict__ dpart, float* __restrict__ dzpart,
@@ -178,7 +191,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   using P = typename Ops<T>::P;
   using XS = typename BwdOps<T>::XS;
   using XB = typename BwdOps<T>::XB;
-  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
   static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
@@ -186,23 +199,28 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   constexpr int NB = DV / 16 + 1;
   constexpr int NFC = (M + 31) / 32;
   constexpr int NFCW = (FB + 1) / 2;
+  constexpr int BPW = 2 * NDB / NW;  // dq^T blocks (dims db, queries tb) per wave
+  static_assert(BPW >= 1 && (2 * NDB) % NW == 0, "dq blocks split evenly over the waves");
+  constexpr int NDBW = (BPW + 1) / 2;  // dimension blocks per wave
   constexpr int RC = Rows<DV>::RC, KC = Rows<DV>::KC;
   constexpr int KROW = D + 8;
   constexpr int EROW = FB * 16 + 8;
   constexpr int WROW = RC + 8;
+  constexpr int PROW = NFC * 32 + 8;
   constexpr int CPR = DV / 8;                     // 8-column chunks of a g row
   constexpr int IPT = (32 * CPR + NT - 1) / NT;  // (query, chunk) items per thread
-  using Rg = Ring<T, D, DV, NT, false>;
+  using Rg = Ring<T, D, DV, NT, true>;  // Q rows and dOut rows of a tile
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) P qs[32 * KROW];
   constexpr int NSPL = sizeof(XB) == 2 ? 2 : 1;  // bf16 operands of dS_aug as a sum of two (hi + lo)
   __shared__ __attribute__((aligned(16))) XB erow[NSPL][NW][32 * EROW];
   __shared__ __attribute__((aligned(16))) XS gsr[32 * WROW];
   __shared__ __attribute__((aligned(16))) XB wbr[NSPL][32 * WROW];
-  __shared__ __attribute__((aligned(16))) float xq[NW][2 * NDB * 256];
-  __shared__ __attribute__((aligned(16))) float qmx[NW][32];
-  __shared__ __attribute__((aligned(16))) float dsum[NW][32];
-  __shared__ __attribute__((aligned(16))) float asum[NW][32];
+  __shared__ __attribute__((aligned(16))) XS prow[32 * PROW];
+  // per-wave partials across the waves, [query][wave] so a lane reads a query's NW at once
+  __shared__ __attribute__((aligned(16))) float qmx[32][NW];
+  __shared__ __attribute__((aligned(16))) float dsum[32][NW];
+  __shared__ __attribute__((aligned(16))) float asum[32][NW];
   __shared__ __attribute__((aligned(16))) float gex[32], rsc[32];
   __shared__ float xch[NW];
 
@@ -216,12 +234,35 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
 
   vec8<P> om[FB][DC];
-  vec8<P> omt[NDB][NFCW];
+  vec8<P> omt[NDBW][NFC];
   vec8<XS> sa[FB][KC];
   float zv[FB][4];  // z of this lane's features (4g + i of each block)
   f32x4 sacc[FB][NB];
   int eS = 0;  // S rows were scaled by 2^-eS
   int cur_bh = -1;
+  // dq blocks of the previous tile, scaled: stored one tile late, after the next tile's first
+  // barriers, so the stores' latency is not waited for at the top of the next tile
+  f32x4 pend[BPW];
+  int pend_bh = -1, pend_tok0 = 0;
+  auto store_pending = [&]() {
+    if (pend_bh < 0) return;
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = w * BPW + bi, db = blk >> 1, tb = blk & 1;
+      const int tok = pend_tok0 + tb * 16 + c;
+      if (tok < L) {
+        const size_t off = ((size_t)pend_bh * L + tok) * D + db * 16 + 4 * g;
+        if (grad_f32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = pend[bi];
+        } else {
+          vec4<T> o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = to_t<T>(pend[bi][i]);
+          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dq) + off) = o4;
+        }
+      }
+    }
+  };
 
   auto zero_sums = [&]() {
 #pragma unroll
@@ -249,16 +290,18 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
     }
   };
 
-  Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), true, ring0);
+  Rg::issue(Q, dOut, L, ahead.bh, ahead.tok0(), true, ring0);
   ahead.next();
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
     const int bh = cur.bh, tok0 = cur.tok0();
-    // ---- this tile's Q rows land and are converted; the next tile's copies start
+    // ---- this tile's Q and dOut rows land (the dOut rows are read across threads), Q is
+    // converted; the next tile's copies start
     wait_vmcnt<0>();  // the copies, and every store of the previous tile
+    lds_barrier();
     Rg::template convert<P, KROW, kNormNone>(ring[buf], qs, nullptr, 0.f, L);
     if (it + 1 < n_tiles) {
-      Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), true, ring0 + (buf ^ 1) * Rg::SLOT);
+      Rg::issue(Q, dOut, L, ahead.bh, ahead.tok0(), true, ring0 + (buf ^ 1) * Rg::SLOT);
       ahead.next();
     }
     // ---- a new (b,h): close the old one's sums, load this one's operands
@@ -272,10 +315,10 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         for (int dc = 0; dc < DC; ++dc)
           om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int i = 0; i < NDBW; ++i)
 #pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw)
-          omt[db][fcw] = ld8<P>(omT + ((((size_t)h * NDB + db) * NFC + (w * FB) / 2 + fcw) * 64 + lane) * 8);
+        for (int fc = 0; fc < NFC; ++fc)
+          omt[i][fc] = ld8<P>(omT + ((((size_t)h * NDB + (w * BPW) / 2 + i) * NFC + fc) * 64 + lane) * 8);
       const float* rows = srow + (size_t)bh * M * RC;
       f32x8 sf[FB][KC];
       float amax = 0.f;
@@ -312,8 +355,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       const int item = threadIdx.x + u * NT;
       const int row = item / CPR, c8 = item % CPR;
       const bool ok = item < 32 * CPR && tok0 + row < L;
-      const size_t off = ((size_t)bh * L + min(tok0 + row, L - 1)) * DV + c8 * 8;
-      const vec8<T> g8 = ld8<T>(dOut + off);
+      const vec8<T> g8 = ld8<T>(reinterpret_cast<const T*>(ring[buf] + Rg::v_off(min(row, 31), c8 * 8)));
       float mabs = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -357,7 +399,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
       mx = group_max(mx);
-      if (g == 0) qmx[w][tb * 16 + c] = mx;
+      if (g == 0) qmx[tb * 16 + c][w] = mx;
     }
     // ---- u = S g (scaled), [feature][query]
     f32x4 uq[2][FB];
@@ -374,13 +416,14 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       }
     }
     lds_barrier();  // B1: row maxima
+    store_pending();
 
     // ---- phi' = 2^(a' - max); D' and A partials; phi' rows for the dS transposes
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      float mx = qmx[0][tb * 16 + c];
+      float mx = qmx[tb * 16 + c][0];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
       float dz = 0.f, da = 0.f;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
@@ -400,36 +443,28 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       dz = group_sum(dz);
       da = group_sum(da);
       if (g == 0) {
-        dsum[w][tb * 16 + c] = dz;
-        asum[w][tb * 16 + c] = da;
+        dsum[tb * 16 + c][w] = dz;
+        asum[tb * 16 + c][w] = da;
       }
     }
     lds_barrier();  // B2: D' and A partials, phi' rows
 
-    // ---- dPhi_Q (scaled) times phi', and the dq^T partial over this wave's features
+    // ---- phi' * dPhi_Q (scaled) as rows [query][feature]
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       float den = 0.f, aa = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
-        den += dsum[ww][tb * 16 + c];
-        aa += asum[ww][tb * 16 + c];
+        den += dsum[tb * 16 + c][ww];
+        aa += asum[tb * 16 + c][ww];
       }
       const float ad = aa / den;
-      vec8<XS> pb[NFCW];
 #pragma unroll
-      for (int fcw = 0; fcw < NFCW; ++fcw)
+      for (int fb = 0; fb < FB; ++fb) {
+        vec4<XS> p4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int fb = 2 * fcw + (j >> 2), i = j & 3;
-          pb[fcw][j] = to_t<XS>(fb < FB ? pq[tb][fb][i] * (uq[tb][fb][i] - zv[fb][i] * ad) : 0.f);
-        }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, omt[db][fcw], pb[fcw]);
-        *reinterpret_cast<f32x4*>(&xq[w][((db * 2 + tb) * 64 + lane) * 4]) = a;
+        for (int i = 0; i < 4; ++i) p4[i] = to_t<XS>(pq[tb][fb][i] * (uq[tb][fb][i] - zv[fb][i] * ad));
+        *reinterpret_cast<vec4<XS>*>(&prow[(tb * 16 + c) * PROW + (w * FB + fb) * 16 + 4 * g]) = p4;
       }
     }
     // ---- W rows (bf16): [g, -gamma] / D'
@@ -441,8 +476,8 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         float den = 0.f, aa = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-          den += dsum[ww][row];
-          aa += asum[ww][row];
+          den += dsum[row][ww];
+          aa += asum[row][ww];
         }
         const float rd = 1.f / den;
         vec8<XB> wb, wl;
@@ -467,7 +502,19 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         }
       }
     }
-    lds_barrier();  // B3: dq partials, W rows
+    lds_barrier();  // B3: dPhi_Q rows, W rows
+
+    // ---- dq: this wave's blocks of dq^T over all features, unscaled (stored later)
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = w * BPW + bi, tb = blk & 1;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int fc = 0; fc < NFC; ++fc) mma16(a, omt[bi >> 1][fc], ld8<XS>(&prow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
+      pend[bi] = a * rsc[tb * 16 + c];
+    }
+    pend_bh = bh;
+    pend_tok0 = tok0;
 
     // ---- dS_aug += phi'^T W over the tile's queries: with bf16 operands as hi + lo pairs,
     // hi*hi + hi*lo + lo*hi (the sums over the queries cancel, so 8-bit operands would not do)
@@ -508,55 +555,28 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         }
       }
     }
-
-    // ---- dq: the waves' partials summed, unscaled, stored (rows past L skipped)
-    constexpr int CD = D / 8;
-    for (int e = threadIdx.x; e < 32 * CD; e += NT) {
-      const int qrow = e / CD, c8 = e % CD;
-      const int tok = tok0 + qrow;
-      if (tok >= L) continue;
-      const int tb = qrow >> 4, cq = qrow & 15;
-      const int db = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
-      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float* base = &xq[ww][((db * 2 + tb) * 64 + cq + 16 * g0) * 4];
-        lo += *reinterpret_cast<const f32x4*>(base);
-        hi += *reinterpret_cast<const f32x4*>(base + 64);
-      }
-      const float r = rsc[qrow];
-      const size_t off = ((size_t)bh * L + tok) * D + c8 * 8;
-      if (grad_f32) {
-        f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off);
-        o4[0] = lo * r;
-        o4[1] = hi * r;
-      } else {
-        vec8<T> o8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o8[i] = to_t<T>(lo[i] * r);
-          o8[i + 4] = to_t<T>(hi[i] * r);
-        }
-        st8<T>(reinterpret_cast<T*>(dq) + off, o8);
-      }
-    }
     cur.next();
   }
+  store_pending();
   flush(cur_bh);
 }
 
 // ---------------------------------------------------------------- key side
-// Workgroup = NW waves over one piece of the flattened key-tile space. Per tile of 32 keys:
+// Workgroup = NW waves over one piece of the flattened key-tile space; wave w owns FB*16
+// features. Per tile of 32 keys:
 //   projection   A = Omega', B = K rows (fp16, converted with |k|^2 n'-norms) -> a'[feature][key];
 //                exact row maximum across the waves; phi' = 2^(a' - max) in (0, 1]; the key's
 //                scale F_j = 2^(max_j - n'_j - M) (0 for keys past L)
 //   [V 1] rows   scaled per key to [1/2, 1), fp16, in LDS
-//   dPhi_K       A = dS_aug rows (fp16, scaled per (b,h)), B = [V 1] rows -> [feature][key]
-//   dk           A = Omega'^T, B = phi' * dPhi_K; minus d^-1/2 k_j sum_r phi'_r dPhi_K,r
-//   dV           A = dS^T (bf16 fragments, paired features), B = phi' (bf16) -> dV^T
-//   partial sums over the waves through LDS, scaled by F_j (and the operand scales), stored.
+//   dPhi_K       A = dS_aug rows (fp16, scaled per (b,h)), B = [V 1] rows -> [feature][key];
+//                P = phi' * dPhi_K and phi' written as rows [key][feature] to LDS
+//   dk           per wave, blocks of dk^T: A = Omega'^T over all features, B = P rows; minus
+//                d^-1/2 k_j sum_r P_jr (that sum across the waves through LDS)
+//   dV           per wave, blocks of dV^T: A = dS^T (bf16 fragments over all features),
+//                B = phi' rows (bf16)
+//   both scaled by F_j (and the operand scales) and stored.
 template <typename T, int D, int DV, int M>
-__global__ void __launch_bounds__(64 * RedSplit<M>::NW, 1)
+__global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ dsrow,
              const float* __restrict__ gmx, int H, int L, int tpb, long long T_all, int G, float nscale,
@@ -564,17 +584,21 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
   using P = typename Ops<T>::P;
   using XS = typename BwdOps<T>::XS;
   using XB = typename BwdOps<T>::XB;
-  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
   static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
   constexpr int NDB = D / 16;
   constexpr int NVB = DV / 16;
   constexpr int NFC = (M + 31) / 32;
-  constexpr int NFCW = (FB + 1) / 2;
+  constexpr int BPWK = 2 * NDB / NW, BPWV = 2 * NVB / NW;  // dk^T and dV^T blocks per wave
+  static_assert(BPWK >= 1 && (2 * NDB) % NW == 0 && BPWV >= 1 && (2 * NVB) % NW == 0,
+                "gradient blocks split evenly over the waves");
+  constexpr int NDBW = (BPWK + 1) / 2, NVBW = (BPWV + 1) / 2;
   constexpr int RC = Rows<DV>::RC, KC = Rows<DV>::KC;
   constexpr int KROW = D + 8;
   constexpr int WROW = RC + 8;
+  constexpr int PROW = NFC * 32 + 8;
   constexpr int CPR = DV / 8;
   constexpr int IPT = (32 * CPR + NT - 1) / NT;
   using Rg = Ring<T, D, DV, NT, true>;
@@ -582,10 +606,10 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
   __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
   __shared__ __attribute__((aligned(16))) XS vsr[32 * WROW];
-  __shared__ __attribute__((aligned(16))) float xk[NW][2 * NDB * 256];
-  __shared__ __attribute__((aligned(16))) float xv[NW][2 * NVB * 256];
-  __shared__ __attribute__((aligned(16))) float qmx[NW][32];
-  __shared__ __attribute__((aligned(16))) float rho[NW][32];
+  __shared__ __attribute__((aligned(16))) XS prow[32 * PROW];
+  __shared__ __attribute__((aligned(16))) XB frow[32 * PROW];
+  __shared__ __attribute__((aligned(16))) float qmx[32][NW];  // [key][wave]
+  __shared__ __attribute__((aligned(16))) float rho[32][NW];
   __shared__ __attribute__((aligned(16))) float vex[32];
   __shared__ float xch[NW];
 
@@ -599,11 +623,39 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
   TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
 
   vec8<P> om[FB][DC];
-  vec8<P> omt[NDB][NFCW];
+  vec8<P> omt[NDBW][NFC];
   vec8<XS> da[FB][KC];
-  vec8<XB> dt[NVB][NFCW];
+  vec8<XB> dt[NVBW][NFC];
   float eD = 0.f, gm = 0.f;
   int cur_bh = -1;
+  // dk and dV blocks of the previous tile, scaled: stored one tile late (after the next
+  // tile's first barriers), so the top of a tile does not wait for them
+  constexpr int NBLK = BPWK + BPWV;
+  f32x4 pend[NBLK];
+  int pend_bh = -1, pend_tok0 = 0;
+  auto store_pending = [&]() {
+    if (pend_bh < 0) return;
+#pragma unroll
+    for (int bi = 0; bi < NBLK; ++bi) {
+      const bool isk = bi < BPWK;
+      const int blk = isk ? w * BPWK + bi : w * BPWV + (bi - BPWK);
+      const int cb = blk >> 1, tb = blk & 1;
+      const int tok = pend_tok0 + tb * 16 + c;
+      if (tok < L) {
+        const int ncol = isk ? D : DV;
+        void* dst = isk ? dk : dv;
+        const size_t off = ((size_t)pend_bh * L + tok) * ncol + cb * 16 + 4 * g;
+        if (grad_f32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + off) = pend[bi];
+        } else {
+          vec4<T> o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = to_t<T>(pend[bi][i]);
+          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dst) + off) = o4;
+        }
+      }
+    }
+  };
 
   Rg::issue(K, V, L, ahead.bh, ahead.tok0(), true, ring0);
   ahead.next();
@@ -624,10 +676,10 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
         for (int dc = 0; dc < DC; ++dc)
           om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int i = 0; i < NDBW; ++i)
 #pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw)
-          omt[db][fcw] = ld8<P>(omT + ((((size_t)h * NDB + db) * NFC + (w * FB) / 2 + fcw) * 64 + lane) * 8);
+        for (int fc = 0; fc < NFC; ++fc)
+          omt[i][fc] = ld8<P>(omT + ((((size_t)h * NDB + (w * BPWK) / 2 + i) * NFC + fc) * 64 + lane) * 8);
       const float* rows = dsrow + (size_t)bh * M * RC;
       f32x8 sf[FB][KC];
       float amax = 0.f;
@@ -645,16 +697,15 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
             amax = fmaxf(amax, fmaxf(fabsf(a[j]), fabsf(b[j])));
           }
         }
-      // dS^T fragments for dV: A[m = column][k = feature, paired slots], unscaled bf16
+      // dS^T fragments for dV: A[m = value column][k = feature fc*32 + 8g + j], unscaled bf16
 #pragma unroll
-      for (int cb = 0; cb < NVB; ++cb)
+      for (int i = 0; i < NVBW; ++i)
 #pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw)
+        for (int fc = 0; fc < NFC; ++fc)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const int fb = 2 * fcw + (j >> 2);
-            const int f = (w * FB + fb) * 16 + 4 * g + (j & 3);
-            dt[cb][fcw][j] = to_t<XB>(fb < FB ? rows[(size_t)f * RC + cb * 16 + c] : 0.f);
+            const int f = fc * 32 + 8 * g + j;
+            dt[i][fc][j] = to_t<XB>(f < M ? rows[(size_t)f * RC + ((w * BPWV) / 2 + i) * 16 + c] : 0.f);
           }
       gm = gmx[bh];
       eD = (float)(scale_exp(wg_absmax<NW>(amax, xch)) - 4);
@@ -666,7 +717,7 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
           for (int j = 0; j < 8; ++j) da[fb][kc][j] = to_t<XS>(ldexpf(sf[fb][kc][j], -(int)eD));
       cur_bh = bh;
     }
-    lds_barrier();  // ks, kn of this tile
+    lds_barrier();  // ks, kn of this tile; every thread's copies landed
 
     // ---- projection and row maxima
     f32x4 pk[2][FB];
@@ -690,7 +741,7 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pk[tb][fb][i]);
       mx = group_max(mx);
-      if (g == 0) qmx[w][tb * 16 + c] = mx;
+      if (g == 0) qmx[tb * 16 + c][w] = mx;
     }
     // ---- [V 1] rows scaled per key to [1/2, 1) (fp16)
 #pragma unroll
@@ -699,11 +750,10 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
       const int row = item / CPR, c8 = item % CPR;
       float vals[8];
       float mabs = 0.f;
+      const vec8<T> v8 = ld8<T>(reinterpret_cast<const T*>(ring[buf] + Rg::v_off(min(row, 31), c8 * 8)));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        vals[j] = item < 32 * CPR
-                      ? to_f(*reinterpret_cast<const T*>(ring[buf] + Rg::v_off(row < 32 ? row : 31, c8 * 8 + j)))
-                      : 0.f;
+        vals[j] = item < 32 * CPR ? to_f(v8[j]) : 0.f;
         mabs = fmaxf(mabs, fabsf(vals[j]));
       }
       mabs = lanes_max<CPR>(mabs);
@@ -720,127 +770,80 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
       }
     }
     lds_barrier();  // B1: row maxima, [V 1] rows
+    store_pending();
 
-    // ---- phi', dPhi_K, P, rho; dk and dV partials
-    vec8<XS> pb[2][NFCW];
-    vec8<XB> fk[2][NFCW];
+    // ---- phi', dPhi_K, P, rho; P and phi' rows
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      float mx = qmx[0][tb * 16 + c];
+      float mx = qmx[tb * 16 + c][0];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][tb * 16 + c]);
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[tb][fb][i] = fast_exp2(pk[tb][fb][i] - mx);
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
       vec8<XS> vf[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) vf[kc] = ld8<XS>(&vsr[(tb * 16 + c) * WROW + kc * 32 + 8 * g]);
-      f32x4 dp[FB];
       float r = 0.f;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        dp[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) mma16(dp[fb], da[fb][kc], vf[kc]);
+        for (int kc = 0; kc < KC; ++kc) mma16(dp, da[fb][kc], vf[kc]);
+        vec4<XS> p4;
+        vec4<XB> f4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          dp[fb][i] *= pk[tb][fb][i];  // P = phi' * dPhi_K (scaled)
-          r += dp[fb][i];
+          const float ph = fast_exp2(pk[tb][fb][i] - mx);
+          const float pp = ph * dp[i];  // P = phi' * dPhi_K (scaled)
+          r += pp;
+          p4[i] = to_t<XS>(pp);
+          f4[i] = to_t<XB>(ph);
         }
+        const int off = (tb * 16 + c) * PROW + (w * FB + fb) * 16 + 4 * g;
+        *reinterpret_cast<vec4<XS>*>(&prow[off]) = p4;
+        *reinterpret_cast<vec4<XB>*>(&frow[off]) = f4;
       }
       r = group_sum(r);
-      if (g == 0) rho[w][tb * 16 + c] = r;
-#pragma unroll
-      for (int fcw = 0; fcw < NFCW; ++fcw)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int fb = 2 * fcw + (j >> 2);
-          pb[tb][fcw][j] = to_t<XS>(fb < FB ? dp[fb][j & 3] : 0.f);
-          fk[tb][fcw][j] = to_t<XB>(fb < FB ? pk[tb][fb][j & 3] : 0.f);
-        }
+      if (g == 0) rho[tb * 16 + c][w] = r;
     }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, omt[db][fcw], pb[tb][fcw]);
-        *reinterpret_cast<f32x4*>(&xk[w][((db * 2 + tb) * 64 + lane) * 4]) = a;
-      }
-#pragma unroll
-    for (int cb = 0; cb < NVB; ++cb)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int fcw = 0; fcw < NFCW; ++fcw) mma16(a, dt[cb][fcw], fk[tb][fcw]);
-        *reinterpret_cast<f32x4*>(&xv[w][((cb * 2 + tb) * 64 + lane) * 4]) = a;
-      }
-    lds_barrier();  // B2: partials
+    lds_barrier();  // B2: P and phi' rows, rho partials
 
-    // ---- dk and dV: sums over the waves, the key's scale, stored (keys past L skipped)
-    constexpr int CD = D / 8;
-    for (int e = threadIdx.x; e < 32 * (CD + CPR); e += NT) {
-      const bool isk = e < 32 * CD;
-      const int e2 = isk ? e : e - 32 * CD;
-      const int ncol8 = isk ? CD : CPR;
-      const int krow = e2 / ncol8, c8 = e2 % ncol8;
-      const int tok = tok0 + krow;
-      if (tok >= L) continue;
-      const int tb = krow >> 4, cq = krow & 15;
-      const int blk = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
-      float mx = qmx[0][krow];
+    // ---- dk and dV blocks over all features, times the key's scale (stored later)
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[ww][krow]);
-      const float lf = mx - kn[buf][krow] - gm;  // log2 of the key's scale F_j
-      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
+    for (int bi = 0; bi < NBLK; ++bi) {
+      const bool isk = bi < BPWK;
+      const int blk = isk ? w * BPWK + bi : w * BPWV + (bi - BPWK);
+      const int cb = blk >> 1, tb = blk & 1;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (isk) {
+#pragma unroll
+        for (int fc = 0; fc < NFC; ++fc) mma16(a, omt[bi >> 1][fc], ld8<XS>(&prow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
+      } else {
+#pragma unroll
+        for (int fc = 0; fc < NFC; ++fc)
+          mma16(a, dt[(bi - BPWK) >> 1][fc], ld8<XB>(&frow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
+      }
+      const int krow = tb * 16 + c;
+      float mx = qmx[krow][0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[krow][ww]);
+      const float lf = mx - kn[buf][krow] - gm;  // log2 of the key's scale F_j (keys past L: -inf)
       if (isk) {
         float rs = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float* base = &xk[ww][((blk * 2 + tb) * 64 + cq + 16 * g0) * 4];
-          lo += *reinterpret_cast<const f32x4*>(base);
-          hi += *reinterpret_cast<const f32x4*>(base + 64);
-          rs += rho[ww][krow];
-        }
+        for (int ww = 0; ww < NW; ++ww) rs += rho[krow][ww];
         const float f = fast_exp2(lf + eD + vex[krow]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo[i] = f * (lo[i] * (1.f / kLog2e) - s2 * to_f(ks[buf][krow * KROW + c8 * 8 + i]) * rs);
-          hi[i] = f * (hi[i] * (1.f / kLog2e) - s2 * to_f(ks[buf][krow * KROW + c8 * 8 + 4 + i]) * rs);
-        }
+        for (int i = 0; i < 4; ++i)
+          a[i] = f * (a[i] * (1.f / kLog2e) - s2 * to_f(ks[buf][krow * KROW + cb * 16 + 4 * g + i]) * rs);
       } else {
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float* base = &xv[ww][((blk * 2 + tb) * 64 + cq + 16 * g0) * 4];
-          lo += *reinterpret_cast<const f32x4*>(base);
-          hi += *reinterpret_cast<const f32x4*>(base + 64);
-        }
-        const float f = fast_exp2(lf);
-        lo = lo * f;
-        hi = hi * f;
+        a = a * fast_exp2(lf);
       }
-      const int ncol = isk ? D : DV;
-      void* dst = isk ? dk : dv;
-      const size_t off = ((size_t)bh * L + tok) * ncol + c8 * 8;
-      if (grad_f32) {
-        f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + off);
-        o4[0] = lo;
-        o4[1] = hi;
-      } else {
-        vec8<T> o8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o8[i] = to_t<T>(lo[i]);
-          o8[i + 4] = to_t<T>(hi[i]);
-        }
-        st8<T>(reinterpret_cast<T*>(dst) + off, o8);
-      }
+      pend[bi] = a;
     }
+    pend_bh = bh;
+    pend_tok0 = tok0;
     cur.next();
   }
+  store_pending();
 }
 
 // ---------------------------------------------------------------- host side
@@ -852,7 +855,7 @@ bool bwd_shape_built(int d, int dv, int m) {
   return false;
 }
 
-constexpr int kBwdPieces = 256;  // one 4-wave workgroup per CU (one wave per SIMD)
+constexpr int kBwdPieces = 256;  // one workgroup per CU (eight waves: two per SIMD)
 
 BackwardPlan plan_backward(const Shape& s, int dtype) {
   BackwardPlan p;
@@ -898,6 +901,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
   constexpr int NWR = RedSplit<M>::NW;
+  constexpr int NWB = BwdSplit<M>::NW;
   const BackwardPlan p = plan_backward(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + p.off_omf);
@@ -935,17 +939,17 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   }
   {
     FAVOR_TIMED("bwd_q", st);
-    bwd_q_kernel<T, D, DV, M><<<p.G, 64 * NWR, 0, st>>>(q, dout, omf, omt, srow, s.H, s.L, p.tpb, p.T_all, p.G,
+    bwd_q_kernel<T, D, DV, M><<<p.G, 64 * NWB, 0, st>>>(q, dout, omf, omt, srow, s.H, s.L, p.tpb, p.T_all, p.G,
                                                         grad_f32, dpart, dzpart, dq);
   }
   {
     FAVOR_TIMED("combine_d", st);
-    combine_rows_kernel<DV, M, NWR><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
+    combine_rows_kernel<DV, M, NWB><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
         dpart, dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
   }
   {
     FAVOR_TIMED("bwd_k", st);
-    bwd_k_kernel<T, D, DV, M><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb, p.T_all, p.G,
+    bwd_k_kernel<T, D, DV, M><<<p.G, 64 * NWB, 0, st>>>(k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb, p.T_all, p.G,
                                                         nscale, sc * sc, grad_f32, dk, dv);
   }
   return hipGetLastError();

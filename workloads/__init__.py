@@ -18,6 +18,9 @@ bidirectional attention, causal attention and recurrent decoding):
                build the state, then 1000 steps of q,k,v ~ N(0,1)         seed 4
   decode_gated_bf16  the same, each step with a gate g ~ U[0.9, 1) per
                (sequence, head) and input weight 1 - g                   seed 5
+  backward_bf16  bidir_bf16's inputs plus an upstream gradient dOut ~ N(0,1)
+               [B,H,L,dv] (its own generator, seed + 100): the gradients
+               of the bidirectional estimator                            seed 2
 
 Draw order for one workload: Q, then K, then V, each one `torch.randn` call on
 a CPU generator seeded with the workload's seed, scaled, then rounded to the
@@ -37,7 +40,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "bidir" | "cross" | "causal" | "decode" | "decode_gated"
+    kind: str            # "bidir" | "cross" | "causal" | "decode" | "decode_gated" | "backward"
     dtype: str           # "f32" | "bf16"
     B: int
     H: int
@@ -72,6 +75,8 @@ WORKLOADS = {
                            1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "cross_bf16": Workload("cross_bf16", "cross", "bf16", 8, 12, 4096, 64, 64, 256, 6,
                            1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0, Lq=1024),
+    "backward_bf16": Workload("backward_bf16", "backward", "bf16", 8, 12, 4096, 64, 64, 256, 2,
+                              1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
                             steps=1000, prior=2048),
@@ -116,6 +121,14 @@ def make_decode_prior(w: Workload, n_seq: Optional[int] = None, device: str = "c
     if device != "cpu":
         k, v = k.to(device), v.to(device)
     return k, v
+
+
+def make_dout(w: Workload, device: str = "cpu") -> torch.Tensor:
+    """Upstream gradient of the attention output, [B,H,Lq,dv] ~ N(0,1) in the workload dtype, drawn on a CPU
+    generator seeded with the workload's seed + 100."""
+    gen = torch.Generator("cpu").manual_seed(w.seed + 100)
+    g = _randn(gen, (w.B, w.H, w.Lq_eff, w.dv), 1.0, w.torch_dtype)
+    return g.to(device) if device != "cpu" else g
 
 
 def make_decode_steps(w: Workload, device: str, steps: Optional[int] = None):
