@@ -26,7 +26,10 @@
 // The two products that subtract nearly equal terms (dPhi_Q's S g - z (g . out) and dPhi_K's
 // dS v + dz) take fp16 operands (11-bit mantissas) scaled by powers of two: S_aug and dS_aug
 // per (b,h) to a largest magnitude in [8, 16), W and [V 1] per row to one in [1/2, 1); the
-// scales are undone exactly on the results. Products without cancellation use bf16.
+// scales are undone exactly on the results. The sums whose terms cancel across tokens take
+// bf16 operands as hi + lo pairs: the recomputed S_aug (key features split, two MFMAs) and
+// dS_aug (phi' and W split, three MFMAs), which keeps them near fp32 accuracy. Products
+// without cancellation use bf16.
 #include "favor_device.hpp"
 #include "favor_plan.hpp"
 #include "favor_reduce.hpp"
