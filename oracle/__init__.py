@@ -12,7 +12,8 @@ Contents
             The bit-level recipe is fixed so that two independent
             implementations produce identical fp32 bits.
   favor.py  the feature maps (positive softmax features, Lemma 1, and their
-            hyperbolic form; ReLU features, appendix A.4), the bidirectional estimator (equation 4 /
+            hyperbolic form; trigonometric features, equation 5 with sin and
+            cos; ReLU features, appendix A.4), the bidirectional estimator (equation 4 /
             Algorithm 1), the causal estimator as the prefix-sum recurrence
             (appendix B.1 equation 11; the RNN form in the linear-attention
             blog's "Autoregressive Generation" section), the single-token
@@ -32,14 +33,14 @@ convergence to exact softmax attention as m grows, invariants).
 """
 from .omega import make_omega, splitmix64_mix, stream_key, uniform52, gaussians, OMEGA_MODES
 from .favor import (
-    features, features_hyperbolic, bidir, bidir_from_features, bidir_backward, causal, causal_bruteforce, causal_bruteforce_from_features,
+    features, features_hyperbolic, features_trig, bidir, bidir_from_features, bidir_backward, causal, causal_bruteforce, causal_bruteforce_from_features,
     decode_step, decode_run, decode_gated_step, decode_gated_run, decode_gated_unrolled, state_from_prior,
     softmax_attention, attention_matrix, row_norm_rel_err,
 )
 
 __all__ = [
     "make_omega", "splitmix64_mix", "stream_key", "uniform52", "gaussians", "OMEGA_MODES",
-    "features", "features_hyperbolic", "bidir", "bidir_from_features", "bidir_backward", "causal", "causal_bruteforce",
+    "features", "features_hyperbolic", "features_trig", "bidir", "bidir_from_features", "bidir_backward", "causal", "causal_bruteforce",
     "causal_bruteforce_from_features", "decode_step", "decode_run", "decode_gated_step", "decode_gated_run",
     "decode_gated_unrolled", "state_from_prior",
     "softmax_attention", "attention_matrix", "row_norm_rel_err",

@@ -13,6 +13,9 @@ unless stated otherwise):
   * ReLU features (equation 5 with h = 1, f = ReLU; the generalised-attention
     defaults of appendix A.4 add a small kernel epsilon to every feature):
         phi_r(x) = max(omega_r . x, 0) / sqrt(m) + eps;
+  * trigonometric features (equation 5 with h(x) = exp(|x|^2/2), l = 2, f1 = sin,
+    f2 = cos: the estimator SM^trig of section 2.3), m vectors -> 2m features:
+        phi(x) = exp(|x|^2/2) / sqrt(m) (sin(w_1.x), ..., sin(w_m.x), cos(w_1.x), ..., cos(w_m.x));
   * bidirectional estimator (equation 4; Algorithm 1 with C = [V 1]):
         S = Phi_K^T V,  z = Phi_K^T 1,  out_i = (Phi_Q,i . S) / (Phi_Q,i . z);
   * causal estimator (appendix B.1, equation 11, prefix sums that include the
@@ -41,7 +44,8 @@ def _f64(x) -> np.ndarray:
 
 def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
     """phi(x) for raw queries or keys x [B,H,L,d] and omega [H,m,d] -> [B,H,L,m] (fp64);
-    kind "hyperbolic": the 2m hyperbolic features of the m rows (features_hyperbolic)."""
+    kind "hyperbolic": the 2m hyperbolic features of the m rows (features_hyperbolic); kind "trig": the 2m
+    trigonometric features of the m rows (features_trig)."""
     x = _f64(x)
     om = _f64(omega)
     d = x.shape[-1]
@@ -55,7 +59,25 @@ def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
         return np.maximum(a, 0.0) / math.sqrt(m) + eps
     if kind == "hyperbolic":  # the rows of omega are the random vectors; 2m features
         return features_hyperbolic(x, omega)
+    if kind == "trig":  # likewise
+        return features_trig(x, omega)
     raise ValueError(f"unknown feature kind {kind!r}")
+
+
+def features_trig(x, omega) -> np.ndarray:
+    """The trigonometric features (Performer paper, equation 5 with h(x) = exp(|x|^2/2), l = 2, f1 = sin,
+    f2 = cos; section 2.3's SM^trig) for raw x [B,H,L,d] and the random vectors w_i = rows of omega [H,m,d]:
+    with x scaled by d^-1/4,
+        phi(x) = exp(|x|^2/2) / sqrt(m) * (sin(w_1.x), ..., sin(w_m.x), cos(w_1.x), ..., cos(w_m.x)),
+    so phi(x).phi(y) = exp((|x|^2+|y|^2)/2) (1/m) sum_i cos(w_i.(x-y)). Returns [B,H,L,2m] (fp64)."""
+    x = _f64(x)
+    om = _f64(omega)
+    d = x.shape[-1]
+    m = om.shape[-2]
+    xs = x * (float(d) ** -0.25)
+    a = np.einsum("bhld,hmd->bhlm", xs, om)
+    h = np.exp(0.5 * np.sum(xs * xs, axis=-1, keepdims=True)) / math.sqrt(m)
+    return np.concatenate([h * np.sin(a), h * np.cos(a)], axis=-1)
 
 
 def features_hyperbolic(x, omega) -> np.ndarray:

@@ -49,7 +49,7 @@ import numpy as np
 MASK64 = (1 << 64) - 1
 GAMMA = 0x9E3779B97F4A7C15
 TWO_PI = 6.283185307179586  # the binary64 value nearest to 2*pi (== 2 * math.pi)
-OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2, "hyperbolic": 3}
+OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2, "hyperbolic": 3, "trig_pairs": 4}
 
 
 def splitmix64_mix(z: int) -> int:
@@ -136,6 +136,14 @@ def _make_omega_cached(seed: int, H: int, m: int, d: int, mode: int) -> bytes:
             raise ValueError("hyperbolic mode needs an even m")
         half = np.frombuffer(_make_omega_cached(seed, H, m // 2, d, 0), dtype=np.float32).reshape(H, m // 2, d)
         return np.concatenate([half, -half], axis=1).tobytes()
+    if mode == 4:
+        # trigonometric features (Performer paper, equation 5 with f1 = sin, f2 = cos): the m/2 vectors of the
+        # orthogonal chi(d) mode, then the same rows again; a feature map that takes the sine of the first m/2
+        # projections and the cosine of the last m/2 gives the 2(m/2) features of those m/2 vectors
+        if m % 2:
+            raise ValueError("trig_pairs mode needs an even m")
+        half = np.frombuffer(_make_omega_cached(seed, H, m // 2, d, 0), dtype=np.float32).reshape(H, m // 2, d)
+        return np.concatenate([half, half], axis=1).tobytes()
     out = np.empty((H, m, d), dtype=np.float32)
     nblocks = (m + d - 1) // d
     for h in range(H):

@@ -311,6 +311,78 @@ def test_hyperbolic_omega_mode_gives_the_hyperbolic_features():
     assert np.max(np.abs(a - b) / b) < 1e-13
 
 
+def test_trig_features_exact_on_the_diagonal_and_ordered_as_equation_5():
+    """Equation 5 with h(x) = exp(|x|^2/2), l = 2, f1 = sin, f2 = cos (section 2.3, SM^trig): since
+    sin^2 + cos^2 = 1, phi(x).phi(x) = exp(|x|^2) = SM(x, x) exactly for any omega (a dropped h, a wrong
+    1/sqrt(m) or a missing cosine block fails this); the sine block comes first."""
+    d, m = 16, 8
+    s = float(d) ** 0.25
+    om = make_omega(5, 1, m, d, "iid")
+    for _ in range(3):
+        x = RNG.normal(size=d) * 0.4
+        f = oracle.features_trig((x * s)[None, None, None], om)[0, 0, 0]
+        assert f.shape == (2 * m,)
+        assert float(f @ f) == pytest.approx(math.exp(float(x @ x)), rel=1e-13)
+    # one vector e_1 and x = (pi/2) e_1: sin = 1, cos = 0, h = exp((pi/2)^2 / 2)
+    om1 = np.zeros((1, 1, d))
+    om1[0, 0, 0] = 1.0
+    x1 = np.zeros(d)
+    x1[0] = math.pi / 2
+    f1 = oracle.features_trig((x1 * s)[None, None, None], om1)[0, 0, 0]
+    h = math.exp(0.5 * (math.pi / 2) ** 2)
+    assert f1[0] == pytest.approx(h, rel=1e-14) and abs(f1[1]) < 1e-14 * h
+
+
+def test_trig_features_unbiased_with_lemma2_variance():
+    """SM^trig is unbiased for exp(x.y), and one vector's estimate exp((|x|^2+|y|^2)/2) cos(w.(x-y)) has
+    variance m * MSE^trig = (1/2) exp(|x|^2 + |y|^2) (1 - exp(-|x-y|^2))^2 (Lemma 2, equation 8, first line,
+    read with the squares of appendix F equations 13-15: exp(|z|^2) SM^-2 = exp(|x|^2 + |y|^2))."""
+    d, m = 16, 32768
+    om = make_omega(2026, 1, m, d, "iid")
+    s = float(d) ** 0.25
+    for trial in range(3):
+        x = RNG.normal(size=d) * 0.15
+        y = RNG.normal(size=d) * 0.15
+        sm = math.exp(float(x @ y))
+        dl2 = float((x - y) @ (x - y))
+        var1 = 0.5 * math.exp(float(x @ x) + float(y @ y)) * (1.0 - math.exp(-dl2)) ** 2
+        fx = oracle.features_trig((x * s)[None, None, None], om)[0, 0, 0]
+        fy = oracle.features_trig((y * s)[None, None, None], om)[0, 0, 0]
+        assert float(fx @ fy) == pytest.approx(sm, abs=4.0 * math.sqrt(var1 / m))
+        est = m * (fx[:m] * fy[:m] + fx[m:] * fy[m:])   # one vector each
+        assert float(est.var()) == pytest.approx(var1, rel=0.12)
+
+
+def test_trig_pairs_omega_mode_repeats_the_rows():
+    """The trig_pairs Omega mode: the m/2 orthogonal chi(d) rows, then the same rows again, so that the
+    sine of the first m/2 projections and the cosine of the last m/2 are equation 5's 2(m/2) features."""
+    H, d, m = 2, 16, 64
+    x = RNG.normal(size=(1, H, 7, d))
+    om_p = make_omega(31, H, m, d, "trig_pairs")
+    om_half = make_omega(31, H, m // 2, d, "ortho_chi")
+    assert np.array_equal(om_p[:, :m // 2], om_half) and np.array_equal(om_p[:, m // 2:], om_half)
+    xs = x * d ** -0.25
+    a = np.einsum("bhld,hmd->bhlm", xs, om_p.astype(np.float64))
+    h = np.exp(0.5 * np.sum(xs * xs, axis=-1, keepdims=True)) / math.sqrt(m // 2)
+    paired = np.concatenate([h * np.sin(a[..., :m // 2]), h * np.cos(a[..., m // 2:])], axis=-1)
+    assert np.max(np.abs(paired - oracle.features_trig(x, om_half))) < 1e-13
+
+
+def test_trig_attention_converges_to_softmax_attention():
+    """With trigonometric features the ratio of equation 4 also approximates softmax attention (section
+    2.3: SM^trig is unbiased; the per-key h(k) does not cancel) and improves with m."""
+    B, H, L, d, dv = 1, 1, 24, 16, 8
+    q = RNG.normal(size=(B, H, L, d)) * 0.3
+    k = RNG.normal(size=(B, H, L, d)) * 0.3
+    v = RNG.normal(size=(B, H, L, dv))
+    exact = oracle.softmax_attention(q, k, v)
+    errs = []
+    for m in (16, 1024, 65536):
+        approx = bidir(q, k, v, make_omega(3 + m, H, m, d, "iid"), kind="trig")
+        errs.append(float(np.max(np.abs(approx - exact))))
+    assert errs[2] < errs[0] and errs[2] < 0.02, errs
+
+
 def test_features_apply_the_sqrt_d_temperature():
     """Section 2.3 under equation 6: raw q, k are scaled so that the kernel is exp(q.k / sqrt(d))."""
     d, m = 16, 16384
