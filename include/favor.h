@@ -58,15 +58,30 @@ typedef enum {
  * FAVOR_BF16 projects and contracts on bf16 MFMA with fp32 accumulation. */
 typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
 
-/* Feature map: positive softmax features (Lemma 1) or ReLU features (appendix A.4). */
-typedef enum { FAVOR_PRF = 0, FAVOR_RELU = 1 } favor_kind;
+/* Feature map: positive softmax features (Lemma 1), ReLU features (appendix A.4) or
+ * trigonometric features (equation 5 with h(x) = exp(|x|^2/2), f1 = sin, f2 = cos; section
+ * 2.3's SM^trig). FAVOR_TRIG (m even): feature r < m/2 is sin(omega_r.x), feature r >= m/2 is
+ * cos(omega_r.x), scaled by exp(|x|^2/2)/sqrt(m/2); with an Omega of FAVOR_TRIG_PAIRS (the
+ * same m/2 vectors twice) these are the sine and cosine features of m/2 vectors. Supported by
+ * favor_features and favor_bidir / favor_bidir_cross (renormalize = 1); the projection of
+ * every token must stay within 1600 radians (the hardware cosine's range). Trigonometric
+ * features can be negative, so the denominators of the ratio can vanish (section 2.3). */
+typedef enum { FAVOR_PRF = 0, FAVOR_RELU = 1, FAVOR_TRIG = 2 } favor_kind;
 
 /* Omega rows: orthogonal blocks with chi(d) lengths (section 2.4, appendix B.2/F.4),
  * independent Gaussian rows, or orthogonal rows of length sqrt(d) (SMREG, section 2.3).
  * FAVOR_HYPERBOLIC (m even): the m/2 rows of FAVOR_ORTHO_CHI, then their negatives; with
  * FAVOR_PRF every entry point then computes the hyperbolic positive features of Lemma 1
- * (second form): exp(-|x|^2/2)/sqrt(m) (exp(w_i.x), exp(-w_i.x)) for the m/2 vectors w_i. */
-typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2, FAVOR_HYPERBOLIC = 3 } favor_omega_mode;
+ * (second form): exp(-|x|^2/2)/sqrt(m) (exp(w_i.x), exp(-w_i.x)) for the m/2 vectors w_i.
+ * FAVOR_TRIG_PAIRS (m even): the m/2 rows of FAVOR_ORTHO_CHI, then the same rows again, for
+ * FAVOR_TRIG. */
+typedef enum {
+  FAVOR_ORTHO_CHI = 0,
+  FAVOR_IID = 1,
+  FAVOR_ORTHO_SQRTD = 2,
+  FAVOR_HYPERBOLIC = 3,
+  FAVOR_TRIG_PAIRS = 4
+} favor_omega_mode;
 
 /* favor_make_omega — random features omega [H,m,d] fp32 into device memory.
  * Section 2.4 and appendix B.2 of the Performer paper: for each head, ceil(m/d)
@@ -77,7 +92,8 @@ typedef enum { FAVOR_ORTHO_CHI = 0, FAVOR_IID = 1, FAVOR_ORTHO_SQRTD = 2, FAVOR_
  * bits depend only on (seed, H, m, d, mode): head h's rows do not depend on H.
  * Then copied with hipMemcpyAsync on `stream` (the host buffer stays alive
  * until the copy completes: the call synchronises `stream` before returning).
- * Requires 1 <= d <= 256, 1 <= m <= 4096, 1 <= H <= 65536 (m even for FAVOR_HYPERBOLIC). */
+ * Requires 1 <= d <= 256, 1 <= m <= 4096, 1 <= H <= 65536 (m even for FAVOR_HYPERBOLIC and
+ * FAVOR_TRIG_PAIRS). */
 favor_status favor_make_omega(uint64_t seed, int H, int m, int d, favor_omega_mode mode,
                               float* omega_dev, hipStream_t stream);
 
@@ -90,7 +106,8 @@ favor_status favor_make_omega_host(uint64_t seed, int H, int m, int d, favor_ome
  *   phi_true[b,h,l,r] = phi[b,h,l,r] * exp(logscale[b,h,l]).
  * PRF: phi is exp(omega_r.x - max_r' omega_r'.x) / sqrt(m) (each row's largest
  * entry is 1/sqrt(m)) and logscale = max_r omega_r.x - |x|^2/2, so no row over- or
- * underflows. RELU: phi = max(omega_r.x, 0)/sqrt(m) + eps and logscale = 0.
+ * underflows. RELU: phi = max(omega_r.x, 0)/sqrt(m) + eps and logscale = 0. TRIG: phi is
+ * sin or cos(omega_r.x) / sqrt(m/2) and logscale = |x|^2/2.
  * Supported (d, m): see favor_bidir. */
 favor_status favor_features(const void* x, const float* omega, int B, int H, int L, int d, int m,
                             favor_dtype dtype, favor_kind kind, float eps,
@@ -115,7 +132,8 @@ favor_status favor_bidir(const void* q, const void* k, const void* v, const floa
  *   renormalize != 0: out_i = phi(q_i).S / phi(q_i).z   (as favor_bidir)
  *   renormalize == 0: out_i = phi(q_i).S with S = sum_j phi(k_j) v_j^T and the features
  *     in canonical scale, phi = exp(omega.x - |x|^2/2)/sqrt(m) (PRF) or
- *     max(omega.x, 0)/sqrt(m) + eps (ReLU); the stabilisers are undone exactly.
+ *     max(omega.x, 0)/sqrt(m) + eps (ReLU); the stabilisers are undone exactly
+ *     (FAVOR_TRIG: FAVOR_ERR_UNSUPPORTED).
  * Workspace: favor_workspace_size(0, B, H, Lk, d, dv, m, dtype). Built shapes, dtypes,
  * errors as favor_bidir, and 1 <= Lq <= 2^28. favor_bidir(..., L, ...) is
  * favor_bidir_cross(..., L, L, ..., renormalize = 1, ...). */
@@ -130,7 +148,8 @@ favor_status favor_bidir_cross(const void* q, const void* k, const void* v, cons
  * z_final [B,H,m] (fp32, both or neither) are non-NULL, the state after the last
  * token is written in canonical (unstabilised) scale: exactly what
  * favor_decode continues from. Canonical state needs PRF with d <= 64
- * (exp(omega.x - |x|^2/2) <= exp(|omega|^2/2) stays inside fp32). */
+ * (exp(omega.x - |x|^2/2) <= exp(|omega|^2/2) stays inside fp32). FAVOR_TRIG:
+ * FAVOR_ERR_UNSUPPORTED. */
 favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega,
                           int B, int H, int L, int d, int dv, int m,
                           favor_dtype dtype, favor_kind kind, float eps, int out_f32,
@@ -142,7 +161,7 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
  * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical
  * scale, updated in place; out [N,H,dv] fp32.
  * Requires d in {16, 32, 64}, dv a power of two in [16, 256], m a multiple of 16
- * with m <= 1024 (other values: FAVOR_ERR_UNSUPPORTED). */
+ * with m <= 1024 (other values, and FAVOR_TRIG: FAVOR_ERR_UNSUPPORTED). */
 favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega,
                           float* S, float* z, int N, int H, int d, int dv, int m,
                           favor_dtype dtype, favor_kind kind, float eps,

@@ -26,9 +26,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
-PRF, RELU = 0, 1
-OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2, "hyperbolic": 3}
-KINDS = {"prf": PRF, "relu": RELU}
+PRF, RELU, TRIG = 0, 1, 2
+OMEGA_MODES = {"ortho_chi": 0, "iid": 1, "ortho_sqrtd": 2, "hyperbolic": 3, "trig_pairs": 4}
+KINDS = {"prf": PRF, "relu": RELU, "trig": TRIG}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "hip error"}
 
 _vp = ctypes.c_void_p

@@ -15,10 +15,10 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_dtype(favor_dtype t) { return t == FAVOR_F32 || t == FAVOR_BF16; }
-bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU; }
+bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU || k == FAVOR_TRIG; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool valid_omega_mode(favor_omega_mode mode, int m) {
-  if (mode == FAVOR_HYPERBOLIC) return m % 2 == 0;
+  if (mode == FAVOR_HYPERBOLIC || mode == FAVOR_TRIG_PAIRS) return m % 2 == 0;
   return mode == FAVOR_ORTHO_CHI || mode == FAVOR_IID || mode == FAVOR_ORTHO_SQRTD;
 }
 
@@ -86,6 +86,7 @@ favor_status favor_features(const void* x, const float* omega, int B, int H, int
   for (int dv : {16, 32, 64})
     if (favor::shape_built(dtype, d, dv, m)) built = true;
   if (!built) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
   return hip_status(favor::launch_features(x, omega, s, dtype, kind, eps, phi, logscale, stream));
 }
 
@@ -101,6 +102,8 @@ favor_status favor_bidir_cross(const void* q, const void* k, const void* v, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out) || !aligned16(ws))
     return FAVOR_ERR_INVALID_ARG;
   if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
+  if (kind == FAVOR_TRIG && !renormalize) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_bidir(s, dtype).total) return FAVOR_ERR_WORKSPACE;
   return hip_status(favor::launch_bidir(q, k, v, omega, s, Lq, renormalize ? 1 : 0, dtype, kind, eps,
                                         out_f32 ? 1 : 0, out, ws, stream));
@@ -149,6 +152,7 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
     return FAVOR_ERR_INVALID_ARG;
   if (S_final && (!aligned16(S_final) || !aligned16(z_final))) return FAVOR_ERR_INVALID_ARG;
   if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
   if (S_final && (kind != FAVOR_PRF || d > 64)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_causal(s, dtype).total) return FAVOR_ERR_WORKSPACE;
   return hip_status(
@@ -168,6 +172,7 @@ static favor_status decode_common(const void* q, const void* k, const void* v, c
   if (!(d == 16 || d == 32 || d == 64)) return FAVOR_ERR_UNSUPPORTED;
   if (!pow2(dv) || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
   if (m % 16 != 0 || m > 1024) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
   return hip_status(
       favor::launch_decode(q, k, v, omega, S, z, N, H, d, dv, m, dtype, kind, eps, gate, inw, out, stream));
 }

@@ -29,6 +29,12 @@
 
 namespace favor {
 
+// Scale folded into the Omega' fragments: d^-1/4, times log2(e) for the exponential map (the
+// hardware exp2) or 1/(2 pi) for the trigonometric map (the hardware cosine takes revolutions).
+inline float omega_scale(int kind, float sc) {
+  return kind == kPrf ? sc * kLog2e : (kind == kTrig ? sc * 0.15915494309189535f : sc);
+}
+
 // ---------------------------------------------------------------- combine
 // One workgroup per (b*h, 32-feature chunk), one thread per (value block, lane): the
 // partials of the pieces of that (b,h), already in fragment layout, scaled by
@@ -48,9 +54,10 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
   const int np = (int)(i_hi - i_lo + 1);
   const int wv = (fc * 32) / (FB * 16);  // the reducing wave that owned this chunk
   float gmax = -INFINITY;
-  if (kind == kPrf)
+  const bool scaled = kind != kRelu;  // ReLU features carry no key stabiliser
+  if (scaled)
     for (int k = 0; k < np * NW; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW]);
-  if (fc == 0 && threadIdx.x == 0) gmx[bh] = (kind == kPrf) ? gmax : 0.f;  // the keys' common maximum
+  if (fc == 0 && threadIdx.x == 0) gmx[bh] = scaled ? gmax : 0.f;  // the keys' common maximum
   for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {
     const int nb = e >> 6, lane = e & 63;
     const int c = lane & 15, g = lane >> 4;
@@ -66,7 +73,7 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
         for (int j = 0; j < KP; ++j) {
           const int k = k0 + j < np ? k0 + j : np - 1;
           const size_t slot = (size_t)(i_lo + k) + bh;
-          sc[j] = k0 + j < np ? ((kind == kPrf) ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f) : 0.f;
+          sc[j] = k0 + j < np ? (scaled ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f) : 0.f;
           const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
                                            : zpart + ((slot * NFC + fc) * 4 + g) * 8;
           pl[j] = reinterpret_cast<const f32x4*>(src)[0];
@@ -100,7 +107,9 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
 //                 constant per row cancel in the ratio). If some row of the tile has
 //                 b_t > kQueryBoundLimit, the tile takes the exact row maximum across the
 //                 waves instead (one more barrier).
-//     feature map Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps); the accumulator pairs are
+//     feature map Phi = exp2(.) (ReLU: max(a,0)/sqrt(m) + eps; trigonometric: the sine or
+//                 cosine of the projection, whose scale exp(|x|^2/2)/sqrt(m) cancels in the
+//                 ratio); the accumulator pairs are
 //                 B operands of the contraction as they stand (paired feature slots) and go
 //                 to LDS; the wave's share of the denominator z^T Phi^T goes with them
 //   every thread then lands, converts and norms its own chunk of tile t+1 and copies its
@@ -257,6 +266,13 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) pacc[tb][fb][i] = fast_exp2(pacc[tb][fb][i]);
+    } else if constexpr (KIND == kTrig) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pacc[tb][fb][i] = trig_feature(pacc[tb][fb][i], (w * FB + fb) * 16 + 4 * g + i, M);
     } else {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -429,6 +445,13 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
 #pragma unroll
         for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - mx) * inv_sqrt_m;
       ls = mx * kLn2 - s2 * nscale_ln;
+    } else if (kind == kTrig) {
+      // m/2 vectors: the scale 1/sqrt(m/2); exp(|x|^2/2) goes to the log scale
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pacc[fb][i] = trig_feature(pacc[fb][i], fb * 16 + 4 * g + i, M) * (inv_sqrt_m * 1.41421356f);
+      ls = s2 * nscale_ln;
     } else {
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb)
@@ -504,7 +527,7 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   float* gmx = reinterpret_cast<float*>(base + p.off_gmax);
   const float log2_m = std::log2((float)M);
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
+  const float wscale = omega_scale(kind, sc);
   const float nscale = sc * sc * kLog2e * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
 
@@ -520,6 +543,9 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
     if (kind == kPrf)
       kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps,
                                                                         inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+    else if (kind == kTrig)
+      kv_reduce_kernel<T, D, DV, M, kReduceRing, kTrig><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
+                                                                         eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
     else
       kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
                                                                          eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
@@ -535,6 +561,10 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
       q_output_kernel<T, D, DV, M, kPrf><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
                                                                   eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
                                                                   log2_m, out);
+    else if (kind == kTrig)
+      q_output_kernel<T, D, DV, M, kTrig><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
+                                                                   eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
+                                                                   log2_m, out);
     else
       q_output_kernel<T, D, DV, M, kRelu><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
                                                                    eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
@@ -567,7 +597,7 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
+  const float wscale = omega_scale(kind, sc);
   const float nscale_ln = sc * sc * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
   const int tpw = 256;

@@ -7,6 +7,15 @@ namespace favor {
 
 constexpr int kPrf = 0;
 constexpr int kRelu = 1;
+constexpr int kTrig = 2;
+
+// Trigonometric feature of a projection in revolutions (the Omega' fragments carry the
+// 1/(2 pi)): the first half of the m features are sines, the second half cosines, written
+// as one cosine with a quarter-turn phase so that every lane issues one transcendental.
+// The hardware cosine takes |a| <= 256 revolutions.
+__device__ __forceinline__ float trig_feature(float a, int feature, int m) {
+  return __builtin_amdgcn_cosf(a - (feature < (m >> 1) ? 0.25f : 0.f));
+}
 
 // ---------------------------------------------------------------- omega fragments
 // frag[h][fb][dc][lane][j] = scale * omega[h][fb*16 + c][dc*32 + 8g + j] (0 beyond d),

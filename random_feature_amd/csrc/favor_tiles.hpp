@@ -345,6 +345,41 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       wait_vmcnt<0>();  // no stores may stay in flight under the partial waits of the ring
     }
     // stabiliser of tile t (its projection is complete)
+    // trigonometric features: the keys' own scale exp(|y|^2/2) = 2^(n'_t) rides on a running
+    // maximum of n'_t in the same way (rows past L carry an infinite norm: weight 0)
+    float tw[2][4];
+    if constexpr (KIND == kTrig) {
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tw[tb][i] = n4[i] < INFINITY ? n4[i] - (first ? 0.f : runmax) : -INFINITY;
+          lmax = fmaxf(lmax, tw[tb][i]);
+        }
+      }
+      if (first || __builtin_amdgcn_ballot_w64(lmax > 0.f) != 0) {
+        const float shift = wave_max(lmax) + kKeyMargin;
+        if (!first) {
+          const float sc = fast_exp2(-shift);
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sacc[fb][nb] *= sc;
+        }
+        runmax = first ? shift : runmax + shift;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tw[tb][i] -= shift;
+        first = false;
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tw[tb][i] = fast_exp2(tw[tb][i]);
+    }
     if constexpr (KIND == kPrf) {
       float lmax = -INFINITY;
 #pragma unroll
@@ -393,6 +428,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         float f;
         if constexpr (KIND == kPrf) {
           f = fast_exp2(a);  // rows past L carry an infinite norm: exp2(-inf) = 0
+        } else if constexpr (KIND == kTrig) {
+          f = trig_feature(a, (w * FB + fb) * 16 + c, M) * tw[j >> 2][j & 3];
         } else {
           const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L;
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;

@@ -94,9 +94,11 @@ static void block_rows(uint64_t seed, int head, int block, int d, int mode, std:
 }
 
 void make_omega(uint64_t seed, int H, int m, int d, int mode, float* out) {
-  if (mode == 3) {
-    // hyperbolic positive features: the m/2 rows of the orthogonal chi(d) mode, then their
-    // negatives (m is even)
+  if (mode == 3 || mode == 4) {
+    // hyperbolic positive features (3): the m/2 rows of the orthogonal chi(d) mode, then their
+    // negatives; trigonometric pairs (4): the same rows twice, for the sine and the cosine
+    // features of each vector (m is even)
+    const float sign = mode == 3 ? -1.f : 1.f;
     const int half = m / 2;
     std::vector<float> base(static_cast<size_t>(H) * half * d);
     make_omega(seed, H, half, d, 0, base.data());
@@ -105,7 +107,7 @@ void make_omega(uint64_t seed, int H, int m, int d, int mode, float* out) {
         for (int t = 0; t < d; ++t) {
           const float x = base[(static_cast<size_t>(h) * half + r) * d + t];
           out[(static_cast<size_t>(h) * m + r) * d + t] = x;
-          out[(static_cast<size_t>(h) * m + half + r) * d + t] = -x;
+          out[(static_cast<size_t>(h) * m + half + r) * d + t] = sign * x;
         }
     return;
   }

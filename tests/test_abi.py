@@ -80,6 +80,19 @@ def test_causal_argument_checks():
     assert call(S=FAKE, z=None) == INVALID          # both or neither
     assert call(wsb=8) == WORKSPACE
     assert call(d=48) == UNSUPPORTED
+    assert call(kind=2) == UNSUPPORTED          # trigonometric features: bidirectional and features only
+
+
+def test_trig_argument_checks():
+    def cross(renorm=1, m=256):
+        return rf.raw_call("favor_bidir_cross", FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 64, m, 1, 2,
+                           ctypes.c_float(0.0), renorm, 0, FAKE, FAKE, ctypes.c_size_t(8), None)
+    assert cross() == WORKSPACE                 # accepted up to the workspace check
+    assert cross(renorm=0) == UNSUPPORTED       # no canonical scale for the trigonometric map
+    dec = rf.raw_call("favor_decode", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 64, 256, 1, 2,
+                      ctypes.c_float(0.0), FAKE, None)
+    assert dec == UNSUPPORTED
+    assert rf.raw_call("favor_make_omega_host", ctypes.c_uint64(0), 1, 33, 16, 4, FAKE) == INVALID
 
 
 def test_decode_argument_checks():
@@ -142,6 +155,7 @@ def test_workspace_size_query():
     (3, 2, 40, 16, "ortho_chi"),
     (4, 2, 96, 32, "ortho_sqrtd"),
     (6, 3, 128, 64, "hyperbolic"),
+    (7, 2, 64, 16, "trig_pairs"),
     (5, 2, 48, 16, "iid"),
     (2 ** 64 - 1, 1, 64, 64, "ortho_chi"),
     (12345678901234, 1, 20, 7, "ortho_chi"),

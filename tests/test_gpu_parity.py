@@ -39,7 +39,7 @@ def _inputs(B, H, L, d, dv, dtype, seed, scale=0.5):
 # ---------------------------------------------------------------- Omega
 
 @pytest.mark.parametrize("seed,H,m,d,mode", [(0, 1, 32, 16, "ortho_chi"), (2, 12, 256, 64, "ortho_chi"),
-                                             (4, 16, 256, 64, "iid")])
+                                             (4, 16, 256, 64, "iid"), (5, 2, 256, 64, "trig_pairs")])
 def test_device_omega_bits_match_oracle(seed, H, m, d, mode):
     om = rf.make_omega(seed, H, m, d, mode).cpu().numpy()
     assert np.array_equal(om.view(np.uint32), oracle.make_omega(seed, H, m, d, mode).view(np.uint32))
@@ -456,6 +456,59 @@ def test_hyperbolic_features_decode():
     outs = torch.stack([rf.decode(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), om_dev, Sd, zd) for t in range(T)])
     torch.cuda.synchronize()
     assert rel_err(outs, refs) < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- trigonometric features
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d,m", [(16, 32), (64, 256), (32, 64)])
+def test_trig_feature_map(dtype, d, m):
+    """favor_features with FAVOR_TRIG over the trig_pairs Omega: phi * exp(logscale) equals the oracle's
+    trigonometric features of the m/2 vectors (equation 5: sines, then cosines, times exp(|x|^2/2)/sqrt(m/2))."""
+    B, H, L = 2, 3, 77
+    x = workloads.make_tensor((B, H, L, d), 21 + d, 0.5, dtype)
+    om_dev = rf.make_omega(44, H, m, d, "trig_pairs")
+    om_half = oracle.make_omega(44, H, m // 2, d, "ortho_chi")
+    phi, ls = rf.features(x.to(DEV), om_dev, kind="trig")
+    true = (phi.double() * torch.exp(ls.double())[..., None]).cpu()
+    e = rel_err(true, oracle.features_trig(x, om_half))
+    assert e < TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(16, 16, 32), (32, 32, 64), (64, 64, 128), (64, 64, 256)])
+@pytest.mark.parametrize("L", [300, 33])
+def test_trig_features_bidir(dtype, shape, L):
+    """Bidirectional attention with trigonometric features (the trig_pairs Omega under FAVOR_TRIG): the
+    per-key scale exp(|k|^2/2) rides on the keys' stabiliser, the queries' cancels; against the oracle's
+    estimator on features_trig of the m/2 vectors."""
+    d, dv, m = shape
+    B, H = 2, 2
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 700 + m + L, scale=0.4)
+    om_dev = rf.make_omega(43, H, m, d, "trig_pairs")
+    om_half = oracle.make_omega(43, H, m // 2, d, "ortho_chi")
+    ref = oracle.bidir(q, k, v, om_half, kind="trig")
+    out = rf.bidir(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind="trig", out_f32=True)
+    torch.cuda.synchronize()
+    e = rel_err(out, ref)
+    assert e < TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_trig_features_cross(dtype):
+    """Cross attention (Lq != Lk) with trigonometric features."""
+    d, dv, m = 64, 64, 256
+    B, H, Lq, Lk = 2, 2, 100, 513
+    q = workloads.make_tensor((B, H, Lq, d), 81, 0.4, dtype)
+    k = workloads.make_tensor((B, H, Lk, d), 82, 0.4, dtype)
+    v = workloads.make_tensor((B, H, Lk, dv), 83, 1.0, dtype)
+    om_dev = rf.make_omega(45, H, m, d, "trig_pairs")
+    om_half = oracle.make_omega(45, H, m // 2, d, "ortho_chi")
+    ref = oracle.bidir(q, k, v, om_half, kind="trig")
+    out = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind="trig", out_f32=True)
+    torch.cuda.synchronize()
+    e = rel_err(out, ref)
+    assert e < TOL[dtype], e
 
 
 # ---------------------------------------------------------------- cross attention, renormalisation off
