@@ -10,6 +10,7 @@ seeded inputs already resident in device memory:
   decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
   decode_gated_bf16 the same with favor_decode_gated (gates U[0.9,1), input weight 1 - g)
   backward_bf16 favor_bidir_backward (dq, dk, dv) at bidir_bf16's shape, bf16 gradients
+  trig_bf16   favor_bidir with trigonometric features (FAVOR_TRIG) at bidir_bf16's shape
   bidir_fp32 / bidir_small  the fp32 parity workloads
 Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
 decode, head-tokens/s), the dominant kernel's roofline fraction (per-launch
@@ -110,7 +111,9 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
     from threadpoolctl import threadpool_limits
 
     import oracle
-    if omega_mode == "hyperbolic":  # the oracle takes the m/2 vectors and builds the 2 x m/2 features itself
+    if w.feature == "trig":  # likewise for the sine and cosine features
+        om, kind = oracle.make_omega(w.seed, w.H, w.m // 2, w.d), "trig"
+    elif omega_mode == "hyperbolic":  # the oracle takes the m/2 vectors and builds the 2 x m/2 features itself
         om, kind = oracle.make_omega(w.seed, w.H, w.m // 2, w.d), "hyperbolic"
     else:
         om, kind = oracle.make_omega(w.seed, w.H, w.m, w.d, omega_mode), "prf"
@@ -183,7 +186,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     dt = w.torch_dtype
-    om = rf.make_omega(w.seed, w.H, w.m, w.d, a.omega_mode, device=dev)
+    fkind = w.feature
+    om = rf.make_omega(w.seed, w.H, w.m, w.d, "trig_pairs" if fkind == "trig" else a.omega_mode, device=dev)
 
     if w.kind in ("decode", "decode_gated"):
         S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
@@ -240,7 +244,7 @@ def main():
 
             def step(i=None):
                 qq, kk, vv = sets[cur[0]]
-                fn(qq, kk, vv, om, ws=ws, out=out)
+                fn(qq, kk, vv, om, kind=fkind, ws=ws, out=out)
         tokens_per_step = w.B * w.H * w.Lq_eff   # output (query) tokens
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4
@@ -316,8 +320,8 @@ def main():
         "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d, "dv": w.dv,
-                   "m": w.m, "feature_map": "prf" if a.omega_mode != "hyperbolic" else "prf_hyperbolic",
-                   "omega": a.omega_mode, "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
+                   "m": w.m, "feature_map": fkind if a.omega_mode != "hyperbolic" else "prf_hyperbolic",
+                   "omega": "trig_pairs" if fkind == "trig" else a.omega_mode, "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
         "roofline": roofline,
     }

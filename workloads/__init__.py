@@ -18,6 +18,8 @@ bidirectional attention, causal attention and recurrent decoding):
                build the state, then 1000 steps of q,k,v ~ N(0,1)         seed 4
   decode_gated_bf16  the same, each step with a gate g ~ U[0.9, 1) per
                (sequence, head) and input weight 1 - g                   seed 5
+  trig_bf16    bf16  B8 H12 L4096 d64 dv64 m256 with trigonometric features
+               (128 vectors, sine and cosine), Q,K ~ 0.4 N(0,1), V ~ N(0,1)  seed 7
   backward_bf16  bidir_bf16's inputs plus an upstream gradient dOut ~ N(0,1)
                [B,H,L,dv] (its own generator, seed + 100): the gradients
                of the bidirectional estimator                            seed 2
@@ -55,6 +57,7 @@ class Workload:
     steps: int = 0       # decode only
     prior: int = 0       # decode only: tokens folded into the initial state
     Lq: int = 0          # cross attention: query length (L is then the key length); 0 = L
+    feature: str = "prf"  # feature map: "prf" or "trig" (Omega of m/2 vectors, each twice)
 
     @property
     def Lq_eff(self) -> int:
@@ -75,6 +78,8 @@ WORKLOADS = {
                            1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "cross_bf16": Workload("cross_bf16", "cross", "bf16", 8, 12, 4096, 64, 64, 256, 6,
                            1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0, Lq=1024),
+    "trig_bf16": Workload("trig_bf16", "bidir", "bf16", 8, 12, 4096, 64, 64, 256, 7, 0.4, 0.4, 1.0,
+                          feature="trig"),
     "backward_bf16": Workload("backward_bf16", "backward", "bf16", 8, 12, 4096, 64, 64, 256, 2,
                               1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
