@@ -33,14 +33,14 @@ convergence to exact softmax attention as m grows, invariants).
 """
 from .omega import make_omega, splitmix64_mix, stream_key, uniform52, gaussians, OMEGA_MODES
 from .favor import (
-    features, features_hyperbolic, features_trig, bidir, bidir_from_features, bidir_backward, causal, causal_bruteforce, causal_bruteforce_from_features,
+    features, features_hyperbolic, features_trig, bidir, bidir_from_features, bidir_backward, causal, causal_backward, causal_bruteforce, causal_bruteforce_from_features,
     decode_step, decode_run, decode_gated_step, decode_gated_run, decode_gated_unrolled, state_from_prior,
     softmax_attention, attention_matrix, row_norm_rel_err,
 )
 
 __all__ = [
     "make_omega", "splitmix64_mix", "stream_key", "uniform52", "gaussians", "OMEGA_MODES",
-    "features", "features_hyperbolic", "features_trig", "bidir", "bidir_from_features", "bidir_backward", "causal", "causal_bruteforce",
+    "features", "features_hyperbolic", "features_trig", "bidir", "bidir_from_features", "bidir_backward", "causal", "causal_backward", "causal_bruteforce",
     "causal_bruteforce_from_features", "decode_step", "decode_run", "decode_gated_step", "decode_gated_run",
     "decode_gated_unrolled", "state_from_prior",
     "softmax_attention", "attention_matrix", "row_norm_rel_err",

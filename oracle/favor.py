@@ -187,6 +187,36 @@ def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bo
     return out
 
 
+def causal_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
+    """Gradients of the causal output (appendix B.1, equation 11: out_i = (Phi_Q,i . S_i) / (Phi_Q,i . z_i)
+    with the prefix sums S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j)) with respect to the raw q,
+    k and v, for the upstream gradient dout. By the chain rule, position by position:
+        dN_i = dout_i / D_i,  dD_i = -(dout_i . out_i) / D_i,  dPhi_Q,i = S_i dN_i + z_i dD_i,
+    and since S_i and z_i sum the keys j <= i, key j collects the suffix sums over i >= j:
+        R_j = sum_{i>=j} Phi_Q,i dN_i^T,  r_j = sum_{i>=j} Phi_Q,i dD_i,
+        dPhi_K,j = R_j v_j + r_j,  dV_j = R_j^T Phi_K,j,
+    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64."""
+    pq = features(q, omega, kind, eps)
+    pk = features(k, omega, kind, eps)
+    v = _f64(v)
+    g = _f64(dout)
+    # prefix states S_i [B,H,L,m,dv], z_i [B,H,L,m] (inclusive)
+    S = np.cumsum(pk[..., :, None] * v[..., None, :], axis=-3)
+    z = np.cumsum(pk, axis=-2)
+    N = np.einsum("...lm,...lme->...le", pq, S)
+    D = np.einsum("...lm,...lm->...l", pq, z)
+    out = N / D[..., None]
+    dN = g / D[..., None]
+    dD = -np.sum(g * out, axis=-1) / D
+    dpq = np.einsum("...lme,...le->...lm", S, dN) + z * dD[..., None]
+    # suffix sums over i >= j (reverse cumulative sums)
+    R = np.flip(np.cumsum(np.flip(pq[..., :, None] * dN[..., None, :], axis=-3), axis=-3), axis=-3)
+    r = np.flip(np.cumsum(np.flip(pq * dD[..., None], axis=-2), axis=-2), axis=-2)
+    dpk = np.einsum("...lme,...le->...lm", R, v) + r
+    dv = np.einsum("...lme,...lm->...le", R, pk)
+    return (_feature_backward(q, omega, pq, dpq, kind), _feature_backward(k, omega, pk, dpk, kind), dv)
+
+
 def causal_bruteforce_from_features(phi_q, phi_k, v, rows: int | None = None):
     """Equation 2 applied to the explicit matrix A_hat = Phi_Q Phi_K^T, masked by tril."""
     phi_q, phi_k, v = _f64(phi_q), _f64(phi_k), _f64(v)

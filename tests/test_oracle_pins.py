@@ -217,6 +217,61 @@ def test_bidir_backward_matches_finite_differences(kind, eps):
         assert np.max(np.abs(num - gx)) < 1e-6 * max(1.0, np.max(np.abs(gx))), (kind, np.max(np.abs(num - gx)))
 
 
+@pytest.mark.parametrize("kind,eps", [("prf", 0.0), ("relu", 1e-3)])
+def test_causal_backward_matches_finite_differences(kind, eps):
+    """The chain-rule gradients of the causal estimator (appendix B.1, equation 11, prefix sums including the
+    diagonal) against central differences of the forward recurrence (fp64): every entry of dq, dk and dv for a
+    random linear functional of the output. A key that only later queries see, a missing diagonal term or a
+    prefix sum taken in the wrong direction fails it."""
+    B, H, L, d, dv, m = 1, 2, 7, 8, 4, 16
+    rng = np.random.default_rng(5)
+    q = rng.normal(size=(B, H, L, d)) * 0.6
+    k = rng.normal(size=(B, H, L, d)) * 0.6
+    v = rng.normal(size=(B, H, L, dv))
+    g = rng.normal(size=(B, H, L, dv))
+    om = make_omega(17, H, m, d)
+    grads = oracle.causal_backward(q, k, v, om, g, kind, eps)
+    h = 1e-6
+    for x, gx in zip((q, k, v), grads):
+        num = np.empty_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fp = np.sum(g * causal(*args_p, om, kind, eps))
+            fm = np.sum(g * causal(*args_m, om, kind, eps))
+            num[i] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - gx)) < 1e-6 * max(1.0, np.max(np.abs(gx))), (kind, np.max(np.abs(num - gx)))
+
+
+def test_causal_backward_last_position_and_single_token():
+    """Two special cases: with L = 1 the causal and bidirectional estimators coincide, so do their gradients;
+    and the last key is seen only by the last query, so with dout zero except at the last position its dv is
+    the bidirectional one of that row (the last row of the causal output is the bidirectional output)."""
+    B, H, d, dv, m = 1, 1, 8, 4, 16
+    rng = np.random.default_rng(9)
+    om = make_omega(21, H, m, d)
+    q, k, v, g = (rng.normal(size=(B, H, 1, n)) * s for n, s in ((d, 0.6), (d, 0.6), (dv, 1.0), (dv, 1.0)))
+    for a, b in zip(oracle.causal_backward(q, k, v, om, g), oracle.bidir_backward(q, k, v, om, g)):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+    L = 9
+    q, k, v = (rng.normal(size=(B, H, L, n)) * s for n, s in ((d, 0.6), (d, 0.6), (dv, 1.0)))
+    g = np.zeros((B, H, L, dv))
+    g[..., -1, :] = rng.normal(size=dv)
+    c = oracle.causal_backward(q, k, v, om, g)
+    # only the last query carries a gradient and it sees every key: dv_j = A_Lj g_L / sum_j A_Lj from the
+    # explicit last row of A_hat = Phi_Q Phi_K^T
+    pq = oracle.features(q, om)[..., -1, :]
+    pk = oracle.features(k, om)
+    A = np.einsum("...m,...jm->...j", pq, pk)
+    dv_ref = A[..., :, None] / A.sum(axis=-1)[..., None, None] * g[..., -1, None, :]
+    assert np.allclose(c[2], dv_ref, rtol=1e-12, atol=1e-14)
+
+
 def test_bidir_backward_query_features_gradient_is_orthogonal_to_features():
     """The output is invariant to a per-row scale of the query features (it cancels in the ratio), so
     phi(q_i) . dPhi_Q_i = 0 for every row; hence dq has no |q|^2 term. Checked by rescaling q's features:
