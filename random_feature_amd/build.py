@@ -81,6 +81,9 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the pipe-rate microbenchmark (exp, FMA, MFMA issue rates on the device)
+    _run([hipcc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], os.path.join(ROOT, "random_feature_amd", "tools", "rates.hip"),
+          "-o", os.path.join(BUILD, "rates")], verbose)
     return LIB
 
 
