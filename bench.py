@@ -270,6 +270,17 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
+    # per-step distribution (a separate pass, an event pair around every step)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for p0, p1 in pairs:
+        p0.record()
+        step()
+        p1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(p0.elapsed_time(p1) for p0, p1 in pairs)
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     rf.timing_enable(True)
     for _ in range(a.steps):
         step()
@@ -317,7 +328,9 @@ def main():
     res = {
         "metric": METRIC if w.name == "bidir_bf16" else f"FAVOR+ {w.kind} {unit}, workload {w.name}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": total_ms / a.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": total_ms / a.steps,
+        "ms_per_step_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d, "dv": w.dv,
                    "m": w.m, "feature_map": fkind if a.omega_mode != "hyperbolic" else "prf_hyperbolic",

@@ -480,14 +480,27 @@ bool shape_built(int dtype, int d, int dv, int m) {
 
 constexpr int kMaxPieces = 512;  // two resident 4-wave workgroups on each of 256 CUs
 
+// Pieces of the flattened tile space: at most kMaxPieces, and a whole number per (b,h) when
+// that still gives at least 7/8 of them, so that no piece straddles two (b,h) (one set of
+// operands per workgroup, one partial per piece).
+static int pieces(long long bh, long long tpb) {
+  const long long total = bh * tpb;
+  long long g = std::min<long long>(total, kMaxPieces);
+  if (bh <= kMaxPieces) {
+    const long long per = std::min<long long>(tpb, kMaxPieces / bh);
+    if (per * bh * 8 >= g * 7) g = per * bh;
+  }
+  return (int)g;
+}
+
 BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
   BidirPlan p;
   p.tpb = (s.L + 31) / 32;  // keys
   p.T_all = s.bh() * p.tpb;
-  p.G = (int)std::min<long long>(p.T_all, kMaxPieces);
+  p.G = pieces(s.bh(), p.tpb);
   p.tpb_q = ((Lq > 0 ? Lq : s.L) + 31) / 32;  // queries
   p.T_all_q = s.bh() * p.tpb_q;
-  p.G_q = (int)std::min<long long>(p.T_all_q, kMaxPieces);
+  p.G_q = pieces(s.bh(), p.tpb_q);
   p.nw_reduce = reduce_waves(s.m);
   const int dc = (s.d + 31) / 32, nb = s.dv / 16 + 1;
   const size_t slots = (size_t)p.G + (size_t)s.bh();
