@@ -21,6 +21,10 @@ import sys
 
 # mangled kernel name fragment -> timer name used by the library and bench.py
 _SHORT = [
+    ("bwd_q_kernel", "bwd_q"),
+    ("bwd_k_kernel", "bwd_k"),
+    ("combine_rows_kernel", "combine_rows"),
+    ("omegaT_frag_kernel", "omega_frag"),
     ("kv_reduce_kernel", "reduce"),
     ("q_output_kernel", "output"),
     ("combine_kernel", "combine"),
