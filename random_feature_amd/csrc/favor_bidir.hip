@@ -42,7 +42,7 @@ inline float omega_scale(int kind, float sc) {
 // sfr[bh][fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c]; in the last
 // block only row c == 0 (the z column) is nonzero.
 template <typename C, int DV, int M>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
                int tpb, long long T_all, int G, int kind, C* __restrict__ sfr, float* __restrict__ gmx) {
   constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
@@ -565,7 +565,9 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   }
   {
     FAVOR_TIMED("combine", st);
-    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
+    // one thread per (value block, lane): every partial is requested in a single round
+    constexpr int NBC = DV / 16 + 1;
+    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0, st>>>(
         part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
   }
   {
