@@ -478,7 +478,10 @@ bool shape_built(int dtype, int d, int dv, int m) {
   return false;
 }
 
-constexpr int kMaxPieces = 512;  // two resident 4-wave workgroups on each of 256 CUs
+#ifndef FAVOR_BIDIR_PIECES
+#define FAVOR_BIDIR_PIECES 512
+#endif
+constexpr int kMaxPieces = FAVOR_BIDIR_PIECES;  // two resident 4-wave workgroups on each of 256 CUs
 
 // Pieces of the flattened tile space: at most kMaxPieces, and a whole number per (b,h) when
 // that still gives at least 7/8 of them, so that no piece straddles two (b,h) (one set of
