@@ -44,6 +44,15 @@ __device__ __forceinline__ void st_state(float* p, const f32x4& x) {
   if constexpr (FAVOR_DECODE_NT & 2) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
   else *reinterpret_cast<f32x4*>(p) = x;
 }
+#ifndef FAVOR_DECODE_AHEAD
+#define FAVOR_DECODE_AHEAD 128
+#endif
+constexpr int kDecodeAhead = FAVOR_DECODE_AHEAD;  // input prefetch distance, in workgroups of one XCD
+#ifndef FAVOR_DECODE_PREFETCH
+#define FAVOR_DECODE_PREFETCH 4
+#endif
+constexpr int kDecodePrefetch = FAVOR_DECODE_PREFETCH;  // later workgroups whose inputs each one requests
+static_assert(kDecodePrefetch <= kDecodeThreads / 64, "one wave per prefetched workgroup");
 constexpr int kDecodeSeqs = 1;                  // sequences of one head per workgroup (they share Omega's rows)
 
 // One workgroup per (head, group of kDecodeSeqs sequences); every thread owns 4 columns of
@@ -61,7 +70,8 @@ __global__ void __launch_bounds__(kDecodeThreads)
 decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
               const float* __restrict__ omega, float* __restrict__ S, float* __restrict__ z, int N, int H,
               int dv, int m, int kind, float eps, float inv_sqrt_m, float wscale, float nscale, float log2_sqrt_m,
-              const float* __restrict__ gate, const float* __restrict__ inw, float* __restrict__ out) {
+              const float* __restrict__ gate, const float* __restrict__ inw, float* __restrict__ out, int ahead,
+              int sink) {
   constexpr int U = kDecodeRows, G = kDecodeSeqs;
   constexpr int NWV = kDecodeThreads / 64;
   constexpr int DH = D / 2;  // the d-half of a feature this thread projects
@@ -90,10 +100,42 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
   // the first one's data for its loads and writes nothing
   auto pair_of = [&](int g) -> size_t { return (size_t)(s0 + (g < ng ? g : 0)) * H + h; };
 
-  // loads the features wait for: q, k, this thread's v columns, its Omega half-row
-  for (int i = tid; i < G * 2 * D; i += kDecodeThreads) {
-    const int g = i / (2 * D), w2 = (i / D) & 1, dd = i % D;
-    xs[i] = to_f((w2 == 0 ? q : k)[pair_of(g) * D + dd]);
+  // the q, k and v rows of the workgroups that this XCD starts ahead, 2*ahead, ...,
+  // kDecodePrefetch*ahead workgroups later are requested now (16 bytes per lane), so that
+  // they are cache-resident when those start instead of queued behind the state stream in
+  // HBM; the values are kept only under the flag `sink`, which the host passes as 0
+  f32x4 pf = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int per = gridDim.x >> 3;  // xcd_remap: workgroups of one XCD take consecutive logical ids
+    constexpr int RB = D * (int)sizeof(T);
+    const int rbv = dv * (int)sizeof(T);
+    const int jpf = wv + 1;  // wave w requests the workgroup (w + 1) * ahead later
+    if (ahead > 0 && (gridDim.x & 7) == 0 && jpf <= kDecodePrefetch && logical % per + ahead * jpf < per) {
+      const int l2 = logical + ahead * jpf;
+      const size_t pair2 = (size_t)((l2 % n_grp) * G) * H + l2 / n_grp;
+      const int which = lane >> 4, off = (lane & 15) * 16;  // lanes 0-15 q, 16-31 k, 32-47 v, then the gates
+      if (which < 3) {
+        const char* base = which == 0   ? reinterpret_cast<const char*>(q + pair2 * D)
+                           : which == 1 ? reinterpret_cast<const char*>(k + pair2 * D)
+                                        : reinterpret_cast<const char*>(v + pair2 * dv);
+        if (off < (which < 2 ? RB : rbv)) pf = *reinterpret_cast<const f32x4*>(base + off);
+      } else if (lane == 48 && gate) {
+        pf[0] = gate[pair2];
+      } else if (lane == 49 && gate && inw) {
+        pf[0] = inw[pair2];
+      }
+    }
+  }
+  // loads the features wait for: q, k (raw, into registers: their copy to LDS waits until
+  // every load below is in flight), this thread's v columns, its Omega half-row
+  constexpr int XPT = (G * 2 * D + kDecodeThreads - 1) / kDecodeThreads;
+  T xraw[XPT];
+#pragma unroll
+  for (int u = 0; u < XPT; ++u) {
+    const int i = tid + u * kDecodeThreads;
+    const int ii = i < G * 2 * D ? i : 0;
+    const int g = ii / (2 * D), w2 = (ii / D) & 1, dd = ii % D;
+    xraw[u] = (w2 == 0 ? q : k)[pair_of(g) * D + dd];
   }
   f32x4 vv[G];
 #pragma unroll
@@ -135,6 +177,11 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 #pragma unroll
       for (int u = 0; u < U; ++u) buf[g][u] = ld_state(row_ptr(g, r0 + u));
     }
+  }
+#pragma unroll
+  for (int u = 0; u < XPT; ++u) {
+    const int i = tid + u * kDecodeThreads;
+    if (i < G * 2 * D) xs[i] = to_f(xraw[u]);
   }
   __syncthreads();
 
@@ -268,6 +315,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     for (int i = 0; i < NWV; ++i) den += wred[g][1][i];
     out[pair_of(g) * dv + col] = num / den;
   }
+  if (sink) out[tid] = pf[0] + pf[1] + pf[2] + pf[3];
 }
 
 template <typename T, int D>
@@ -286,7 +334,8 @@ static hipError_t run_decode(const T* q, const T* k, const T* v, const float* om
   {
     FAVOR_TIMED("decode", st);
     decode_kernel<T, D><<<(unsigned)(n_grp * H), kDecodeThreads, lds, st>>>(
-        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, gate, inw, out);
+        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, gate, inw, out,
+        kDecodeAhead, 0);
   }
   return hipGetLastError();
 }
