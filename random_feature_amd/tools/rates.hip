@@ -121,6 +121,39 @@ __global__ void __launch_bounds__(kBlock) mixed_chain(float* out, long long* cyc
   if ((threadIdx.x & 63) == 0) cyc[(blockIdx.x * kBlock + threadIdx.x) >> 6] = t1 - t0;
 }
 
+// kAcc MFMAs and 2*kChains FMAs per iteration, independent of each other
+__global__ void __launch_bounds__(kBlock) mixed_fma_chain(float* out, long long* cyc, float seed) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(seed + 0.001f * j);
+    b[j] = (__bf16)(0.5f - 0.001f * j);
+  }
+  f32x4 acc[kAcc];
+#pragma unroll
+  for (int c = 0; c < kAcc; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float x[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) x[c] = seed + 0.01f * c + 1e-6f * threadIdx.x;
+  const long long t0 = clock64();
+  for (int it = 0; it < kIters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kAcc; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) x[c] = __builtin_fmaf(x[c], 0.999f, 0.0001f);
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) x[c] = __builtin_fmaf(x[c], 0.999f, 0.0001f);
+  }
+  const long long t1 = clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kAcc; ++c) s += acc[c][0];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += x[c];
+  out[blockIdx.x * kBlock + threadIdx.x] = s;
+  if ((threadIdx.x & 63) == 0) cyc[(blockIdx.x * kBlock + threadIdx.x) >> 6] = t1 - t0;
+}
+
 typedef void (*Kern)(float*, long long*, float);
 
 static int run(const char* name, Kern k, double instr_per_wave, const char* unit) {
@@ -160,6 +193,7 @@ int main() {
   rc |= run("fma", fma_chain, (double)kIters * kChains, "v_fma_f32 wave-instr");
   rc |= run("mfma", mfma_chain, (double)kIters * kAcc, "mfma_16x16x32_bf16");
   rc |= run("mixed", mixed_chain, (double)kIters * kAcc, "mfma_16x16x32_bf16 (+2 exp each)");
+  rc |= run("mixfma", mixed_fma_chain, (double)kIters * kAcc, "mfma_16x16x32_bf16 (+4 fma each)");
   printf("status %s\n", rc ? "error" : "ok");
   return rc;
 }
