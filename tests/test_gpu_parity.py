@@ -477,7 +477,7 @@ def test_trig_feature_map(dtype, d, m):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", [(16, 16, 32), (32, 32, 64), (64, 64, 128), (64, 64, 256)])
-@pytest.mark.parametrize("L", [300, 33])
+@pytest.mark.parametrize("L", [300, 33, 1])
 def test_trig_features_bidir(dtype, shape, L):
     """Bidirectional attention with trigonometric features (the trig_pairs Omega under FAVOR_TRIG): the
     per-key scale exp(|k|^2/2) rides on the keys' stabiliser, the queries' cancels; against the oracle's
@@ -567,7 +567,7 @@ BWD_SHAPES = [(16, 16, 32), (32, 32, 64), (64, 64, 128), (64, 64, 256)]
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("shape", BWD_SHAPES)
-@pytest.mark.parametrize("L", [300, 33])
+@pytest.mark.parametrize("L", [300, 33, 32])
 def test_bidir_backward(dtype, shape, L):
     """Gradients of the bidirectional estimator (chain rule through equation 4 and Lemma 1's map) against
     the oracle's: dq, dk, dv row by row."""
@@ -582,6 +582,25 @@ def test_bidir_backward(dtype, shape, L):
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         e = rel_err(a, b)
         assert e < TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bidir_backward_single_token(dtype):
+    """The degenerate sequence L = 1: the output is v itself, so dv = dout exactly and dq, dk vanish; the
+    kernels' dq and dk are the rounding residue of the cancelling terms, far below the scale of the
+    gradient at L = 2 for the same first token."""
+    d, dv, m = 64, 64, 256
+    B, H = 1, 2
+    q, k, v = _inputs(B, H, 2, d, dv, dtype, 900)
+    g = workloads.make_tensor((B, H, 2, dv), 901, 1.0, dtype)
+    om_dev, om = _omega(45, H, m, d)
+    one = [t[:, :, :1].contiguous() for t in (q, k, v, g)]
+    got1 = rf.bidir_backward(*(t.to(DEV) for t in one[:3]), om_dev, one[3].to(DEV), grad_f32=True)
+    got2 = rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    assert rel_err(got1[2], one[3].double().numpy()) < TOL[dtype]
+    for a1, a2 in zip(got1[:2], got2[:2]):
+        assert float(a1.abs().max()) < 0.02 * float(a2[:, :, :1].abs().max())
 
 
 def test_bidir_backward_workload_sampled():
