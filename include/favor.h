@@ -202,6 +202,24 @@ favor_status favor_bidir_backward(const void* q, const void* k, const void* v, c
 /* Bytes of device workspace favor_bidir_backward needs; 0 if the arguments are invalid. */
 size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype);
 
+/* favor_causal_backward — gradients of favor_causal's output (Performer appendix B.1,
+ * equation 11: prefix sums S_i, z_i over j <= i, diagonal included) with respect to the raw q,
+ * k and v, for positive softmax features (kind must be FAVOR_PRF; ReLU and trigonometric
+ * features return FAVOR_ERR_UNSUPPORTED), given dout [B,H,L,dv] in `dtype`. The forward is
+ * recomputed. With W_i = [dout_i, -(dout_i . out_i)] / (Phi_Q z)_i:
+ *   dPhi_Q,i = [S_i z_i] W_i,  R_j = sum_{i>=j} Phi_Q,i W_i^T,  dPhi_K,j = R_j [v_j 1],
+ *   dv_j = R_j^T Phi_K,j (value columns),  then through the feature map as favor_bidir_backward.
+ * dq, dk [B,H,L,d] and dv_grad [B,H,L,dv] are written in `dtype`, or fp32 when grad_f32 != 0.
+ * ws: at least favor_causal_backward_workspace_size(B, H, L, d, dv, m, dtype) bytes. Built shapes
+ * as favor_bidir_backward; checks and errors as favor_bidir_backward. */
+favor_status favor_causal_backward(const void* q, const void* k, const void* v, const float* omega,
+                                   const void* dout, int B, int H, int L, int d, int dv, int m,
+                                   favor_dtype dtype, favor_kind kind, int grad_f32, void* dq, void* dk,
+                                   void* dv_grad, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace favor_causal_backward needs; 0 if the arguments are invalid. */
+size_t favor_causal_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype);
+
 /* Bytes of device workspace favor_bidir (causal = 0) or favor_causal (causal = 1)
  * needs for these sizes; 0 if the arguments are invalid. */
 size_t favor_workspace_size(int causal, int B, int H, int L, int d, int dv, int m, favor_dtype dtype);

@@ -51,6 +51,9 @@ _lib.favor_bidir_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _
                                       _vp, _sz, _vp]
 _lib.favor_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.favor_backward_workspace_size.restype = _sz
+_lib.favor_causal_backward.argtypes = _lib.favor_bidir_backward.argtypes
+_lib.favor_causal_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.favor_causal_backward_workspace_size.restype = _sz
 _lib.favor_workspace_size.restype = _sz
 _lib.favor_timing_enable.argtypes = [_i]
 _lib.favor_timing_enable.restype = _i
@@ -59,11 +62,12 @@ _lib.favor_timing_read.restype = _i
 _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
 for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
-            "favor_bidir_backward", "favor_causal", "favor_decode", "favor_decode_gated"):
+            "favor_bidir_backward", "favor_causal", "favor_causal_backward", "favor_decode", "favor_decode_gated"):
     getattr(_lib, _fn).restype = _i
 
 EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
-            "favor_bidir_backward", "favor_backward_workspace_size", "favor_causal",
+            "favor_bidir_backward", "favor_backward_workspace_size", "favor_causal", "favor_causal_backward",
+            "favor_causal_backward_workspace_size",
             "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
             "favor_status_string"]
 
@@ -149,6 +153,15 @@ def backward_workspace(q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) ->
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
+def causal_backward_workspace(q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) -> torch.Tensor:
+    """Device scratch for causal_backward() at q's shape (reusable across calls of that shape)."""
+    B, H, L, d = q.shape
+    n = int(_lib.favor_causal_backward_workspace_size(B, H, L, d, v.shape[-1], omega.shape[1], _dtype_code(q)))
+    if n == 0:
+        raise FavorError("favor_causal_backward_workspace_size", 1)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0):
     """phi [B,H,L,m] and logscale [B,H,L] with phi_true = phi * exp(logscale)."""
     _need(x, "x", 4)
@@ -207,6 +220,10 @@ def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool 
 def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None, out=None):
     """Gradients (dq, dk, dv) of bidir()'s output for the upstream gradient `dout` (the forward sums are
     recomputed). `out`: optional preallocated (dq, dk, dv)."""
+    return _backward("favor_bidir_backward", backward_workspace, q, k, v, omega, dout, kind, grad_f32, ws, out)
+
+
+def _backward(fn, wsfn, q, k, v, omega, dout, kind, grad_f32, ws, out):
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, n, 4)
     _need(omega, "omega", 3)
@@ -214,7 +231,7 @@ def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=
     dv = v.shape[-1]
     m = omega.shape[1]
     if ws is None:
-        ws = backward_workspace(q, v, omega)
+        ws = wsfn(q, v, omega)
     gdt = torch.float32 if grad_f32 else q.dtype
     if out is None:
         dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
@@ -225,11 +242,17 @@ def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=
         for t, n, last in ((dq, "dq", d), (dk, "dk", d), (dvv, "dv", dv)):
             if tuple(t.shape) != (B, H, L, last) or t.dtype != gdt or not t.is_contiguous():
                 raise ValueError(f"{n}: expected a contiguous {gdt} tensor of shape {(B, H, L, last)}")
-    _check("favor_bidir_backward",
-           _lib.favor_bidir_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv,
-                                     m, _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk),
-                                     _ptr(dvv), _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
+    _check(fn, getattr(_lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv, m,
+                                 _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk), _ptr(dvv),
+                                 _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
     return dq, dk, dvv
+
+
+def causal_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None, out=None):
+    """Gradients (dq, dk, dv) of causal()'s output for the upstream gradient `dout` (the forward is
+    recomputed). `out`: optional preallocated (dq, dk, dv)."""
+    return _backward("favor_causal_backward", causal_backward_workspace, q, k, v, omega, dout, kind, grad_f32, ws,
+                     out)
 
 
 def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,

@@ -26,7 +26,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfavor.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["favor_bidir.hip", "favor_causal.hip", "favor_decode.hip", "favor_backward.hip"]
+HIP_SOURCES = ["favor_bidir.hip", "favor_causal.hip", "favor_decode.hip", "favor_backward.hip",
+               "favor_causal_bwd.hip"]
 HOST_HIP_SOURCES = ["favor_api.cpp", "favor_timing.cpp"]       # host code that calls the HIP runtime
 PLAIN_SOURCES = ["omega_host.cpp"]         # pure C++ (no HIP)
 

@@ -156,18 +156,6 @@ __device__ __forceinline__ int scale_exp(float x) {
   return e;
 }
 
-// ---------------------------------------------------------------- wave split
-// Waves of the gradient kernels: one per 32 features, at most FAVOR_BWD_WAVES. Eight waves in
-// one workgroup per CU put two waves on every SIMD, so one wave's vector work overlaps
-// another's matrix work.
-#ifndef FAVOR_BWD_WAVES
-#define FAVOR_BWD_WAVES 8
-#endif
-template <int M> struct BwdSplit {
-  static constexpr int NW = M < 32 ? 1 : ((M / 32) < FAVOR_BWD_WAVES ? (M / 32) : FAVOR_BWD_WAVES);
-  static constexpr int FB = M / (16 * NW);
-};
-
 // ---------------------------------------------------------------- query side
 // Workgroup = NW waves over one piece of the flattened query-tile space; wave w owns FB*16
 // features. Per tile of 32 queries (Q and dOut rows arrive through a two-slot DMA ring):

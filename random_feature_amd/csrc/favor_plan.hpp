@@ -74,12 +74,21 @@ struct BackwardPlan {
          off_dpart = 0, off_dzpart = 0, off_dsrow = 0, total = 0;
 };
 
+// Causal backward: the forward's causal plan (Omega fragments, segment partials, carries and key
+// maxima), Omega'^T fragments (hi and lo parts), per-query l and gamma, and one [m][dv+16] fp32
+// block per segment (the query-side totals, then the suffix carries in place).
+struct CausalBackwardPlan {
+  CausalPlan f;
+  size_t off_omth = 0, off_omtl = 0, off_lg = 0, off_gam = 0, off_trow = 0, total = 0;
+};
+
 bool shape_built(int dtype, int d, int dv, int m);
 bool bwd_shape_built(int d, int dv, int m);
 BackwardPlan plan_backward(const Shape& s, int dtype);
 // s.L is the key length; Lq > 0 sets a different query length (cross attention).
 BidirPlan plan_bidir(const Shape& s, int dtype, int Lq = 0);
 CausalPlan plan_causal(const Shape& s, int dtype);
+CausalBackwardPlan plan_causal_backward(const Shape& s, int dtype);
 
 hipError_t launch_features(const void* x, const float* omega, const Shape& s, int dtype, int kind, float eps,
                            float* phi, float* logscale, hipStream_t st);
@@ -91,6 +100,9 @@ hipError_t launch_causal(const void* q, const void* k, const void* v, const floa
                          void* ws, hipStream_t st);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout, const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv,
                            void* ws, hipStream_t st);
+hipError_t launch_causal_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
+                                  const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
+                                  hipStream_t st);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
                          int N, int H, int d, int dv, int m, int dtype, int kind, float eps, const float* gate,
                          const float* inw, float* out, hipStream_t st);

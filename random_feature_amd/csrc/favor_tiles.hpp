@@ -22,6 +22,17 @@ template <int M> struct RedSplit {
   static constexpr int FB = M / (16 * NW);
 };
 
+// Waves of the gradient kernels: one per 32 features, at most FAVOR_BWD_WAVES. Eight waves in
+// one workgroup per CU put two waves on every SIMD, so one wave's vector work overlaps
+// another's matrix work.
+#ifndef FAVOR_BWD_WAVES
+#define FAVOR_BWD_WAVES 8
+#endif
+template <int M> struct BwdSplit {
+  static constexpr int NW = M < 32 ? 1 : ((M / 32) < FAVOR_BWD_WAVES ? (M / 32) : FAVOR_BWD_WAVES);
+  static constexpr int FB = M / (16 * NW);
+};
+
 constexpr int kNormNone = 0, kNormSq = 1, kNormAbs = 2;
 
 // ---------------------------------------------------------------- tile ring

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -118,16 +118,19 @@ def test_decode_gated_argument_checks():
     assert call(d=128) == UNSUPPORTED
 
 
-def test_backward_argument_checks():
+@pytest.mark.parametrize("fn,wsfn", [("favor_bidir_backward", "favor_backward_workspace_size"),
+                                     ("favor_causal_backward", "favor_causal_backward_workspace_size")])
+def test_backward_argument_checks(fn, wsfn):
     def call(kind=0, d=64, dv=64, m=256, wsb=1 << 30, q=FAKE):
-        return rf.raw_call("favor_bidir_backward", q, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, dv, m, 1, kind, 0, FAKE,
+        return rf.raw_call(fn, q, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, dv, m, 1, kind, 0, FAKE,
                            FAKE, FAKE, FAKE, ctypes.c_size_t(wsb), None)
     assert call(q=None) == INVALID
     assert call(kind=1) == UNSUPPORTED          # ReLU has no backward kernels
+    assert call(kind=2) == UNSUPPORTED          # nor the trigonometric features
     assert call(d=16, dv=16, m=256) == UNSUPPORTED
     assert call(wsb=8) == WORKSPACE
-    assert rf._lib.favor_backward_workspace_size(1, 1, 64, 64, 64, 256, 1) > 0
-    assert rf._lib.favor_backward_workspace_size(0, 1, 64, 64, 64, 256, 1) == 0
+    assert getattr(rf._lib, wsfn)(1, 1, 64, 64, 64, 256, 1) > 0
+    assert getattr(rf._lib, wsfn)(0, 1, 64, 64, 64, 256, 1) == 0
 
 
 def test_features_and_omega_argument_checks():

@@ -603,6 +603,87 @@ def test_bidir_backward_single_token(dtype):
         assert float(a1.abs().max()) < 0.02 * float(a2[:, :, :1].abs().max())
 
 
+def _causal_grad_errs(got, ref):
+    """Row-wise errors of (dq, dk, dv) against the oracle. Row 0 of dq is exactly zero (query 0 sees only key
+    0, so out_0 = v_0 whatever q_0 is): it is held to the scale of the other rows instead."""
+    errs = {}
+    for name, a, r in zip(("dq", "dk", "dv"), got, ref):
+        a = a.detach().float().cpu().double().numpy()
+        r = np.asarray(r, np.float64)
+        if name == "dq":
+            assert float(np.abs(a[..., 0, :]).max()) <= 1e-3 * float(np.abs(r).max()) + 1e-30, "dq row 0"
+            a, r = a[..., 1:, :], r[..., 1:, :]
+        if a.shape[-2] > 0:
+            errs[name] = rel_err(a, r)
+    return errs
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("L", [300, 33, 32])
+def test_causal_backward(dtype, shape, L):
+    """Gradients of the causal estimator (chain rule through equation 11's prefix sums: prefix states for the
+    queries, suffix sums for the keys) against the oracle's, row by row. L = 300 runs as two segments."""
+    d, dv, m = shape
+    B, H = 2, 2
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 1700 + m + L)
+    g = workloads.make_tensor((B, H, L, dv), 1777 + L, 1.0, dtype)
+    om_dev, om = _omega(46, H, m, d)
+    ref = oracle.causal_backward(q, k, v, om, g)
+    got = rf.causal_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    for name, e in _causal_grad_errs(got, ref).items():
+        assert e < TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_causal_backward_many_segments(dtype):
+    """A single (b,h) of 1100 tokens runs as five segments (the suffix carries cross four boundaries, the
+    last segment is ragged); bf16 output gradients as the training step would store them."""
+    d, dv, m = 64, 64, 256
+    q, k, v = _inputs(1, 1, 1100, d, dv, dtype, 1900)
+    g = workloads.make_tensor((1, 1, 1100, dv), 1901, 1.0, dtype)
+    om_dev, om = _omega(47, 1, m, d)
+    ref = oracle.causal_backward(q, k, v, om, g)
+    got = rf.causal_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=dtype == torch.float32)
+    torch.cuda.synchronize()
+    for name, e in _causal_grad_errs(got, ref).items():
+        assert e < TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_causal_backward_single_token(dtype):
+    """L = 1: out = v, so dv = dout and dq, dk are exactly zero in exact arithmetic."""
+    d, dv, m = 64, 64, 256
+    q, k, v = _inputs(1, 2, 1, d, dv, dtype, 910)
+    g = workloads.make_tensor((1, 2, 1, dv), 911, 1.0, dtype)
+    om_dev, om = _omega(48, 2, m, d)
+    got = rf.causal_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    assert rel_err(got[2], g.double().numpy()) < TOL[dtype]
+    scale = float(g.double().abs().max())
+    for a in got[:2]:
+        assert float(a.abs().max()) < 1e-3 * scale
+
+
+def test_causal_backward_workload_sampled():
+    """The causal backward at the causal workload's size (B4 H8 L8192 d64 m256, bf16, sixteen segments per
+    (b,h)) in the benchmark's launch configuration, sampled (b,h) pairs against the oracle."""
+    w = workloads.WORKLOADS["causal_bf16"]
+    q, k, v = workloads.make_qkv(w)
+    g = workloads.make_dout(w)
+    om_dev, om = _omega(w.seed, w.H, w.m, w.d)
+    got = [t.cpu() for t in rf.causal_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV))]
+    worst = 0.0
+    for b, h in _sample_pairs(w.B, w.H, 2, 5):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.causal_backward(q[sl], k[sl], v[sl], om[h:h + 1], g[sl])
+        errs = _causal_grad_errs([a[sl] for a in got], ref)
+        worst = max([worst, *errs.values()])
+    print(f"causal_bf16 backward sampled rel err {worst:.3e}")
+    assert worst < TOL[torch.bfloat16]
+
+
 def test_bidir_backward_workload_sampled():
     """The backward at the headline workload's size (B8 H12 L4096 d64 m256, bf16) in the benchmark's launch
     configuration, sampled (b,h) pairs against the oracle."""
