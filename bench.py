@@ -10,6 +10,7 @@ seeded inputs already resident in device memory:
   decode_bf16 one favor_decode step for 256 sequences x 16 heads, d64 dv64 m256 (fp32 state)
   decode_gated_bf16 the same with favor_decode_gated (gates U[0.9,1), input weight 1 - g)
   backward_bf16 favor_bidir_backward (dq, dk, dv) at bidir_bf16's shape, bf16 gradients
+  causal_backward_bf16 favor_causal_backward (dq, dk, dv) at causal_bf16's shape, bf16 gradients
   trig_bf16   favor_bidir with trigonometric features (FAVOR_TRIG) at bidir_bf16's shape
   bidir_fp32 / bidir_small  the fp32 parity workloads
 Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
@@ -62,6 +63,14 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
         return thq * (2 * proj + 2 * w.m * w.dv + contr), thq * ((w.d + w.dv) * eb + w.d * out_bytes)
     if name == "bwd_k":       # projection, dPhi_K = dS_aug [v 1], dk = Omega^T P, dv = dS^T phi
         return th * (2 * proj + contr + 2 * w.m * w.dv), th * ((w.d + w.dv) * eb + (w.d + w.dv) * out_bytes)
+    if name == "cbwd_fwd":    # the forward recomputed: phi_K, phi_Q, S update, output; l and gamma written
+        return th * (2 * proj + 2 * contr), th * ((2 * w.d + 2 * w.dv) * eb + 8)
+    if name == "cbwd_q":      # phi_K, phi~_Q, S update, dPhi_Q = [S z] W, dq = Omega^T P
+        return th * (3 * proj + 2 * contr), th * ((2 * w.d + 2 * w.dv) * eb + 8 + w.d * out_bytes)
+    if name == "cbwd_k":      # phi_K, phi~_Q, R update, dPhi_K = R [v 1], dk = Omega^T P
+        return th * (3 * proj + 2 * contr), th * ((2 * w.d + 2 * w.dv) * eb + 8 + w.d * out_bytes)
+    if name == "cbwd_v":      # phi_K, phi~_Q, R update (value columns), dv = R^T phi_K
+        return th * (2 * proj + 4 * w.m * w.dv), th * ((2 * w.d + 2 * w.dv) * eb + 4 + w.dv * out_bytes)
     if name == "decode":      # per (sequence, head): q,k projections, state read+write, out (+ gate, weight)
         sb = (w.m * w.dv + w.m) * 4
         gb = 8 if w.kind == "decode_gated" else 0
@@ -73,10 +82,13 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
 _PATH_SOURCES = {
     "bidir": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "cross": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
-    "causal": ["favor_causal.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
+    "causal": ["favor_causal.hip", "favor_segments.hpp", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp",
+               "favor_plan.hpp"],
     "decode": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
     "decode_gated": ["favor_decode.hip", "favor_device.hpp", "favor_plan.hpp"],
     "backward": ["favor_backward.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
+    "causal_backward": ["favor_causal_bwd.hip", "favor_segments.hpp", "favor_tiles.hpp", "favor_reduce.hpp",
+                        "favor_device.hpp", "favor_plan.hpp"],
 }
 
 
@@ -118,11 +130,12 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
     else:
         om, kind = oracle.make_omega(w.seed, w.H, w.m, w.d, omega_mode), "prf"
     with threadpool_limits(1):
-        if w.kind in ("bidir", "cross", "causal", "backward"):
+        if w.kind in ("bidir", "cross", "causal", "backward", "causal_backward"):
             q, k, v = workloads.make_qkv(w)
-            if w.kind == "backward":
+            if w.kind in ("backward", "causal_backward"):
                 dout = workloads.make_dout(w)
-                fn = lambda q_, k_, v_, o_, kd, sl: oracle.bidir_backward(q_, k_, v_, o_, dout[sl], kd)  # noqa: E731
+                fb = oracle.bidir_backward if w.kind == "backward" else oracle.causal_backward
+                fn = lambda q_, k_, v_, o_, kd, sl: fb(q_, k_, v_, o_, dout[sl], kd)  # noqa: E731
             else:
                 f0 = oracle.causal if w.kind == "causal" else oracle.bidir
                 fn = lambda q_, k_, v_, o_, kd, sl: f0(q_, k_, v_, o_, kd)  # noqa: E731
@@ -228,15 +241,17 @@ def main():
             sets.append((q, k, v))
         q, k, v = sets[0]
         cur = [0]
-        if w.kind == "backward":
+        if w.kind in ("backward", "causal_backward"):
             douts = [workloads.make_dout(w.with_(seed=w.seed + 1000 * r) if r else w, device=dev)
                      for r in range(nset)]
-            ws = rf.backward_workspace(q, v, om)
+            wsfn, bfn = ((rf.backward_workspace, rf.bidir_backward) if w.kind == "backward"
+                         else (rf.causal_backward_workspace, rf.causal_backward))
+            ws = wsfn(q, v, om)
             grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
 
             def step(i=None):
                 qq, kk, vv = sets[cur[0]]
-                rf.bidir_backward(qq, kk, vv, om, douts[cur[0]], ws=ws, out=grads)
+                bfn(qq, kk, vv, om, douts[cur[0]], ws=ws, out=grads)
         else:
             ws = rf.workspace(w.kind == "causal", k, v, om)
             out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)

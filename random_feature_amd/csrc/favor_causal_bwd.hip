@@ -19,15 +19,18 @@
 // which are the true gradients: the 1/sqrt(m) factors and the scales of both sides cancel.
 // Kernels, in launch order (after the forward's Omega fragments, segment reduction and scan):
 //   omegaT_pair_kernel  Omega'^T as hi + lo fragments for the back-projections
-//   cbwd_q_kernel       per segment, forwards: the forward output of every chunk (carried term and
-//                       masked intra term), gamma and l per query (to HBM), dPhi_Q from the prefix
-//                       state and the chunk's masked scores, dq
+//   cbwd_fwd_kernel     per segment, forwards: the forward output of every chunk (carried term and
+//                       masked intra term); gamma and l per query to HBM
+//   cbwd_q_kernel       per segment, forwards: dPhi_Q from the prefix state and the chunk's masked
+//                       scores, dq
 //   cbwd_t_kernel       per segment: T_p = sum over its queries of phi~_i [g_i, -gamma_i]^T
 //   cbwd_rscan_kernel   suffix carries over segments: C_p = sum_{q>p} T_q 2^(M_p - M_q)
 //   cbwd_k_kernel       per segment, backwards: dPhi_K from the suffix state and the chunk's masked
-//                       scores, dk; dv from the suffix state and the masked score matrix
-// The states are held twice in registers, [feature][column] and [column][feature], because each
-// kernel contracts them over both indices. Inputs enter the products exactly (bf16 values); the
+//                       scores, dk
+//   cbwd_v_kernel       per segment, backwards: dv from the suffix state and the masked score matrix
+// Each kernel holds one layout of its state in registers ([feature][column] where it contracts over
+// features, [column][feature] where over columns): a kernel holding both would need more than the
+// 256 registers of two waves per SIMD. Inputs enter the products exactly (bf16 values); the
 // features, states and scores enter as hi + lo bf16 pairs (two or three MFMAs), since the sums
 // over tokens and over features cancel.
 #include "favor_device.hpp"
@@ -140,55 +143,47 @@ __global__ void omegaT_pair_kernel(const float* __restrict__ omega, int H, int m
   }
 }
 
-// ---------------------------------------------------------------- query side
+// ---------------------------------------------------------------- forward recomputed
 // Workgroup = NW waves on segment sp of (b,h) (piece pc = bh * nseg + sp), wave w owning the 32
 // features [32w, 32w + 32). The segment's carry S' (from the scan, in the scale of its key maximum
-// M) is held as Sc[fb][nb] = C[feature][column] and St[nb][fb] = C[column][feature]. Per chunk of
-// 32 tokens (Q, K, V and dOut rows through a two-slot DMA ring):
+// M) is held as Sc[fb][nb] = C[feature][column]. Per chunk of 32 tokens (Q, K, V and dOut rows
+// through a two-slot DMA ring):
 //   X   projections as in the forward sweep (keys against M, queries against the norm bound or,
-//       rarely, their exact maximum: the bias b_i); Phi'_K and Phi'_Q as hi + lo operands
-//       forward: o^T = S'^T Phi'_Q^T (A = Sc) + [V 1]^T masked (Phi'_K Phi'_Q^T), summed over the
-//       waves by LDS atomics; Sc takes the chunk
+//       rarely, their exact maximum: the bias b_i); Phi'_K and Phi'_Q as hi + lo operands;
+//       o^T = S'^T Phi'_Q^T (A = Sc) + [V 1]^T masked (Phi'_K Phi'_Q^T), the wave's partial to its
+//       LDS buffer (fp32 inputs: LDS atomics into one sum, for want of LDS); Sc takes the chunk
 //   Y   per query: D' = o_z, out = o / D', gamma = g . out; l = b + log2 D' and gamma to HBM
-//   Z   dPhi'_Q^T = (S' [g, -gamma]^T (A = St) + Phi'_K^T B) / D' with the masked scores
-//       B[key][q] = g_q . v_key - gamma_q; P = Phi'_Q * dPhi'_Q as rows [query][feature]; St takes
-//       the chunk
-//   P   dq^T blocks = Omega'^T P / log2(e), every wave its share over all features
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
-cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
-              const typename Ops<T>::P* __restrict__ omf, const typename Ops<T>::C* __restrict__ omTh,
-              const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ cpart,
-              const float* __restrict__ cz, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
-              float nscale, int grad_f32, void* __restrict__ dq, float* __restrict__ lg, float* __restrict__ gam) {
+cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
+                const float* __restrict__ cpart, const float* __restrict__ cz, const float* __restrict__ cmax, int H,
+                int L, int seg_len, int nseg, float nscale, float* __restrict__ lg, float* __restrict__ gam) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
   static_assert(FB == 2, "one 32-feature chunk per wave");
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NDB = D / 16, NVB = DV / 16, NB = NVB + 1;
+  constexpr int NVB = DV / 16, NB = NVB + 1;
   constexpr int NFC = M / 32;
-  constexpr int KC = (NB + 1) / 2;     // 32-column chunks of [value columns, z]
-  constexpr int KCV = (DV + 31) / 32;  // 32-column chunks of the value columns
-  constexpr int BPW = 2 * NDB / NW;    // dq^T blocks (dims db, queries tb) per wave
-  static_assert(BPW >= 1 && (2 * NDB) % NW == 0, "dq blocks split evenly over the waves");
   constexpr int NSPL = CbwdOps<T>::NSPL;
   constexpr int CPR = DV / 8;  // 8-column items of a row
   static_assert(32 * CPR <= NT && (32 * CPR) % 64 == 0, "one (row, 8 columns) item per thread, whole waves");
-  constexpr int PROW = M + 8;  // P rows [query][feature]
   constexpr int KPROW = 36;    // a wave's Phi'_K transpose [feature][key]
   constexpr int OROW = NB * 16 + 4;
-  constexpr int UB = NSPL * 32 * PROW > NW * 32 * KPROW ? NSPL * 32 * PROW : NW * 32 * KPROW;
+  constexpr bool XOW = sizeof(T) == 2;      // per-wave partial outputs (else LDS atomics)
+  constexpr int XO = 2 * NVB * 256 + 32;    // floats of one wave's partial output
   using Rg = SweepRing<T, D, DV, NT, true>;
   using VR = Ring<T, D, DV, NT, true>;  // V and G rows share its layout
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
-  __shared__ __attribute__((aligned(16))) C ubuf[UB];  // the waves' Phi'_K transposes, then the P rows
-  __shared__ __attribute__((aligned(16))) float osum[2][32 * OROW];
+  __shared__ __attribute__((aligned(16))) C ubuf[NW * 32 * KPROW];  // the waves' Phi'_K transposes
+  __shared__ __attribute__((aligned(16))) float osum[XOW ? 1 : 2][XOW ? 4 : 32 * OROW];
+  __shared__ __attribute__((aligned(16))) float xo[XOW ? NW : 1][XOW ? XO : 4];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
   __shared__ __attribute__((aligned(16))) float qn[2][32];
   __shared__ __attribute__((aligned(16))) float qmx[NW][32];
-  __shared__ float qbias[32], rden[32], rgam[32];
+  __shared__ float qbias[32];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -200,7 +195,8 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const uint32_t ring0 = lds_addr(&ring[0][0]);
 
   Rg::issue(Q, K, V, L, rowbase, t0, ring0, dOut);
-  for (int e = threadIdx.x; e < 2 * 32 * OROW; e += NT) (&osum[0][0])[e] = 0.f;
+  if constexpr (!XOW)
+    for (int e = threadIdx.x; e < 2 * 32 * OROW; e += NT) (&osum[0][0])[e] = 0.f;
 
   vec8<P> om[FB][DC];
 #pragma unroll
@@ -209,7 +205,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     for (int dc = 0; dc < DC; ++dc)
       om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
   // the carry at the segment's start: this wave's 32-feature chunk of the scan's fragments
-  f32x4 Sc[FB][NB], St[NB][FB];
+  f32x4 Sc[FB][NB];
   {
     const size_t fcb = (size_t)pc * NFC + w;
 #pragma unroll
@@ -227,22 +223,6 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       Sc[0][nb] = lo;
       Sc[1][nb] = hi;
     }
-    // St[nb][fb][i] = S'[feature 16fb + c][column 16nb + 4g + i]: fragment lane (4g + i) + 16(c >> 2),
-    // slot 4fb + (c & 3)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = nb * 16 + 4 * g + i, j = 4 * fb + (c & 3);
-          float x = 0.f;
-          if (nb < NVB)
-            x = cpart[((fcb * NVB + nb) * 64 + (4 * g + i) + 16 * (c >> 2)) * 8 + j];
-          else if (col == DV)
-            x = cz[(fcb * 4 + (c >> 2)) * 8 + j];
-          St[nb][fb][i] = x;
-        }
   }
   const float mk = cmax[pc];
   const float omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
@@ -255,8 +235,8 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     const unsigned char* vbase = sl + Rg::XC * 16;
     const unsigned char* gbase = sl + (Rg::XC + Rg::VC) * 16;
     const int tok0 = t0 + 32 * t;
-    float* os = osum[buf];
-    lds_barrier();  // X: chunk t converted; the previous chunk's reads of the other slot and of ubuf done
+    float* os = osum[XOW ? 0 : buf];
+    lds_barrier();  // X: chunk t converted; the previous chunk's reads of the other slot and of osum done
     if (t + 1 < n) Rg::issue(Q, K, V, L, rowbase, tok0 + 32, ring0 + (buf ^ 1) * Rg::SLOT, dOut);
 
     // ---- projections: keys [key][feature] from -(n'_k + M), queries [feature][query] from -b
@@ -385,17 +365,27 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         if constexpr (NSPL == 2) mma16(o[cb][tb], vf[cb], sbl);
       }
     }
-    // the waves' partial outputs summed in LDS (value columns and the denominator)
+    // the wave's partial outputs (value columns and the denominator)
+    if constexpr (XOW) {
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
+      for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int cb = 0; cb < NVB; ++cb)
+          *reinterpret_cast<f32x4*>(&xo[w][((tb * NVB + cb) * 64 + lane) * 4]) = o[cb][tb];
+        if (g == 0) xo[w][2 * NVB * 256 + tb * 16 + c] = o[NB - 1][tb][0];
+      }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = cb * 16 + 4 * g + i;
-          if (col <= DV) atomicAdd(&os[(tb * 16 + c) * OROW + col], o[cb][tb][i]);
-        }
-    // ---- Sc takes the chunk (St after its use below)
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int col = cb * 16 + 4 * g + i;
+            if (col <= DV) atomicAdd(&os[(tb * 16 + c) * OROW + col], o[cb][tb][i]);
+          }
+    }
+    // ---- Sc takes the chunk
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -408,10 +398,23 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     // ---- per query: D' and gamma = g . out; l = b + log2 D' and gamma to HBM
     if (threadIdx.x < 32 * CPR) {
       const int row = threadIdx.x / CPR, c8 = threadIdx.x % CPR;
-      const float* orow = &os[row * OROW];
-      const float den = orow[DV];
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + c8 * 8);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + c8 * 8 + 4);
+      float den = 0.f;
+      f32x4 o0 = f32x4{0.f, 0.f, 0.f, 0.f}, o1 = o0;
+      if constexpr (XOW) {
+        const int tb = row >> 4, cq = row & 15, cb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float* base = &xo[ww][((tb * NVB + cb) * 64 + cq + 16 * g0) * 4];
+          o0 += *reinterpret_cast<const f32x4*>(base);
+          o1 += *reinterpret_cast<const f32x4*>(base + 64);
+          den += xo[ww][2 * NVB * 256 + tb * 16 + cq];
+        }
+      } else {
+        const float* orow = &os[row * OROW];
+        den = orow[DV];
+        o0 = *reinterpret_cast<const f32x4*>(orow + c8 * 8);
+        o1 = *reinterpret_cast<const f32x4*>(orow + c8 * 8 + 4);
+      }
       const vec8<T> g8 = ld8<T>(reinterpret_cast<const T*>(gbase + VR::v_off(row, c8 * 8)));
       float ga = 0.f;
 #pragma unroll
@@ -419,8 +422,6 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       ga = lanes_sum<CPR>(ga);
       if (c8 == 0) {
         const float gm = ga / den;
-        rden[row] = 1.f / den;
-        rgam[row] = gm;
         const int tok = tok0 + row;
         if (tok < tend) {
           lg[rowbase + tok] = qbias[row] + log2f(den);
@@ -428,10 +429,156 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
       }
     }
-    for (int e = threadIdx.x; e < 32 * OROW; e += NT) osum[buf ^ 1][e] = 0.f;  // for chunk t+1
-    lds_barrier();  // Z: 1/D' and gamma of every query
+    if constexpr (!XOW)
+      for (int e = threadIdx.x; e < 32 * OROW; e += NT) osum[buf ^ 1][e] = 0.f;  // for chunk t+1
+    // ---- chunk t+1 lands and is converted
+    if (t + 1 < n) {
+      wait_vmcnt<0>();
+      Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - tok0 - 32);
+    }
+  }
+}
 
-    // ---- carried part of dPhi'_Q^T[f][q] = S'[f][col] (A: St, paired column slots, hi + lo) x
+// ---------------------------------------------------------------- query gradient
+// Workgroup = NW waves on segment sp of (b,h), wave w owning features [32w, 32w + 32). The carry
+// S' is held as St[nb][fb] = C[column][feature]. Per chunk (Q, K, V and dOut rows through a
+// two-slot DMA ring; l and gamma per query prefetched a chunk ahead):
+//   X   projections: keys [key][feature] against M (Phi'_K, hi + lo A operand), queries
+//       [feature][query] against l (phi~ = Phi'_Q / D')
+//       dPhi~^T[f][q] = S'[f][col] (A: St, hi + lo) x [g_q, -gamma_q] (B) + Phi'_K^T (A) x B with
+//       the masked scores B[key][q] = g_q . v_key - gamma_q (key <= q, hi + lo); then
+//       P = phi~ * dPhi~ = phi_Q * dPhi_Q as rows [query][feature] (hi + lo); St takes the chunk
+//   P   dq^T blocks = Omega'^T P / log2(e), every wave its share over all features
+template <typename T, int D, int DV, int M>
+__global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
+cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
+              const typename Ops<T>::P* __restrict__ omf, const typename Ops<T>::C* __restrict__ omTh,
+              const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ cpart,
+              const float* __restrict__ cz, const float* __restrict__ cmax, const float* __restrict__ lg,
+              const float* __restrict__ gam, int H, int L, int seg_len, int nseg, float nscale, int grad_f32,
+              void* __restrict__ dq) {
+  using P = typename Ops<T>::P;
+  using C = typename Ops<T>::C;
+  constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
+  static_assert(FB == 2, "one 32-feature chunk per wave");
+  constexpr int NT = 64 * NW;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NDB = D / 16, NVB = DV / 16, NB = NVB + 1;
+  constexpr int NFC = M / 32;
+  constexpr int KC = (NB + 1) / 2;     // 32-column chunks of [value columns, z]
+  constexpr int KCV = (DV + 31) / 32;  // 32-column chunks of the value columns
+  constexpr int BPW = 2 * NDB / NW;    // dq^T blocks (dims db, queries tb) per wave
+  static_assert(BPW >= 1 && (2 * NDB) % NW == 0, "dq blocks split evenly over the waves");
+  constexpr int NSPL = CbwdOps<T>::NSPL;
+  constexpr int PROW = M + 8;  // P rows [query][feature]
+  using Rg = SweepRing<T, D, DV, NT, true>;
+  using VR = Ring<T, D, DV, NT, true>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) C prow[NSPL][32 * PROW];
+  __shared__ __attribute__((aligned(16))) float kn[2][32];
+  __shared__ __attribute__((aligned(16))) float qn[2][32];
+  __shared__ __attribute__((aligned(16))) float rl[2][32];
+  __shared__ __attribute__((aligned(16))) float rgm[2][32];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int pc = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = pc / nseg, sp = pc % nseg, h = bh % H;
+  const int t0 = sp * seg_len, tend = min(t0 + seg_len, L);
+  const int n = (tend - t0 + 31) / 32;
+  const size_t rowbase = (size_t)bh * L;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+
+  float pl = INFINITY, pg = 0.f;  // l and gamma of a chunk, threads < 32
+  auto fetch = [&](int tok0) {
+    if (threadIdx.x < 32) {
+      const int tok = tok0 + threadIdx.x;
+      pl = tok < tend ? lg[rowbase + tok] : INFINITY;
+      pg = tok < tend ? gam[rowbase + tok] : 0.f;
+    }
+  };
+  Rg::issue(Q, K, V, L, rowbase, t0, ring0, dOut);
+  fetch(t0);
+
+  vec8<P> om[FB][DC];
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+  // St[nb][fb][i] = S'[feature 16fb + c][column 16nb + 4g + i]: lane (4g + i) + 16(c >> 2), slot 4fb + (c & 3)
+  // of the scan's fragments of this wave's 32-feature chunk
+  f32x4 St[NB][FB];
+  {
+    const size_t fcb = (size_t)pc * NFC + w;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = nb * 16 + 4 * g + i, j = 4 * fb + (c & 3);
+          float x = 0.f;
+          if (nb < NVB)
+            x = cpart[((fcb * NVB + nb) * 64 + (4 * g + i) + 16 * (c >> 2)) * 8 + j];
+          else if (col == DV)
+            x = cz[(fcb * 4 + (c >> 2)) * 8 + j];
+          St[nb][fb][i] = x;
+        }
+  }
+  const float mk = cmax[pc];
+  wait_vmcnt<0>();
+  Rg::template convert<P>(ring[0], qn[0], kn[0], nscale, tend - t0);
+  if (threadIdx.x < 32) {
+    rl[0][threadIdx.x] = pl;
+    rgm[0][threadIdx.x] = pg;
+  }
+
+  for (int t = 0; t < n; ++t) {
+    const int buf = t & 1;
+    const unsigned char* sl = ring[buf];
+    const unsigned char* vbase = sl + Rg::XC * 16;
+    const unsigned char* gbase = sl + (Rg::XC + Rg::VC) * 16;
+    const int tok0 = t0 + 32 * t;
+    lds_barrier();  // X: chunk t converted; the previous chunk's reads of the other slot and of the P rows done
+    if (t + 1 < n) {
+      Rg::issue(Q, K, V, L, rowbase, tok0 + 32, ring0 + (buf ^ 1) * Rg::SLOT, dOut);
+      fetch(tok0 + 32);
+    }
+    // ---- projections: keys [key][feature] from -(n'_k + M), queries [feature][query] from -l
+    vec8<C> afh[FB], afl[FB];  // Phi'_K^T: A [feature][key], paired key slots
+    f32x4 pq[2][FB];           // phi~ [feature][query]
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x4 kbias;
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kbias[i] = -(n4[i] + mk);
+      const float qb = -rl[buf][tb * 16 + c];
+      vec8<P> kf[DC], qf[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int col = dc * 32 + 8 * g;
+        kf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 1, tb * 16 + c, col) : zero8<P>();
+        qf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 0, tb * 16 + c, col) : zero8<P>();
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        f32x4 pk = kbias;
+        pq[tb][fb] = f32x4{qb, qb, qb, qb};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          mma16(pk, kf[dc], om[fb][dc]);
+          mma16(pq[tb][fb], om[fb][dc], qf[dc]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          split2(fast_exp2(pk[i]), afh[fb], afl[fb], 4 * tb + i);
+          pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+        }
+      }
+    }
+    // ---- carried part: dPhi~^T[f][q] = S'[f][col] (A: St, paired column slots, hi + lo) x
     // [g_q, -gamma_q] (B, paired column slots)
     f32x4 dph[FB][2];
 #pragma unroll
@@ -462,7 +609,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) split2(col0 + i == DV ? -rgam[qr] : 0.f, gh, gl, 4 * hf + i);
+            for (int i = 0; i < 4; ++i) split2(col0 + i == DV ? -rgm[buf][qr] : 0.f, gh, gl, 4 * hf + i);
           }
         }
 #pragma unroll
@@ -476,32 +623,31 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       }
     }
     // ---- intra part: B[key][q] = g_q . v_key - gamma_q for key <= q (A: V rows, B: g rows, linear
-    // column slots), dPhi'^T += Phi'_K^T (A, hi + lo) x B (hi + lo)
+    // column slots), dPhi~^T += Phi'_K^T (A, hi + lo) x B (hi + lo)
     {
       f32x4 bs[2][2];
-      vec8<C> va[2][KCV], gb[2][KCV];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int kb = 0; kb < 2; ++kb) bs[kb][0] = bs[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kcv = 0; kcv < KCV; ++kcv) {
-          const int col = kcv * 32 + 8 * g;
-          va[x][kcv] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(vbase + VR::v_off(x * 16 + c, col))))
-                                : zero8<C>();
-          gb[x][kcv] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(gbase + VR::v_off(x * 16 + c, col))))
-                                : zero8<C>();
+      for (int kcv = 0; kcv < KCV; ++kcv) {
+        const int col = kcv * 32 + 8 * g;
+        vec8<C> va[2], gb[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          va[x] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(vbase + VR::v_off(x * 16 + c, col))))
+                           : zero8<C>();
+          gb[x] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(gbase + VR::v_off(x * 16 + c, col))))
+                           : zero8<C>();
         }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          bs[kb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kcv = 0; kcv < KCV; ++kcv) mma16(bs[kb][tb], va[kb][kcv], gb[tb][kcv]);
-        }
+          for (int tb = 0; tb < 2; ++tb) mma16(bs[kb][tb], va[kb], gb[tb]);
+      }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int qr = tb * 16 + c;
-        const float gq = rgam[qr];
+        const float gq = rgm[buf][qr];
         vec8<C> bh, bl;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -513,67 +659,58 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         for (int fb = 0; fb < FB; ++fb) mma_split<NSPL>(dph[fb][tb], afh[fb], afl[fb], bh, bl);
       }
     }
-    // ---- P = Phi'_Q * dPhi'_Q (dPhi'_Q = the above / D'), rows [query][feature] as hi + lo
-    {
-      C* prh = ubuf;
-      C* prl = ubuf + (NSPL - 1) * 32 * PROW;
+    // ---- P = phi~ * dPhi~, rows [query][feature] as hi + lo
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const float rd = rden[tb * 16 + c];
-#pragma unroll
-        for (int fb = 0; fb < FB; ++fb) {
-          vec4<C> h4, l4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float phi = to_f(bqh[tb][4 * fb + i]) + to_f(bql[tb][4 * fb + i]);
-            split2(phi * dph[fb][tb][i] * rd, h4, l4, i);
-          }
-          const int off = (tb * 16 + c) * PROW + w * 32 + fb * 16 + 4 * g;
-          *reinterpret_cast<vec4<C>*>(prh + off) = h4;
-          if constexpr (NSPL == 2) *reinterpret_cast<vec4<C>*>(prl + off) = l4;
-        }
-      }
-    }
-    // ---- St takes the chunk: St[col][f] += [V 1]^T (A) x Phi'_K (B)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        mma16(St[nb][fb], vf[nb], afh[fb]);
-        if constexpr (NSPL == 2) mma16(St[nb][fb], vf[nb], afl[fb]);
+        vec4<C> h4, l4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split2(pq[tb][fb][i] * dph[fb][tb][i], h4, l4, i);
+        const int off = (tb * 16 + c) * PROW + w * 32 + fb * 16 + 4 * g;
+        *reinterpret_cast<vec4<C>*>(&prow[0][off]) = h4;
+        if constexpr (NSPL == 2) *reinterpret_cast<vec4<C>*>(&prow[NSPL - 1][off]) = l4;
       }
+    // ---- St takes the chunk: St[col][f] += [V 1]^T (A) x Phi'_K (B)
+    {
+      vec8<C> vf[NB];
+      value_frags<T, D, DV, NT>(vbase, vf, c, g);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+          mma16(St[nb][fb], vf[nb], afh[fb]);
+          if constexpr (NSPL == 2) mma16(St[nb][fb], vf[nb], afl[fb]);
+        }
+    }
     lds_barrier();  // P rows of every wave
 
     // ---- dq: this wave's blocks of dq^T over all features: A = Omega'^T (hi + lo), B = P rows
-    {
-      const C* prh = ubuf;
-      const C* prl = ubuf + (NSPL - 1) * 32 * PROW;
 #pragma unroll
-      for (int bi = 0; bi < BPW; ++bi) {
-        const int blk = w * BPW + bi, db = blk >> 1, tb = blk & 1;
-        const int qr = tb * 16 + c;
-        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = w * BPW + bi, db = blk >> 1, tb = blk & 1;
+      const int qr = tb * 16 + c;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int fc = 0; fc < NFC; ++fc) {
-          const size_t fo = ((((size_t)h * NDB + db) * NFC + fc) * 64 + lane) * 8;
-          const vec8<C> oh = ld8<C>(omTh + fo);
-          const vec8<C> ol = NSPL == 2 ? ld8<C>(omTl + fo) : oh;
-          const vec8<C> p8h = pair_read8<C>(prh + qr * PROW, fc * 32, g);
-          const vec8<C> p8l = NSPL == 2 ? pair_read8<C>(prl + qr * PROW, fc * 32, g) : p8h;
-          mma_split<NSPL>(a, oh, ol, p8h, p8l);
-        }
-        const int tok = tok0 + qr;
-        if (tok < tend) {
-          const size_t off = (rowbase + tok) * D + db * 16 + 4 * g;
-          a = a * (1.f / kLog2e);
-          if (grad_f32) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = a;
-          } else {
-            vec4<T> o4;
+      for (int fc = 0; fc < NFC; ++fc) {
+        const size_t fo = ((((size_t)h * NDB + db) * NFC + fc) * 64 + lane) * 8;
+        const vec8<C> oh = ld8<C>(omTh + fo);
+        const vec8<C> ol = NSPL == 2 ? ld8<C>(omTl + fo) : oh;
+        const vec8<C> p8h = pair_read8<C>(&prow[0][qr * PROW], fc * 32, g);
+        const vec8<C> p8l = NSPL == 2 ? pair_read8<C>(&prow[NSPL - 1][qr * PROW], fc * 32, g) : p8h;
+        mma_split<NSPL>(a, oh, ol, p8h, p8l);
+      }
+      const int tok = tok0 + qr;
+      if (tok < tend) {
+        const size_t off = (rowbase + tok) * D + db * 16 + 4 * g;
+        a = a * (1.f / kLog2e);
+        if (grad_f32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = a;
+        } else {
+          vec4<T> o4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = to_t<T>(a[i]);
-            *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dq) + off) = o4;
-          }
+          for (int i = 0; i < 4; ++i) o4[i] = to_t<T>(a[i]);
+          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dq) + off) = o4;
         }
       }
     }
@@ -581,6 +718,10 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     if (t + 1 < n) {
       wait_vmcnt<0>();
       Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - tok0 - 32);
+      if (threadIdx.x < 32) {
+        rl[buf ^ 1][threadIdx.x] = pl;
+        rgm[buf ^ 1][threadIdx.x] = pg;
+      }
     }
   }
 }
@@ -735,28 +876,23 @@ cbwd_rscan_kernel(float* __restrict__ trow, const float* __restrict__ cmax, int 
   }
 }
 
-// ---------------------------------------------------------------- key side
+// ---------------------------------------------------------------- key gradient
 // Workgroup = NW waves on segment sp of (b,h), wave w owning features [32w, 32w + 32); the chunks
 // run backwards from the segment's end. The suffix state R'' (the later segments' carry, then the
-// chunks already passed) is held as Rc[nb][fb] = C[column][feature] and Rt[fb][nb] =
-// C[feature][value column]. Per chunk:
+// chunks already passed) is held as Rc[nb][fb] = C[column][feature]. Per chunk:
 //   X   projections [token][feature]: keys against M (phi'_K), queries against l (phi~)
 //       Bt[q][key] = g_q . v_key (A = g rows, B = V rows), B = Bt - gamma_q for q >= key
 //       dPhi''_K[key][f] = [V 1] (A, exact) x Rc (B, hi + lo) + B (A, hi + lo) x phi~ (B, hi + lo)
-//       P = phi'_K * dPhi''_K, rho = its sum over the wave's features
-//       dv partial = phi'_K (A, transposing reads of the wave's phi'_K rows) x Rt (B)
-//                  + masked (phi~ phi'_K^T) (A) x g (B: value fragments of the g rows),
-//       summed over the waves by LDS atomics; P replaces the wave's phi'_K rows
-//       Rc, Rt take the chunk's queries
-//   B1  dk^T blocks = Omega'^T P / log2(e) - d^-1/2 k rho over all features; dv stored
+//       P = phi'_K * dPhi''_K as rows [feature][key] (hi + lo), rho = its sum over the wave's
+//       features; Rc takes the chunk's queries
+//   B1  dk^T blocks = Omega'^T P / log2(e) - d^-1/2 k rho over all features
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
               const typename Ops<T>::P* __restrict__ omf, const typename Ops<T>::C* __restrict__ omTh,
               const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ rcar,
               const float* __restrict__ cmax, const float* __restrict__ lg, const float* __restrict__ gam, int H,
-              int L, int seg_len, int nseg, float nscale, float s2, int grad_f32, void* __restrict__ dk,
-              void* __restrict__ dv) {
+              int L, int seg_len, int nseg, float nscale, float s2, int grad_f32, void* __restrict__ dk) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -770,16 +906,11 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   constexpr int BPWK = 2 * NDB / NW;
   static_assert(BPWK >= 1 && (2 * NDB) % NW == 0, "dk blocks split evenly over the waves");
   constexpr int NSPL = CbwdOps<T>::NSPL;
-  constexpr int CPR = DV / 8;
-  static_assert(32 * CPR <= NT, "one (row, 8 columns) item per thread");
   constexpr int FROW = 36;  // [feature][token] rows
-  constexpr int DVROW = DV + 4;
   using Rg = SweepRing<T, D, DV, NT, true>;
   using VR = Ring<T, D, DV, NT, true>;
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
-  __shared__ __attribute__((aligned(16))) C ft[NSPL][M * FROW];  // phi'_K, then P: [feature][key]
-  __shared__ __attribute__((aligned(16))) C qt[NSPL][M * FROW];  // phi~: [feature][query]
-  __shared__ __attribute__((aligned(16))) float dvs[32 * DVROW];
+  __shared__ __attribute__((aligned(16))) C ft[NSPL][M * FROW];  // P: [feature][key]
   __shared__ __attribute__((aligned(16))) float kn[2][32];
   __shared__ __attribute__((aligned(16))) float qn[2][32];
   __shared__ __attribute__((aligned(16))) float rl[2][32];
@@ -806,7 +937,6 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   const int last0 = t0 + 32 * (n - 1);
   Rg::issue(Q, K, V, L, rowbase, last0, ring0, dOut);
   fetch(last0);
-  for (int e = threadIdx.x; e < 32 * DVROW; e += NT) dvs[e] = 0.f;
 
   vec8<P> om[FB][DC];
 #pragma unroll
@@ -814,7 +944,7 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
-  f32x4 Rc[NB][FB], Rt[FB][NVB];
+  f32x4 Rc[NB][FB];
   {
     const float* src = rcar + (size_t)pc * M * NBC;
 #pragma unroll
@@ -822,12 +952,6 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb)
         Rc[nb][fb] = *reinterpret_cast<const f32x4*>(src + (size_t)(w * 32 + fb * 16 + c) * NBC + nb * 16 + 4 * g);
-#pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int nb = 0; nb < NVB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Rt[fb][nb][i] = src[(size_t)(w * 32 + fb * 16 + 4 * g + i) * NBC + nb * 16 + c];
   }
   const float mk = cmax[pc];
   wait_vmcnt<0>();
@@ -884,53 +1008,34 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
       }
     }
-    // phi~ as B [query][feature] (paired query slots), hi + lo; phi'_K and phi~ rows [feature][token]
+    // phi~ as B [query][feature] (paired query slots), hi + lo
     vec8<C> qbh[FB], qbl[FB];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) split2(pq[j >> 2][fb][j & 3], qbh[fb], qbl[fb], j);
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb) {
-        vec4<C> kh4, kl4, qh4, ql4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          split2(pk[tb][fb][i], kh4, kl4, i);
-          split2(pq[tb][fb][i], qh4, ql4, i);
-        }
-        const int off = (w * 32 + fb * 16 + c) * FROW + tb * 16 + 4 * g;
-        *reinterpret_cast<vec4<C>*>(&ft[0][off]) = kh4;
-        *reinterpret_cast<vec4<C>*>(&qt[0][off]) = qh4;
-        if constexpr (NSPL == 2) {
-          *reinterpret_cast<vec4<C>*>(&ft[NSPL - 1][off]) = kl4;
-          *reinterpret_cast<vec4<C>*>(&qt[NSPL - 1][off]) = ql4;
-        }
-      }
     // ---- scores Bt[q][key] = g_q . v_key; A operand [key][query] of B = Bt - gamma_q, q >= key
     vec8<C> bah[2], bal[2];
     {
       f32x4 bt[2][2];
-      vec8<C> ga[2][KCV], va[2][KCV];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int qb = 0; qb < 2; ++qb) bt[qb][0] = bt[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kcv = 0; kcv < KCV; ++kcv) {
-          const int col = kcv * 32 + 8 * g;
-          ga[x][kcv] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(gbase + VR::v_off(x * 16 + c, col))))
-                                : zero8<C>();
-          va[x][kcv] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(vbase + VR::v_off(x * 16 + c, col))))
-                                : zero8<C>();
+      for (int kcv = 0; kcv < KCV; ++kcv) {
+        const int col = kcv * 32 + 8 * g;
+        vec8<C> ga[2], va[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          ga[x] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(gbase + VR::v_off(x * 16 + c, col))))
+                           : zero8<C>();
+          va[x] = col < DV ? cvt8<C, T>(ld8<T>(reinterpret_cast<const T*>(vbase + VR::v_off(x * 16 + c, col))))
+                           : zero8<C>();
         }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          bt[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kcv = 0; kcv < KCV; ++kcv) mma16(bt[qb][kb], ga[qb][kcv], va[kb][kcv]);
-        }
+          for (int kb = 0; kb < 2; ++kb) mma16(bt[qb][kb], ga[qb], va[kb]);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -996,64 +1101,7 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         if (c == 0) rho[kb * 16 + 4 * g + i][w] = r;
       }
     }
-    // ---- dv partial over this wave's features
-    f32x4 dva[2][NVB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int nb = 0; nb < NVB; ++nb) dva[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    vec8<C> gv[NB];  // g rows as value fragments: [query][col], paired query slots
-    value_frags<T, D, DV, NT>(gbase, gv, c, g);
-    {
-      vec8<C> fah[2], fal[2];  // phi'_K: A [key][feature] / B [feature][key], paired feature slots
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        fah[kb] = tr_read8<C>(ft[0], FROW, w * 32, kb * 16, c, g);
-        fal[kb] = NSPL == 2 ? tr_read8<C>(ft[NSPL - 1], FROW, w * 32, kb * 16, c, g) : fah[kb];
-      }
-#pragma unroll
-      for (int nb = 0; nb < NVB; ++nb) {
-        vec8<C> rth, rtl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split2(Rt[j >> 2][nb][j & 3], rth, rtl, j);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma_split<NSPL>(dva[kb][nb], fah[kb], fal[kb], rth, rtl);
-      }
-      // A^T[q][key] = phi~ (A [query][feature]) x phi'_K (B), over this wave's features
-      f32x4 at[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const vec8<C> qah = tr_read8<C>(qt[0], FROW, w * 32, qb * 16, c, g);
-        const vec8<C> qal = NSPL == 2 ? tr_read8<C>(qt[NSPL - 1], FROW, w * 32, qb * 16, c, g) : qah;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          at[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          mma_split<NSPL>(at[qb][kb], qah, qal, fah[kb], fal[kb]);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        vec8<C> aah, aal;  // A [key][query], paired query slots, q >= key
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int qb = jj >> 2, i = jj & 3;
-          const int q = qb * 16 + 4 * g + i, key = kb * 16 + c;
-          split2(q >= key ? at[qb][kb][i] : 0.f, aah, aal, jj);
-        }
-#pragma unroll
-        for (int nb = 0; nb < NVB; ++nb) {
-          mma16(dva[kb][nb], aah, gv[nb]);
-          if constexpr (NSPL == 2) mma16(dva[kb][nb], aal, gv[nb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int nb = 0; nb < NVB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(&dvs[(kb * 16 + 4 * g + i) * DVROW + nb * 16 + c], dva[kb][nb][i]);
-    // ---- P replaces this wave's phi'_K rows (read above by this wave only)
+    // ---- P rows [feature][key] (hi + lo)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1065,8 +1113,10 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         *reinterpret_cast<vec4<C>*>(&ft[0][off]) = h4;
         if constexpr (NSPL == 2) *reinterpret_cast<vec4<C>*>(&ft[NSPL - 1][off]) = l4;
       }
-    // ---- the suffix state takes the chunk's queries:
-    // Rc[col][f] += [g, -gamma]^T (A, paired query slots) x phi~ (B); Rt[f][col] += phi~^T (A) x g (B)
+    // ---- the suffix state takes the chunk's queries: Rc[col][f] += [g, -gamma]^T (A, paired query
+    // slots) x phi~ (B)
+    vec8<C> gv[NB];
+    value_frags<T, D, DV, NT>(gbase, gv, c, g);
     {
       vec8<C> zh, zl;
 #pragma unroll
@@ -1080,13 +1130,11 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         for (int nb = 0; nb < NVB; ++nb) {
           mma16(Rc[nb][fb], gv[nb], qbh[fb]);
           if constexpr (NSPL == 2) mma16(Rc[nb][fb], gv[nb], qbl[fb]);
-          mma16(Rt[fb][nb], qbh[fb], gv[nb]);
-          if constexpr (NSPL == 2) mma16(Rt[fb][nb], qbl[fb], gv[nb]);
         }
         mma_split<NSPL>(Rc[NVB][fb], zh, zl, qbh[fb], qbl[fb]);
       }
     }
-    lds_barrier();  // B1: P rows, rho, dv sums of every wave
+    lds_barrier();  // B1: P rows and rho of every wave
 
     // ---- dk: blocks of dk^T over all features: A = Omega'^T (hi + lo), B = P (transposing reads)
 #pragma unroll
@@ -1124,12 +1172,249 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
       }
     }
-    // ---- dv of the chunk, stored; the sums cleared for the next chunk
+    // ---- chunk t-1 lands and is converted
+    if (t > 0) {
+      wait_vmcnt<0>();
+      Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - (tok0 - 32));
+      if (threadIdx.x < 32) {
+        rl[buf ^ 1][threadIdx.x] = pl;
+        rgm[buf ^ 1][threadIdx.x] = pg;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- value gradient
+// Workgroup = NW waves on segment sp of (b,h), wave w owning features [32w, 32w + 32); the chunks
+// run backwards. The suffix state's value columns are held as Rt[fb][nb] = C[feature][column].
+// Per chunk:
+//   X   projections [token][feature]: keys against M (phi'_K), queries against l (phi~), written
+//       as the wave's rows [feature][token] (hi + lo)
+//       dv^T partial [col][key] = Rt (A, hi + lo) x phi'_K (B, transposing reads of those rows)
+//                  + g^T (A: value fragments of the g rows) x masked (phi~ phi'_K^T, q >= key) (B),
+//       written over the wave's rows once they are read; Rt takes the chunk's queries
+//   B1  the waves' partials summed, dv stored
+template <typename T, int D, int DV, int M>
+__global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
+cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
+              const typename Ops<T>::P* __restrict__ omf, const float* __restrict__ rcar,
+              const float* __restrict__ cmax, const float* __restrict__ lg, int H, int L, int seg_len, int nseg,
+              float nscale, int grad_f32, void* __restrict__ dv) {
+  using P = typename Ops<T>::P;
+  using C = typename Ops<T>::C;
+  constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
+  static_assert(FB == 2, "one 32-feature chunk per wave");
+  constexpr int NT = 64 * NW;
+  constexpr int DC = (D + 31) / 32;
+  constexpr int NVB = DV / 16, NB = NVB + 1, NBC = NB * 16;
+  constexpr int NSPL = CbwdOps<T>::NSPL;
+  constexpr int CPR = DV / 8;
+  static_assert(32 * CPR <= NT, "one (row, 8 columns) item per thread");
+  constexpr int FROW = 36;  // [feature][token] rows
+  constexpr int FQ = 2 * NSPL * 32 * FROW;  // a wave's rows: phi'_K (hi, lo), phi~ (hi, lo)
+  static_assert(FQ * (int)sizeof(C) >= 2 * NVB * 256 * 4, "a wave's partial dv fits over its rows");
+  using Rg = SweepRing<T, D, DV, NT, true>;
+  using VR = Ring<T, D, DV, NT, true>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) C fq[NW][FQ];  // per wave: phi'_K and phi~ rows, then its dv partial
+  __shared__ __attribute__((aligned(16))) float kn[2][32];
+  __shared__ __attribute__((aligned(16))) float qn[2][32];
+  __shared__ __attribute__((aligned(16))) float rl[2][32];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int pc = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = pc / nseg, sp = pc % nseg, h = bh % H;
+  const int t0 = sp * seg_len, tend = min(t0 + seg_len, L);
+  const int n = (tend - t0 + 31) / 32;
+  const size_t rowbase = (size_t)bh * L;
+  const uint32_t ring0 = lds_addr(&ring[0][0]);
+
+  float pl = INFINITY;
+  auto fetch = [&](int tok0) {
+    if (threadIdx.x < 32) {
+      const int tok = tok0 + threadIdx.x;
+      pl = tok < tend ? lg[rowbase + tok] : INFINITY;
+    }
+  };
+  const int last0 = t0 + 32 * (n - 1);
+  Rg::issue(Q, K, V, L, rowbase, last0, ring0, dOut);
+  fetch(last0);
+  C* const fth = &fq[w][0];
+  C* const ftl = &fq[w][(NSPL - 1) * 32 * FROW];
+  C* const qth = &fq[w][NSPL * 32 * FROW];
+  C* const qtl = &fq[w][(2 * NSPL - 1) * 32 * FROW];
+
+  vec8<P> om[FB][DC];
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+  f32x4 Rt[FB][NVB];
+  {
+    const float* src = rcar + (size_t)pc * M * NBC;
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NVB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Rt[fb][nb][i] = src[(size_t)(w * 32 + fb * 16 + 4 * g + i) * NBC + nb * 16 + c];
+  }
+  const float mk = cmax[pc];
+  wait_vmcnt<0>();
+  Rg::template convert<P>(ring[0], qn[0], kn[0], nscale, tend - last0);
+  if (threadIdx.x < 32) rl[0][threadIdx.x] = pl;
+
+  for (int it = 0; it < n; ++it) {
+    const int t = n - 1 - it;
+    const int buf = it & 1;
+    const unsigned char* sl = ring[buf];
+    const unsigned char* vbase = sl + Rg::XC * 16;
+    const unsigned char* gbase = sl + (Rg::XC + Rg::VC) * 16;
+    const int tok0 = t0 + 32 * t;
+    lds_barrier();  // X: chunk t converted; the previous chunk's reads done
+    if (t > 0) {
+      Rg::issue(Q, K, V, L, rowbase, tok0 - 32, ring0 + (buf ^ 1) * Rg::SLOT, dOut);
+      fetch(tok0 - 32);
+    }
+    // ---- projections [token][feature]: keys from -(n'_k + M), queries from -l_q; then the features
+    f32x4 pk[2][FB], pq[2][FB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x4 kbias, qbias;
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][tb * 16 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kbias[i] = -(n4[i] + mk);
+        qbias[i] = -l4[i];
+      }
+      vec8<P> kf[DC], qf[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int col = dc * 32 + 8 * g;
+        kf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 1, tb * 16 + c, col) : zero8<P>();
+        qf[dc] = (col < D) ? Rg::template ld_x8<P>(sl, 0, tb * 16 + c, col) : zero8<P>();
+      }
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        pk[tb][fb] = kbias;
+        pq[tb][fb] = qbias;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          mma16(pk[tb][fb], kf[dc], om[fb][dc]);
+          mma16(pq[tb][fb], qf[dc], om[fb][dc]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pk[tb][fb][i] = fast_exp2(pk[tb][fb][i]);
+          pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+        }
+      }
+    }
+    // phi~ as B [query][feature] (paired query slots), hi + lo; phi'_K and phi~ rows [feature][token]
+    vec8<C> qbh[FB], qbl[FB];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) split2(pq[j >> 2][fb][j & 3], qbh[fb], qbl[fb], j);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        vec4<C> kh4, kl4, qh4, ql4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          split2(pk[tb][fb][i], kh4, kl4, i);
+          split2(pq[tb][fb][i], qh4, ql4, i);
+        }
+        const int off = (fb * 16 + c) * FROW + tb * 16 + 4 * g;
+        *reinterpret_cast<vec4<C>*>(fth + off) = kh4;
+        *reinterpret_cast<vec4<C>*>(qth + off) = qh4;
+        if constexpr (NSPL == 2) {
+          *reinterpret_cast<vec4<C>*>(ftl + off) = kl4;
+          *reinterpret_cast<vec4<C>*>(qtl + off) = ql4;
+        }
+      }
+    // ---- dv partial over this wave's features
+    f32x4 dvt[NVB][2];  // dv^T [col][key]
+#pragma unroll
+    for (int nb = 0; nb < NVB; ++nb) dvt[nb][0] = dvt[nb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    vec8<C> gv[NB];  // g rows as value fragments: [query][col], paired query slots
+    value_frags<T, D, DV, NT>(gbase, gv, c, g);
+    {
+      vec8<C> fah[2], fal[2];  // phi'_K: A [key][feature] / B [feature][key], paired feature slots
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        fah[kb] = tr_read8<C>(fth, FROW, 0, kb * 16, c, g);
+        fal[kb] = NSPL == 2 ? tr_read8<C>(ftl, FROW, 0, kb * 16, c, g) : fah[kb];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NVB; ++nb) {
+        vec8<C> rth, rtl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split2(Rt[j >> 2][nb][j & 3], rth, rtl, j);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma_split<NSPL>(dvt[nb][kb], rth, rtl, fah[kb], fal[kb]);
+      }
+      // A^T[q][key] = phi~ (A [query][feature]) x phi'_K (B), over this wave's features
+      f32x4 at[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const vec8<C> qah = tr_read8<C>(qth, FROW, 0, qb * 16, c, g);
+        const vec8<C> qal = NSPL == 2 ? tr_read8<C>(qtl, FROW, 0, qb * 16, c, g) : qah;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          at[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mma_split<NSPL>(at[qb][kb], qah, qal, fah[kb], fal[kb]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        vec8<C> aah, aal;  // B [query][key], paired query slots, q >= key
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int qb = jj >> 2, i = jj & 3;
+          const int q = qb * 16 + 4 * g + i, key = kb * 16 + c;
+          split2(q >= key ? at[qb][kb][i] : 0.f, aah, aal, jj);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NVB; ++nb) {
+          mma16(dvt[nb][kb], gv[nb], aah);
+          if constexpr (NSPL == 2) mma16(dvt[nb][kb], gv[nb], aal);
+        }
+      }
+    }
+    // the wave's partial over its own rows (read above by this wave only): [kb][nb][lane] f32x4
+    {
+      float* part = reinterpret_cast<float*>(&fq[w][0]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < NVB; ++nb) *reinterpret_cast<f32x4*>(&part[((kb * NVB + nb) * 64 + lane) * 4]) = dvt[nb][kb];
+    }
+    // ---- the suffix state takes the chunk's queries: Rt[f][col] += phi~^T (A) x g (B)
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+      for (int nb = 0; nb < NVB; ++nb) {
+        mma16(Rt[fb][nb], qbh[fb], gv[nb]);
+        if constexpr (NSPL == 2) mma16(Rt[fb][nb], qbl[fb], gv[nb]);
+      }
+    lds_barrier();  // B1: the dv sums of every wave
+
+    // ---- dv of the chunk: the waves' partials summed, stored
     if (threadIdx.x < 32 * CPR) {
       const int row = threadIdx.x / CPR, c8 = threadIdx.x % CPR;
-      f32x4* src = reinterpret_cast<f32x4*>(&dvs[row * DVROW + c8 * 8]);
-      const f32x4 a = src[0], b = src[1];
-      src[0] = src[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int kb = row >> 4, ck = row & 15, nb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* base = reinterpret_cast<const float*>(&fq[ww][0]) + ((kb * NVB + nb) * 64 + ck + 16 * g0) * 4;
+        a += *reinterpret_cast<const f32x4*>(base);
+        b += *reinterpret_cast<const f32x4*>(base + 64);
+      }
       const int tok = tok0 + row;
       if (tok < tend) {
         const size_t off = (rowbase + tok) * DV + c8 * 8;
@@ -1152,10 +1437,7 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     if (t > 0) {
       wait_vmcnt<0>();
       Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - (tok0 - 32));
-      if (threadIdx.x < 32) {
-        rl[buf ^ 1][threadIdx.x] = pl;
-        rgm[buf ^ 1][threadIdx.x] = pg;
-      }
+      if (threadIdx.x < 32) rl[buf ^ 1][threadIdx.x] = pl;
     }
   }
 }
@@ -1233,9 +1515,14 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
         part, zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr);
   }
   {
+    FAVOR_TIMED("cbwd_fwd", st);
+    cbwd_fwd_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, cpart, cz, cmax, s.H, s.L, f.seg_len,
+                                                            f.nseg, nscale, lg, gam);
+  }
+  {
     FAVOR_TIMED("cbwd_q", st);
-    cbwd_q_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, omth, omtl, cpart, cz, cmax, s.H,
-                                                          s.L, f.seg_len, f.nseg, nscale, grad_f32, dq, lg, gam);
+    cbwd_q_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, omth, omtl, cpart, cz, cmax, lg, gam,
+                                                          s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq);
   }
   {
     FAVOR_TIMED("cbwd_t", st);
@@ -1250,7 +1537,12 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   {
     FAVOR_TIMED("cbwd_k", st);
     cbwd_k_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, omth, omtl, trow, cmax, lg, gam, s.H,
-                                                          s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk, dv);
+                                                          s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk);
+  }
+  {
+    FAVOR_TIMED("cbwd_v", st);
+    cbwd_v_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, trow, cmax, lg, s.H, s.L, f.seg_len,
+                                                          f.nseg, nscale, grad_f32, dv);
   }
   return hipGetLastError();
 }

@@ -21,6 +21,13 @@ import sys
 
 # mangled kernel name fragment -> timer name used by the library and bench.py
 _SHORT = [
+    ("cbwd_fwd_kernel", "cbwd_fwd"),
+    ("cbwd_q_kernel", "cbwd_q"),
+    ("cbwd_v_kernel", "cbwd_v"),
+    ("cbwd_t_kernel", "cbwd_t"),
+    ("cbwd_k_kernel", "cbwd_k"),
+    ("cbwd_rscan_kernel", "rscan"),
+    ("omegaT_pair_kernel", "omega_frag"),
     ("bwd_q_kernel", "bwd_q"),
     ("bwd_k_kernel", "bwd_k"),
     ("combine_rows_kernel", "combine_rows"),

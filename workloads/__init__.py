@@ -23,6 +23,8 @@ bidirectional attention, causal attention and recurrent decoding):
   backward_bf16  bidir_bf16's inputs plus an upstream gradient dOut ~ N(0,1)
                [B,H,L,dv] (its own generator, seed + 100): the gradients
                of the bidirectional estimator                            seed 2
+  causal_backward_bf16  causal_bf16's inputs plus dOut ~ N(0,1) drawn the same
+               way: the gradients of the causal estimator                seed 3
 
 Draw order for one workload: Q, then K, then V, each one `torch.randn` call on
 a CPU generator seeded with the workload's seed, scaled, then rounded to the
@@ -83,6 +85,8 @@ WORKLOADS = {
     "backward_bf16": Workload("backward_bf16", "backward", "bf16", 8, 12, 4096, 64, 64, 256, 2,
                               1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
+    "causal_backward_bf16": Workload("causal_backward_bf16", "causal_backward", "bf16", 4, 8, 8192, 64, 64, 256, 3,
+                                     0.5, 0.5, 0.5),
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
                             steps=1000, prior=2048),
     "decode_gated_bf16": Workload("decode_gated_bf16", "decode_gated", "bf16", 256, 16, 1, 64, 64, 256, 5,
