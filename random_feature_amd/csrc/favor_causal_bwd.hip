@@ -113,6 +113,21 @@ __device__ __forceinline__ vec8<C> cvt8(const vec8<T>& x) {
   return r;
 }
 
+// A head's Omega'^T fragments (hi and lo, BYTES each) copied into LDS with asynchronous 16-byte
+// copies, whole waves per round; the caller waits (vmcnt) and synchronises before the first read.
+template <int NT, int BYTES, typename C>
+__device__ __forceinline__ void stage_omT(const C* hi, const C* lo, C* dst_hi, C* dst_lo) {
+  static_assert(BYTES % (16 * NT) == 0, "whole rounds of 16-byte copies");
+  const int tid = threadIdx.x, w = tid >> 6;
+#pragma unroll
+  for (int u = 0; u < BYTES / (16 * NT); ++u) {
+    const size_t off = (size_t)(u * NT + tid) * 16;
+    const uint32_t dst = (uint32_t)(u * NT + w * 64) * 16u;
+    lds_dma16(reinterpret_cast<const unsigned char*>(hi) + off, lds_addr(dst_hi) + dst);
+    if (lo != nullptr) lds_dma16(reinterpret_cast<const unsigned char*>(lo) + off, lds_addr(dst_lo) + dst);
+  }
+}
+
 // Omega'^T as the A operand of the back-projections with paired feature slots, split into a
 // rounded part and its remainder: hi[h][db][fc][lane][j] = rnd(scale * omega[h][f][db*16 + c]),
 // f = fc*32 + 16(j>>2) + 4g + (j&3) (0 past m or d), lo the rounding remainder (0 for fp32).
@@ -473,7 +488,10 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   constexpr int PROW = M + 8;  // P rows [query][feature]
   using Rg = SweepRing<T, D, DV, NT, true>;
   using VR = Ring<T, D, DV, NT, true>;
+  constexpr int OMT = NDB * NFC * 512;  // elements of one head's Omega'^T fragments
+  constexpr bool STAGE = sizeof(C) == 2;  // those fragments in LDS (fp32: read from the cache, for want of LDS)
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) C omts[NSPL][STAGE ? OMT : 8];
   __shared__ __attribute__((aligned(16))) C prow[NSPL][32 * PROW];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
   __shared__ __attribute__((aligned(16))) float qn[2][32];
@@ -498,6 +516,9 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     }
   };
   Rg::issue(Q, K, V, L, rowbase, t0, ring0, dOut);
+  if constexpr (STAGE)
+    stage_omT<NT, OMT * (int)sizeof(C), C>(omTh + (size_t)h * OMT, NSPL == 2 ? omTl + (size_t)h * OMT : nullptr,
+                                           omts[0], omts[NSPL - 1]);
   fetch(t0);
 
   vec8<P> om[FB][DC];
@@ -693,9 +714,11 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int fc = 0; fc < NFC; ++fc) {
-        const size_t fo = ((((size_t)h * NDB + db) * NFC + fc) * 64 + lane) * 8;
-        const vec8<C> oh = ld8<C>(omTh + fo);
-        const vec8<C> ol = NSPL == 2 ? ld8<C>(omTl + fo) : oh;
+        const int fo = ((db * NFC + fc) * 64 + lane) * 8;
+        const C* oth = STAGE ? &omts[0][0] : omTh + (size_t)h * OMT;
+        const C* otl = STAGE ? &omts[NSPL - 1][0] : omTl + (size_t)h * OMT;
+        const vec8<C> oh = ld8<C>(oth + fo);
+        const vec8<C> ol = NSPL == 2 ? ld8<C>(otl + fo) : oh;
         const vec8<C> p8h = pair_read8<C>(&prow[0][qr * PROW], fc * 32, g);
         const vec8<C> p8l = NSPL == 2 ? pair_read8<C>(&prow[NSPL - 1][qr * PROW], fc * 32, g) : p8h;
         mma_split<NSPL>(a, oh, ol, p8h, p8l);
@@ -909,7 +932,10 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   constexpr int FROW = 36;  // [feature][token] rows
   using Rg = SweepRing<T, D, DV, NT, true>;
   using VR = Ring<T, D, DV, NT, true>;
+  constexpr int OMT = NDB * NFC * 512;  // elements of one head's Omega'^T fragments
+  constexpr bool STAGE = sizeof(C) == 2;  // those fragments in LDS (fp32: read from the cache, for want of LDS)
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
+  __shared__ __attribute__((aligned(16))) C omts[NSPL][STAGE ? OMT : 8];
   __shared__ __attribute__((aligned(16))) C ft[NSPL][M * FROW];  // P: [feature][key]
   __shared__ __attribute__((aligned(16))) float kn[2][32];
   __shared__ __attribute__((aligned(16))) float qn[2][32];
@@ -936,6 +962,9 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   };
   const int last0 = t0 + 32 * (n - 1);
   Rg::issue(Q, K, V, L, rowbase, last0, ring0, dOut);
+  if constexpr (STAGE)
+    stage_omT<NT, OMT * (int)sizeof(C), C>(omTh + (size_t)h * OMT, NSPL == 2 ? omTl + (size_t)h * OMT : nullptr,
+                                           omts[0], omts[NSPL - 1]);
   fetch(last0);
 
   vec8<P> om[FB][DC];
@@ -1144,9 +1173,11 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int fc = 0; fc < NFC; ++fc) {
-        const size_t fo = ((((size_t)h * NDB + db) * NFC + fc) * 64 + lane) * 8;
-        const vec8<C> oh = ld8<C>(omTh + fo);
-        const vec8<C> ol = NSPL == 2 ? ld8<C>(omTl + fo) : oh;
+        const int fo = ((db * NFC + fc) * 64 + lane) * 8;
+        const C* oth = STAGE ? &omts[0][0] : omTh + (size_t)h * OMT;
+        const C* otl = STAGE ? &omts[NSPL - 1][0] : omTl + (size_t)h * OMT;
+        const vec8<C> oh = ld8<C>(oth + fo);
+        const vec8<C> ol = NSPL == 2 ? ld8<C>(otl + fo) : oh;
         const vec8<C> p8h = tr_read8<C>(ft[0], FROW, fc * 32, kb * 16, c, g);
         const vec8<C> p8l = NSPL == 2 ? tr_read8<C>(ft[NSPL - 1], FROW, fc * 32, kb * 16, c, g) : p8h;
         mma_split<NSPL>(a, oh, ol, p8h, p8l);
