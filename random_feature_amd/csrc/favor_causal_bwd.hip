@@ -1245,7 +1245,6 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   constexpr int FQ = 2 * NSPL * 32 * FROW;  // a wave's rows: phi'_K (hi, lo), phi~ (hi, lo)
   static_assert(FQ * (int)sizeof(C) >= 2 * NVB * 256 * 4, "a wave's partial dv fits over its rows");
   using Rg = SweepRing<T, D, DV, NT, true>;
-  using VR = Ring<T, D, DV, NT, true>;
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) C fq[NW][FQ];  // per wave: phi'_K and phi~ rows, then its dv partial
   __shared__ __attribute__((aligned(16))) float kn[2][32];
@@ -1301,7 +1300,6 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     const int t = n - 1 - it;
     const int buf = it & 1;
     const unsigned char* sl = ring[buf];
-    const unsigned char* vbase = sl + Rg::XC * 16;
     const unsigned char* gbase = sl + (Rg::XC + Rg::VC) * 16;
     const int tok0 = t0 + 32 * t;
     lds_barrier();  // X: chunk t converted; the previous chunk's reads done
