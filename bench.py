@@ -92,13 +92,20 @@ _PATH_SOURCES = {
 }
 
 
+_HOST_MARK = b"// ---------------------------------------------------------------- host side"
+
+
 def _src_hash(kind: str) -> str:
-    """Digest of the sources of one path's kernels: a counter summary is valid while it matches."""
+    """Digest of the device code of one path's kernels (each .hip file up to its host-side section, and the
+    headers): a counter summary is valid while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "random_feature_amd", "csrc")
     for f in _PATH_SOURCES[kind]:
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        if f.endswith(".hip"):
+            data = data.split(_HOST_MARK)[0]
+        h.update(data)
     return h.hexdigest()[:16]
 
 

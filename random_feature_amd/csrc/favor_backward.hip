@@ -912,42 +912,37 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
-    FAVOR_TIMED("omega_frag", st);
-    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omf);
-    omegaT_frag_kernel<P><<<(unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omegaT_frag_kernel<P>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omt);
   }
   {
-    FAVOR_TIMED("reduce", st);
-    kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true><<<p.G_red, 64 * NWR, 0, st>>>(
-        k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true>, p.G_red, 64 * NWR, 0, st, k, v, omf, s.H,
+        s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
   }
   {
-    FAVOR_TIMED("combine", st);
-    combine_rows_kernel<DV, M, NWR><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
-        part, zpart, pmax, p.tpb, p.T_all, p.G_red, 1, srow, gmx);
+    launch("combine", combine_rows_kernel<DV, M, NWR>, (unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st, part, zpart,
+        pmax, p.tpb, p.T_all, p.G_red, 1, srow, gmx);
   }
   {
-    FAVOR_TIMED("bwd_q", st);
-    bwd_q_kernel<T, D, DV, M><<<p.G, 64 * NWB, 0, st>>>(q, dout, omf, omt, srow, s.H, s.L, p.tpb, p.T_all, p.G,
-                                                        grad_f32, dpart, dzpart, dq);
+    launch("bwd_q", bwd_q_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, q, dout, omf, omt, srow, s.H, s.L, p.tpb,
+        p.T_all, p.G, grad_f32, dpart, dzpart, dq);
   }
   {
-    FAVOR_TIMED("combine_d", st);
-    combine_rows_kernel<DV, M, NWB><<<(unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st>>>(
-        dpart, dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
+    launch("combine_d", combine_rows_kernel<DV, M, NWB>, (unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st, dpart,
+        dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
   }
   {
-    FAVOR_TIMED("bwd_k", st);
-    bwd_k_kernel<T, D, DV, M><<<p.G, 64 * NWB, 0, st>>>(k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb, p.T_all, p.G,
-                                                        nscale, sc * sc, grad_f32, dk, dv);
+    launch("bwd_k", bwd_k_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb,
+        p.T_all, p.G, nscale, sc * sc, grad_f32, dk, dv);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout, const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv,
-                           void* ws, hipStream_t st) {
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
+                           const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
+                           hipStream_t st) {
 #define X(D_, DV_, M_)                                                                                          \
   if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
     if (dtype == 0)                                                                                             \

@@ -549,44 +549,37 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   {
-    FAVOR_TIMED("omega_frag", st);
-    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omf);
   }
   {
-    FAVOR_TIMED("reduce", st);
     constexpr int NWR = RedSplit<M>::NW;
     if (kind == kPrf)
-      kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps,
-                                                                        inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
     else if (kind == kTrig)
-      kv_reduce_kernel<T, D, DV, M, kReduceRing, kTrig><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
-                                                                         eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kTrig>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
     else
-      kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G,
-                                                                         eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
   }
   {
-    FAVOR_TIMED("combine", st);
     // one thread per (value block, lane): every partial is requested in a single round
     constexpr int NBC = DV / 16 + 1;
-    combine_kernel<C, DV, M><<<(unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0, st>>>(
-        part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
+    launch("combine", combine_kernel<C, DV, M>, (unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0,
+        st, part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
   }
   {
-    FAVOR_TIMED("output", st);
     if (kind == kPrf)
-      q_output_kernel<T, D, DV, M, kPrf><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
-                                                                  eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
-                                                                  log2_m, out);
+      launch("output", q_output_kernel<T, D, DV, M, kPrf>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
+          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
     else if (kind == kTrig)
-      q_output_kernel<T, D, DV, M, kTrig><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
-                                                                   eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
-                                                                   log2_m, out);
+      launch("output", q_output_kernel<T, D, DV, M, kTrig>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
+          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
     else
-      q_output_kernel<T, D, DV, M, kRelu><<<p.G_q, 64 * NW, 0, st>>>(q, omf, sfr, s.H, Lq, p.tpb_q, p.T_all_q, p.G_q,
-                                                                   eps, inv_sqrt_m, out_f32, renorm, gmx, nscale,
-                                                                   log2_m, out);
+      launch("output", q_output_kernel<T, D, DV, M, kRelu>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
+          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
   }
   return hipGetLastError();
 }
@@ -629,9 +622,8 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
     attr_set = true;
   }
   {
-    FAVOR_TIMED("features", st);
-    features_kernel<T, D, M><<<(unsigned)(s.bh() * n_tiles), 256, lds, st>>>(
-        x, omega, s.H, s.L, kind, eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
+    launch("features", features_kernel<T, D, M>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H, s.L, kind,
+        eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
   }
   return hipGetLastError();
 }

@@ -421,34 +421,30 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   {
-    FAVOR_TIMED("omega_frag", st);
-    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omf);
   }
   {
-    FAVOR_TIMED("reduce", st);
     const int seg_tiles = p.seg_len / 32;
     if (kind == kPrf)
-      kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf><<<p.G, 64 * NWR, 0, st>>>(
-          k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
     else
-      kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu><<<p.G, 64 * NWR, 0, st>>>(
-          k, v, omf, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
   }
   {
-    FAVOR_TIMED("scan", st);
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    scan_kernel<DV, M><<<(unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st>>>(
-        part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final, z_final);
+    launch("scan", scan_kernel<DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st, part,
+        zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final, z_final);
   }
   {
-    FAVOR_TIMED("sweep", st);
     if (kind == kPrf)
-      sweep_kernel<T, D, DV, M, kPrf><<<p.G, 64 * NWR, 0, st>>>(q, k, v, omf, cpart, cz, cmax, s.H, s.L, p.seg_len,
-                                                                p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
+      launch("sweep", sweep_kernel<T, D, DV, M, kPrf>, p.G, 64 * NWR, 0, st, q, k, v, omf, cpart, cz, cmax, s.H, s.L,
+          p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
     else
-      sweep_kernel<T, D, DV, M, kRelu><<<p.G, 64 * NWR, 0, st>>>(q, k, v, omf, cpart, cz, cmax, s.H, s.L, p.seg_len,
-                                                                 p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
+      launch("sweep", sweep_kernel<T, D, DV, M, kRelu>, p.G, 64 * NWR, 0, st, q, k, v, omf, cpart, cz, cmax, s.H, s.L,
+          p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
   }
   return hipGetLastError();
 }

@@ -1525,53 +1525,43 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
-    FAVOR_TIMED("omega_frag", st);
-    omega_frag_kernel<P><<<(unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omf);
-    omegaT_pair_kernel<C><<<(unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st>>>(
+    launch("omega_frag", omegaT_pair_kernel<C>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omth, omtl);
   }
   {
-    FAVOR_TIMED("reduce", st);
-    kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true><<<f.G, 64 * NWR, 0, st>>>(
-        k, v, omf, s.H, s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32,
-        f.nseg);
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true>, f.G, 64 * NWR, 0, st, k, v, omf, s.H,
+        s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg);
   }
   {
-    FAVOR_TIMED("scan", st);
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    scan_kernel<DV, M><<<(unsigned)(s.bh() * ((NQ + 255) / 256)), 256, f.nseg * sizeof(float), st>>>(
-        part, zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr);
+    launch("scan", scan_kernel<DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, f.nseg * sizeof(float), st, part,
+        zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr);
   }
   {
-    FAVOR_TIMED("cbwd_fwd", st);
-    cbwd_fwd_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, cpart, cz, cmax, s.H, s.L, f.seg_len,
-                                                            f.nseg, nscale, lg, gam);
+    launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, cpart, cz, cmax, s.H,
+        s.L, f.seg_len, f.nseg, nscale, lg, gam);
   }
   {
-    FAVOR_TIMED("cbwd_q", st);
-    cbwd_q_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, omth, omtl, cpart, cz, cmax, lg, gam,
-                                                          s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq);
+    launch("cbwd_q", cbwd_q_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omth, omtl, cpart, cz,
+        cmax, lg, gam, s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq);
   }
   {
-    FAVOR_TIMED("cbwd_t", st);
-    cbwd_t_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, dout, omf, lg, gam, s.H, s.L, f.seg_len, f.nseg,
-                                                          trow);
+    launch("cbwd_t", cbwd_t_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, dout, omf, lg, gam, s.H, s.L, f.seg_len,
+        f.nseg, trow);
   }
   {
-    FAVOR_TIMED("rscan", st);
     const int per = M * NBC, nblk = (per + 255) / 256;
-    cbwd_rscan_kernel<<<(unsigned)(s.bh() * nblk), 256, 0, st>>>(trow, cmax, f.nseg, per, nblk);
+    launch("rscan", cbwd_rscan_kernel, (unsigned)(s.bh() * nblk), 256, 0, st, trow, cmax, f.nseg, per, nblk);
   }
   {
-    FAVOR_TIMED("cbwd_k", st);
-    cbwd_k_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, omth, omtl, trow, cmax, lg, gam, s.H,
-                                                          s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk);
+    launch("cbwd_k", cbwd_k_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omth, omtl, trow, cmax, lg,
+        gam, s.H, s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk);
   }
   {
-    FAVOR_TIMED("cbwd_v", st);
-    cbwd_v_kernel<T, D, DV, M><<<f.G, 64 * NWB, 0, st>>>(q, k, v, dout, omf, trow, cmax, lg, s.H, s.L, f.seg_len,
-                                                          f.nseg, nscale, grad_f32, dv);
+    launch("cbwd_v", cbwd_v_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, trow, cmax, lg, s.H, s.L,
+        f.seg_len, f.nseg, nscale, grad_f32, dv);
   }
   return hipGetLastError();
 }

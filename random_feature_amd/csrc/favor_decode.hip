@@ -318,6 +318,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
   if (sink) out[tid] = pf[0] + pf[1] + pf[2] + pf[3];
 }
 
+// ---------------------------------------------------------------- host side
 template <typename T, int D>
 static hipError_t run_decode(const T* q, const T* k, const T* v, const float* omega, float* S, float* z, int N, int H,
                              int dv, int m, int kind, float eps, const float* gate, const float* inw, float* out,
@@ -332,10 +333,8 @@ static hipError_t run_decode(const T* q, const T* k, const T* v, const float* om
   if (N == 0) return hipSuccess;
   const size_t n_grp = ((size_t)N + kDecodeSeqs - 1) / kDecodeSeqs;
   {
-    FAVOR_TIMED("decode", st);
-    decode_kernel<T, D><<<(unsigned)(n_grp * H), kDecodeThreads, lds, st>>>(
-        q, k, v, omega, S, z, N, H, dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, gate, inw, out,
-        kDecodeAhead, 0);
+    launch("decode", decode_kernel<T, D>, (unsigned)(n_grp * H), kDecodeThreads, lds, st, q, k, v, omega, S, z, N, H,
+        dv, m, kind, eps, inv_sqrt_m, wscale, nscale, log2_sqrt_m, gate, inw, out, kDecodeAhead, 0);
   }
   return hipGetLastError();
 }

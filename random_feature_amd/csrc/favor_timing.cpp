@@ -15,7 +15,6 @@ struct Rec {
 std::mutex g_mu;
 bool g_on = false;
 std::vector<Rec> g_recs;
-int g_open = -1;
 
 void clear_locked() {
   for (auto& r : g_recs) {
@@ -23,27 +22,25 @@ void clear_locked() {
     if (r.b) hipEventDestroy(r.b);
   }
   g_recs.clear();
-  g_open = -1;
 }
 }  // namespace
 
-void timing_mark_begin(const char* name, hipStream_t st) {
-  if (!g_on) return;
+bool timing_on() { return g_on; }
+
+bool timing_pair(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return false;
   Rec r;
   r.name = name;
-  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
-  hipEventRecord(r.a, st);
+  if (hipEventCreate(&r.a) != hipSuccess) return false;
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    hipEventDestroy(r.a);
+    return false;
+  }
   g_recs.push_back(r);
-  g_open = (int)g_recs.size() - 1;
-}
-
-void timing_mark_end(hipStream_t st) {
-  if (!g_on) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (g_open < 0) return;
-  hipEventRecord(g_recs[g_open].b, st);
-  g_open = -1;
+  *start = r.a;
+  *stop = r.b;
+  return true;
 }
 }  // namespace favor
 
