@@ -13,11 +13,12 @@ seeded inputs already resident in device memory:
   causal_backward_bf16 favor_causal_backward (dq, dk, dv) at causal_bf16's shape, bf16 gradients
   trig_bf16   favor_bidir with trigonometric features (FAVOR_TRIG) at bidir_bf16's shape
   bidir_fp32 / bidir_small  the fp32 parity workloads
-Prints one JSON line with whole-job throughput (tokens/s = B*H*L per second; for
-decode, head-tokens/s), the dominant kernel's roofline fraction (per-launch
-durations from HIP events recorded on the launch stream during a second pass of
-the same steps, right after the timed one), and the fp64 oracle timed on the
-host on a bounded sample.
+The step first runs untimed for --settle-ms (200 ms) so the GPU reaches its working
+clock, then W warm-up steps, then K timed steps. Prints one JSON line with
+whole-job throughput (tokens/s = B*H*L per second; for decode, head-tokens/s), the
+dominant kernel's roofline fraction (per-launch durations from start and stop events
+recorded in each kernel's own dispatch during a second pass of the same steps, right
+after the timed one), and the fp64 oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -211,6 +212,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--omega-mode", default="ortho_chi", choices=["ortho_chi", "iid", "ortho_sqrtd", "hyperbolic"],
                     help="random features: hyperbolic gives Lemma 1's hyperbolic features (m/2 vectors)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps for this long before the warm-up, so the GPU reaches its working clock")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="launch one elementwise copy of this many MiB first (counter calibration)")
     ap.add_argument("--rotate", type=int, default=4,
@@ -303,6 +306,14 @@ def main():
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    # settle: the GPU raises its clocks over the first tens of milliseconds of load (a 5-step warm-up leaves
+    # the timed steps 10-15 % slow), so the step runs untimed for settle_ms of wall-clock time first
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < a.settle_ms:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
     for _ in range(a.warmup):
         step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -372,6 +383,7 @@ def main():
     res = {
         "metric": METRIC if w.name == "bidir_bf16" else f"FAVOR+ {w.kind} {unit}, workload {w.name}",
         "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "settle": {"ms": a.settle_ms, "steps": settle_steps},
         "ms_per_step": total_ms / a.steps,
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
