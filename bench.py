@@ -96,9 +96,22 @@ _PATH_SOURCES = {
 _HOST_MARK = b"// ---------------------------------------------------------------- host side"
 
 
+def _code_only(data: bytes) -> bytes:
+    """The source without // comments, trailing blanks and empty lines (comments do not change a kernel)."""
+    out = []
+    for line in data.split(b"\n"):
+        k = line.find(b"//")
+        if k >= 0:
+            line = line[:k]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return b"\n".join(out)
+
+
 def _src_hash(kind: str) -> str:
     """Digest of the device code of one path's kernels (each .hip file up to its host-side section, and the
-    headers): a counter summary is valid while it matches."""
+    headers; comments left out): a counter summary is valid while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "random_feature_amd", "csrc")
     for f in _PATH_SOURCES[kind]:
@@ -106,7 +119,7 @@ def _src_hash(kind: str) -> str:
             data = fh.read()
         if f.endswith(".hip"):
             data = data.split(_HOST_MARK)[0]
-        h.update(data)
+        h.update(_code_only(data))
     return h.hexdigest()[:16]
 
 

@@ -463,7 +463,8 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 //       dPhi~^T[f][q] = S'[f][col] (A: St, hi + lo) x [g_q, -gamma_q] (B) + Phi'_K^T (A) x B with
 //       the masked scores B[key][q] = g_q . v_key - gamma_q (key <= q, hi + lo); then
 //       P = phi~ * dPhi~ = phi_Q * dPhi_Q as rows [query][feature] (hi + lo); St takes the chunk
-//   P   dq^T blocks = Omega'^T P / log2(e), every wave its share over all features
+//   P   dq^T blocks = Omega'^T P / log2(e), every wave its share over all features (the head's
+//       Omega'^T hi/lo fragments staged in LDS once per workgroup)
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
@@ -908,7 +909,8 @@ cbwd_rscan_kernel(float* __restrict__ trow, const float* __restrict__ cmax, int 
 //       dPhi''_K[key][f] = [V 1] (A, exact) x Rc (B, hi + lo) + B (A, hi + lo) x phi~ (B, hi + lo)
 //       P = phi'_K * dPhi''_K as rows [feature][key] (hi + lo), rho = its sum over the wave's
 //       features; Rc takes the chunk's queries
-//   B1  dk^T blocks = Omega'^T P / log2(e) - d^-1/2 k rho over all features
+//   B1  dk^T blocks = Omega'^T P / log2(e) - d^-1/2 k rho over all features (Omega'^T staged in
+//       LDS once per workgroup)
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
