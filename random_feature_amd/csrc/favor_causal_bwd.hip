@@ -192,7 +192,7 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
   using Rg = SweepRing<T, D, DV, NT, true>;
   using VR = Ring<T, D, DV, NT, true>;  // V and G rows share its layout
   __shared__ __attribute__((aligned(16))) unsigned char ring[2][Rg::SLOT];
-  __shared__ __attribute__((aligned(16))) C ubuf[NW * 32 * KPROW];  // the waves' Phi'_K transposes
+  __shared__ __attribute__((aligned(16))) C ubuf[NSPL][NW * 32 * KPROW];  // the waves' Phi'_K transposes (hi, lo)
   __shared__ __attribute__((aligned(16))) float osum[XOW ? 1 : 2][XOW ? 4 : 32 * OROW];
   __shared__ __attribute__((aligned(16))) float xo[XOW ? NW : 1][XOW ? XO : 4];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
@@ -338,28 +338,33 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         mma_split<NSPL>(o[cb][tb], sh, slo, bqh[tb], bql[tb]);
       }
     }
-    // ---- forward, intra-chunk scores over this wave's features: A^T[key][q] = Phi'_K Phi'_Q^T
+    // ---- forward, intra-chunk scores over this wave's features: A^T[key][q] = Phi'_K Phi'_Q^T, hi + lo
+    // (for peaked attention a few features carry a score, so their roundings do not average out)
     f32x4 sc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      C* ph = ubuf + w * 32 * KPROW;  // wave-private: [feature][key]
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        vec4<C> lo4, hi4;
+      for (int sp = 0; sp < NSPL; ++sp) {
+        C* ph = &ubuf[sp][w * 32 * KPROW];  // wave-private: [feature][key]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo4[i] = afh[hh][i];
-          hi4[i] = afh[hh][i + 4];
+        for (int hh = 0; hh < 2; ++hh) {
+          vec4<C> lo4, hi4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lo4[i] = sp == 0 ? afh[hh][i] : afl[hh][i];
+            hi4[i] = sp == 0 ? afh[hh][i + 4] : afl[hh][i + 4];
+          }
+          *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * KPROW + 4 * g) = lo4;
+          *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * KPROW + 16 + 4 * g) = hi4;
         }
-        *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * KPROW + 4 * g) = lo4;
-        *reinterpret_cast<vec4<C>*>(ph + (16 * hh + c) * KPROW + 16 + 4 * g) = hi4;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const vec8<C> ka = tr_read8<C>(ph, KPROW, 0, kb * 16, c, g);  // A [key][feature]
-        mma16(sc[kb][0], ka, bqh[0]);
-        mma16(sc[kb][1], ka, bqh[1]);
+        const vec8<C> kah = tr_read8<C>(&ubuf[0][w * 32 * KPROW], KPROW, 0, kb * 16, c, g);  // A [key][feature]
+        const vec8<C> kal = NSPL == 2 ? tr_read8<C>(&ubuf[NSPL - 1][w * 32 * KPROW], KPROW, 0, kb * 16, c, g) : kah;
+        mma_split<NSPL>(sc[kb][0], kah, kal, bqh[0], bql[0]);
+        mma_split<NSPL>(sc[kb][1], kah, kal, bqh[1], bql[1]);
       }
     }
     // ---- forward, intra term: o^T += [V 1]^T (A: value fragments) x masked A^T (B, hi + lo)
