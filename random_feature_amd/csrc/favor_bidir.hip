@@ -209,6 +209,10 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
     }
 
     // ---- phase 1: this wave's features of the tile
+    // The feature map is a long run of dependent vector work; raised issue priority lets this
+    // wave's VALU stream go first while the other wave of the SIMD fills the gaps with its
+    // MFMAs (dropped again before the copies of the next tile).
+    __builtin_amdgcn_s_setprio(1);
     f32x4 bias[2];
     float shf[2];  // the exponent shift of this lane's query row of each token half
     bool exact = false;
@@ -309,6 +313,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       if (g == 0) dpart[buf][tb][c][w] = dacc[0];
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // land, convert and norm this thread's chunk of tile t+1; copy its chunk of tile t+2
     wait_vmcnt<0>();
     Rg::template convert<P, KROW, kNormAbs>(ring[buf ^ 1], qs[buf ^ 1], qb[buf ^ 1], kQueryMargin, L);
@@ -350,6 +355,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) mma16(acc[cb][tt], sf[cb][fc], phi);
       }
+
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int nb = cb0 + cb * NW2;

@@ -425,7 +425,10 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
     if (next_new) load_om(nx.bh);  // Omega' of tile t+1's head (tile t's projection is done)
     wait_vmcnt<WAIT_NEXT>();
 
-    // stretch 1: projection of tile t+1 beside the feature map of tile t
+    // stretch 1: projection of tile t+1 beside the feature map of tile t, at raised issue
+    // priority so that the feature map's vector work of this wave goes ahead of the other
+    // wave's contraction, which fills the gaps
+    __builtin_amdgcn_s_setprio(1);
     project(pnext, buf ^ 1, next_new ? 0.f : runmax);
     // SPLIT (16-bit contraction type): each feature as the sum of two values of that type,
     // both contracted, so S_aug carries the features' fp32 precision
@@ -448,6 +451,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         af[fb][j] = to_t<C>(f);
         if constexpr (LO) al[fb][j] = to_t<C>(f - to_f(af[fb][j]));
       }
+    __builtin_amdgcn_s_setprio(0);
     // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
     // the piece: a filler slot into an unused buffer) and the next copies
     vec8<C> vf[NB];
