@@ -100,8 +100,12 @@ combine_rows_kernel(const float* __restrict__ part, const float* __restrict__ zp
   const int np = (int)(i_hi - i_lo + 1);
   const int wv = (fc * 32) / (FBP * 16);
   float gmax = -INFINITY;
-  if (scaled)
-    for (int k = 0; k < np * NWP; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NWP + bh) * NWP + k % NWP]);
+  if (scaled) {
+    // the np*NWP maxima of this (b,h) are contiguous: one load per lane, then a wave maximum
+    const float* pm = pmax + (size_t)(i_lo + bh) * NWP;
+    for (int k = threadIdx.x & 63; k < np * NWP; k += 64) gmax = fmaxf(gmax, pm[k]);
+    gmax = wave_max(gmax);
+  }
   if (gmx && fc == 0 && threadIdx.x == 0) gmx[bh] = scaled ? gmax : 0.f;
   float* out = rows + (size_t)bh * M * RC;
   for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {

@@ -55,8 +55,12 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
   const int wv = (fc * 32) / (FB * 16);  // the reducing wave that owned this chunk
   float gmax = -INFINITY;
   const bool scaled = kind != kRelu;  // ReLU features carry no key stabiliser
-  if (scaled)
-    for (int k = 0; k < np * NW; ++k) gmax = fmaxf(gmax, pmax[(size_t)(i_lo + k / NW + bh) * NW + k % NW]);
+  if (scaled) {
+    // the np*NW maxima of this (b,h) are contiguous: one load per lane, then a wave maximum
+    const float* pm = pmax + (size_t)(i_lo + bh) * NW;
+    for (int k = threadIdx.x & 63; k < np * NW; k += 64) gmax = fmaxf(gmax, pm[k]);
+    gmax = wave_max(gmax);
+  }
   if (fc == 0 && threadIdx.x == 0) gmx[bh] = scaled ? gmax : 0.f;  // the keys' common maximum
   for (int e = threadIdx.x; e < NB * 64; e += blockDim.x) {
     const int nb = e >> 6, lane = e & 63;
