@@ -233,8 +233,8 @@ def main():
                     help="also time with this many input sets in rotation (> the 256 MB MALL); 0 to skip")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
-              f"(the path shards over (b,h) pairs with no communication; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU; --gpus {a.gpus} is not supported "
+              f"(the path shards over (b,h) pairs with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import random_feature_amd as rf
