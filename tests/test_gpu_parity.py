@@ -94,6 +94,26 @@ def test_bidir_small(dtype, shape):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("B,H,L", [(8, 12, 96), (3, 100, 100), (1, 600, 40)])
+def test_bidir_piece_layouts(dtype, B, H, L):
+    """Both ways the key tiles are cut into pieces.
+
+    The reduction cuts the B*H*ceil(L/32) key tiles into at most 512 pieces, one partial per (piece, pair). 8x12x96
+    gives 96 pairs of 3 whole pieces. 300 pairs of 4 tiles and 600 pairs of 2 tiles both get 512 pieces, some of
+    which cover parts of two pairs and write a partial for each; the combine sums the right slots in every case.
+    """
+    d, dv, m = 64, 64, 256
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 11 * H + L)
+    om_dev, om = _omega(5, H, m, d)
+    for kind, eps in (("prf", 0.0), ("relu", 1e-3)):
+        ref = oracle.bidir(q, k, v, om, kind, eps)
+        out = rf.bidir(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind=kind, eps=eps, out_f32=True)
+        torch.cuda.synchronize()
+        e = rel_err(out, ref)
+        assert e < TOL[dtype], (B, H, L, dtype, kind, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("L", [1, 31, 33, 600, 1000])
 def test_bidir_lengths_and_relu(dtype, L):
     d, dv, m = 64, 64, 128
