@@ -213,9 +213,10 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
     }
 
     // ---- phase 1: this wave's features of the tile
-    // The feature map is a long run of dependent vector work; raised issue priority lets this
-    // wave's VALU stream go first while the other wave of the SIMD fills the gaps with its
-    // MFMAs (dropped again before the copies of the next tile).
+    // The feature map, and the conversion of the next tile after it, are long runs of dependent
+    // vector work; raised issue priority lets this wave's VALU stream go first while the other
+    // wave of the SIMD fills the gaps with its MFMAs (dropped again at the barrier before the
+    // contraction).
     __builtin_amdgcn_s_setprio(1);
     f32x4 bias[2];
     float shf[2];  // the exponent shift of this lane's query row of each token half
@@ -317,7 +318,6 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       if (g == 0) dpart[buf][tb][c][w] = dacc[0];
     }
 
-    __builtin_amdgcn_s_setprio(0);
     // land, convert and norm this thread's chunk of tile t+1; copy its chunk of tile t+2
     wait_vmcnt<0>();
     Rg::template convert<P, KROW, kNormAbs>(ring[buf ^ 1], qs[buf ^ 1], qb[buf ^ 1], kQueryMargin, L);
@@ -326,6 +326,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       Rg::issue(Q, nullptr, L, ahead.bh, ahead.tok0(), live, ring0 + buf * Rg::SLOT);
       if (live) ahead.next();
     }
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
 
     // ---- phase 2: this wave's value columns over all features
