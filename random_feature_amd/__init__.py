@@ -99,13 +99,70 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, ndim: int):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _need(t: torch.Tensor, name: str, ndim: int, shape=None, dtype=None):
+    """Rank, then (when given) exact shape and dtype, then contiguity of one argument. The C ABI sees only
+    pointers and the sizes taken from q, so these checks are what keeps every kernel read and write inside the
+    caller's buffers. Device residence is checked after every argument's structure (_resident)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _resident(**named):
+    """Every named tensor (None: absent) is a device tensor, all on one device."""
+    devs = set()
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
+def _check_seq(q, k, v, omega, cross: bool = False, resident: bool = True):
+    """q [B,H,Lq,d], k [B,H,Lk,d], v [B,H,Lk,dv] of one dtype (fp32 or bf16), Lq = Lk unless cross;
+    omega fp32 [H,m,d]. Returns (B, H, Lq, Lk, d, dv, m)."""
+    _need(q, "q", 4)
+    _dtype_code(q)
+    B, H, Lq, d = q.shape
+    _need(k, "k", 4, dtype=q.dtype)
+    Lk = k.shape[2]
+    if not cross and Lk != Lq:
+        raise ValueError(f"k must have the length of q ({Lq}), got {Lk}")
+    _need(k, "k", 4, shape=(B, H, Lk, d), dtype=q.dtype)
+    _need(v, "v", 4, dtype=q.dtype)
+    dv = v.shape[-1]
+    _need(v, "v", 4, shape=(B, H, Lk, dv), dtype=q.dtype)
+    _need(omega, "omega", 3, dtype=torch.float32)
+    m = omega.shape[1]
+    _need(omega, "omega", 3, shape=(H, m, d), dtype=torch.float32)
+    if resident:
+        _resident(q=q, k=k, v=v, omega=omega)
+    return B, H, Lq, Lk, d, dv, m
+
+
+def _check_ws(ws, device, need: int):
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous() or not ws.is_cuda or ws.device != device:
+        raise ValueError("ws must be a contiguous device tensor on the inputs' device")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"ws holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws.numel() * ws.element_size()
+
+
+def _check_out(out, name, shape, dtype, device):
+    _need(out, name, len(shape), shape=shape, dtype=dtype)
+    _resident(**{name: out})
+    if out.device != device:
+        raise ValueError(f"{name} must be on {device}")
 
 
 def _kind(kind) -> int:
@@ -137,11 +194,11 @@ def workspace_size(causal: bool, B, H, L, d, dv, m, dtype: torch.dtype) -> int:
 
 
 def workspace(causal: bool, q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) -> torch.Tensor:
+    """Device scratch for bidir()/causal() (k's length for cross attention), reusable across calls of that shape."""
     B, H, L, d = q.shape
     n = workspace_size(causal, B, H, L, d, v.shape[-1], omega.shape[1], q.dtype)
-    if n == 0:
-        raise FavorError("favor_workspace_size", 1)
-    return torch.empty(n, dtype=torch.uint8, device=q.device)
+    # 0: arguments the library rejects; the entry point itself then reports which status applies
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
 def backward_workspace(q: torch.Tensor, v: torch.Tensor, omega: torch.Tensor) -> torch.Tensor:
@@ -165,9 +222,12 @@ def causal_backward_workspace(q: torch.Tensor, v: torch.Tensor, omega: torch.Ten
 def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0):
     """phi [B,H,L,m] and logscale [B,H,L] with phi_true = phi * exp(logscale)."""
     _need(x, "x", 4)
-    _need(omega, "omega", 3)
+    _dtype_code(x)
     B, H, L, d = x.shape
+    _need(omega, "omega", 3, dtype=torch.float32)
     m = omega.shape[1]
+    _need(omega, "omega", 3, shape=(H, m, d), dtype=torch.float32)
+    _resident(x=x, omega=omega)
     phi = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
     ls = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
     _check("favor_features",
@@ -178,42 +238,33 @@ def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0)
 
 def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, ws=None, out=None):
     """Bidirectional FAVOR+ (Performer equation 4). Returns out [B,H,L,dv]."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, 4)
-    _need(omega, "omega", 3)
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
-    m = omega.shape[1]
-    if ws is None:
-        ws = workspace(False, q, v, omega)
-    if out is None:
-        out = torch.empty((B, H, L, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
-    _check("favor_bidir",
-           _lib.favor_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
-                            float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(ws), ws.numel(),
-                            ctypes.c_void_p(_stream(q.device))))
-    return out
+    _check_seq(q, k, v, omega)
+    return bidir_cross(q, k, v, omega, kind=kind, eps=eps, renormalize=True, out_f32=out_f32, ws=ws, out=out,
+                       _fn="favor_bidir")
 
 
 def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool = True, out_f32: bool = False,
-                ws=None, out=None):
+                ws=None, out=None, _fn="favor_bidir_cross"):
     """Bidirectional FAVOR+ between q [B,H,Lq,d] and k [B,H,Lk,d], v [B,H,Lk,dv]; without renormalisation the
     output is phi(q).S in canonical feature scale. Returns out [B,H,Lq,dv]."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, 4)
-    _need(omega, "omega", 3)
-    B, H, Lq, d = q.shape
-    Lk = k.shape[2]
-    dv = v.shape[-1]
-    m = omega.shape[1]
+    B, H, Lq, Lk, d, dv, m = _check_seq(q, k, v, omega, cross=True)
+    need = workspace_size(False, B, H, Lk, d, dv, m, q.dtype)
     if ws is None:
         ws = workspace(False, k, v, omega)
+    ws_bytes = _check_ws(ws, q.device, need)
+    odt = torch.float32 if out_f32 else q.dtype
     if out is None:
-        out = torch.empty((B, H, Lq, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
-    _check("favor_bidir_cross",
-           _lib.favor_bidir_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, Lq, Lk, d, dv, m, _dtype_code(q),
-                                  _kind(kind), float(eps), 1 if renormalize else 0, 1 if out_f32 else 0, _ptr(out),
-                                  _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
+        out = torch.empty((B, H, Lq, dv), dtype=odt, device=q.device)
+    _check_out(out, "out", (B, H, Lq, dv), odt, q.device)
+    st = ctypes.c_void_p(_stream(q.device))
+    if _fn == "favor_bidir":
+        r = _lib.favor_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, Lq, d, dv, m, _dtype_code(q),
+                             _kind(kind), float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(ws), ws_bytes, st)
+    else:
+        r = _lib.favor_bidir_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, Lq, Lk, d, dv, m, _dtype_code(q),
+                                   _kind(kind), float(eps), 1 if renormalize else 0, 1 if out_f32 else 0,
+                                   _ptr(out), _ptr(ws), ws_bytes, st)
+    _check(_fn, r)
     return out
 
 
@@ -224,14 +275,14 @@ def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=
 
 
 def _backward(fn, wsfn, q, k, v, omega, dout, kind, grad_f32, ws, out):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
-        _need(t, n, 4)
-    _need(omega, "omega", 3)
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
-    m = omega.shape[1]
+    B, H, L, _, d, dv, m = _check_seq(q, k, v, omega, resident=False)
+    _need(dout, "dout", 4, shape=(B, H, L, dv), dtype=q.dtype)
+    _resident(q=q, k=k, v=v, omega=omega, dout=dout)
     if ws is None:
         ws = wsfn(q, v, omega)
+    sz = (_lib.favor_backward_workspace_size if fn == "favor_bidir_backward"
+          else _lib.favor_causal_backward_workspace_size)
+    ws_bytes = _check_ws(ws, q.device, int(sz(B, H, L, d, dv, m, _dtype_code(q))))
     gdt = torch.float32 if grad_f32 else q.dtype
     if out is None:
         dq = torch.empty((B, H, L, d), dtype=gdt, device=q.device)
@@ -240,11 +291,10 @@ def _backward(fn, wsfn, q, k, v, omega, dout, kind, grad_f32, ws, out):
     else:
         dq, dk, dvv = out
         for t, n, last in ((dq, "dq", d), (dk, "dk", d), (dvv, "dv", dv)):
-            if tuple(t.shape) != (B, H, L, last) or t.dtype != gdt or not t.is_contiguous():
-                raise ValueError(f"{n}: expected a contiguous {gdt} tensor of shape {(B, H, L, last)}")
+            _check_out(t, n, (B, H, L, last), gdt, q.device)
     _check(fn, getattr(_lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv, m,
                                  _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk), _ptr(dvv),
-                                 _ptr(ws), ws.numel(), ctypes.c_void_p(_stream(q.device))))
+                                 _ptr(ws), ws_bytes, ctypes.c_void_p(_stream(q.device))))
     return dq, dk, dvv
 
 
@@ -258,37 +308,50 @@ def causal_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws
 def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,
            ws=None, out=None):
     """Causal FAVOR+ (Performer appendix B.1). Returns out, or (out, S_final, z_final) in canonical scale."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, 4)
-    _need(omega, "omega", 3)
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
-    m = omega.shape[1]
+    B, H, L, _, d, dv, m = _check_seq(q, k, v, omega)
+    need = workspace_size(True, B, H, L, d, dv, m, q.dtype)
     if ws is None:
         ws = workspace(True, q, v, omega)
+    ws_bytes = _check_ws(ws, q.device, need)
+    odt = torch.float32 if out_f32 else q.dtype
     if out is None:
-        out = torch.empty((B, H, L, dv), dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+        out = torch.empty((B, H, L, dv), dtype=odt, device=q.device)
+    _check_out(out, "out", (B, H, L, dv), odt, q.device)
     S = z = None
     if return_state:
         S = torch.empty((B, H, m, dv), dtype=torch.float32, device=q.device)
         z = torch.empty((B, H, m), dtype=torch.float32, device=q.device)
     _check("favor_causal",
            _lib.favor_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
-                             float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(S), _ptr(z), _ptr(ws), ws.numel(),
+                             float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(S), _ptr(z), _ptr(ws), ws_bytes,
                              ctypes.c_void_p(_stream(q.device))))
     return (out, S, z) if return_state else out
 
 
+def _check_decode(q, k, v, omega, S, z, out):
+    """q, k [N,H,d] and v [N,H,dv] of one dtype; omega fp32 [H,m,d]; S fp32 [N,H,m,dv]; z fp32 [N,H,m];
+    out fp32 [N,H,dv] if given. Returns (N, H, d, dv, m)."""
+    _need(q, "q", 3)
+    _dtype_code(q)
+    N, H, d = q.shape
+    _need(k, "k", 3, shape=(N, H, d), dtype=q.dtype)
+    _need(v, "v", 3, dtype=q.dtype)
+    dv = v.shape[-1]
+    _need(v, "v", 3, shape=(N, H, dv), dtype=q.dtype)
+    _need(omega, "omega", 3, dtype=torch.float32)
+    m = omega.shape[1]
+    _need(omega, "omega", 3, shape=(H, m, d), dtype=torch.float32)
+    _need(S, "S", 4, shape=(N, H, m, dv), dtype=torch.float32)
+    _need(z, "z", 3, shape=(N, H, m), dtype=torch.float32)
+    if out is not None:
+        _need(out, "out", 3, shape=(N, H, dv), dtype=torch.float32)
+    return N, H, d, dv, m
+
+
 def decode(q, k, v, omega, S, z, kind="prf", eps: float = 0.0, out=None):
     """One decode step: q,k [N,H,d], v [N,H,dv]; S [N,H,m,dv], z [N,H,m] updated in place. Returns out [N,H,dv]."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, 3)
-    _need(S, "S", 4)
-    _need(z, "z", 3)
-    _need(omega, "omega", 3)
-    N, H, d = q.shape
-    dv = v.shape[-1]
-    m = omega.shape[1]
+    N, H, d, dv, m = _check_decode(q, k, v, omega, S, z, out)
+    _resident(q=q, k=k, v=v, omega=omega, S=S, z=z, out=out)
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
     _check("favor_decode",
@@ -300,19 +363,11 @@ def decode(q, k, v, omega, S, z, kind="prf", eps: float = 0.0, out=None):
 def decode_gated(q, k, v, omega, S, z, gate, in_weight=None, kind="prf", eps: float = 0.0, out=None):
     """One gated decode step: S = g S + w phi(k) v^T, z = g z + w phi(k) with gate g and optional input weight w
     (fp32 [N,H], device); otherwise as decode(). Returns out [N,H,dv]."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, 3)
-    _need(S, "S", 4)
-    _need(z, "z", 3)
-    _need(omega, "omega", 3)
-    for t, n in ((gate, "gate"), (in_weight, "in_weight")):
-        if t is not None:
-            _need(t, n, 2)
-            if t.dtype != torch.float32:
-                raise ValueError(f"{n} must be float32")
-    N, H, d = q.shape
-    dv = v.shape[-1]
-    m = omega.shape[1]
+    N, H, d, dv, m = _check_decode(q, k, v, omega, S, z, out)
+    _need(gate, "gate", 2, shape=(N, H), dtype=torch.float32)
+    if in_weight is not None:
+        _need(in_weight, "in_weight", 2, shape=(N, H), dtype=torch.float32)
+    _resident(q=q, k=k, v=v, omega=omega, S=S, z=z, out=out, gate=gate, in_weight=in_weight)
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
     _check("favor_decode_gated",

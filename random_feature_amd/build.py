@@ -1,6 +1,6 @@
 """Build libfavor.so in-tree for gfx950 (MI355X).
 
-    python random_feature_amd/build.py [--jobs N] [--verbose]
+    python random_feature_amd/build.py [--jobs N] [--verbose] [--tools]
 
 (Run it as a script: importing the package itself needs the built library.)
 
@@ -8,7 +8,9 @@ Each HIP source is compiled separately (in parallel) with hipcc for
 --offload-arch=gfx950; the host-side Omega generator is compiled with g++
 without floating-point contraction or fast-math (its fp64 arithmetic must
 round exactly as written). Objects go to random_feature_amd/_build/, the
-shared library to random_feature_amd/libfavor.so.
+shared library to random_feature_amd/libfavor.so. --tools also builds the
+pipe-rate microbenchmark (random_feature_amd/tools/rates.hip) as
+random_feature_amd/_build/rates; it is measurement tooling, not part of the library.
 """
 from __future__ import annotations
 
@@ -55,7 +57,7 @@ def _run(cmd, verbose):
     return r.stdout
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, tools: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     cmds = []
@@ -82,18 +84,27 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
-    # the pipe-rate microbenchmark (exp, FMA, MFMA issue rates on the device)
-    _run([hipcc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], os.path.join(ROOT, "random_feature_amd", "tools", "rates.hip"),
-          "-o", os.path.join(BUILD, "rates")], verbose)
+    if tools:
+        build_tools(verbose)
     return LIB
+
+
+def build_tools(verbose: bool = False) -> str:
+    """The pipe-rate microbenchmark (exp, FMA and MFMA issue rates on the device), a standalone program."""
+    os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "rates")
+    _run([_hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"],
+          os.path.join(ROOT, "random_feature_amd", "tools", "rates.hip"), "-o", exe], verbose)
+    return exe
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--tools", action="store_true", help="also build the pipe-rate microbenchmark")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.tools))
 
 
 if __name__ == "__main__":

@@ -625,13 +625,11 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
   const int tpw = 256;
   const int n_tiles = (s.L + tpw - 1) / tpw;
   const size_t lds = (size_t)(M / 16) * DC * 512 * sizeof(P);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&features_kernel<T, D, M>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per instantiation (a function-local static is initialised exactly once, also under concurrent
+  // first calls)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&features_kernel<T, D, M>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
   {
     launch("features", features_kernel<T, D, M>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H, s.L, kind,
         eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
