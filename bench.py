@@ -93,9 +93,6 @@ _PATH_SOURCES = {
 }
 
 
-_HOST_MARK = b"// ---------------------------------------------------------------- host side"
-
-
 def _code_only(data: bytes) -> bytes:
     """The source without // comments, trailing blanks and empty lines (comments do not change a kernel)."""
     out = []
@@ -110,16 +107,14 @@ def _code_only(data: bytes) -> bytes:
 
 
 def _src_hash(kind: str) -> str:
-    """Digest of the device code of one path's kernels (each .hip file up to its host-side section, and the
-    headers; comments left out): a counter summary is valid while it matches."""
+    """Digest of the code one path's kernels are built and launched from (the .hip files whole, launch
+    plans and launchers included, and the headers; comments left out): a counter summary is valid while it
+    matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "random_feature_amd", "csrc")
     for f in _PATH_SOURCES[kind]:
         with open(os.path.join(csrc, f), "rb") as fh:
-            data = fh.read()
-        if f.endswith(".hip"):
-            data = data.split(_HOST_MARK)[0]
-        h.update(_code_only(data))
+            h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 
@@ -215,37 +210,15 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
                            f"BLAS threads, median of 3 passes of {dt:.1f} s")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 50; decode workloads: the workload's 1000 steps)")
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--omega-mode", default="ortho_chi", choices=["ortho_chi", "iid", "ortho_sqrtd", "hyperbolic"],
-                    help="random features: hyperbolic gives Lemma 1's hyperbolic features (m/2 vectors)")
-    ap.add_argument("--settle-ms", type=float, default=200.0,
-                    help="untimed steps for this long before the warm-up, so the GPU reaches its working clock")
-    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
-                    help="launch one elementwise copy of this many MiB first (counter calibration)")
-    ap.add_argument("--rotate", type=int, default=4,
-                    help="also time with this many input sets in rotation (> the 256 MB MALL); 0 to skip")
-    a = ap.parse_args()
-    if a.gpus != 1:
-        print(f"bench.py: runs on one GPU; --gpus {a.gpus} is not supported "
-              f"(the path shards over (b,h) pairs with no communication between GPUs)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
+    """Time one workload (see the module docstring) and return its result fields."""
     import random_feature_amd as rf
-    w = workloads.WORKLOADS[a.workload]
-    if a.steps is None:
-        a.steps = w.steps if w.kind in ("decode", "decode_gated") else 50
+    w = workloads.WORKLOADS[wname]
+    steps = a.steps if a.steps is not None else (w.steps if w.kind in ("decode", "decode_gated") else 50)
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     dt = w.torch_dtype
     fkind = w.feature
-    om = rf.make_omega(w.seed, w.H, w.m, w.d, "trig_pairs" if fkind == "trig" else a.omega_mode, device=dev)
+    om = rf.make_omega(w.seed, w.H, w.m, w.d, "trig_pairs" if fkind == "trig" else omega_mode, device=dev)
 
     if w.kind in ("decode", "decode_gated"):
         S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
@@ -260,7 +233,7 @@ def main():
             S[s0:s0 + n] = S_
             z[s0:s0 + n] = z_
             del kp, vp
-        n_steps = a.warmup + a.steps
+        n_steps = a.warmup + steps
         qs, ks, vs = workloads.make_decode_steps(w, dev, steps=n_steps)
         out = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
         it = iter(range(10 ** 9))
@@ -268,7 +241,7 @@ def main():
             gs = workloads.make_gates((n_steps, w.B, w.H), w.seed, device=dev)
             wts = 1.0 - gs
 
-        def step(i=None):
+        def step():
             t = next(it) % n_steps
             if w.kind == "decode_gated":
                 rf.decode_gated(qs[t], ks[t], vs[t], om, S, z, gs[t], wts[t], out=out)
@@ -294,7 +267,7 @@ def main():
             ws = wsfn(q, v, om)
             grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
 
-            def step(i=None):
+            def step():
                 qq, kk, vv = sets[cur[0]]
                 bfn(qq, kk, vv, om, douts[cur[0]], ws=ws, out=grads)
         else:
@@ -302,12 +275,16 @@ def main():
             out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
             fn = {"bidir": rf.bidir, "cross": rf.bidir_cross, "causal": rf.causal}[w.kind]
 
-            def step(i=None):
+            def step():
                 qq, kk, vv = sets[cur[0]]
                 fn(qq, kk, vv, om, kind=fkind, ws=ws, out=out)
         tokens_per_step = w.B * w.H * w.Lq_eff   # output (query) tokens
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4
+
+    def rotate(i):
+        if sets is not None:
+            cur[0] = i % len(sets)
 
     if a.copy_calib:
         # a plain elementwise copy of known size: hardware counters of the same run are
@@ -323,24 +300,40 @@ def main():
     # the timed steps 10-15 % slow), so the step runs untimed for settle_ms of wall-clock time first
     settle_steps, t_settle = 0, time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < a.settle_ms:
-        for _ in range(8):
+        for i in range(8):
+            rotate(i)
             step()
         settle_steps += 8
         torch.cuda.synchronize()
-    for _ in range(a.warmup):
+    for i in range(a.warmup):
+        rotate(i)
         step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # the timed steps run uninstrumented; a second pass records every kernel's own events
+    # the timed steps run uninstrumented, each on the next of the rotating input sets (together larger than
+    # the 256 MB last-level cache, so every step reads its inputs from HBM); later passes are instrumented
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(a.steps):
+    for i in range(steps):
+        rotate(i)
         step()
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
+    # the same steps on one input set only (it stays resident in the last-level cache): the warm figure
+    warm_ms = None
+    if sets is not None and len(sets) > 1:
+        rotate(0)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_ms = e0.elapsed_time(e1)
     # per-step distribution (a separate pass, an event pair around every step)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for p0, p1 in pairs:
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (p0, p1) in enumerate(pairs):
+        rotate(i)
         p0.record()
         step()
         p1.record()
@@ -350,7 +343,8 @@ def main():
     def pct(q):
         return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
     rf.timing_enable(True)
-    for _ in range(a.steps):
+    for i in range(steps):
+        rotate(i)
         step()
     torch.cuda.synchronize()
     recs = rf.timing_read()
@@ -379,39 +373,92 @@ def main():
                         mfma_tflops=round(tfl, 2), mfma_frac=round(tfl / peak_f, 4),
                         hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
                         algorithmic_flops=flops, algorithmic_bytes=nbytes)
+    # the whole step against the peaks: the workload's algorithmic flops and bytes (every token-head's work
+    # once, as _kernel_work counts them) over the measured time per step
+    step_flops = step_bytes = 0
+    for name in {"bidir": ("reduce", "output"), "cross": ("reduce", "output"), "causal": ("sweep",),
+                 "decode": ("decode",), "decode_gated": ("decode",)}.get(w.kind, ()):
+        f_, b_ = _kernel_work(w, name, out_bytes)
+        step_flops += f_
+        step_bytes += b_
+    whole = None
+    if step_flops:
+        t_step = total_ms * 1e-3 / steps
+        peak_f = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        whole = dict(algorithmic_flops=step_flops, algorithmic_bytes=step_bytes,
+                     mfma_frac=round(step_flops / t_step / 1e12 / peak_f, 4),
+                     hbm_frac=round(step_bytes / t_step / 1e9 / PEAK_HBM_GBS, 4))
 
-    cold = None
-    if sets is not None and len(sets) > 1:
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(a.steps):
-            cur[0] = i % len(sets)
-            step()
-        e1.record()
-        torch.cuda.synchronize()
-        cold = tokens_per_step * a.steps / (e0.elapsed_time(e1) * 1e-3)
-        cur[0] = 0
-
-    value = tokens_per_step * a.steps / (total_ms * 1e-3)
     res = {
         "metric": METRIC if w.name == "bidir_bf16" else f"FAVOR+ {w.kind} {unit}, workload {w.name}",
-        "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "settle": {"ms": a.settle_ms, "steps": settle_steps},
-        "ms_per_step": total_ms / a.steps,
+        "value": tokens_per_step * steps / (total_ms * 1e-3), "unit": unit, "n_gpus": 1, "steps": steps,
+        "warmup": a.warmup, "settle": {"ms": a.settle_ms, "steps": settle_steps},
+        "ms_per_step": total_ms / steps,
         "ms_per_step_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d, "dv": w.dv,
-                   "m": w.m, "feature_map": fkind if a.omega_mode != "hyperbolic" else "prf_hyperbolic",
-                   "omega": "trig_pairs" if fkind == "trig" else a.omega_mode, "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
+        "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d,
+                   "dv": w.dv, "m": w.m, "feature_map": fkind if omega_mode != "hyperbolic" else "prf_hyperbolic",
+                   "omega": "trig_pairs" if fkind == "trig" else omega_mode,
+                   "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
         "roofline": roofline,
+        "whole_step": whole,
     }
-    if cold is not None:
-        res["value_rotating_inputs"] = cold
-        res["rotating_input_sets"] = len(sets)
+    if sets is not None:
+        res["inputs"] = (f"{len(sets)} input sets in rotation, one per step"
+                         if len(sets) > 1 else "one input set, reused every step")
+        if warm_ms is not None:
+            res["value_warm_inputs"] = tokens_per_step * steps / (warm_ms * 1e-3)
+            res["ms_per_step_warm_inputs"] = warm_ms / steps
+    else:
+        res["inputs"] = f"{w.steps} decode steps' inputs pre-generated in device memory, the state updated in place"
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+# the workloads whose figures the default (headline) line also carries
+COMPANIONS = ("causal_bf16", "decode_bf16")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; decode workloads: the workload's 1000 steps)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-companions", action="store_true",
+                    help="headline workload only (without the causal and decode figures)")
+    ap.add_argument("--omega-mode", default="ortho_chi", choices=["ortho_chi", "iid", "ortho_sqrtd", "hyperbolic"],
+                    help="random features: hyperbolic gives Lemma 1's hyperbolic features (m/2 vectors)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps for this long before the warm-up, so the GPU reaches its working clock")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="launch one elementwise copy of this many MiB first (counter calibration)")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="input sets in rotation, one per timed step (together larger than the 256 MB "
+                         "last-level cache); 1 reuses one set")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: runs on one GPU; --gpus {a.gpus} is not supported "
+              f"(the path shards over (b,h) pairs with no communication between GPUs)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    res = measure(a, a.workload, a.omega_mode)
+    if a.workload == "bidir_bf16" and not a.no_companions:
+        for cname in COMPANIONS:
+            a2 = argparse.Namespace(**vars(a))
+            a2.steps = None  # each companion at its own default step count
+            a2.copy_calib = 0
+            c = measure(a2, cname)
+            res[cname] = {k: c[k] for k in ("metric", "value", "unit", "steps", "ms_per_step",
+                                            "ms_per_step_p10_p50_p90", "config", "kernels_us", "roofline",
+                                            "whole_step", "inputs")}
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, omega_mode=a.omega_mode)
+        res["cpu_baseline"] = cpu_baseline(workloads.WORKLOADS[a.workload], omega_mode=a.omega_mode)
     print(json.dumps(res), flush=True)
 
 
