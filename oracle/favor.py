@@ -35,19 +35,21 @@ import math
 import numpy as np
 
 
-def _f64(x) -> np.ndarray:
+def _f64(x, work_dtype=np.float64) -> np.ndarray:
+    """x widened exactly to fp64 (then rounded to work_dtype when that is narrower)."""
     if hasattr(x, "detach"):  # torch tensor (possibly bf16): widen exactly
         import torch
-        return x.detach().to("cpu").to(torch.float64).numpy()
-    return np.asarray(x, dtype=np.float64)
+        x = x.detach().to("cpu").to(torch.float64).numpy()
+    return np.asarray(np.asarray(x, dtype=np.float64), dtype=work_dtype)
 
 
-def features(x, omega, kind: str = "prf", eps: float = 0.0) -> np.ndarray:
+def features(x, omega, kind: str = "prf", eps: float = 0.0, work_dtype=np.float64) -> np.ndarray:
     """phi(x) for raw queries or keys x [B,H,L,d] and omega [H,m,d] -> [B,H,L,m] (fp64);
     kind "hyperbolic": the 2m hyperbolic features of the m rows (features_hyperbolic); kind "trig": the 2m
-    trigonometric features of the m rows (features_trig)."""
-    x = _f64(x)
-    om = _f64(omega)
+    trigonometric features of the m rows (features_trig). work_dtype = np.float32 evaluates the PRF and ReLU
+    maps in fp32 instead (the same formulas; it shows what that precision loses, it is no reference)."""
+    x = _f64(x, work_dtype)
+    om = _f64(omega, work_dtype)
     d = x.shape[-1]
     m = om.shape[-2]
     xs = x * (float(d) ** -0.25)
@@ -115,15 +117,15 @@ def bidir(q, k, v, omega, kind: str = "prf", eps: float = 0.0, renormalize: bool
     return np.einsum("...lm,...me->...le", features(q, omega, kind, eps), S)
 
 
-def _feature_backward(x, omega, phi, dphi, kind: str):
+def _feature_backward(x, omega, phi, dphi, kind: str, work_dtype=np.float64):
     """d loss / d x (raw x) from d loss / d phi for the feature map of `features`.
 
     PRF: phi = exp(w.xs - |xs|^2/2)/sqrt(m), xs = d^-1/4 x, so
         d/dxs = Omega^T (phi * dphi) - xs * sum_r phi_r dphi_r;
     ReLU: phi = max(w.xs, 0)/sqrt(m) + eps, so d/dxs = Omega^T (1[w.xs > 0]/sqrt(m) * dphi).
     The chain rule through xs = d^-1/4 x multiplies by d^-1/4."""
-    x = _f64(x)
-    om = _f64(omega)
+    x = _f64(x, work_dtype)
+    om = _f64(omega, work_dtype)
     d = x.shape[-1]
     m = om.shape[-2]
     s = float(d) ** -0.25
@@ -139,18 +141,19 @@ def _feature_backward(x, omega, phi, dphi, kind: str):
     return g * s
 
 
-def bidir_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
+def bidir_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0, work_dtype=np.float64):
     """Gradients of equation 4's output out = (Phi_Q S) / (Phi_Q z) (S = Phi_K^T V, z = Phi_K^T 1) with respect
     to the raw q, k and v, for the upstream gradient dout [B,H,L,dv]. By the chain rule, with N = Phi_Q S and
     D = Phi_Q z:
         dN = dout / D,  dD = -(dout . out) / D,
         dPhi_Q = dN S^T + dD z^T,  dS = Phi_Q^T dN,  dz = Phi_Q^T dD,
         dPhi_K = V dS^T + 1 dz^T,  dV = Phi_K dS,
-    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64."""
-    pq = features(q, omega, kind, eps)
-    pk = features(k, omega, kind, eps)
-    v = _f64(v)
-    g = _f64(dout)
+    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64 (work_dtype = np.float32:
+    every step in fp32 instead, to show what that precision loses; no reference)."""
+    pq = features(q, omega, kind, eps, work_dtype)
+    pk = features(k, omega, kind, eps, work_dtype)
+    v = _f64(v, work_dtype)
+    g = _f64(dout, work_dtype)
     S = np.einsum("...lm,...le->...me", pk, v)
     z = np.sum(pk, axis=-2)
     N = np.einsum("...lm,...me->...le", pq, S)
@@ -163,7 +166,8 @@ def bidir_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
     dz = np.einsum("...lm,...l->...m", pq, dD)
     dpk = np.einsum("...le,...me->...lm", v, dS) + dz[..., None, :]
     dv = np.einsum("...lm,...me->...le", pk, dS)
-    return (_feature_backward(q, omega, pq, dpq, kind), _feature_backward(k, omega, pk, dpk, kind), dv)
+    return (_feature_backward(q, omega, pq, dpq, kind, work_dtype), _feature_backward(k, omega, pk, dpk, kind, work_dtype),
+            dv)
 
 
 def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bool = False):
@@ -187,7 +191,7 @@ def causal(q, k, v, omega, kind: str = "prf", eps: float = 0.0, return_state: bo
     return out
 
 
-def causal_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
+def causal_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0, work_dtype=np.float64):
     """Gradients of the causal output (appendix B.1, equation 11: out_i = (Phi_Q,i . S_i) / (Phi_Q,i . z_i)
     with the prefix sums S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j)) with respect to the raw q,
     k and v, for the upstream gradient dout. By the chain rule, position by position:
@@ -195,11 +199,12 @@ def causal_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
     and since S_i and z_i sum the keys j <= i, key j collects the suffix sums over i >= j:
         R_j = sum_{i>=j} Phi_Q,i dN_i^T,  r_j = sum_{i>=j} Phi_Q,i dD_i,
         dPhi_K,j = R_j v_j + r_j,  dV_j = R_j^T Phi_K,j,
-    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64."""
-    pq = features(q, omega, kind, eps)
-    pk = features(k, omega, kind, eps)
-    v = _f64(v)
-    g = _f64(dout)
+    then through the feature map (_feature_backward). Returns (dq, dk, dv), fp64 (work_dtype as in
+    bidir_backward)."""
+    pq = features(q, omega, kind, eps, work_dtype)
+    pk = features(k, omega, kind, eps, work_dtype)
+    v = _f64(v, work_dtype)
+    g = _f64(dout, work_dtype)
     # prefix states S_i [B,H,L,m,dv], z_i [B,H,L,m] (inclusive)
     S = np.cumsum(pk[..., :, None] * v[..., None, :], axis=-3)
     z = np.cumsum(pk, axis=-2)
@@ -214,7 +219,8 @@ def causal_backward(q, k, v, omega, dout, kind: str = "prf", eps: float = 0.0):
     r = np.flip(np.cumsum(np.flip(pq * dD[..., None], axis=-2), axis=-2), axis=-2)
     dpk = np.einsum("...lme,...le->...lm", R, v) + r
     dv = np.einsum("...lme,...lm->...le", R, pk)
-    return (_feature_backward(q, omega, pq, dpq, kind), _feature_backward(k, omega, pk, dpk, kind), dv)
+    return (_feature_backward(q, omega, pq, dpq, kind, work_dtype), _feature_backward(k, omega, pk, dpk, kind, work_dtype),
+            dv)
 
 
 def causal_bruteforce_from_features(phi_q, phi_k, v, rows: int | None = None):

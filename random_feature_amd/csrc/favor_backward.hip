@@ -180,6 +180,7 @@ __device__ __forceinline__ int scale_exp(float x) {
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ srow, int H, int L, int tpb,
              long long T_all, int G, int grad_f32, float* __restrict__ dpart, float* __restrict__ dzpart,
              void* __restrict__ dq) {
@@ -229,6 +230,8 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
   vec8<P> omt[NDBW][NFC];
   vec8<XS> sa[FB][KC];
   float zv[FB][4];  // z of this lane's features (4g + i of each block)
@@ -308,7 +311,11 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-          om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+          {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
 #pragma unroll
       for (int i = 0; i < NDBW; ++i)
 #pragma unroll
@@ -386,7 +393,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       for (int fb = 0; fb < FB; ++fb) {
         pq[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) mma16(pq[tb][fb], om[fb][dc], qf[dc]);
+        for (int dc = 0; dc < DC; ++dc) mma16_split_a<PSO>(pq[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], qf[dc]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -573,6 +580,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ dsrow,
              const float* __restrict__ gmx, int H, int L, int tpb, long long T_all, int G, float nscale,
              float s2, int grad_f32, void* __restrict__ dk, void* __restrict__ dv) {
@@ -618,6 +626,8 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
   TileCursor cur(t_beg, tpb), ahead(t_beg, tpb);
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
   vec8<P> omt[NDBW][NFC];
   vec8<XS> da[FB][KC];
   vec8<XB> dt[NVBW][NFC];
@@ -669,7 +679,11 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
       for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-          om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+          {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
 #pragma unroll
       for (int i = 0; i < NDBW; ++i)
 #pragma unroll
@@ -728,7 +742,7 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
       for (int fb = 0; fb < FB; ++fb) {
         pk[tb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) mma16(pk[tb][fb], om[fb][dc], kf[dc]);
+        for (int dc = 0; dc < DC; ++dc) mma16_split_a<PSO>(pk[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], kf[dc]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -867,6 +881,8 @@ BackwardPlan plan_backward(const Shape& s, int dtype) {
   size_t off = 0;
   p.off_omf = off;
   off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
+  p.off_omlo = off;
+  off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
   p.off_omt = off;
   off = align256(off + (size_t)s.H * (s.d / 16) * nfc * 512 * elt(dtype));
   p.off_part = off;
@@ -900,6 +916,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   const BackwardPlan p = plan_backward(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + p.off_omf);
+  P* omlo = reinterpret_cast<P*>(base + p.off_omlo);
   P* omt = reinterpret_cast<P*>(base + p.off_omt);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
@@ -917,12 +934,16 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
     launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf);
+        omega, s.H, M, D, wscale, omf, 0);
+    if constexpr (sizeof(P) == 2)
+      launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0,
+          st, omega, s.H, M, D, wscale, omlo, 1);
     launch("omega_frag", omegaT_frag_kernel<P>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omt);
   }
   {
-    launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true>, p.G_red, 64 * NWR, 0, st, k, v, omf, s.H,
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, p.G_red, 64 * NWR, 0, st, k, v, omf,
+        omlo, s.H,
         s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
   }
   {
@@ -930,7 +951,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
         pmax, p.tpb, p.T_all, p.G_red, 1, srow, gmx);
   }
   {
-    launch("bwd_q", bwd_q_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, q, dout, omf, omt, srow, s.H, s.L, p.tpb,
+    launch("bwd_q", bwd_q_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, q, dout, omf, omlo, omt, srow, s.H, s.L, p.tpb,
         p.T_all, p.G, grad_f32, dpart, dzpart, dq);
   }
   {
@@ -938,7 +959,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
         dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
   }
   {
-    launch("bwd_k", bwd_k_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, k, v, omf, omt, dsrow, gmx, s.H, s.L, p.tpb,
+    launch("bwd_k", bwd_k_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, k, v, omf, omlo, omt, dsrow, gmx, s.H, s.L, p.tpb,
         p.T_all, p.G, nscale, sc * sc, grad_f32, dk, dv);
   }
   return hipGetLastError();

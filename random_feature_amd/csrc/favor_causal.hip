@@ -422,15 +422,15 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
   {
     launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf);
+        omega, s.H, M, D, wscale, omf, 0);
   }
   {
     const int seg_tiles = p.seg_len / 32;
     if (kind == kPrf)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
           p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
     else
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, s.H, s.L,
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
           p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
   }
   {

@@ -172,6 +172,7 @@ template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo,
                 const float* __restrict__ cpart, const float* __restrict__ cz, const float* __restrict__ cmax, int H,
                 int L, int seg_len, int nseg, float nscale, float* __restrict__ lg, float* __restrict__ gam) {
   using P = typename Ops<T>::P;
@@ -214,11 +215,17 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     for (int e = threadIdx.x; e < 2 * 32 * OROW; e += NT) (&osum[0][0])[e] = 0.f;
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
   // the carry at the segment's start: this wave's 32-feature chunk of the scan's fragments
   f32x4 Sc[FB][NB];
   {
@@ -278,8 +285,8 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
         pq[tb][fb] = f32x4{-b, -b, -b, -b};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          mma16(pk[tb][fb], kf[dc], om[fb][dc]);
-          mma16(pq[tb][fb], om[fb][dc], qf[dc]);
+          mma16_split_b<PSO>(pk[tb][fb], kf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
+          mma16_split_a<PSO>(pq[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], qf[dc]);
         }
       }
     }
@@ -473,7 +480,8 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
-              const typename Ops<T>::P* __restrict__ omf, const typename Ops<T>::C* __restrict__ omTh,
+              const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo, const typename Ops<T>::C* __restrict__ omTh,
               const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ cpart,
               const float* __restrict__ cz, const float* __restrict__ cmax, const float* __restrict__ lg,
               const float* __restrict__ gam, int H, int L, int seg_len, int nseg, float nscale, int grad_f32,
@@ -528,11 +536,17 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   fetch(t0);
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
   // St[nb][fb][i] = S'[feature 16fb + c][column 16nb + 4g + i]: lane (4g + i) + 16(c >> 2), slot 4fb + (c & 3)
   // of the scan's fragments of this wave's 32-feature chunk
   f32x4 St[NB][FB];
@@ -595,8 +609,8 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         pq[tb][fb] = f32x4{qb, qb, qb, qb};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          mma16(pk, kf[dc], om[fb][dc]);
-          mma16(pq[tb][fb], om[fb][dc], qf[dc]);
+          mma16_split_b<PSO>(pk, kf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
+          mma16_split_a<PSO>(pq[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], qf[dc]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -765,6 +779,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo,
               const float* __restrict__ lg, const float* __restrict__ gam, int H, int L, int seg_len, int nseg,
               float* __restrict__ trow) {
   using P = typename Ops<T>::P;
@@ -802,11 +817,17 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
   Rg::issue(Q, dOut, L, bh, t0, true, ring0);
   fetch(t0);
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
   f32x4 Ta[FB][NB];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
@@ -844,7 +865,7 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
       for (int fb = 0; fb < FB; ++fb) {
         pq[qb][fb] = bias;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) mma16(pq[qb][fb], qf[dc], om[fb][dc]);
+        for (int dc = 0; dc < DC; ++dc) mma16_split_b<PSO>(pq[qb][fb], qf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
       }
     }
     vec8<C> ah[FB], al[FB];  // phi~^T: A [feature][query], paired query slots
@@ -919,7 +940,8 @@ cbwd_rscan_kernel(float* __restrict__ trow, const float* __restrict__ cmax, int 
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
-              const typename Ops<T>::P* __restrict__ omf, const typename Ops<T>::C* __restrict__ omTh,
+              const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo, const typename Ops<T>::C* __restrict__ omTh,
               const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ rcar,
               const float* __restrict__ cmax, const float* __restrict__ lg, const float* __restrict__ gam, int H,
               int L, int seg_len, int nseg, float nscale, float s2, int grad_f32, void* __restrict__ dk) {
@@ -975,11 +997,17 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   fetch(last0);
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
   f32x4 Rc[NB][FB];
   {
     const float* src = rcar + (size_t)pc * M * NBC;
@@ -1034,8 +1062,8 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         pq[tb][fb] = qbias;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          mma16(pk[tb][fb], kf[dc], om[fb][dc]);
-          mma16(pq[tb][fb], qf[dc], om[fb][dc]);
+          mma16_split_b<PSO>(pk[tb][fb], kf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
+          mma16_split_b<PSO>(pq[tb][fb], qf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1235,7 +1263,8 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 template <typename T, int D, int DV, int M>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
-              const typename Ops<T>::P* __restrict__ omf, const float* __restrict__ rcar,
+              const typename Ops<T>::P* __restrict__ omf,
+    const typename Ops<T>::P* __restrict__ omf_lo, const float* __restrict__ rcar,
               const float* __restrict__ cmax, const float* __restrict__ lg, int H, int L, int seg_len, int nseg,
               float nscale, int grad_f32, void* __restrict__ dv) {
   using P = typename Ops<T>::P;
@@ -1283,11 +1312,17 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
   C* const qtl = &fq[w][(2 * NSPL - 1) * 32 * FROW];
 
   vec8<P> om[FB][DC];
+  constexpr bool PSO = sizeof(P) == 2;  // the projections through Omega' hi + lo (fp16 fragments)
+  vec8<P> oml[PSO ? FB : 1][PSO ? DC : 1];
 #pragma unroll
   for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
-      om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      {
+            const size_t o_ = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+            om[fb][dc] = ld8<P>(omf + o_);
+            if constexpr (PSO) oml[fb][dc] = ld8<P>(omf_lo + o_);
+          }
   f32x4 Rt[FB][NVB];
   {
     const float* src = rcar + (size_t)pc * M * NBC;
@@ -1339,8 +1374,8 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         pq[tb][fb] = qbias;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          mma16(pk[tb][fb], kf[dc], om[fb][dc]);
-          mma16(pq[tb][fb], qf[dc], om[fb][dc]);
+          mma16_split_b<PSO>(pk[tb][fb], kf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
+          mma16_split_b<PSO>(pq[tb][fb], qf[dc], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1485,6 +1520,8 @@ CausalBackwardPlan plan_causal_backward(const Shape& s, int dtype) {
   const size_t ndb = s.d / 16, nfc = (s.m + 31) / 32, nbc = (s.dv / 16 + 1) * 16;
   const size_t omt = (size_t)s.H * ndb * nfc * 512 * elt(dtype);
   size_t off = p.f.total;
+  p.off_omlo = off;
+  off = align256(off + (size_t)s.H * (s.m / 16) * ((s.d + 31) / 32) * 512 * elt(dtype));
   p.off_omth = off;
   off = align256(off + omt);
   p.off_omtl = off;
@@ -1513,6 +1550,7 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   const CausalPlan& f = p.f;
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + f.off_omf);
+  P* omlo = reinterpret_cast<P*>(base + p.off_omlo);
   float* part = reinterpret_cast<float*>(base + f.off_part);
   float* zpart = reinterpret_cast<float*>(base + f.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + f.off_pmax);
@@ -1533,12 +1571,16 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
     launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf);
+        omega, s.H, M, D, wscale, omf, 0);
+    if constexpr (sizeof(P) == 2)
+      launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0,
+          st, omega, s.H, M, D, wscale, omlo, 1);
     launch("omega_frag", omegaT_pair_kernel<C>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omth, omtl);
   }
   {
-    launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, true>, f.G, 64 * NWR, 0, st, k, v, omf, s.H,
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, f.G, 64 * NWR, 0, st, k, v, omf,
+        omlo, s.H,
         s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg);
   }
   {
@@ -1547,15 +1589,15 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
         zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr);
   }
   {
-    launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, cpart, cz, cmax, s.H,
+    launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, cpart, cz, cmax, s.H,
         s.L, f.seg_len, f.nseg, nscale, lg, gam);
   }
   {
-    launch("cbwd_q", cbwd_q_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omth, omtl, cpart, cz,
+    launch("cbwd_q", cbwd_q_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, cpart, cz,
         cmax, lg, gam, s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq);
   }
   {
-    launch("cbwd_t", cbwd_t_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, dout, omf, lg, gam, s.H, s.L, f.seg_len,
+    launch("cbwd_t", cbwd_t_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, dout, omf, omlo, lg, gam, s.H, s.L, f.seg_len,
         f.nseg, trow);
   }
   {
@@ -1563,11 +1605,11 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
     launch("rscan", cbwd_rscan_kernel, (unsigned)(s.bh() * nblk), 256, 0, st, trow, cmax, f.nseg, per, nblk);
   }
   {
-    launch("cbwd_k", cbwd_k_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omth, omtl, trow, cmax, lg,
+    launch("cbwd_k", cbwd_k_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, trow, cmax, lg,
         gam, s.H, s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk);
   }
   {
-    launch("cbwd_v", cbwd_v_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, trow, cmax, lg, s.H, s.L,
+    launch("cbwd_v", cbwd_v_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, trow, cmax, lg, s.H, s.L,
         f.seg_len, f.nseg, nscale, grad_f32, dv);
   }
   return hipGetLastError();

@@ -53,6 +53,20 @@ __device__ __forceinline__ void mma16(f32x4& acc, const f32x8& a, const f32x8& b
   for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
 }
 
+// A product whose A (or B) operand is a projection matrix held as hi + lo fragments: with LO the
+// residual fragments are contracted too (one more MFMA), so the sum sees the matrix to about
+// fp32 accuracy instead of its 16-bit rounding.
+template <bool LO, typename V8>
+__device__ __forceinline__ void mma16_split_a(f32x4& acc, const V8& a_hi, const V8& a_lo, const V8& b) {
+  mma16(acc, a_hi, b);
+  if constexpr (LO) mma16(acc, a_lo, b);
+}
+template <bool LO, typename V8>
+__device__ __forceinline__ void mma16_split_b(f32x4& acc, const V8& a, const V8& b_hi, const V8& b_lo) {
+  mma16(acc, a, b_hi);
+  if constexpr (LO) mma16(acc, a, b_lo);
+}
+
 template <typename T> __device__ __forceinline__ T to_t(float x);
 template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return static_cast<bf16>(x); }

@@ -65,21 +65,23 @@ struct CausalPlan {
          total = 0;
 };
 
-// Bidirectional backward: the forward reduction's pieces and partials, S_aug rows, the
-// backward's own pieces (G, one workgroup per CU) and their dS_aug partials, dS_aug rows.
+// Bidirectional backward: Omega' fragments and their residuals (the projections run through both),
+// the forward reduction's pieces and partials, S_aug rows, the backward's own pieces (G, one
+// workgroup per CU) and their dS_aug partials, dS_aug rows.
 struct BackwardPlan {
   int tpb = 0, G_red = 0, G = 0, nw_reduce = 0;
   long long T_all = 0;
-  size_t off_omf = 0, off_omt = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_srow = 0, off_gmax = 0,
-         off_dpart = 0, off_dzpart = 0, off_dsrow = 0, total = 0;
+  size_t off_omf = 0, off_omlo = 0, off_omt = 0, off_part = 0, off_zpart = 0, off_pmax = 0, off_srow = 0,
+         off_gmax = 0, off_dpart = 0, off_dzpart = 0, off_dsrow = 0, total = 0;
 };
 
 // Causal backward: the forward's causal plan (Omega fragments, segment partials, carries and key
-// maxima), Omega'^T fragments (hi and lo parts), per-query l and gamma, and one [m][dv+16] fp32
-// block per segment (the query-side totals, then the suffix carries in place).
+// maxima), the Omega' fragments' residuals, Omega'^T fragments (hi and lo parts), per-query l and
+// gamma, and one [m][dv+16] fp32 block per segment (the query-side totals, then the suffix carries
+// in place).
 struct CausalBackwardPlan {
   CausalPlan f;
-  size_t off_omth = 0, off_omtl = 0, off_lg = 0, off_gam = 0, off_trow = 0, total = 0;
+  size_t off_omlo = 0, off_omth = 0, off_omtl = 0, off_lg = 0, off_gam = 0, off_trow = 0, total = 0;
 };
 
 bool shape_built(int dtype, int d, int dv, int m);

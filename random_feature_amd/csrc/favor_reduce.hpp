@@ -21,9 +21,11 @@ __device__ __forceinline__ float trig_feature(float a, int feature, int m) {
 // frag[h][fb][dc][lane][j] = scale * omega[h][fb*16 + c][dc*32 + 8g + j] (0 beyond d),
 // which is both the B operand (k = d, n = feature) of the key projection and the
 // A operand (row = feature, k = d) of the transposed query projection.
+// residual != 0 writes instead what rounding to T left out, x - (float)(T)x rounded to T: a
+// projection through both fragment sets (two MFMAs) sees the fp32 value to about 2^-22.
 template <typename T>
 __global__ void omega_frag_kernel(const float* __restrict__ omega, int H, int m, int d, float scale,
-                                  T* __restrict__ frag) {
+                                  T* __restrict__ frag, int residual = 0) {
   const int dc_n = (d + 31) / 32;
   const long long total = (long long)H * (m / 16) * dc_n * 64;
   for (long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x; id < total;
@@ -40,7 +42,8 @@ __global__ void omega_frag_kernel(const float* __restrict__ omega, int H, int m,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int col = dc * 32 + 8 * g + j;
-      x[j] = to_t<T>(col < d ? row[col] * scale : 0.f);
+      const float v = col < d ? row[col] * scale : 0.f;
+      x[j] = residual ? to_t<T>(v - to_f(to_t<T>(v))) : to_t<T>(v);
     }
     st8<T>(frag + (size_t)id * 8, x);
   }

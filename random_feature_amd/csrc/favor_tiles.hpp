@@ -207,9 +207,15 @@ constexpr int kReduceRing = 5;
 // feature after a shift is 2^-8, far above the bottom of the fp32/bf16 range.
 constexpr float kKeyMargin = 8.f;
 
-template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false>
+// PSPLIT (16-bit projection type): the projection runs through the Omega' fragments and their
+// residuals (omf_lo, see omega_frag_kernel), two MFMAs per block, so the exponents carry the fp32
+// Omega' instead of its 11-bit rounding (the gradient kernels need that at large input norms).
+// Each wave keeps its residual fragments in its own part of LDS (registers are full); launch this
+// variant with a 4-slot ring so that two workgroups still fit on a CU.
+template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false, bool PSPLIT = false>
 __global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
+                 const typename Ops<T>::P* __restrict__ omf_lo,
                  int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
                  float* __restrict__ part, float* __restrict__ zpart, float* __restrict__ pmax, int seg_tiles,
                  int nseg) {
@@ -230,6 +236,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
+  constexpr bool PS = PSPLIT && sizeof(P) == 2;
+  __shared__ __attribute__((aligned(16))) P oml_s[PS ? NW * FB * DC * 64 * 8 : 8];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -287,8 +295,12 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        om[fb][dc] = ld8<P>(omf + ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8);
+      for (int dc = 0; dc < DC; ++dc) {
+        const size_t o = ((((size_t)h * (M / 16) + w * FB + fb) * DC + dc) * 64 + lane) * 8;
+        om[fb][dc] = ld8<P>(omf + o);
+        // written and read back by this wave only (LDS operations of a wave complete in order)
+        if constexpr (PS) st8<P>(&oml_s[(((w * FB + fb) * DC + dc) * 64 + lane) * 8], ld8<P>(omf_lo + o));
+      }
     wait_vmcnt<0>();  // settle the fragment (and any partial) traffic here, off the per-tile path
   };
   // projection of the converted tile in ks[kb], exponents relative to the running maximum rm
@@ -311,7 +323,11 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       for (int fb = 0; fb < FB; ++fb) {
         pa[tb][fb] = bias;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) mma16(pa[tb][fb], kf[dc], om[fb][dc]);
+        for (int dc = 0; dc < DC; ++dc) {
+          mma16(pa[tb][fb], kf[dc], om[fb][dc]);
+          if constexpr (PS)
+            mma16(pa[tb][fb], kf[dc], ld8<P>(&oml_s[(((w * FB + fb) * DC + dc) * 64 + lane) * 8]));
+        }
       }
     }
   };
