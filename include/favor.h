@@ -17,7 +17,8 @@
  *   - Layouts are dense row-major: q, k [B,H,L,d]; v [B,H,L,dv]; out [B,H,L,dv];
  *     omega [H,m,d] fp32 (one random-feature matrix per head).
  *   - Device pointers must be 16-byte aligned. The caller owns every buffer;
- *     the library allocates no device memory and keeps no state between calls.
+ *     the library allocates no device memory and keeps no state between calls
+ *     (except favor_bidir_noalloc's workspace array, described there).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *     and the call returns without waiting. FAVOR_ERR_HIP reports a launch
  *     error; errors inside kernels surface at the caller's next synchronisation.
@@ -124,6 +125,21 @@ favor_status favor_bidir(const void* q, const void* k, const void* v, const floa
                          int B, int H, int L, int d, int dv, int m,
                          favor_dtype dtype, favor_kind kind, float eps, int out_f32,
                          void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* favor_bidir_noalloc — favor_bidir without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, results, shapes and checks as favor_bidir, and the same kernels. The workspace is
+ * an array of FAVOR_BIDIR_NOALLOC_MAX_BYTES inside the library, one per device, which each device holds from
+ * the first call on it until the process ends. Calls whose workspace (favor_workspace_size(0, ...)) exceeds it
+ * return FAVOR_ERR_WORKSPACE and launch nothing. `stream` must belong to the current device
+ * (FAVOR_ERR_INVALID_ARG otherwise). Every call on one device shares that device's array: calls that overlap
+ * on one device (on different streams, or from several threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe. The array needs no clearing between calls. */
+#define FAVOR_BIDIR_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+favor_status favor_bidir_noalloc(const void* q, const void* k, const void* v, const float* omega,
+                                 int B, int H, int L, int d, int dv, int m,
+                                 favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                                 void* out, hipStream_t stream);
 
 /* favor_bidir_cross — bidirectional FAVOR+ between Lq queries and Lk keys (the RFA
  * page's cross-attention procedure; Performer Algorithm 1 with Q' of Lq rows and K' of

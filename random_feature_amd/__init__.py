@@ -40,6 +40,7 @@ _lib.favor_make_omega.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp, _vp]
 _lib.favor_make_omega_host.argtypes = [ctypes.c_uint64, _i, _i, _i, _i, _vp]
 _lib.favor_features.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp]
 _lib.favor_bidir.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _sz, _vp]
+_lib.favor_bidir_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]
 _lib.favor_bidir_cross.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _sz,
                                    _vp]
 _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp,
@@ -61,11 +62,13 @@ _lib.favor_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINT
 _lib.favor_timing_read.restype = _i
 _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
-for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
+for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_noalloc",
+            "favor_bidir_cross",
             "favor_bidir_backward", "favor_causal", "favor_causal_backward", "favor_decode", "favor_decode_gated"):
     getattr(_lib, _fn).restype = _i
 
-EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_cross",
+EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_noalloc",
+            "favor_bidir_cross",
             "favor_bidir_backward", "favor_backward_workspace_size", "favor_causal", "favor_causal_backward",
             "favor_causal_backward_workspace_size",
             "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
@@ -241,6 +244,24 @@ def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, w
     _check_seq(q, k, v, omega)
     return bidir_cross(q, k, v, omega, kind=kind, eps=eps, renormalize=True, out_f32=out_f32, ws=ws, out=out,
                        _fn="favor_bidir")
+
+
+NOALLOC_MAX_BYTES = 64 << 20  # FAVOR_BIDIR_NOALLOC_MAX_BYTES
+
+
+def bidir_noalloc(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, out=None):
+    """bidir() through favor_bidir_noalloc: the library's own workspace array on the device (no allocation in
+    the library; `out` is allocated here unless given). Calls overlapping on one device race."""
+    B, H, L, _, d, dv, m = _check_seq(q, k, v, omega)
+    odt = torch.float32 if out_f32 else q.dtype
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=odt, device=q.device)
+    _check_out(out, "out", (B, H, L, dv), odt, q.device)
+    _check("favor_bidir_noalloc",
+           _lib.favor_bidir_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q),
+                                    _kind(kind), float(eps), 1 if out_f32 else 0, _ptr(out),
+                                    ctypes.c_void_p(_stream(q.device))))
+    return out
 
 
 def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool = True, out_f32: bool = False,

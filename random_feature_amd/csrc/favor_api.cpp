@@ -90,23 +90,49 @@ favor_status favor_features(const void* x, const float* omega, int B, int H, int
   return hip_status(favor::launch_features(x, omega, s, dtype, kind, eps, phi, logscale, stream));
 }
 
+// Checks of the bidirectional entry points, everything but the workspace.
+static favor_status check_bidir(const void* q, const void* k, const void* v, const float* omega,
+                                const favor::Shape& s, int Lq, favor_dtype dtype, favor_kind kind, float eps,
+                                int renormalize, void* out) {
+  favor_status st = check_seq(s, dtype, kind, eps);
+  if (st != FAVOR_OK) return st;
+  if (Lq < 1 || Lq > (1 << 28)) return FAVOR_ERR_INVALID_ARG;
+  if (!q || !k || !v || !omega || !out) return FAVOR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out))
+    return FAVOR_ERR_INVALID_ARG;
+  if (!favor::shape_built(dtype, s.d, s.dv, s.m)) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && s.m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
+  if (kind == FAVOR_TRIG && !renormalize) return FAVOR_ERR_UNSUPPORTED;
+  return FAVOR_OK;
+}
+
 favor_status favor_bidir_cross(const void* q, const void* k, const void* v, const float* omega, int B, int H,
                                int Lq, int Lk, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps,
                                int renormalize, int out_f32, void* out, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
   const favor::Shape s{B, H, Lk, d, dv, m};
-  favor_status st = check_seq(s, dtype, kind, eps);
+  favor_status st = check_bidir(q, k, v, omega, s, Lq, dtype, kind, eps, renormalize, out);
   if (st != FAVOR_OK) return st;
-  if (Lq < 1 || Lq > (1 << 28)) return FAVOR_ERR_INVALID_ARG;
-  if (!q || !k || !v || !omega || !out || !ws) return FAVOR_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out) || !aligned16(ws))
-    return FAVOR_ERR_INVALID_ARG;
-  if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
-  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
-  if (kind == FAVOR_TRIG && !renormalize) return FAVOR_ERR_UNSUPPORTED;
+  if (!ws || !aligned16(ws)) return FAVOR_ERR_INVALID_ARG;
   if (ws_bytes < favor::plan_bidir(s, dtype).total) return FAVOR_ERR_WORKSPACE;
   return hip_status(favor::launch_bidir(q, k, v, omega, s, Lq, renormalize ? 1 : 0, dtype, kind, eps,
                                         out_f32 ? 1 : 0, out, ws, stream));
+}
+
+favor_status favor_bidir_noalloc(const void* q, const void* k, const void* v, const float* omega, int B, int H,
+                                 int L, int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps,
+                                 int out_f32, void* out, hipStream_t stream) {
+  const favor::Shape s{B, H, L, d, dv, m};
+  favor_status st = check_bidir(q, k, v, omega, s, L, dtype, kind, eps, 1, out);
+  if (st != FAVOR_OK) return st;
+  if (favor::plan_bidir(s, dtype).total > FAVOR_BIDIR_NOALLOC_MAX_BYTES) return FAVOR_ERR_WORKSPACE;
+  int dev = -1;
+  hipDevice_t sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) return FAVOR_ERR_HIP;
+  if (sdev != dev) return FAVOR_ERR_INVALID_ARG;  // the stream must belong to the current device
+  void* ws = nullptr;
+  if (favor::noalloc_scratch(dev, &ws) != hipSuccess) return FAVOR_ERR_HIP;
+  return hip_status(favor::launch_bidir(q, k, v, omega, s, L, 1, dtype, kind, eps, out_f32 ? 1 : 0, out, ws, stream));
 }
 
 favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,

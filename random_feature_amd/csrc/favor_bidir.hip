@@ -24,8 +24,11 @@
 #include "favor_tiles.hpp"
 #include "favor_timing.hpp"
 
+#include "../../include/favor.h"
+
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 namespace favor {
 
@@ -611,6 +614,35 @@ hipError_t launch_bidir(const void* q, const void* k, const void* v, const float
   FAVOR_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+}  // namespace favor
+
+// ---------------------------------------------------------------- workspace without allocation
+// The workspace of favor_bidir_noalloc: one array per device, held from the library's first use on that device
+// until the process ends. In host code `scratch` names a host-side stand-in, not the device memory: the device
+// address is resolved once per device with hipGetSymbolAddress and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[FAVOR_BIDIR_NOALLOC_MAX_BYTES];
+
+namespace favor {
+namespace {
+constexpr int kNoallocDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kNoallocDevices];  // device address of `scratch` on each device, null until resolved
+}  // namespace
+
+hipError_t noalloc_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kNoallocDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // `dev` is the current device
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *ptr = scratch_addr[dev];
+  return hipSuccess;
 }
 
 template <typename T, int D, int M>

@@ -105,6 +105,9 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
 hipError_t launch_causal_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
                                   const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
                                   hipStream_t st);
+// Device address of the library's own workspace array (FAVOR_BIDIR_NOALLOC_MAX_BYTES) on device `dev`, which
+// must be the current device; resolved on the first call for that device.
+hipError_t noalloc_scratch(int dev, void** ptr);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* omega, float* S, float* z,
                          int N, int H, int d, int dv, int m, int dtype, int kind, float eps, const float* gate,
                          const float* inw, float* out, hipStream_t st);

@@ -11,6 +11,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -31,7 +32,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -174,3 +175,21 @@ def test_host_omega_head_rows_independent_of_H():
     a = rf.make_omega_host(9, 2, 64, 16)
     b = rf.make_omega_host(9, 5, 64, 16)
     assert np.array_equal(a, b[:2])
+
+
+def test_bidir_noalloc_checks_before_any_device_call():
+    """favor_bidir_noalloc takes favor_bidir's checks, and refuses a workspace beyond its array
+    (FAVOR_BIDIR_NOALLOC_MAX_BYTES) before it touches the device."""
+    def call(**kw):
+        a = dict(q=FAKE, out=FAKE, B=1, H=1, L=64, d=64, dv=64, m=256, dt=1)
+        a.update(kw)
+        return rf.raw_call("favor_bidir_noalloc", a["q"], FAKE, FAKE, FAKE, a["B"], a["H"], a["L"], a["d"], a["dv"],
+                           a["m"], a["dt"], 0, ctypes.c_float(0.0), 0, a["out"], None)
+    assert call(q=None) == INVALID
+    assert call(out=MISALIGNED) == INVALID
+    assert call(d=48) == UNSUPPORTED
+    big = dict(B=64, H=16, L=4096)
+    assert rf.workspace_size(False, 64, 16, 4096, 64, 64, 256, torch.bfloat16) > rf.NOALLOC_MAX_BYTES
+    assert call(**big) == WORKSPACE
+    # the headline workload's workspace fits
+    assert rf.workspace_size(False, 8, 12, 4096, 64, 64, 256, torch.bfloat16) <= rf.NOALLOC_MAX_BYTES
