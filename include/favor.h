@@ -109,7 +109,7 @@ favor_status favor_make_omega_host(uint64_t seed, int H, int m, int d, favor_ome
  * entry is 1/sqrt(m)) and logscale = max_r omega_r.x - |x|^2/2, so no row over- or
  * underflows. RELU: phi = max(omega_r.x, 0)/sqrt(m) + eps and logscale = 0. TRIG: phi is
  * sin or cos(omega_r.x) / sqrt(m/2) and logscale = |x|^2/2.
- * Supported (d, m): see favor_bidir. */
+ * Supported: d in {16, 32, 64, 128}, m a multiple of 16 up to 512. */
 favor_status favor_features(const void* x, const float* omega, int B, int H, int L, int d, int m,
                             favor_dtype dtype, favor_kind kind, float eps,
                             float* phi, float* logscale, hipStream_t stream);
@@ -119,8 +119,13 @@ favor_status favor_features(const void* x, const float* omega, int B, int H, int
  * when out_f32 != 0. ws: device scratch of at least
  * favor_workspace_size(0, B, H, L, d, dv, m, dtype) bytes; its contents on
  * entry do not matter and are garbage on exit.
- * Built shapes (d, dv, m): (16,16,16) (16,16,32) (16,16,64) (16,16,128) (16,16,256)
- * (32,32,64) (32,32,128) (64,64,64) (64,64,128) (64,64,256), both dtypes. */
+ * Shapes: d in {16, 32, 64, 128}; dv a multiple of 16 with 16 <= dv <= 256 (independent of d);
+ * m a multiple of 16 with 16 <= m <= 512. fp32 inputs: d <= 64 and m <= 256, besides the exact
+ * shapes below. Others return FAVOR_ERR_UNSUPPORTED. Exact kernels exist for (d, dv, m) = (16,16,16)
+ * (16,16,32) (16,16,64) (16,16,128) (16,16,256) (32,32,64) (32,32,128) (64,64,64) (64,64,128)
+ * (64,64,256); every other shape runs on general kernels (m rounded up to 32, 64, ..., 512 inside
+ * them with the extra features masked; v and out taken in column groups of 64), which cost more
+ * per token. FAVOR_TRIG only on the exact shapes. */
 favor_status favor_bidir(const void* q, const void* k, const void* v, const float* omega,
                          int B, int H, int L, int d, int dv, int m,
                          favor_dtype dtype, favor_kind kind, float eps, int out_f32,
@@ -176,7 +181,7 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
  * advanced by one token; token t's output reads the state that includes t).
  * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical
  * scale, updated in place; out [N,H,dv] fp32.
- * Requires d in {16, 32, 64}, dv a power of two in [16, 256], m a multiple of 16
+ * Requires d in {16, 32, 64}, dv a multiple of 16 in [16, 256], m a multiple of 16
  * with m <= 1024 (other values, and FAVOR_TRIG: FAVOR_ERR_UNSUPPORTED). */
 favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega,
                           float* S, float* z, int N, int H, int d, int dv, int m,

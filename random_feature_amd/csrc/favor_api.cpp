@@ -16,7 +16,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_dtype(favor_dtype t) { return t == FAVOR_F32 || t == FAVOR_BF16; }
 bool valid_kind(favor_kind k) { return k == FAVOR_PRF || k == FAVOR_RELU || k == FAVOR_TRIG; }
-bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool valid_omega_mode(favor_omega_mode mode, int m) {
   if (mode == FAVOR_HYPERBOLIC || mode == FAVOR_TRIG_PAIRS) return m % 2 == 0;
   return mode == FAVOR_ORTHO_CHI || mode == FAVOR_IID || mode == FAVOR_ORTHO_SQRTD;
@@ -82,11 +81,7 @@ favor_status favor_features(const void* x, const float* omega, int B, int H, int
   if (st != FAVOR_OK) return st;
   if (!x || !omega || !phi || !logscale) return FAVOR_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(omega) || !aligned16(phi) || !aligned16(logscale)) return FAVOR_ERR_INVALID_ARG;
-  bool built = false;
-  for (int dv : {16, 32, 64})
-    if (favor::shape_built(dtype, d, dv, m)) built = true;
-  if (!built) return FAVOR_ERR_UNSUPPORTED;
-  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
+  if (!(d == 16 || d == 32 || d == 64 || d == 128) || m % 16 != 0 || m > 512) return FAVOR_ERR_UNSUPPORTED;
   return hip_status(favor::launch_features(x, omega, s, dtype, kind, eps, phi, logscale, stream));
 }
 
@@ -100,9 +95,10 @@ static favor_status check_bidir(const void* q, const void* k, const void* v, con
   if (!q || !k || !v || !omega || !out) return FAVOR_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(omega) || !aligned16(out))
     return FAVOR_ERR_INVALID_ARG;
-  if (!favor::shape_built(dtype, s.d, s.dv, s.m)) return FAVOR_ERR_UNSUPPORTED;
+  const favor::KShape ks = favor::kernel_shape(dtype, s.d, s.dv, s.m);
+  if (!ks.ok) return FAVOR_ERR_UNSUPPORTED;
   if (kind == FAVOR_TRIG && s.m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
-  if (kind == FAVOR_TRIG && !renormalize) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && (!renormalize || !ks.exact)) return FAVOR_ERR_UNSUPPORTED;
   return FAVOR_OK;
 }
 
@@ -220,7 +216,7 @@ static favor_status decode_common(const void* q, const void* k, const void* v, c
       !aligned16(out))
     return FAVOR_ERR_INVALID_ARG;
   if (!(d == 16 || d == 32 || d == 64)) return FAVOR_ERR_UNSUPPORTED;
-  if (!pow2(dv) || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
+  if (dv % 16 != 0 || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
   if (m % 16 != 0 || m > 1024) return FAVOR_ERR_UNSUPPORTED;
   if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
   return hip_status(

@@ -911,7 +911,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
                                hipStream_t st) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NWR = RedSplit<M>::NW;
+  constexpr int NWR = RedSplit<M, D>::NW;
   constexpr int NWB = BwdSplit<M>::NW;
   const BackwardPlan p = plan_backward(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
@@ -934,17 +934,17 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
     launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf, 0);
+        omega, s.H, M, M, D, wscale, omf, 0);
     if constexpr (sizeof(P) == 2)
       launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0,
-          st, omega, s.H, M, D, wscale, omlo, 1);
+          st, omega, s.H, M, M, D, wscale, omlo, 1);
     launch("omega_frag", omegaT_frag_kernel<P>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omt);
   }
   {
     launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, p.G_red, 64 * NWR, 0, st, k, v, omf,
         omlo, s.H,
-        s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+        s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, DV, DV);
   }
   {
     launch("combine", combine_rows_kernel<DV, M, NWR>, (unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st, part, zpart,

@@ -44,11 +44,11 @@ inline float omega_scale(int kind, float sc) {
 // 2^(M_piece,wave - M_max) and summed, give the A fragments of S_aug^T:
 // sfr[bh][fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c]; in the last
 // block only row c == 0 (the z column) is nonzero.
-template <typename C, int DV, int M>
+template <typename C, int D, int DV, int M>
 __global__ void __launch_bounds__(1024)
 combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
                int tpb, long long T_all, int G, int kind, C* __restrict__ sfr, float* __restrict__ gmx) {
-  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NW = RedSplit<M, D>::NW, FB = RedSplit<M, D>::FB;
   constexpr int NB = DV / 16 + 1;
   constexpr int NFC = (M + 31) / 32;
   const int bh = blockIdx.x / NFC, fc = blockIdx.x % NFC;
@@ -126,15 +126,19 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
 //   phase 2 (wave w: a token half and value-column blocks, or both halves and fewer blocks)
 //     contraction out^T block = S^T block (A, registers) x Phi^T (B, all features from LDS)
 //     division by the summed denominators and the store
-template <typename T, int D, int DV, int M, int KIND>
-__global__ void __launch_bounds__(64 * FeatSplit<M>::NW, 2)
+// Shapes as kv_reduce_kernel (GEN): m_valid <= M features (those past it are masked: their rows of
+// S_aug are zero, and their exponents are -inf so that the exact-maximum fallback ignores them);
+// out rows are ldo elements apart and the call writes its vcols <= DV columns of them.
+template <typename T, int D, int DV, int M, int KIND, bool GEN>
+__global__ void __launch_bounds__(64 * (FeatSplit<M, D>::NW), 2)
 q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ omf,
                 const typename Ops<T>::C* __restrict__ sfr, int H, int L, int tpb, long long T_all, int G,
                 float eps, float inv_sqrt_m, int out_f32, int renorm, const float* __restrict__ gmx, float nscale,
-                float log2_m, void* __restrict__ out) {
+                float log2_m, void* __restrict__ out, int m_valid_, int ldo_, int vcols_) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
-  constexpr int NW = FeatSplit<M>::NW, FB = FeatSplit<M>::FB;
+  constexpr int NW = FeatSplit<M, D>::NW, FB = FeatSplit<M, D>::FB;
+  const int m_valid = GEN ? m_valid_ : M, ldo = GEN ? ldo_ : DV, vcols = GEN ? vcols_ : DV;
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
   constexpr int NB = DV / 16 + 1;           // blocks of S_aug^T in sfr: values, then z
@@ -249,6 +253,15 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       }
     }
     if constexpr (KIND == kPrf) {
+      if (m_valid < M) {  // features past m_valid: exponent -inf
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if ((w * FB + fb) * 16 + 4 * g + i >= m_valid) pacc[tb][fb][i] = -INFINITY;
+      }
       if (exact) {
         // rare: shift every row by its exact maximum, taken across the waves
 #pragma unroll
@@ -367,13 +380,13 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int nb = cb0 + cb * NW2;
-      if (nb < NVB) {
+      if (nb < NVB && nb * 16 < vcols) {
 #pragma unroll
         for (int tt = 0; tt < NTB; ++tt) {
           const int tok = tok0 + (tb0 + tt) * 16 + c;
           if (tok < L) {
             const f32x4 o = acc[cb][tt] * rden[tt];
-            const size_t off = ((size_t)bh * L + tok) * DV + nb * 16 + 4 * g;
+            const size_t off = ((size_t)bh * L + tok) * ldo + nb * 16 + 4 * g;
             if (out_f32) {
               *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
             } else {
@@ -392,41 +405,51 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 
 // ---------------------------------------------------------------- standalone features
 // Transposed projection as in q_output_kernel; writes phi (stabilised, each row's largest
-// entry 1/sqrt(m)) and the per-row log scale. Omega' fragments are built in LDS from the
-// fp32 matrix by the workgroup itself.
-template <typename T, int D, int M>
+// entry 1/sqrt(m)) and the per-row log scale. The m features are taken in groups of MG (the
+// Omega' fragments of one group are built in LDS from the fp32 matrix by the workgroup); with
+// more than one group the positive map first finds every row's maximum over all groups.
+template <typename T, int D, int MG>
 __global__ void __launch_bounds__(256)
-features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H, int L, int kind, float eps,
+features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H, int L, int m, int kind, float eps,
                 float inv_sqrt_m, float wscale, float nscale_ln, float* __restrict__ phi,
                 float* __restrict__ logscale, int tok_per_wg, int n_tiles) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NFB = M / 16;
+  constexpr int NFB = MG / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   P* oms = reinterpret_cast<P*>(smem);
+  float* rmax = reinterpret_cast<float*>(smem + (size_t)NFB * DC * 512 * sizeof(P));  // [tok_per_wg]
   const int bh = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
   const int h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  for (int id = threadIdx.x; id < NFB * DC * 64; id += 256) {
-    const int l = id & 63, dc = (id >> 6) % DC, fb = (id >> 6) / DC;
-    const int lc = l & 15, lg = l >> 4;
-    const float* row = omega + ((size_t)h * M + fb * 16 + lc) * D;
-    vec8<P> x;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = dc * 32 + 8 * lg + j;
-      x[j] = to_t<P>(col < D ? row[col] * wscale : 0.f);
-    }
-    st8<P>(oms + (size_t)id * 8, x);
-  }
-  __syncthreads();
+  const int ng = (m + MG - 1) / MG;
   const T* Xb = X + (size_t)bh * L * D;
   const int tstart = tile * tok_per_wg, tstop = min(L, tstart + tok_per_wg);
-  for (int t0 = tstart + w * 16; t0 < tstop; t0 += 64) {
+
+  auto build = [&](int gi) {  // Omega' fragments of features [gi*MG, gi*MG + MG), zero past m
+    __syncthreads();
+    for (int id = threadIdx.x; id < NFB * DC * 64; id += 256) {
+      const int l = id & 63, dc = (id >> 6) % DC, fb = (id >> 6) / DC;
+      const int lc = l & 15, lg = l >> 4;
+      const int r = gi * MG + fb * 16 + lc;
+      const float* row = omega + ((size_t)h * m + (r < m ? r : 0)) * D;
+      vec8<P> x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = dc * 32 + 8 * lg + j;
+        x[j] = to_t<P>((col < D && r < m) ? row[col] * wscale : 0.f);
+      }
+      st8<P>(oms + (size_t)id * 8, x);
+    }
+    __syncthreads();
+  };
+  // projection of the 16 tokens from t0 against the group in LDS: pacc[fb][i] is feature fb*16 + 4g + i of
+  // token t0 + c; s2 gets |x|^2
+  auto project = [&](int t0, f32x4 (&pacc)[NFB], float& s2) {
     const int tok = t0 + c;
     vec8<P> xf[DC];
-    float s2 = 0.f;
+    s2 = 0.f;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       const int col = dc * 32 + 8 * g;
@@ -439,58 +462,99 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
       }
     }
     s2 = group_sum(s2);
-    f32x4 pacc[NFB];
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb) {
       pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) mma16(pacc[fb], ld8<P>(oms + ((fb * DC + dc) * 64 + lane) * 8), xf[dc]);
     }
-    float ls = 0.f;
-    if (kind == kPrf) {
-      float mx = -INFINITY;
+  };
+  // largest valid exponent of the row among this group's features
+  auto row_max = [&](int gi, const f32x4 (&pacc)[NFB]) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
+    for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pacc[fb][i]);
-      mx = group_max(mx);
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - mx) * inv_sqrt_m;
-      ls = mx * kLn2 - s2 * nscale_ln;
-    } else if (kind == kTrig) {
-      // m/2 vectors: the scale 1/sqrt(m/2); exp(|x|^2/2) goes to the log scale
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pacc[fb][i] = trig_feature(pacc[fb][i], fb * 16 + 4 * g + i, M) * (inv_sqrt_m * 1.41421356f);
-      ls = s2 * nscale_ln;
-    } else {
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pacc[fb][i] = fmaxf(pacc[fb][i], 0.f) * inv_sqrt_m + eps;
+      for (int i = 0; i < 4; ++i)
+        if (gi * MG + fb * 16 + 4 * g + i < m) mx = fmaxf(mx, pacc[fb][i]);
+    return group_max(mx);
+  };
+
+  if (kind == kPrf && ng > 1) {
+    for (int gi = 0; gi < ng; ++gi) {
+      build(gi);
+      for (int t0 = tstart + w * 16; t0 < tstop; t0 += 64) {
+        f32x4 pacc[NFB];
+        float s2;
+        project(t0, pacc, s2);
+        const float mx = row_max(gi, pacc);
+        if (g == 0 && t0 + c < tstop) rmax[t0 + c - tstart] = gi == 0 ? mx : fmaxf(rmax[t0 + c - tstart], mx);
+      }
     }
-    if (tok < L) {
-      float* prow = phi + ((size_t)bh * L + tok) * M;
+  }
+  for (int gi = 0; gi < ng; ++gi) {
+    build(gi);
+    for (int t0 = tstart + w * 16; t0 < tstop; t0 += 64) {
+      const int tok = t0 + c;
+      f32x4 pacc[NFB];
+      float s2;
+      project(t0, pacc, s2);
+      float ls = 0.f;
+      if (kind == kPrf) {
+        const float mx = ng > 1 ? rmax[min(tok, tstop - 1) - tstart] : row_max(gi, pacc);
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) *reinterpret_cast<f32x4*>(prow + fb * 16 + 4 * g) = pacc[fb];
-      if (g == 0) logscale[(size_t)bh * L + tok] = ls;
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - mx) * inv_sqrt_m;
+        ls = mx * kLn2 - s2 * nscale_ln;
+      } else if (kind == kTrig) {
+        // m/2 vectors: the scale 1/sqrt(m/2); exp(|x|^2/2) goes to the log scale
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pacc[fb][i] = trig_feature(pacc[fb][i], gi * MG + fb * 16 + 4 * g + i, m) * (inv_sqrt_m * 1.41421356f);
+        ls = s2 * nscale_ln;
+      } else {
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pacc[fb][i] = fmaxf(pacc[fb][i], 0.f) * inv_sqrt_m + eps;
+      }
+      if (tok < L) {
+        float* prow = phi + ((size_t)bh * L + tok) * m + gi * MG;
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+          if (gi * MG + fb * 16 < m) *reinterpret_cast<f32x4*>(prow + fb * 16 + 4 * g) = pacc[fb];
+        if (g == 0 && gi == 0) logscale[(size_t)bh * L + tok] = ls;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- host side
 
-bool shape_built(int dtype, int d, int dv, int m) {
-  (void)dtype;
-#define X(D_, DV_, M_) \
-  if (d == D_ && dv == DV_ && m == M_) return true;
+KShape kernel_shape(int dtype, int d, int dv, int m) {
+  KShape k;
+#define X(D_, DV_, M_)                          \
+  if (d == D_ && dv == DV_ && m == M_) {        \
+    k.dk = D_, k.dvk = DV_, k.mk = M_;          \
+    k.exact = k.ok = true;                      \
+    return k;                                   \
+  }
   FAVOR_SHAPES(X)
 #undef X
-  return false;
+  if (!(d == 16 || d == 32 || d == 64 || d == 128)) return k;
+  if (dv < 16 || dv > 256 || dv % 16 != 0 || m < 16 || m > 512 || m % 16 != 0) return k;
+  k.dk = d;
+  k.dvk = 64;
+  k.mk = d > 64 ? 64 : 32;
+  while (k.mk < m) k.mk *= 2;
+  k.ok = dtype != 0 || fp32_built(true, d, k.mk);
+  return k;
 }
+
+bool shape_built(int dtype, int d, int dv, int m) { return kernel_shape(dtype, d, dv, m).ok; }
 
 #ifndef FAVOR_BIDIR_PIECES
 #define FAVOR_BIDIR_PIECES 512
@@ -512,27 +576,28 @@ static int pieces(long long bh, long long tpb) {
 
 BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
   BidirPlan p;
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);  // sizes of the compiled kernels (one column group)
   p.tpb = (s.L + 31) / 32;  // keys
   p.T_all = s.bh() * p.tpb;
   p.G = pieces(s.bh(), p.tpb);
   p.tpb_q = ((Lq > 0 ? Lq : s.L) + 31) / 32;  // queries
   p.T_all_q = s.bh() * p.tpb_q;
   p.G_q = pieces(s.bh(), p.tpb_q);
-  p.nw_reduce = reduce_waves(s.m);
-  const int dc = (s.d + 31) / 32, nb = s.dv / 16 + 1;
+  p.nw_reduce = reduce_waves(ks.mk, s.d);
+  const int dc = (s.d + 31) / 32, nb = ks.dvk / 16 + 1;
   const size_t slots = (size_t)p.G + (size_t)s.bh();
   size_t off = 0;
   p.off_omf = off;
-  off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
-  const size_t nfc = (s.m + 31) / 32;
+  off = align256(off + (size_t)s.H * (ks.mk / 16) * dc * 512 * elt(dtype));
+  const size_t nfc = (ks.mk + 31) / 32;
   p.off_part = off;
-  off = align256(off + slots * nfc * (s.dv / 16) * 512 * 4);
+  off = align256(off + slots * nfc * (ks.dvk / 16) * 512 * 4);
   p.off_zpart = off;
   off = align256(off + slots * nfc * 32 * 4);
   p.off_pmax = off;
   off = align256(off + slots * p.nw_reduce * 4);
   p.off_sfr = off;
-  off = align256(off + (size_t)s.bh() * ((s.m + 31) / 32) * nb * 512 * elt(dtype));
+  off = align256(off + (size_t)s.bh() * nfc * nb * 512 * elt(dtype));
   p.off_gmax = off;
   off = align256(off + (size_t)s.bh() * 4);
   p.total = off;
@@ -540,12 +605,16 @@ BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
 }
 
 
-template <typename T, int D, int DV, int M>
+// One call on the compiled (D, DV, M): the Omega' fragments once, then reduce, combine and output per
+// column group of DV columns of v and out (one group when dv = DV). GEN: the general kernels (runtime
+// feature count and column groups); otherwise the exact ones, which also have the trigonometric map.
+template <typename T, int D, int DV, int M, bool GEN>
 static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int Lq,
                             int renorm, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
-  constexpr int NW = FeatSplit<M>::NW;
+  constexpr int NW = FeatSplit<M, D>::NW;
+  constexpr int NWR = RedSplit<M, D>::NW;
   constexpr int DC = (D + 31) / 32;
   const BidirPlan p = plan_bidir(s, sizeof(T) == 4 ? 0 : 1, Lq);
   char* base = static_cast<char*>(ws);
@@ -555,45 +624,42 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   C* sfr = reinterpret_cast<C*>(base + p.off_sfr);
   float* gmx = reinterpret_cast<float*>(base + p.off_gmax);
-  const float log2_m = std::log2((float)M);
+  const float log2_m = std::log2((float)s.m);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = omega_scale(kind, sc);
   const float nscale = sc * sc * kLog2e * 0.5f;
-  const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
+  const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
-  {
-    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf, 0);
-  }
-  {
-    constexpr int NWR = RedSplit<M>::NW;
+  launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
+      omega, s.H, s.m, M, D, wscale, omf, 0);
+  for (int c0 = 0; c0 < s.dv; c0 += DV) {
+    const int vcols = std::min(DV, s.dv - c0);
+    const T* vg = v + c0;
+    void* og = out_f32 ? static_cast<void*>(static_cast<float*>(out) + c0) : static_cast<void*>(static_cast<T*>(out) + c0);
     if (kind == kPrf)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
-          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
-    else if (kind == kTrig)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kTrig>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
-          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv, vcols);
+    else if (!GEN && kind == kTrig)
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, GEN ? kPrf : kTrig, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg,
+          omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv,
+          vcols);
     else
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
-          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0);
-  }
-  {
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv, vcols);
     // one thread per (value block, lane): every partial is requested in a single round
     constexpr int NBC = DV / 16 + 1;
-    launch("combine", combine_kernel<C, DV, M>, (unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0,
+    launch("combine", combine_kernel<C, D, DV, M>, (unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0,
         st, part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
-  }
-  {
     if (kind == kPrf)
-      launch("output", q_output_kernel<T, D, DV, M, kPrf>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
-          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
-    else if (kind == kTrig)
-      launch("output", q_output_kernel<T, D, DV, M, kTrig>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
-          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
+      launch("output", q_output_kernel<T, D, DV, M, kPrf, GEN>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
+          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, og, s.m, s.dv, vcols);
+    else if (!GEN && kind == kTrig)
+      launch("output", q_output_kernel<T, D, DV, M, GEN ? kPrf : kTrig, GEN>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq,
+          p.tpb_q, p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, og, s.m, s.dv, vcols);
     else
-      launch("output", q_output_kernel<T, D, DV, M, kRelu>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
-          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, out);
+      launch("output", q_output_kernel<T, D, DV, M, kRelu, GEN>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,
+          p.T_all_q, p.G_q, eps, inv_sqrt_m, out_f32, renorm, gmx, nscale, log2_m, og, s.m, s.dv, vcols);
   }
   return hipGetLastError();
 }
@@ -601,17 +667,27 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
 hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s, int Lq,
                         int renorm, int dtype, int kind, float eps, int out_f32, void* out, void* ws,
                         hipStream_t st) {
-#define X(D_, DV_, M_)                                                                                         \
-  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                 \
-    if (dtype == 0)                                                                                            \
-      return run_bidir<float, D_, DV_, M_>(static_cast<const float*>(q), static_cast<const float*>(k),        \
-                                           static_cast<const float*>(v), omega, s, Lq, renorm, kind, eps,      \
-                                           out_f32, out, ws, st);                                              \
-    return run_bidir<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),             \
-                                        static_cast<const bf16*>(v), omega, s, Lq, renorm, kind, eps, out_f32,   \
-                                        out, ws, st);                                                            \
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
+  if (!ks.ok || (!ks.exact && kind == kTrig)) return hipErrorInvalidValue;
+#define X(D_, DV_, M_, GEN_)                                                                                   \
+  if (ks.exact == !GEN_ && ks.dk == D_ && ks.dvk == DV_ && ks.mk == M_) {                                      \
+    if (dtype == 0) {                                                                                          \
+      if constexpr (fp32_built(GEN_, D_, M_))                                                                  \
+        return run_bidir<float, D_, DV_, M_, GEN_>(static_cast<const float*>(q), static_cast<const float*>(k), \
+                                                   static_cast<const float*>(v), omega, s, Lq, renorm, kind,   \
+                                                   eps, out_f32, out, ws, st);                                  \
+      return hipErrorInvalidValue;                                                                             \
+    }                                                                                                          \
+    return run_bidir<bf16, D_, DV_, M_, GEN_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),        \
+                                              static_cast<const bf16*>(v), omega, s, Lq, renorm, kind, eps,     \
+                                              out_f32, out, ws, st);                                            \
   }
-  FAVOR_SHAPES(X)
+#define XE(D_, DV_, M_) X(D_, DV_, M_, false)
+#define XG(D_, DV_, M_) X(D_, DV_, M_, true)
+  FAVOR_SHAPES(XE)
+  FAVOR_GENERAL_SHAPES(XG)
+#undef XG
+#undef XE
 #undef X
   return hipErrorInvalidValue;
 }
@@ -645,7 +721,8 @@ hipError_t noalloc_scratch(int dev, void** ptr) {
   return hipSuccess;
 }
 
-template <typename T, int D, int M>
+// The feature map on groups of MG features (every m up to MG; 512 as two groups of 256).
+template <typename T, int D, int MG>
 static hipError_t run_features(const T* x, const float* omega, const Shape& s, int kind, float eps, float* phi,
                                float* logscale, hipStream_t st) {
   using P = typename Ops<T>::P;
@@ -653,31 +730,37 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = omega_scale(kind, sc);
   const float nscale_ln = sc * sc * 0.5f;
-  const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
+  const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
   const int tpw = 256;
   const int n_tiles = (s.L + tpw - 1) / tpw;
-  const size_t lds = (size_t)(M / 16) * DC * 512 * sizeof(P);
+  const size_t lds = (size_t)(MG / 16) * DC * 512 * sizeof(P) + tpw * sizeof(float);
   // once per instantiation (a function-local static is initialised exactly once, also under concurrent
   // first calls)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&features_kernel<T, D, M>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&features_kernel<T, D, MG>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
-  {
-    launch("features", features_kernel<T, D, M>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H, s.L, kind,
-        eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
-  }
+  launch("features", features_kernel<T, D, MG>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H, s.L, s.m,
+      kind, eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_features(const void* x, const float* omega, const Shape& s, int dtype, int kind, float eps,
                            float* phi, float* logscale, hipStream_t st) {
-#define X(D_, DV_, M_)                                                                                   \
-  if (s.d == D_ && s.m == M_) {                                                                          \
-    if (dtype == 0)                                                                                      \
-      return run_features<float, D_, M_>(static_cast<const float*>(x), omega, s, kind, eps, phi, logscale, st); \
-    return run_features<bf16, D_, M_>(static_cast<const bf16*>(x), omega, s, kind, eps, phi, logscale, st);     \
+  // feature groups: up to 256 features, 128 where the fragments and accumulators of a group would not fit the
+  // registers (fp32 at d >= 64, 16-bit inputs at d = 128)
+  const int mg_max = (dtype == 0 ? s.d >= 64 : s.d > 64) ? 128 : 256;
+  int mg = 16;
+  while (mg < s.m && mg < mg_max) mg *= 2;
+#define X(D_, MG_)                                                                                                \
+  if (s.d == D_ && mg == MG_) {                                                                                  \
+    if (dtype == 0)                                                                                              \
+      return run_features<float, D_, MG_>(static_cast<const float*>(x), omega, s, kind, eps, phi, logscale, st); \
+    return run_features<bf16, D_, MG_>(static_cast<const bf16*>(x), omega, s, kind, eps, phi, logscale, st);     \
   }
-  FAVOR_SHAPES(X)
+#define XD(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
+  XD(16) XD(32) XD(64) XD(128)
+  X(16, 256) X(32, 256) X(64, 256)
+#undef XD
 #undef X
   return hipErrorInvalidValue;
 }

@@ -53,15 +53,20 @@ namespace favor {
 //     intra term    o^T         += [V 1]^T (A: the value fragments) x masked A^T (B)
 //   chunk t+1 lands and is converted in place by the threads that copied it
 //   barrier Y; the wave's partial o^T goes to LDS; chunk t+2 is copied into slot (t+2) mod 3
-template <typename T, int D, int DV, int M, int KIND>
-__global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
+// Shapes as kv_reduce_kernel (GEN): m_valid <= M features (the query features past it are zero, which
+// keeps the rest of those features out of every output), a column group of vcols <= DV columns of V
+// and out whose rows are ld elements apart.
+template <typename T, int D, int DV, int M, int KIND, bool GEN>
+__global__ void __launch_bounds__(64 * (RedSplit<M, D>::NW), (RedSplit<M, D>::WPE))
 sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
              const typename Ops<T>::P* __restrict__ omf, const float* __restrict__ cpart,
              const float* __restrict__ cz, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
-             float eps, float inv_sqrt_m, float nscale, int out_f32, void* __restrict__ out) {
+             float eps, float inv_sqrt_m, float nscale, int out_f32, void* __restrict__ out, int m_valid_, int ld_,
+             int vcols_) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
-  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NW = RedSplit<M, D>::NW, FB = RedSplit<M, D>::FB;
+  const int m_valid = GEN ? m_valid_ : M, ld = GEN ? ld_ : DV, vcols = GEN ? vcols_ : DV;
   constexpr int NT = 64 * NW;
   constexpr int DC = (D + 31) / 32;
   constexpr int NB = DV / 16 + 1;  // value-column blocks + the ones column
@@ -90,8 +95,8 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
   const uint32_t ring0 = lds_addr(&ring[0][0]);
 
   // chunks 0 and 1 in flight
-  Rg::issue(Q, K, V, L, rowbase, t0, ring0);
-  if (n > 1) Rg::issue(Q, K, V, L, rowbase, t0 + 32, ring0 + Rg::SLOT);
+  Rg::issue(Q, K, V, L, rowbase, t0, ring0, nullptr, ld, vcols);
+  if (n > 1) Rg::issue(Q, K, V, L, rowbase, t0 + 32, ring0 + Rg::SLOT, nullptr, ld, vcols);
 
   vec8<P> om[FB][DC];
 #pragma unroll
@@ -133,7 +138,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     for (int e = threadIdx.x; e < 32 * C8; e += NT) {
       const int qrow = e / C8, c8 = e % C8;
       const int tok = tok0 + qrow;
-      if (tok >= tend) continue;
+      if (tok >= tend || c8 * 8 >= vcols) continue;
       const int tb = qrow >> 4, cq = qrow & 15;
       const int cb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
       f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
@@ -146,7 +151,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         den += xo[ww][2 * NVB * 256 + tb * 16 + cq];
       }
       const float rden = 1.0f / den;
-      const size_t off = (rowbase + tok) * DV + c8 * 8;
+      const size_t off = (rowbase + tok) * ld + c8 * 8;
       if (out_f32) {
         f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off);
         o4[0] = lo * rden;
@@ -205,14 +210,16 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     }
     if constexpr (KIND == kPrf) {
       if (__builtin_amdgcn_ballot_w64(exact) != 0) {  // the same in every wave
-        // rare: shift every query row by its exact maximum, taken across the waves
+        // rare: shift every query row by its exact maximum (over the m_valid real features), taken across
+        // the waves
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           float mx = -INFINITY;
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
+            for (int i = 0; i < 4; ++i)
+              if ((w * FB + fb) * 16 + 4 * g + i < m_valid) mx = fmaxf(mx, pq[tb][fb][i]);
           mx = group_max(mx);
           if (g == 0) qmx[w][tb * 16 + c] = mx;
         }
@@ -252,7 +259,9 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         for (int j = 0; j < 8; ++j) {
           const int fb = 2 * fcw + (j >> 2);
           float f = 0.f;
-          if (fb < FB) {
+          // features past m_valid: zero query features, so the state rows and scores they would feed (the
+          // keys' features there are not masked) never reach an output
+          if (fb < FB && (w * FB + fb) * 16 + 4 * g + (j & 3) < m_valid) {
             const float a = pq[tb][fb][j & 3];
             f = (KIND == kPrf) ? fast_exp2(a) : fmaxf(a, 0.f) * inv_sqrt_m + eps;
           }
@@ -278,7 +287,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     }
     // ---- state update
     vec8<C> vf[NB];
-    value_frags<T, D, DV, NT>(sl + Rg::XC * 16, vf, c, g);
+    value_frags<T, D, DV, NT>(sl + Rg::XC * 16, vf, c, g, vcols);
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -350,7 +359,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         *reinterpret_cast<f32x4*>(&xo[w][((tb * NVB + cb) * 64 + lane) * 4]) = o[cb][tb];
       if (g == 0) xo[w][2 * NVB * 256 + tb * 16 + c] = o[NB - 1][tb][0];
     }
-    if (t + 2 < n) Rg::issue(Q, K, V, L, rowbase, tok0 + 64, ring0 + s_is * Rg::SLOT);
+    if (t + 2 < n) Rg::issue(Q, K, V, L, rowbase, tok0 + 64, ring0 + s_is * Rg::SLOT, nullptr, ld, vcols);
     s_cur = s_nx;
   }
   lds_barrier();
@@ -375,20 +384,21 @@ CausalPlan plan_causal(const Shape& s, int dtype) {
   p.tpb = (s.L + 31) / 32;
   p.T_all = s.bh() * p.tpb;
   p.G = (int)(s.bh() * p.nseg);
-  p.nw_reduce = reduce_waves(s.m);
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);  // sizes of the compiled kernels (one column group)
+  p.nw_reduce = reduce_waves(ks.mk, s.d);
   const int dc = (s.d + 31) / 32;
-  const size_t nfc = (s.m + 31) / 32, G = (size_t)p.G;
+  const size_t nfc = (ks.mk + 31) / 32, G = (size_t)p.G;
   size_t off = 0;
   p.off_omf = off;
-  off = align256(off + (size_t)s.H * (s.m / 16) * dc * 512 * elt(dtype));
+  off = align256(off + (size_t)s.H * (ks.mk / 16) * dc * 512 * elt(dtype));
   p.off_part = off;
-  off = align256(off + G * nfc * (s.dv / 16) * 512 * 4);
+  off = align256(off + G * nfc * (ks.dvk / 16) * 512 * 4);
   p.off_zpart = off;
   off = align256(off + G * nfc * 32 * 4);
   p.off_pmax = off;
   off = align256(off + G * p.nw_reduce * 4);
   p.off_cpart = off;
-  off = align256(off + G * nfc * (s.dv / 16) * 512 * 4);
+  off = align256(off + G * nfc * (ks.dvk / 16) * 512 * 4);
   p.off_cz = off;
   off = align256(off + G * nfc * 32 * 4);
   p.off_cmax = off;
@@ -397,13 +407,15 @@ CausalPlan plan_causal(const Shape& s, int dtype) {
   return p;
 }
 
-template <typename T, int D, int DV, int M>
+// One call on the compiled (D, DV, M): the Omega' fragments once, then reduce, scan and sweep per column
+// group of DV columns of v and out (one group when dv = DV). GEN: the general kernels.
+template <typename T, int D, int DV, int M, bool GEN>
 static hipError_t run_causal(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int kind,
                              float eps, int out_f32, void* out, float* S_final, float* z_final, void* ws,
                              hipStream_t st) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NWR = RedSplit<M>::NW;
+  constexpr int NWR = RedSplit<M, D>::NW;
   const CausalPlan p = plan_causal(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
   P* omf = reinterpret_cast<P*>(base + p.off_omf);
@@ -416,35 +428,35 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
-  const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
-  const float log2_sqrt_m = 0.5f * std::log2((float)M);
+  const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
+  const float log2_sqrt_m = 0.5f * std::log2((float)s.m);
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
-  {
-    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf, 0);
-  }
-  {
-    const int seg_tiles = p.seg_len / 32;
+  launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
+      omega, s.H, s.m, M, D, wscale, omf, 0);
+  const int seg_tiles = p.seg_len / 32;
+  for (int c0 = 0; c0 < s.dv; c0 += DV) {
+    const int vcols = std::min(DV, s.dv - c0);
+    const T* vg = v + c0;
+    void* og = out_f32 ? static_cast<void*>(static_cast<float*>(out) + c0) : static_cast<void*>(static_cast<T*>(out) + c0);
     if (kind == kPrf)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
-          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg, s.m, s.dv,
+          vcols);
     else
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu>, p.G, 64 * NWR, 0, st, k, v, omf, nullptr, s.H, s.L,
-          p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg);
-  }
-  {
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg, s.m, s.dv,
+          vcols);
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    launch("scan", scan_kernel<DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st, part,
-        zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final, z_final);
-  }
-  {
+    launch("scan", scan_kernel<D, DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st,
+        part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final ? S_final + c0 : nullptr,
+        c0 == 0 ? z_final : nullptr, s.m, s.dv, vcols);
     if (kind == kPrf)
-      launch("sweep", sweep_kernel<T, D, DV, M, kPrf>, p.G, 64 * NWR, 0, st, q, k, v, omf, cpart, cz, cmax, s.H, s.L,
-          p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
+      launch("sweep", sweep_kernel<T, D, DV, M, kPrf, GEN>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
+          s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
     else
-      launch("sweep", sweep_kernel<T, D, DV, M, kRelu>, p.G, 64 * NWR, 0, st, q, k, v, omf, cpart, cz, cmax, s.H, s.L,
-          p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, out);
+      launch("sweep", sweep_kernel<T, D, DV, M, kRelu, GEN>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
+          s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
   }
   return hipGetLastError();
 }
@@ -452,17 +464,27 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
                          void* ws, hipStream_t st) {
-#define X(D_, DV_, M_)                                                                                          \
-  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
-    if (dtype == 0)                                                                                             \
-      return run_causal<float, D_, DV_, M_>(static_cast<const float*>(q), static_cast<const float*>(k),        \
-                                            static_cast<const float*>(v), omega, s, kind, eps, out_f32, out,    \
-                                            S_final, z_final, ws, st);                                          \
-    return run_causal<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),             \
-                                         static_cast<const bf16*>(v), omega, s, kind, eps, out_f32, out,        \
-                                         S_final, z_final, ws, st);                                             \
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
+  if (!ks.ok) return hipErrorInvalidValue;
+#define X(D_, DV_, M_, GEN_)                                                                                    \
+  if (ks.exact == !GEN_ && ks.dk == D_ && ks.dvk == DV_ && ks.mk == M_) {                                       \
+    if (dtype == 0) {                                                                                           \
+      if constexpr (fp32_built(GEN_, D_, M_))                                                                   \
+        return run_causal<float, D_, DV_, M_, GEN_>(static_cast<const float*>(q), static_cast<const float*>(k), \
+                                                    static_cast<const float*>(v), omega, s, kind, eps, out_f32,  \
+                                                    out, S_final, z_final, ws, st);                             \
+      return hipErrorInvalidValue;                                                                              \
+    }                                                                                                           \
+    return run_causal<bf16, D_, DV_, M_, GEN_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),        \
+                                               static_cast<const bf16*>(v), omega, s, kind, eps, out_f32, out,  \
+                                               S_final, z_final, ws, st);                                       \
   }
-  FAVOR_SHAPES(X)
+#define XE(D_, DV_, M_) X(D_, DV_, M_, false)
+#define XG(D_, DV_, M_) X(D_, DV_, M_, true)
+  FAVOR_SHAPES(XE)
+  FAVOR_GENERAL_SHAPES(XG)
+#undef XG
+#undef XE
 #undef X
   return hipErrorInvalidValue;
 }

@@ -1543,7 +1543,7 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int DC = (D + 31) / 32;
-  constexpr int NWR = RedSplit<M>::NW;
+  constexpr int NWR = RedSplit<M, D>::NW;
   constexpr int NWB = BwdSplit<M>::NW;
   constexpr int NBC = (DV / 16 + 1) * 16;
   const CausalBackwardPlan p = plan_causal_backward(s, sizeof(T) == 4 ? 0 : 1);
@@ -1571,22 +1571,22 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   const long long nfragT = (long long)s.H * (D / 16) * ((M + 31) / 32) * 64;
   {
     launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-        omega, s.H, M, D, wscale, omf, 0);
+        omega, s.H, M, M, D, wscale, omf, 0);
     if constexpr (sizeof(P) == 2)
       launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0,
-          st, omega, s.H, M, D, wscale, omlo, 1);
+          st, omega, s.H, M, M, D, wscale, omlo, 1);
     launch("omega_frag", omegaT_pair_kernel<C>, (unsigned)std::min<long long>((nfragT + 255) / 256, 4096), 256, 0, st,
         omega, s.H, M, D, wscale, omth, omtl);
   }
   {
     launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, f.G, 64 * NWR, 0, st, k, v, omf,
         omlo, s.H,
-        s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg);
+        s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg, s.m, DV, DV);
   }
   {
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    launch("scan", scan_kernel<DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, f.nseg * sizeof(float), st, part,
-        zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr);
+    launch("scan", scan_kernel<D, DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, f.nseg * sizeof(float), st, part,
+        zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr, s.m, DV, DV);
   }
   {
     launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, cpart, cz, cmax, s.H,

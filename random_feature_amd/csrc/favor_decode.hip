@@ -89,9 +89,12 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
   const int ng = min(G, N - s0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int tpr = dv / 4;                 // threads per row (power of two, 4..64)
+  const int tpr = dv / 4;                 // threads per row (4..64)
   const int rgs = kDecodeThreads / tpr;   // row groups of U consecutive rows per batch
   const int col4 = tid % tpr, rg0 = tid / tpr;
+  // when tpr does not divide the threads, the last few (rg0 == rgs) own no rows: they load clamped rows
+  // like the others but never store or contribute
+  const bool owns_rows = rg0 < rgs;
   const int rows_per_batch = U * rgs;
   const int nbat = (m + rows_per_batch - 1) / rows_per_batch;
   // this thread's rows in batch b: b*rows_per_batch + rg0*U + u, u < U (consecutive rows,
@@ -290,7 +293,7 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int r = r0 + u;
-        if (r < m) {
+        if (r < m && owns_rows) {
           const f32x4 st = buf[g][u] * gv[g] + (fk[g * m + r] * iw[g]) * vv[g];
           acc[g] += fq[g * m + r] * st;
           if (g < ng) st_state(p0 + u * dv, st);

@@ -162,13 +162,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Reduce over the four lanes that share c (lanes c, c+16, c+32, c+48).
 __device__ __forceinline__ float group_sum(float x) { return pair_sum32(pair_sum16(x)); }
 __device__ __forceinline__ float group_max(float x) { return pair_max32(pair_max16(x)); }
-// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16).
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, ..., 64).
 template <int N> __device__ __forceinline__ float lanes_sum(float x) {
   if constexpr (N >= 2) x += dpp<kDppXor1>(x);
   if constexpr (N >= 4) x += dpp<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppRor8>(x);
-  static_assert(N <= 16, "lanes_sum covers at most 16 lanes");
+  if constexpr (N >= 32) x = pair_sum16(x);
+  if constexpr (N >= 64) x = pair_sum32(x);
+  static_assert(N <= 64, "lanes_sum covers at most 64 lanes");
   return x;
 }
 

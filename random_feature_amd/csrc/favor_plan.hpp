@@ -17,6 +17,31 @@
   X(64, 64, 128)        \
   X(64, 64, 256)
 
+// Compiled (d, dv, m) of the general kernels (value columns in groups of 64, runtime feature count
+// up to the capacity m), for the shapes FAVOR_SHAPES does not list (its shapes keep their exact
+// kernels, without the general kernels' masking). At d = 128 the smallest capacity
+// is 64 (two waves: one wave would have more tile copies in flight than it can count).
+#define FAVOR_GENERAL_SHAPES(X) \
+  X(16, 64, 32)                 \
+  X(16, 64, 64)                 \
+  X(16, 64, 128)                \
+  X(16, 64, 256)                \
+  X(16, 64, 512)                \
+  X(32, 64, 32)                 \
+  X(32, 64, 64)                 \
+  X(32, 64, 128)                \
+  X(32, 64, 256)                \
+  X(32, 64, 512)                \
+  X(64, 64, 32)                 \
+  X(64, 64, 64)                 \
+  X(64, 64, 128)                \
+  X(64, 64, 256)                \
+  X(64, 64, 512)                \
+  X(128, 64, 64)                \
+  X(128, 64, 128)               \
+  X(128, 64, 256)               \
+  X(128, 64, 512)
+
 // (d, dv, m) combinations with compiled kernels for the bidirectional backward.
 #define FAVOR_BWD_SHAPES(X) \
   X(16, 16, 32)             \
@@ -34,13 +59,15 @@ struct Shape {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t elt(int dtype) { return dtype == 0 ? 4 : 2; }
 
-// Waves of the key/value reduction for m features (at most FAVOR_REDUCE_WAVES, at least 32
-// features each); the device-side split (RedSplit) follows the same rule.
+// Waves of the key/value reduction for m features at projection width d (m: the compiled
+// feature capacity); the device-side split (RedSplit) follows the same rule.
 #ifndef FAVOR_REDUCE_WAVES
 #define FAVOR_REDUCE_WAVES 4
 #endif
-inline int reduce_waves(int m) {
-  return m < 32 ? 1 : ((m / 32) < FAVOR_REDUCE_WAVES ? (m / 32) : FAVOR_REDUCE_WAVES);
+inline int reduce_waves(int m, int d) {
+  const int base = m < 32 ? 1 : ((m / 32) < FAVOR_REDUCE_WAVES ? (m / 32) : FAVOR_REDUCE_WAVES);
+  const int fpw = d > 64 ? 32 : 64;
+  return m / base > fpw ? (m / fpw < 8 ? m / fpw : 8) : base;
 }
 
 // Bidirectional path: omega fragments, per-segment partial (S, z) sums with their
@@ -84,6 +111,18 @@ struct CausalBackwardPlan {
   size_t off_omlo = 0, off_omth = 0, off_omtl = 0, off_lg = 0, off_gam = 0, off_trow = 0, total = 0;
 };
 
+// The compiled kernels a call of the sequence entry points runs on: its own (d, dv, m) when FAVOR_SHAPES
+// lists it (exact), else the general kernels (d, 64, mk) with mk the next of 32 (64 at d = 128), 64, 128,
+// 256, 512 at or above m, dv covered by column groups of up to 64. Valid for d in {16, 32, 64, 128} and multiples of 16
+// dv <= 256, m <= 512 (ok = false otherwise).
+struct KShape {
+  int dk = 0, dvk = 0, mk = 0;
+  bool exact = false, ok = false;
+};
+KShape kernel_shape(int dtype, int d, int dv, int m);
+// fp32 inputs on the general kernels: d <= 64 and a feature capacity of at most 256 (fp32 operands
+// take twice the registers and LDS of the 16-bit ones; larger fp32 shapes are not built).
+constexpr bool fp32_built(bool general, int d, int mk) { return !general || (d <= 64 && mk <= 256); }
 bool shape_built(int dtype, int d, int dv, int m);
 bool bwd_shape_built(int d, int dv, int m);
 BackwardPlan plan_backward(const Shape& s, int dtype);

@@ -16,12 +16,15 @@ namespace favor {
 // e < NP: part[fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c];
 // e >= NP: zpart[fc][g][j] = z[fc*32 + 16(j>>2) + 4g + (j&3)] (c = lane & 15, g = lane >> 4);
 // the four elements of a thread share fc and g and differ in j & 3.
-template <int DV, int M>
+// The final state (S_final, z_final: nullable) goes out in canonical scale for the m_valid real features,
+// S_final rows ldS apart (a column group writes its vcols columns; z_final only when non-null).
+template <int D, int DV, int M>
 __global__ void __launch_bounds__(256)
 scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
             int nseg, int kind, float log2_sqrt_m, float* __restrict__ cpart, float* __restrict__ cz,
-            float* __restrict__ cmax, float* __restrict__ S_final, float* __restrict__ z_final) {
-  constexpr int NWR = RedSplit<M>::NW, FBR = RedSplit<M>::FB;
+            float* __restrict__ cmax, float* __restrict__ S_final, float* __restrict__ z_final, int m_valid,
+            int ldS, int vcols) {
+  constexpr int NWR = RedSplit<M, D>::NW, FBR = RedSplit<M, D>::FB;
   constexpr int NFC = (M + 31) / 32, NVB = DV / 16;
   constexpr int NP = NFC * NVB * 512, NZ = NFC * 32;
   constexpr int NQ = (NP + NZ) / 4;  // float4 elements per partial
@@ -93,14 +96,15 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
       }
     }
   }
-  if (S_final && r0 < M) {
+  if (S_final && r0 < m_valid) {
     const float f = (kind == kPrf) ? fast_exp2(prev - log2_sqrt_m) : 1.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (!isz)
-        S_final[((size_t)bh * M + r0 + i) * DV + col] = acc[i] * f;
-      else
-        z_final[(size_t)bh * M + r0 + i] = acc[i] * f;
+      if (!isz) {
+        if (col < vcols) S_final[((size_t)bh * m_valid + r0 + i) * ldS + col] = acc[i] * f;
+      } else if (z_final) {
+        z_final[(size_t)bh * m_valid + r0 + i] = acc[i] * f;
+      }
     }
   }
 }
@@ -129,9 +133,11 @@ struct SweepRing {
     return (x * XC + row * CPR_X + (cc ^ (row & (CPR_X - 1)))) * 16;
   }
 
-  // G (WITH_G): rows of a fourth [.., DV] array (the upstream gradient), laid out like V after it
+  // G (WITH_G): rows of a fourth [.., DV] array (the upstream gradient), laid out like V after it. V rows
+  // are ldv elements apart with vcols valid columns (chunks past them are copied from the row's start
+  // and masked by the consumer).
   static __device__ __forceinline__ void issue(const T* Q, const T* K, const T* V, int L, size_t rowbase, int tok0,
-                                               uint32_t slot, const T* G = nullptr) {
+                                               uint32_t slot, const T* G = nullptr, int ldv = DV, int vcols = DV) {
     const int tid = threadIdx.x, w = tid >> 6;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -145,7 +151,8 @@ struct SweepRing {
         const bool isg = WITH_G && q >= 2 * XC + VC;
         const int p = q - 2 * XC - (isg ? VC : 0), row = p / CPR_V, pc = p % CPR_V;
         const int cc = SWZ_V ? (pc ^ (row & (CPR_V - 1))) : pc;
-        src = (isg ? G : V) + (rowbase + min(tok0 + row, L - 1)) * DV + cc * EPC;
+        src = isg ? G + (rowbase + min(tok0 + row, L - 1)) * DV + cc * EPC
+                  : V + (rowbase + min(tok0 + row, L - 1)) * ldv + (cc * EPC < vcols ? cc * EPC : 0);
       }
       lds_dma16(src, slot + (uint32_t)(u * NT + w * 64) * 16u);
     }

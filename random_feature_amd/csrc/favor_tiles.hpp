@@ -9,17 +9,28 @@
 
 namespace favor {
 
-// Waves per workgroup and 16-feature blocks per wave for m features.
-template <int M> struct FeatSplit {
-  static constexpr int NW = (M / 16) < 4 ? (M / 16) : 4;
+// Most features one wave owns at projection width D: a wave holds its rows of Omega' (D/32
+// fragments per 16 features) and its accumulators in registers, so at D = 128 a wave takes half
+// as many features as at D <= 64.
+template <int D> constexpr int kFeatPerWave = D > 64 ? 32 : 64;
+
+// Waves per workgroup and 16-feature blocks per wave of the query-side kernels for m features:
+// up to four waves of up to kFeatPerWave features, then up to eight.
+template <int M, int D> struct FeatSplit {
+  static constexpr int BASE = (M / 16) < 4 ? (M / 16) : 4;
+  static constexpr int NW = M / BASE > kFeatPerWave<D> ? (M / kFeatPerWave<D> < 8 ? M / kFeatPerWave<D> : 8) : BASE;
   static constexpr int FB = M / (16 * NW);
 };
-// Waves of the key/value reduction (RW_MAX at most, 32 features per wave or more). Two
-// workgroups per CU: NW/2 waves per SIMD (the second launch bound is waves per EU).
-template <int M> struct RedSplit {
+// Waves of the key/value reduction (and of the causal sweep, which shares its split): up to
+// RW_MAX waves of 32 features or more, then up to eight when a wave would own more than
+// kFeatPerWave features. Up to four waves: two workgroups per CU (NW/2 waves per SIMD; the
+// second launch bound is waves per EU); eight waves: one workgroup per CU.
+template <int M, int D> struct RedSplit {
   static constexpr int RW_MAX = FAVOR_REDUCE_WAVES;
-  static constexpr int NW = M < 32 ? 1 : ((M / 32) < RW_MAX ? (M / 32) : RW_MAX);
+  static constexpr int BASE = M < 32 ? 1 : ((M / 32) < RW_MAX ? (M / 32) : RW_MAX);
+  static constexpr int NW = M / BASE > kFeatPerWave<D> ? (M / kFeatPerWave<D> < 8 ? M / kFeatPerWave<D> : 8) : BASE;
   static constexpr int FB = M / (16 * NW);
+  static constexpr int WPE = NW < 2 ? 1 : (NW / 2 < 2 ? NW / 2 : 2);
 };
 
 // Waves of the gradient kernels: one per 32 features, at most FAVOR_BWD_WAVES. Eight waves in
@@ -43,7 +54,9 @@ constexpr int kNormNone = 0, kNormSq = 1, kNormAbs = 2;
 // row-major with the chunk column XOR-swizzled by the row for 16-bit types (spreads the
 // transposing reads over the LDS banks). Rows past L are copied from row L-1 and masked
 // by the consumer; slots past the end of a piece are filled with harmless copies so that
-// every tile costs the same number of copies and the waits stay uniform.
+// every tile costs the same number of copies and the waits stay uniform. V rows are ldv elements
+// apart and hold vcols valid columns (a column group of a wider V: DV columns are compiled,
+// chunks at or past vcols are copied from the row's start and masked by the consumer).
 template <typename T, int D, int DV, int NT, bool WITH_V>
 struct Ring {
   static constexpr int EPC = 16 / (int)sizeof(T);
@@ -57,7 +70,7 @@ struct Ring {
 
   // copies of the tile at (bh, tok0) into the slot at LDS byte address `slot`; !live: filler
   static __device__ __forceinline__ void issue(const T* X, const T* V, int L, int bh, int tok0, bool live,
-                                               uint32_t slot) {
+                                               uint32_t slot, int ldv = DV, int vcols = DV) {
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t rowbase = (size_t)bh * L;
 #pragma unroll
@@ -71,7 +84,7 @@ struct Ring {
         } else if (WITH_V && q < XC + VC) {
           const int p = q - XC, row = p / CPR_V, pc = p % CPR_V;
           const int cc = SWZ ? (pc ^ (row & (CPR_V - 1))) : pc;
-          src = V + (rowbase + min(tok0 + row, L - 1)) * DV + cc * EPC;
+          src = V + (rowbase + min(tok0 + row, L - 1)) * ldv + (cc * EPC < vcols ? cc * EPC : 0);
         }
       }
       lds_dma16(src, slot + (uint32_t)(u * NT + w * 64) * 16u);
@@ -147,10 +160,11 @@ struct TileCursor {
 };
 
 // B fragments of [V 1] for the contraction over tokens (paired token slots) straight from
-// the raw V rows of a slot; the last block is the ones column (z).
+// the raw V rows of a slot; the last block is the ones column (z). Blocks at or past vcols
+// (a narrower column group) are zero.
 template <typename T, int D, int DV, int NT>
 __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<typename Ops<T>::C> (&vf)[DV / 16 + 1],
-                                            int c, int g) {
+                                            int c, int g, int vcols = DV) {
   using C = typename Ops<T>::C;
   using Rg = Ring<T, D, DV, NT, true>;
   constexpr int NB = DV / 16 + 1;
@@ -174,6 +188,11 @@ __device__ __forceinline__ void value_frags(const unsigned char* slot, vec8<type
         vf[nb][j] = *reinterpret_cast<const float*>(slot + Rg::v_off(row, nb * 16 + c));
       }
     }
+  }
+  if (vcols < DV) {
+#pragma unroll
+    for (int nb = 0; nb < NB - 1; ++nb)
+      if (nb * 16 >= vcols) vf[nb] = zero8<C>();
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) vf[NB - 1][j] = to_t<C>(c == 0 ? 1.f : 0.f);
@@ -212,16 +231,21 @@ constexpr float kKeyMargin = 8.f;
 // Omega' instead of its 11-bit rounding (the gradient kernels need that at large input norms).
 // Each wave keeps its residual fragments in its own part of LDS (registers are full); launch this
 // variant with a 4-slot ring so that two workgroups still fit on a CU.
-template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false, bool PSPLIT = false>
-__global__ void __launch_bounds__(64 * RedSplit<M>::NW, RedSplit<M>::NW < 2 ? 1 : RedSplit<M>::NW / 2)
+// Shapes: D, DV and M are compiled. With GEN a call may use fewer features (m_valid <= M, a
+// multiple of 16: the features past it are masked to zero and their wave maxima written as -inf)
+// and a column group of a wider V (rows ldv apart, vcols <= DV valid columns); without GEN those
+// arguments are ignored (m_valid = M, ldv = vcols = DV).
+template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false, bool PSPLIT = false, bool GEN = false>
+__global__ void __launch_bounds__(64 * (RedSplit<M, D>::NW), (RedSplit<M, D>::WPE))
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
                  const typename Ops<T>::P* __restrict__ omf_lo,
                  int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
                  float* __restrict__ part, float* __restrict__ zpart, float* __restrict__ pmax, int seg_tiles,
-                 int nseg) {
+                 int nseg, int m_valid_, int ldv_, int vcols_) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
-  constexpr int NW = RedSplit<M>::NW, FB = RedSplit<M>::FB;
+  constexpr int NW = RedSplit<M, D>::NW, FB = RedSplit<M, D>::FB;
+  const int m_valid = GEN ? m_valid_ : M, ldv = GEN ? ldv_ : DV, vcols = GEN ? vcols_ : DV;
   constexpr int NFC = (M + 31) / 32;
   static_assert(FB % 2 == 0 || NW == 1, "an odd block count per wave only with a single wave");
   constexpr int NT = 64 * NW;
@@ -282,7 +306,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         }
       }
     }
-    if (lane == 0) pmax[slot * NW + w] = fmax;
+    if (lane == 0) pmax[slot * NW + w] = w * FB * 16 < m_valid ? fmax : -INFINITY;  // -inf: no valid feature
   };
   auto zero_sums = [&]() {
 #pragma unroll
@@ -336,7 +360,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   TileCursor ahead(t_beg, tpb), cur(t_beg, tpb), cv(t_beg, tpb);
 #pragma unroll
   for (int s = 0; s < R - 1; ++s) {
-    Rg::issue(K, V, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT);
+    Rg::issue(K, V, L, ahead.bh, ahead.tok0(), s < n_tiles, ring0 + s * Rg::SLOT, ldv, vcols);
     if (s < n_tiles) ahead.next();
   }
   // tiles 0 and 1 converted up front; iteration t converts tile t+2
@@ -408,6 +432,14 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         for (int i = 0; i < 4; ++i) tw[tb][i] = fast_exp2(tw[tb][i]);
     }
     if constexpr (KIND == kPrf) {
+      if (m_valid < M) {  // features past m_valid: exponent -inf, feature 0
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+          if ((w * FB + fb) * 16 + c >= m_valid) {
+            pcur[0][fb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            pcur[1][fb] = pcur[0][fb];
+          }
+      }
       float lmax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
@@ -418,7 +450,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       // the running maximum moves only if some exponent is positive (or on a new (b,h))
       // it moves kKeyMargin past the tile maximum, so later tiles seldom move it again
       if (first || __builtin_amdgcn_ballot_w64(lmax > 0.f) != 0) {
-        const float shift = wave_max(lmax) + kKeyMargin;
+        const float tmx = wave_max(lmax);  // -inf only in a wave without a valid feature
+        const float shift = (tmx > -INFINITY ? tmx : 0.f) + kKeyMargin;
         if (!first) {
           const float sc = fast_exp2(-shift);
 #pragma unroll
@@ -461,7 +494,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         } else if constexpr (KIND == kTrig) {
           f = trig_feature(a, (w * FB + fb) * 16 + c, M) * tw[j >> 2][j & 3];
         } else {
-          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L;
+          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L && (w * FB + fb) * 16 + c < m_valid;
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
         af[fb][j] = to_t<C>(f);
@@ -471,7 +504,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
     // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
     // the piece: a filler slot into an unused buffer) and the next copies
     vec8<C> vf[NB];
-    value_frags<T, D, DV, NT>(ring[s_cur], vf, c, g);
+    value_frags<T, D, DV, NT>(ring[s_cur], vf, c, g, vcols);
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -483,7 +516,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
     cv.next();
     {
       const bool live = it + R - 1 < n_tiles;
-      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT);
+      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT, ldv, vcols);
       if (live) ahead.next();
     }
     lds_barrier();

@@ -104,7 +104,8 @@ def test_decode_argument_checks():
     assert call(S=MISALIGNED) == INVALID
     assert call(N=0) == INVALID
     assert call(d=128) == UNSUPPORTED
-    assert call(dv=48) == UNSUPPORTED
+    assert call(dv=40) == UNSUPPORTED   # value widths: multiples of 16 up to 256
+    assert call(dv=272) == UNSUPPORTED
     assert call(m=100) == UNSUPPORTED
 
 
@@ -193,3 +194,30 @@ def test_bidir_noalloc_checks_before_any_device_call():
     assert call(**big) == WORKSPACE
     # the headline workload's workspace fits
     assert rf.workspace_size(False, 8, 12, 4096, 64, 64, 256, torch.bfloat16) <= rf.NOALLOC_MAX_BYTES
+
+
+@pytest.mark.parametrize("d,dv,m,dt,status", [
+    (128, 256, 512, 1, OK), (64, 208, 240, 1, OK), (16, 48, 16, 1, OK), (32, 80, 96, 0, OK), (64, 256, 256, 0, OK),
+    (128, 64, 64, 0, UNSUPPORTED),   # fp32: d <= 64 and m <= 256 outside the exact shapes
+    (64, 64, 512, 0, UNSUPPORTED),
+    (16, 16, 16, 0, OK),             # an exact shape
+    (64, 64, 528, 1, UNSUPPORTED), (64, 272, 64, 1, UNSUPPORTED), (48, 64, 64, 1, UNSUPPORTED),
+    (64, 40, 64, 1, UNSUPPORTED), (64, 64, 72, 1, UNSUPPORTED),
+])
+def test_shape_set(d, dv, m, dt, status):
+    """The sequence entry points take d in {16, 32, 64, 128}, dv and m multiples of 16 up to 256 and 512 (fp32: d <= 64
+    and m <= 256 outside the exact shapes): a supported shape has a workspace size and passes every check (it fails
+    only on the workspace size given here); others return FAVOR_ERR_UNSUPPORTED."""
+    n = rf._lib.favor_workspace_size(0, 2, 3, 100, d, dv, m, dt)
+    assert (n > 0) == (status == OK)
+    got = _bidir(d=d, dv=dv, m=m, dt=dt, wsb=16)
+    assert got == (WORKSPACE if status == OK else status)
+    c = rf.raw_call("favor_causal", FAKE, FAKE, FAKE, FAKE, 2, 3, 100, d, dv, m, dt, 0, ctypes.c_float(0.0), 0, FAKE,
+                    None, None, FAKE, ctypes.c_size_t(16), None)
+    assert c == (WORKSPACE if status == OK else status)
+
+
+def test_trig_only_on_exact_shapes():
+    assert _bidir(d=64, dv=64, m=256, kind=2, wsb=16) == WORKSPACE
+    assert _bidir(d=64, dv=128, m=256, kind=2, wsb=16) == UNSUPPORTED
+
