@@ -32,8 +32,10 @@
  *     or the exact row maximum; one constant per (b,h) for keys, or per segment
  *     prefix in the causal form) cancel exactly in the ratio, so results equal
  *     the unstabilised definitions up to rounding.
- *   - bf16 inputs are projected in fp16 (exact for 2^-14 <= |x| < 65504); values
- *     of magnitude 65504 or more are outside the supported domain.
+ *   - bf16 inputs are projected in fp16 (exact for 2^-14 <= |x| < 65504). Components
+ *     of magnitude 65504 or more are clamped to +-65504 for the projection only (the
+ *     norm term keeps the true value): keys of such norms get the zero features exact
+ *     arithmetic gives them, and such a query is projected along its clamped direction.
  */
 #ifndef FAVOR_H
 #define FAVOR_H

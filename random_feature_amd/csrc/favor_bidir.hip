@@ -454,12 +454,16 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
     for (int dc = 0; dc < DC; ++dc) {
       const int col = dc * 32 + 8 * g;
       const vec8<T> raw = (tok < L && col < D) ? ld8<T>(Xb + (size_t)tok * D + col) : zero8<T>();
+      float c2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = to_f(raw[j]);
-        s2 += v * v;
+        c2 += v * v;
         xf[dc][j] = to_t<P>(v);
       }
+      if constexpr (sizeof(P) == 2 && sizeof(T) == 2)
+        if (c2 >= kF16MaxSq) clamp_to_f16<P>(raw, xf[dc]);
+      s2 += c2;
     }
     s2 = group_sum(s2);
 #pragma unroll

@@ -76,6 +76,17 @@ __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ float to_f(f16 x) { return static_cast<float>(x); }
 
+// Inputs of a 16-bit projection: a chunk whose sum of squares reaches 65504^2 may hold a value beyond fp16's
+// range; its fp16 copy is taken clamped to +-65504 (rarely taken; the norm keeps the true value, so a key of
+// such a norm still gets the zero features exact arithmetic gives it, and nothing turns into inf or NaN).
+constexpr float kF16Max = 65504.f;
+constexpr float kF16MaxSq = 65504.f * 65504.f;
+template <typename P, typename V8>
+__device__ __forceinline__ void clamp_to_f16(const V8& x, vec8<P>& y) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = to_t<P>(__builtin_fminf(__builtin_fmaxf(to_f(x[j]), -kF16Max), kF16Max));
+}
+
 template <typename T> __device__ __forceinline__ vec8<T> zero8() {
   vec8<T> z;
 #pragma unroll

@@ -180,6 +180,8 @@ struct SweepRing {
             s2 += f * f;
             y[j] = to_t<P>(f);
           }
+          if constexpr (sizeof(P) == 2)
+            if (s2 >= kF16MaxSq) clamp_to_f16<P>(v8, y);
           *reinterpret_cast<vec8<P>*>(slot + q * 16) = y;
         } else {
           const f32x4 v4 = *reinterpret_cast<const f32x4*>(slot + q * 16);

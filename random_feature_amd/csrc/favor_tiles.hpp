@@ -121,6 +121,8 @@ struct Ring {
             s2 += f * f;
             y[j] = to_t<P>(f);
           }
+          if constexpr (sizeof(P) == 2)
+            if (s2 >= kF16MaxSq) clamp_to_f16<P>(x, y);
           *reinterpret_cast<vec8<P>*>(conv + row * KROW + cc * 8) = y;
         } else {
           const f32x4 x = *reinterpret_cast<const f32x4*>(slot + q * 16);

@@ -146,3 +146,27 @@ def test_decode_value_widths(d, dv, m, dtype):
     assert rel_err(outs, outs_ref) < TOL[dtype]
     assert np.max(np.abs(S.cpu().double().numpy() - S_ref)) / np.max(np.abs(S_ref)) < 1e-5
     assert rel_err(z, z_ref) < 1e-5
+
+
+@pytest.mark.parametrize("path", ["bidir", "causal"])
+def test_bf16_values_beyond_fp16_range(path):
+    """bf16 components of magnitude 65504 or more (here 1e6) in a few keys and one query: those keys' features are
+    zero in exact arithmetic (exp(w.y - |y|^2/2) with |y|^2 ~ 1e11), and so they are in the kernels (the fp16
+    projection copy is clamped, the norm is the true one). Every output stays finite; rows of the other queries
+    match the oracle."""
+    d, dv, m = 64, 64, 256
+    B, H, L = 1, 2, 200
+    q, k, v = _inputs(B, H, L, d, dv, torch.bfloat16, 6100)
+    k[0, 0, 5, 3] = 1e6
+    k[0, 1, 150, 0] = -2e6
+    k[0, 1, 40, 10] = 7e4
+    q[0, 0, 7, 1] = 1e6
+    om_dev = rf.make_omega(71, H, m, d)
+    om = om_dev.cpu().numpy()
+    fn, ofn = (rf.bidir, oracle.bidir) if path == "bidir" else (rf.causal, oracle.causal)
+    out = fn(q.cuda(), k.cuda(), v.cuda(), om_dev, out_f32=True).cpu()
+    assert torch.isfinite(out).all()
+    ref = ofn(q, k, v, om)
+    keep = np.ones(L, bool)
+    keep[7] = False  # the query beyond the range is projected along its clamped direction
+    assert rel_err(out[:, :, keep], ref[:, :, keep]) < TOL[torch.bfloat16]
