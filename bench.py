@@ -12,6 +12,7 @@ seeded inputs already resident in device memory:
   backward_bf16 favor_bidir_backward (dq, dk, dv) at bidir_bf16's shape, bf16 gradients
   causal_backward_bf16 favor_causal_backward (dq, dk, dv) at causal_bf16's shape, bf16 gradients
   trig_bf16   favor_bidir with trigonometric features (FAVOR_TRIG) at bidir_bf16's shape
+  features_bf16 favor_features alone on bidir_bf16's queries (phi written as fp32: 402 MB per step)
   bidir_fp32 / bidir_small  the fp32 parity workloads
 The step first runs untimed for --settle-ms (200 ms) so the GPU reaches its working
 clock, then W warm-up steps, then K timed steps. Prints one JSON line with
@@ -72,6 +73,8 @@ def _kernel_work(w: workloads.Workload, name: str, out_bytes: int):
         return th * (3 * proj + 2 * contr), th * ((2 * w.d + 2 * w.dv) * eb + 8 + w.d * out_bytes)
     if name == "cbwd_v":      # phi_K, phi~_Q, R update (value columns), dv = R^T phi_K
         return th * (2 * proj + 4 * w.m * w.dv), th * ((2 * w.d + 2 * w.dv) * eb + 4 + w.dv * out_bytes)
+    if name == "features":    # projection and map of every token-head; x read, phi (fp32, m) and logscale written
+        return th * proj, th * (w.d * eb + w.m * 4 + 4)
     if name == "decode":      # per (sequence, head): q,k projections, state read+write, out (+ gate, weight)
         sb = (w.m * w.dv + w.m) * 4
         gb = 8 if w.kind == "decode_gated" else 0
@@ -90,6 +93,7 @@ _PATH_SOURCES = {
     "backward": ["favor_backward.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
     "causal_backward": ["favor_causal_bwd.hip", "favor_segments.hpp", "favor_tiles.hpp", "favor_reduce.hpp",
                         "favor_device.hpp", "favor_plan.hpp"],
+    "features": ["favor_bidir.hip", "favor_tiles.hpp", "favor_reduce.hpp", "favor_device.hpp", "favor_plan.hpp"],
 }
 
 
@@ -150,9 +154,11 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, omega_mode: str 
     ncpu = len(os.sched_getaffinity(0))
     with threadpool_limits(ncpu):
         threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-        if w.kind in ("bidir", "cross", "causal", "backward", "causal_backward"):
+        if w.kind in ("bidir", "cross", "causal", "backward", "causal_backward", "features"):
             q, k, v = workloads.make_qkv(w)
-            if w.kind in ("backward", "causal_backward"):
+            if w.kind == "features":
+                fn = lambda q_, k_, v_, o_, kd, sl: oracle.features(q_, o_, kd)  # noqa: E731
+            elif w.kind in ("backward", "causal_backward"):
                 dout = workloads.make_dout(w)
                 fb = oracle.bidir_backward if w.kind == "backward" else oracle.causal_backward
                 fn = lambda q_, k_, v_, o_, kd, sl: fb(q_, k_, v_, o_, dout[sl], kd)  # noqa: E731
@@ -270,6 +276,9 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
             def step():
                 qq, kk, vv = sets[cur[0]]
                 bfn(qq, kk, vv, om, douts[cur[0]], ws=ws, out=grads)
+        elif w.kind == "features":
+            def step():
+                rf.features(sets[cur[0]][0], om, kind=fkind)
         else:
             ws = rf.workspace(w.kind == "causal", k, v, om)
             out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
@@ -377,7 +386,7 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
     # once, as _kernel_work counts them) over the measured time per step
     step_flops = step_bytes = 0
     for name in {"bidir": ("reduce", "output"), "cross": ("reduce", "output"), "causal": ("sweep",),
-                 "decode": ("decode",), "decode_gated": ("decode",)}.get(w.kind, ()):
+                 "decode": ("decode",), "decode_gated": ("decode",), "features": ("features",)}.get(w.kind, ()):
         f_, b_ = _kernel_work(w, name, out_bytes)
         step_flops += f_
         step_bytes += b_

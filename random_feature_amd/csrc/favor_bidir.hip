@@ -352,7 +352,7 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       float den = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) den += dpart[buf][tb0 + tt][c][ww];
-      rden[tt] = 1.0f / den;
+      rden[tt] = __builtin_amdgcn_rcpf(den);  // hardware reciprocal (1 ulp)
       if (!renorm) {
         // no D^-1: undo the stabilisers instead, giving phi(q).S in canonical scale
         // (phi = 2^(a' - n') / sqrt(m) on both sides; the keys' constant is gm)

@@ -150,7 +150,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         hi += *reinterpret_cast<const f32x4*>(base + 64);
         den += xo[ww][2 * NVB * 256 + tb * 16 + cq];
       }
-      const float rden = 1.0f / den;
+      const float rden = __builtin_amdgcn_rcpf(den);  // hardware reciprocal (1 ulp)
       const size_t off = (rowbase + tok) * ld + c8 * 8;
       if (out_f32) {
         f32x4* o4 = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off);

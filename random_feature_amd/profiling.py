@@ -5,6 +5,8 @@ reads it and prints
 
 * ``stats DB``: per kernel, the dispatch count and total / average / min / max duration,
   the table that ``rocprofv3 --kernel-trace --stats`` summarises;
+* ``counters``: per kernel, the average per dispatch of every counter in one or more ``--pmc`` runs, with
+  the MFMA pipe's busy fraction and instructions per wave derived from them;
 * ``traffic``: HBM bytes per launch of one kernel from two counter runs, ``--pmc
   FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (KiB per dispatch), each scaled by what the same
   counter reads for a plain copy kernel of known size in the same run (the int32
@@ -116,6 +118,54 @@ def traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int):
     }
 
 
+# SIMDs of the MI355X (256 CUs x 4), its XCDs (GRBM_GUI_ACTIVE as rocprofv3 reports it is the sum of the 8
+# XCDs' active cycles) and the matrix-pipe cycles of one 16x16x32 16-bit MFMA on gfx950
+N_SIMD = 1024
+N_XCD = 8
+MFMA_CYCLES = 16
+
+
+def counters(dbs, kernels=None):
+    """{kernel: {counter: average per dispatch}} over one or more counter runs (one pass per database), and derived
+    figures over the kernel's active cycles (GRBM_GUI_ACTIVE / 8 XCDs): the MFMA pipe's busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs), the same from the instruction count (SQ_INSTS_MFMA x 16
+    cycles), and instructions per wave."""
+    out = {}
+    for db in dbs:
+        con = _con(db)
+        rows = con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+        per = {}
+        for did, kn, cn, v in rows:
+            key = (short_name(kn), cn)
+            per.setdefault(key, {}).setdefault(did, 0.0)
+            per[key][did] += v
+        grbm = {}
+        for (k, cn), d in per.items():
+            if kernels and k not in kernels:
+                continue
+            avg = sum(d.values()) / len(d)
+            if cn == "GRBM_GUI_ACTIVE":
+                grbm[k] = avg
+            else:
+                out.setdefault(k, {})[cn] = avg
+        for k, g in grbm.items():
+            out.setdefault(k, {}).setdefault("GRBM_GUI_ACTIVE", g)
+    for k, c in out.items():
+        g = c.get("GRBM_GUI_ACTIVE")
+        if g:
+            g /= N_XCD
+            c["active_cycles"] = g
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                c["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * N_SIMD)
+            if "SQ_INSTS_MFMA" in c:
+                c["mfma_issue_frac"] = c["SQ_INSTS_MFMA"] * MFMA_CYCLES / (g * N_SIMD)
+        if c.get("SQ_WAVES"):
+            for n in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                if n in c:
+                    c[n + "_per_wave"] = c[n] / c["SQ_WAVES"]
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -128,7 +178,19 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--src-hash", default=None)
     t.add_argument("--out", default=None)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernels", nargs="*", default=None)
+    c.add_argument("--out", default=None)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        d = counters(a.dbs, a.kernels)
+        js = json.dumps(d, indent=1, sort_keys=True)
+        if a.out:
+            with open(a.out, "w") as fh:
+                fh.write(js + "\n")
+        print(js)
+        return 0
     if a.cmd == "stats":
         print(f"{'kernel':14s} {'calls':>6s} {'total_us':>12s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
         for n, k, tot, avg, mn, mx, pct in kernel_stats(a.db):

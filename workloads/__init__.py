@@ -44,7 +44,7 @@ import torch
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "bidir" | "cross" | "causal" | "decode" | "decode_gated" | "backward"
+    kind: str            # "bidir" | "cross" | "causal" | "decode" | "decode_gated" | "backward" | "features"
     dtype: str           # "f32" | "bf16"
     B: int
     H: int
@@ -87,6 +87,8 @@ WORKLOADS = {
     "causal_bf16": Workload("causal_bf16", "causal", "bf16", 4, 8, 8192, 64, 64, 256, 3, 0.5, 0.5, 0.5),
     "causal_backward_bf16": Workload("causal_backward_bf16", "causal_backward", "bf16", 4, 8, 8192, 64, 64, 256, 3,
                                      0.5, 0.5, 0.5),
+    "features_bf16": Workload("features_bf16", "features", "bf16", 8, 12, 4096, 64, 64, 256, 2,
+                              1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0), 1.0),
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 256, 16, 1, 64, 64, 256, 4, 1.0, 1.0, 1.0,
                             steps=1000, prior=2048),
     "decode_gated_bf16": Workload("decode_gated_bf16", "decode_gated", "bf16", 256, 16, 1, 64, 64, 256, 5,
