@@ -207,20 +207,25 @@ favor_status favor_decode_gated(const void* q, const void* k, const void* v, con
 
 /* favor_bidir_backward — gradients of favor_bidir's output (Performer equation 4 /
  * Algorithm 1; the pages time forward and backward, section 4.1) with respect to the raw
- * q, k and v, for positive softmax features (kind must be FAVOR_PRF; ReLU returns
- * FAVOR_ERR_UNSUPPORTED), given dout [B,H,L,dv] = dLoss/dout in `dtype`. The forward's
- * sums are recomputed. The chain rule through out = (Phi_Q S)/(Phi_Q z) and the feature map
- * phi(x) = exp(w.xs - |xs|^2/2)/sqrt(m), xs = d^-1/4 x:
+ * q, k and v, for positive softmax features (FAVOR_PRF) or the ReLU features of appendix A.4
+ * (FAVOR_RELU, with the forward's eps; FAVOR_TRIG returns FAVOR_ERR_UNSUPPORTED), given
+ * dout [B,H,L,dv] = dLoss/dout in `dtype`. The forward's sums are recomputed. The chain rule
+ * through out = (Phi_Q S)/(Phi_Q z), xs = d^-1/4 x:
  *   W_i = [dout_i, -(dout_i . out_i)] / (Phi_Q z)_i,  dPhi_Q = W [S z]^T,  [dS dz] = Phi_Q^T W,
- *   dPhi_K = [V 1] [dS dz]^T,  dv = Phi_K dS,  dx = d^-1/4 (Omega^T (phi*dphi) - xs (phi.dphi)).
+ *   dPhi_K = [V 1] [dS dz]^T,  dv = Phi_K dS,
+ * then through the feature map: PRF phi(x) = exp(w.xs - |xs|^2/2)/sqrt(m) gives
+ *   dx = d^-1/4 (Omega^T (phi*dphi) - xs (phi.dphi)),
+ * ReLU phi(x) = max(w.xs, 0)/sqrt(m) + eps gives dx = d^-1/4 Omega^T (1[w.xs > 0] dphi)/sqrt(m)
+ * (a ReLU row whose features are all zero with eps = 0 has a zero denominator: NaN, as in the
+ * forward). eps must be >= 0 (else FAVOR_ERR_INVALID_ARG); PRF ignores it.
  * dq, dk [B,H,L,d] and dv_grad [B,H,L,dv] are written in `dtype`, or fp32 when grad_f32 != 0.
  * ws: at least favor_backward_workspace_size(B, H, L, d, dv, m, dtype) bytes. Built shapes
  * (d, dv, m): (16,16,32) (32,32,64) (64,64,128) (64,64,256), both dtypes; others return
  * FAVOR_ERR_UNSUPPORTED. Checks and errors otherwise as favor_bidir. */
 favor_status favor_bidir_backward(const void* q, const void* k, const void* v, const float* omega,
                                   const void* dout, int B, int H, int L, int d, int dv, int m,
-                                  favor_dtype dtype, favor_kind kind, int grad_f32, void* dq, void* dk,
-                                  void* dv_grad, void* ws, size_t ws_bytes, hipStream_t stream);
+                                  favor_dtype dtype, favor_kind kind, float eps, int grad_f32, void* dq,
+                                  void* dk, void* dv_grad, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace favor_bidir_backward needs; 0 if the arguments are invalid. */
 size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype);
@@ -237,8 +242,8 @@ size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, 
  * as favor_bidir_backward; checks and errors as favor_bidir_backward. */
 favor_status favor_causal_backward(const void* q, const void* k, const void* v, const float* omega,
                                    const void* dout, int B, int H, int L, int d, int dv, int m,
-                                   favor_dtype dtype, favor_kind kind, int grad_f32, void* dq, void* dk,
-                                   void* dv_grad, void* ws, size_t ws_bytes, hipStream_t stream);
+                                   favor_dtype dtype, favor_kind kind, float eps, int grad_f32, void* dq,
+                                   void* dk, void* dv_grad, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace favor_causal_backward needs; 0 if the arguments are invalid. */
 size_t favor_causal_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype);

@@ -48,8 +48,8 @@ _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i
 _lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_decode_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
-_lib.favor_bidir_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
-                                      _vp, _sz, _vp]
+_lib.favor_bidir_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                      _vp, _vp, _sz, _vp]
 _lib.favor_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.favor_backward_workspace_size.restype = _sz
 _lib.favor_causal_backward.argtypes = _lib.favor_bidir_backward.argtypes
@@ -289,13 +289,13 @@ def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool 
     return out
 
 
-def bidir_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None, out=None):
+def bidir_backward(q, k, v, omega, dout, kind="prf", eps: float = 0.0, grad_f32: bool = False, ws=None, out=None):
     """Gradients (dq, dk, dv) of bidir()'s output for the upstream gradient `dout` (the forward sums are
-    recomputed). `out`: optional preallocated (dq, dk, dv)."""
-    return _backward("favor_bidir_backward", backward_workspace, q, k, v, omega, dout, kind, grad_f32, ws, out)
+    recomputed; kind "prf" or "relu" with the forward's eps). `out`: optional preallocated (dq, dk, dv)."""
+    return _backward("favor_bidir_backward", backward_workspace, q, k, v, omega, dout, kind, eps, grad_f32, ws, out)
 
 
-def _backward(fn, wsfn, q, k, v, omega, dout, kind, grad_f32, ws, out):
+def _backward(fn, wsfn, q, k, v, omega, dout, kind, eps, grad_f32, ws, out):
     B, H, L, _, d, dv, m = _check_seq(q, k, v, omega, resident=False)
     _need(dout, "dout", 4, shape=(B, H, L, dv), dtype=q.dtype)
     _resident(q=q, k=k, v=v, omega=omega, dout=dout)
@@ -314,16 +314,17 @@ def _backward(fn, wsfn, q, k, v, omega, dout, kind, grad_f32, ws, out):
         for t, n, last in ((dq, "dq", d), (dk, "dk", d), (dvv, "dv", dv)):
             _check_out(t, n, (B, H, L, last), gdt, q.device)
     _check(fn, getattr(_lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), _ptr(dout), B, H, L, d, dv, m,
-                                 _dtype_code(q), _kind(kind), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk), _ptr(dvv),
+                                 _dtype_code(q), _kind(kind), float(eps), 1 if grad_f32 else 0, _ptr(dq), _ptr(dk),
+                                 _ptr(dvv),
                                  _ptr(ws), ws_bytes, ctypes.c_void_p(_stream(q.device))))
     return dq, dk, dvv
 
 
-def causal_backward(q, k, v, omega, dout, kind="prf", grad_f32: bool = False, ws=None, out=None):
+def causal_backward(q, k, v, omega, dout, kind="prf", eps: float = 0.0, grad_f32: bool = False, ws=None, out=None):
     """Gradients (dq, dk, dv) of causal()'s output for the upstream gradient `dout` (the forward is
     recomputed). `out`: optional preallocated (dq, dk, dv)."""
-    return _backward("favor_causal_backward", causal_backward_workspace, q, k, v, omega, dout, kind, grad_f32, ws,
-                     out)
+    return _backward("favor_causal_backward", causal_backward_workspace, q, k, v, omega, dout, kind, eps, grad_f32,
+                     ws, out)
 
 
 def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,

@@ -146,20 +146,20 @@ size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, 
 
 favor_status favor_bidir_backward(const void* q, const void* k, const void* v, const float* omega,
                                   const void* dout, int B, int H, int L, int d, int dv, int m, favor_dtype dtype,
-                                  favor_kind kind, int grad_f32, void* dq, void* dk, void* dv_, void* ws,
+                                  favor_kind kind, float eps, int grad_f32, void* dq, void* dk, void* dv_, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
   const favor::Shape s{B, H, L, d, dv, m};
-  favor_status st = check_seq(s, dtype, kind, 0.f);
+  favor_status st = check_seq(s, dtype, kind, eps);
   if (st != FAVOR_OK) return st;
   if (!q || !k || !v || !omega || !dout || !dq || !dk || !dv_ || !ws) return FAVOR_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, (const void*)omega, dout, (const void*)dq, (const void*)dk, (const void*)dv_,
                         (const void*)ws})
     if (!aligned16(p)) return FAVOR_ERR_INVALID_ARG;
-  if (kind != FAVOR_PRF) return FAVOR_ERR_UNSUPPORTED;
+  if (kind != FAVOR_PRF && kind != FAVOR_RELU) return FAVOR_ERR_UNSUPPORTED;
   if (!favor::bwd_shape_built(d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_backward(s, dtype).total) return FAVOR_ERR_WORKSPACE;
-  return hip_status(
-      favor::launch_backward(q, k, v, omega, dout, s, dtype, grad_f32 ? 1 : 0, dq, dk, dv_, ws, stream));
+  return hip_status(favor::launch_backward(q, k, v, omega, dout, s, dtype, kind, eps, grad_f32 ? 1 : 0, dq, dk, dv_,
+                                           ws, stream));
 }
 
 size_t favor_causal_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype) {
@@ -170,10 +170,10 @@ size_t favor_causal_backward_workspace_size(int B, int H, int L, int d, int dv, 
 
 favor_status favor_causal_backward(const void* q, const void* k, const void* v, const float* omega,
                                    const void* dout, int B, int H, int L, int d, int dv, int m, favor_dtype dtype,
-                                   favor_kind kind, int grad_f32, void* dq, void* dk, void* dv_, void* ws,
+                                   favor_kind kind, float eps, int grad_f32, void* dq, void* dk, void* dv_, void* ws,
                                    size_t ws_bytes, hipStream_t stream) {
   const favor::Shape s{B, H, L, d, dv, m};
-  favor_status st = check_seq(s, dtype, kind, 0.f);
+  favor_status st = check_seq(s, dtype, kind, eps);
   if (st != FAVOR_OK) return st;
   if (!q || !k || !v || !omega || !dout || !dq || !dk || !dv_ || !ws) return FAVOR_ERR_INVALID_ARG;
   for (const void* p : {q, k, v, (const void*)omega, dout, (const void*)dq, (const void*)dk, (const void*)dv_,
@@ -182,7 +182,7 @@ favor_status favor_causal_backward(const void* q, const void* k, const void* v, 
   if (kind != FAVOR_PRF) return FAVOR_ERR_UNSUPPORTED;
   if (!favor::bwd_shape_built(d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_causal_backward(s, dtype).total) return FAVOR_ERR_WORKSPACE;
-  return hip_status(favor::launch_causal_backward(q, k, v, omega, dout, s, dtype, grad_f32 ? 1 : 0, dq, dk, dv_,
+  return hip_status(favor::launch_causal_backward(q, k, v, omega, dout, s, dtype, kind, eps, grad_f32 ? 1 : 0, dq, dk, dv_,
                                                   ws, stream));
 }
 

@@ -8,7 +8,9 @@
 // and through the positive feature map phi(x) = exp(w.xs - |xs|^2/2)/sqrt(m), xs = d^-1/4 x:
 //   dx = d^-1/4 (Omega^T (phi * dphi) - xs sum_r phi_r dphi_r).
 // For the queries sum_r phi_r dphi_r = g_i . out_i - g_i . out_i = 0, so only the first term
-// remains. Every per-row constant of the query features and the keys' common constant
+// remains. Through the ReLU map phi_r(x) = max(w_r.xs, 0)/sqrt(m) + eps (appendix A.4 of the
+// Performer paper) the derivative is a mask: dx = d^-1/4 Omega^T (1[w.xs > 0] * dphi)/sqrt(m); the
+// kernels below take KIND = kRelu with phi' = phi itself (no stabiliser, key scale F_j = 1). Every per-row constant of the query features and the keys' common constant
 // cancel in phi * dphi (query side) or come out as one per-key factor (key side), so the
 // kernels work with stabilised features throughout:
 //   query side: phi' = 2^(a' - max_r a'), features of the row scaled to a largest entry of 1;
@@ -177,13 +179,15 @@ __device__ __forceinline__ int scale_exp(float x) {
 //                in LDS), B = W (transposing reads), both as sums of two bf16 parts;
 //                accumulated over the piece's tiles of one (b,h) and written as a partial in
 //                the reduction's fragment layout
-template <typename T, int D, int DV, int M>
+// KIND = kRelu: phi' = max(a, 0)/sqrt(m) + eps (the features themselves, no row maximum), and the
+// rows of dPhi_Q carry the mask 1[a > 0] instead of the factor phi' (1/sqrt(m) goes into the scale).
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ srow, int H, int L, int tpb,
              long long T_all, int G, int grad_f32, float* __restrict__ dpart, float* __restrict__ dzpart,
-             void* __restrict__ dq) {
+             void* __restrict__ dq, float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using XS = typename BwdOps<T>::XS;
   using XB = typename BwdOps<T>::XB;
@@ -395,13 +399,15 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) mma16_split_a<PSO>(pq[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], qf[dc]);
       }
-      float mx = -INFINITY;
+      if constexpr (KIND == kPrf) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
+        for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
-      mx = group_max(mx);
-      if (g == 0) qmx[tb * 16 + c][w] = mx;
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pq[tb][fb][i]);
+        mx = group_max(mx);
+        if (g == 0) qmx[tb * 16 + c][w] = mx;
+      }
     }
     // ---- u = S g (scaled), [feature][query]
     f32x4 uq[2][FB];
@@ -420,19 +426,30 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
     lds_barrier();  // B1: row maxima
     store_pending();
 
-    // ---- phi' = 2^(a' - max); D' and A partials; phi' rows for the dS transposes
+    // ---- phi' = 2^(a' - max) (ReLU: the features); D' and A partials; phi' rows for the dS transposes
+    unsigned pos = 0;  // ReLU: bit (tb*FB + fb)*4 + i set where a > 0
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      float mx = qmx[tb * 16 + c][0];
+      float mx = 0.f;
+      if constexpr (KIND == kPrf) {
+        mx = qmx[tb * 16 + c][0];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
+        for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
+      }
       float dz = 0.f, da = 0.f;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         vec4<XB> e4, e4lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float ph = fast_exp2(pq[tb][fb][i] - mx);
+          float ph;
+          if constexpr (KIND == kPrf) {
+            ph = fast_exp2(pq[tb][fb][i] - mx);
+          } else {
+            const float a = pq[tb][fb][i];
+            if (a > 0.f) pos |= 1u << ((tb * FB + fb) * 4 + i);
+            ph = fmaxf(a, 0.f) * inv_sqrt_m + eps;
+          }
           pq[tb][fb][i] = ph;
           dz += ph * zv[fb][i];
           da += ph * uq[tb][fb][i];
@@ -465,7 +482,10 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       for (int fb = 0; fb < FB; ++fb) {
         vec4<XS> p4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p4[i] = to_t<XS>(pq[tb][fb][i] * (uq[tb][fb][i] - zv[fb][i] * ad));
+        for (int i = 0; i < 4; ++i) {
+          const float fac = (KIND == kPrf) ? pq[tb][fb][i] : ((pos >> ((tb * FB + fb) * 4 + i)) & 1u ? 1.f : 0.f);
+          p4[i] = to_t<XS>(fac * (uq[tb][fb][i] - zv[fb][i] * ad));
+        }
         *reinterpret_cast<vec4<XS>*>(&prow[(tb * 16 + c) * PROW + (w * FB + fb) * 16 + 4 * g]) = p4;
       }
     }
@@ -481,7 +501,8 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
           den += dsum[row][ww];
           aa += asum[row][ww];
         }
-        const float rd = 1.f / den;
+        // rows past L: W = 0 (their denominators are not used; a ReLU row of zero features has D' = 0)
+        const float rd = tok0 + row < L ? 1.f / den : 0.f;
         vec8<XB> wb, wl;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -500,7 +521,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
             wbr[0][row * WROW + col] = xh;
             if constexpr (NSPL == 2) wbr[NSPL - 1][row * WROW + col] = to_t<XB>(x - to_f(xh));
           }
-          rsc[row] = ldexpf(rd * (1.f / kLog2e), e);
+          rsc[row] = ldexpf(rd * (KIND == kPrf ? 1.f / kLog2e : inv_sqrt_m), e);
         }
       }
     }
@@ -577,13 +598,15 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
 //   dV           per wave, blocks of dV^T: A = dS^T (bf16 fragments over all features),
 //                B = phi' rows (bf16)
 //   both scaled by F_j (and the operand scales) and stored.
-template <typename T, int D, int DV, int M>
+// KIND = kRelu: phi' = max(a, 0)/sqrt(m) + eps (no row maximum, F_j = 1), P = 1[a > 0] * dPhi_K with
+// 1/sqrt(m) in the scale of dk, and no norm term.
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo,
              const typename Ops<T>::P* __restrict__ omT, const float* __restrict__ dsrow,
              const float* __restrict__ gmx, int H, int L, int tpb, long long T_all, int G, float nscale,
-             float s2, int grad_f32, void* __restrict__ dk, void* __restrict__ dv) {
+             float s2, int grad_f32, void* __restrict__ dk, void* __restrict__ dv, float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using XS = typename BwdOps<T>::XS;
   using XB = typename BwdOps<T>::XB;
@@ -744,13 +767,15 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) mma16_split_a<PSO>(pk[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], kf[dc]);
       }
-      float mx = -INFINITY;
+      if constexpr (KIND == kPrf) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int fb = 0; fb < FB; ++fb)
+        for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pk[tb][fb][i]);
-      mx = group_max(mx);
-      if (g == 0) qmx[tb * 16 + c][w] = mx;
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pk[tb][fb][i]);
+        mx = group_max(mx);
+        if (g == 0) qmx[tb * 16 + c][w] = mx;
+      }
     }
     // ---- [V 1] rows scaled per key to [1/2, 1) (fp16)
 #pragma unroll
@@ -784,9 +809,12 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
     // ---- phi', dPhi_K, P, rho; P and phi' rows
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      float mx = qmx[tb * 16 + c][0];
+      float mx = 0.f;
+      if constexpr (KIND == kPrf) {
+        mx = qmx[tb * 16 + c][0];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
+        for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[tb * 16 + c][ww]);
+      }
       vec8<XS> vf[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) vf[kc] = ld8<XS>(&vsr[(tb * 16 + c) * WROW + kc * 32 + 8 * g]);
@@ -800,8 +828,15 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
         vec4<XB> f4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float ph = fast_exp2(pk[tb][fb][i] - mx);
-          const float pp = ph * dp[i];  // P = phi' * dPhi_K (scaled)
+          float ph, pp;
+          if constexpr (KIND == kPrf) {
+            ph = fast_exp2(pk[tb][fb][i] - mx);
+            pp = ph * dp[i];  // P = phi' * dPhi_K (scaled)
+          } else {
+            const float a = pk[tb][fb][i];
+            ph = fmaxf(a, 0.f) * inv_sqrt_m + eps;
+            pp = a > 0.f ? dp[i] : 0.f;  // P = 1[a > 0] * dPhi_K (scaled)
+          }
           r += pp;
           p4[i] = to_t<XS>(pp);
           f4[i] = to_t<XB>(ph);
@@ -831,6 +866,12 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
           mma16(a, dt[(bi - BPWK) >> 1][fc], ld8<XB>(&frow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
       }
       const int krow = tb * 16 + c;
+      if constexpr (KIND != kPrf) {
+        // ReLU: no key scale, no norm term
+        a = a * (isk ? ldexpf(inv_sqrt_m, (int)(eD + vex[krow])) : 1.f);
+        pend[bi] = a;
+        continue;
+      }
       float mx = qmx[krow][0];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) mx = fmaxf(mx, qmx[krow][ww]);
@@ -905,9 +946,9 @@ BackwardPlan plan_backward(const Shape& s, int dtype) {
   return p;
 }
 
-template <typename T, int D, int DV, int M>
+template <typename T, int D, int DV, int M, int KIND>
 static hipError_t run_backward(const T* q, const T* k, const T* v, const float* omega, const T* dout,
-                               const Shape& s, int grad_f32, void* dq, void* dk, void* dv, void* ws,
+                               const Shape& s, float eps, int grad_f32, void* dq, void* dk, void* dv, void* ws,
                                hipStream_t st) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
@@ -927,7 +968,7 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
   float* dzpart = reinterpret_cast<float*>(base + p.off_dzpart);
   float* dsrow = reinterpret_cast<float*>(base + p.off_dsrow);
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = sc * kLog2e;
+  const float wscale = KIND == kPrf ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
@@ -942,41 +983,50 @@ static hipError_t run_backward(const T* q, const T* k, const T* v, const float* 
         omega, s.H, M, D, wscale, omt);
   }
   {
-    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, p.G_red, 64 * NWR, 0, st, k, v, omf,
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, KIND, true, true>, p.G_red, 64 * NWR, 0, st, k, v, omf,
         omlo, s.H,
-        s.L, p.tpb, p.T_all, p.G_red, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, DV, DV);
+        s.L, p.tpb, p.T_all, p.G_red, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, DV, DV);
   }
   {
     launch("combine", combine_rows_kernel<DV, M, NWR>, (unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st, part, zpart,
-        pmax, p.tpb, p.T_all, p.G_red, 1, srow, gmx);
+        pmax, p.tpb, p.T_all, p.G_red, KIND == kPrf ? 1 : 0, srow, gmx);
   }
   {
-    launch("bwd_q", bwd_q_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, q, dout, omf, omlo, omt, srow, s.H, s.L, p.tpb,
-        p.T_all, p.G, grad_f32, dpart, dzpart, dq);
+    launch("bwd_q", bwd_q_kernel<T, D, DV, M, KIND>, p.G, 64 * NWB, 0, st, q, dout, omf, omlo, omt, srow, s.H, s.L,
+        p.tpb, p.T_all, p.G, grad_f32, dpart, dzpart, dq, inv_sqrt_m, eps);
   }
   {
     launch("combine_d", combine_rows_kernel<DV, M, NWB>, (unsigned)(s.bh() * ((M + 31) / 32)), 256, 0, st, dpart,
         dzpart, nullptr, p.tpb, p.T_all, p.G, 0, dsrow, nullptr);
   }
   {
-    launch("bwd_k", bwd_k_kernel<T, D, DV, M>, p.G, 64 * NWB, 0, st, k, v, omf, omlo, omt, dsrow, gmx, s.H, s.L, p.tpb,
-        p.T_all, p.G, nscale, sc * sc, grad_f32, dk, dv);
+    launch("bwd_k", bwd_k_kernel<T, D, DV, M, KIND>, p.G, 64 * NWB, 0, st, k, v, omf, omlo, omt, dsrow, gmx, s.H, s.L,
+        p.tpb, p.T_all, p.G, nscale, sc * sc, grad_f32, dk, dv, inv_sqrt_m, eps);
   }
   return hipGetLastError();
 }
 
+template <typename T, int D, int DV, int M>
+static hipError_t run_backward_kind(const void* q, const void* k, const void* v, const float* omega, const void* dout,
+                                    const Shape& s, int kind, float eps, int grad_f32, void* dq, void* dk, void* dv,
+                                    void* ws, hipStream_t st) {
+  const T* q_ = static_cast<const T*>(q);
+  const T* k_ = static_cast<const T*>(k);
+  const T* v_ = static_cast<const T*>(v);
+  const T* o_ = static_cast<const T*>(dout);
+  if (kind == kPrf) return run_backward<T, D, DV, M, kPrf>(q_, k_, v_, omega, o_, s, eps, grad_f32, dq, dk, dv, ws, st);
+  if (kind == kRelu) return run_backward<T, D, DV, M, kRelu>(q_, k_, v_, omega, o_, s, eps, grad_f32, dq, dk, dv, ws, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
-                           const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
-                           hipStream_t st) {
-#define X(D_, DV_, M_)                                                                                          \
-  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
-    if (dtype == 0)                                                                                             \
-      return run_backward<float, D_, DV_, M_>(static_cast<const float*>(q), static_cast<const float*>(k),      \
-                                              static_cast<const float*>(v), omega,                              \
-                                              static_cast<const float*>(dout), s, grad_f32, dq, dk, dv, ws, st); \
-    return run_backward<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),           \
-                                           static_cast<const bf16*>(v), omega, static_cast<const bf16*>(dout),  \
-                                           s, grad_f32, dq, dk, dv, ws, st);                                    \
+                           const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk, void* dv,
+                           void* ws, hipStream_t st) {
+#define X(D_, DV_, M_)                                                                                           \
+  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                   \
+    if (dtype == 0) return run_backward_kind<float, D_, DV_, M_>(q, k, v, omega, dout, s, kind, eps, grad_f32, dq, \
+                                                                 dk, dv, ws, st);                                 \
+    return run_backward_kind<bf16, D_, DV_, M_>(q, k, v, omega, dout, s, kind, eps, grad_f32, dq, dk, dv, ws, st); \
   }
   FAVOR_BWD_SHAPES(X)
 #undef X

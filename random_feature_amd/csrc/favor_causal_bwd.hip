@@ -1616,8 +1616,10 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
 }
 
 hipError_t launch_causal_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
-                                  const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
-                                  hipStream_t st) {
+                                  const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk,
+                                  void* dv, void* ws, hipStream_t st) {
+  (void)eps;
+  if (kind != kPrf) return hipErrorInvalidValue;  // positive features only
 #define X(D_, DV_, M_)                                                                                          \
   if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
     if (dtype == 0)                                                                                             \

@@ -139,11 +139,12 @@ hipError_t launch_bidir(const void* q, const void* k, const void* v, const float
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
                          void* ws, hipStream_t st);
-hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout, const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv,
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
+                           const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk, void* dv,
                            void* ws, hipStream_t st);
 hipError_t launch_causal_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
-                                  const Shape& s, int dtype, int grad_f32, void* dq, void* dk, void* dv, void* ws,
-                                  hipStream_t st);
+                                  const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk,
+                                  void* dv, void* ws, hipStream_t st);
 // Device address of the library's own workspace array (FAVOR_BIDIR_NOALLOC_MAX_BYTES) on device `dev`, which
 // must be the current device; resolved on the first call for that device.
 hipError_t noalloc_scratch(int dev, void** ptr);

@@ -123,12 +123,14 @@ def test_decode_gated_argument_checks():
 @pytest.mark.parametrize("fn,wsfn", [("favor_bidir_backward", "favor_backward_workspace_size"),
                                      ("favor_causal_backward", "favor_causal_backward_workspace_size")])
 def test_backward_argument_checks(fn, wsfn):
-    def call(kind=0, d=64, dv=64, m=256, wsb=1 << 30, q=FAKE):
-        return rf.raw_call(fn, q, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, dv, m, 1, kind, 0, FAKE,
+    def call(kind=0, d=64, dv=64, m=256, wsb=1 << 30, q=FAKE, eps=0.0):
+        return rf.raw_call(fn, q, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, d, dv, m, 1, kind, ctypes.c_float(eps), 0, FAKE,
                            FAKE, FAKE, FAKE, ctypes.c_size_t(wsb), None)
     assert call(q=None) == INVALID
-    assert call(kind=1) == UNSUPPORTED          # ReLU has no backward kernels
-    assert call(kind=2) == UNSUPPORTED          # nor the trigonometric features
+    assert call(kind=1, eps=-1.0) == INVALID
+    if fn == "favor_causal_backward":
+        assert call(kind=1) == UNSUPPORTED      # ReLU: bidirectional backward only
+    assert call(kind=2) == UNSUPPORTED          # the trigonometric features have no backward kernels
     assert call(d=16, dv=16, m=256) == UNSUPPORTED
     assert call(wsb=8) == WORKSPACE
     assert getattr(rf._lib, wsfn)(1, 1, 64, 64, 64, 256, 1) > 0

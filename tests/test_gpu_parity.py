@@ -658,6 +658,44 @@ def test_bidir_backward(dtype, shape, L):
         assert e < TOL[dtype], (name, e)
 
 
+def _relu_decided_rows(x, om, rel=2e-6):
+    """Rows of x [B,H,L,d] whose every ReLU pre-activation w_r.xs (fp64) is farther than rel * max|w.xs| of the
+    head from zero: there the mask 1[w.xs > 0] of the gradient is the same in any precision near fp32. At a
+    pre-activation within rounding of zero the two sides may take different (equally valid) masks, and that
+    row's dq or dk then differs by one feature's term."""
+    xs = x.double().numpy() * float(x.shape[-1]) ** -0.25
+    a = np.einsum("bhld,hmd->bhlm", xs, np.asarray(om, np.float64))
+    thr = rel * np.abs(a).max(axis=(-2, -1), keepdims=True)
+    return np.abs(a).min(axis=-1) > thr[..., 0]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("L", [300, 33])
+@pytest.mark.parametrize("eps", [1e-3, 0.0])
+def test_bidir_backward_relu(dtype, shape, L, eps):
+    """Gradients through the ReLU feature map (appendix A.4: phi = max(w.xs, 0)/sqrt(m) + eps, whose derivative
+    is the mask 1[w.xs > 0]/sqrt(m)) against the oracle's, row by row: dv everywhere, dq and dk on the rows
+    whose mask is decided (the few others are counted and must stay few)."""
+    d, dv, m = shape
+    B, H = 2, 2
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 1700 + m + L)
+    g = workloads.make_tensor((B, H, L, dv), 1777 + L, 1.0, dtype)
+    om_dev, om = _omega(46, H, m, d)
+    ref = oracle.bidir_backward(q, k, v, om, g, kind="relu", eps=eps)
+    got = rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), kind="relu", eps=eps,
+                            grad_f32=True)
+    torch.cuda.synchronize()
+    errs = {"dv": rel_err(got[2], ref[2])}
+    for name, a, r, x in (("dq", got[0], ref[0], q), ("dk", got[1], ref[1], k)):
+        ok = _relu_decided_rows(x, om)
+        assert ok.mean() > 0.98, (name, ok.mean())
+        errs[name] = rel_err(a.cpu()[torch.from_numpy(ok)], np.asarray(r)[ok])
+    print(f"relu backward {dtype} {shape} L={L} eps={eps}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e < TOL[dtype], (name, e)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_bidir_backward_single_token(dtype):
     """The degenerate sequence L = 1: the output is v itself, so dv = dout exactly and dq, dk vanish; the
