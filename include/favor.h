@@ -232,9 +232,9 @@ size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, 
 
 /* favor_causal_backward — gradients of favor_causal's output (Performer appendix B.1,
  * equation 11: prefix sums S_i, z_i over j <= i, diagonal included) with respect to the raw q,
- * k and v, for positive softmax features (kind must be FAVOR_PRF; ReLU and trigonometric
- * features return FAVOR_ERR_UNSUPPORTED), given dout [B,H,L,dv] in `dtype`. The forward is
- * recomputed. With W_i = [dout_i, -(dout_i . out_i)] / (Phi_Q z)_i:
+ * k and v, for positive softmax features (FAVOR_PRF) or the ReLU features (FAVOR_RELU, with the
+ * forward's eps; trigonometric features return FAVOR_ERR_UNSUPPORTED), given dout [B,H,L,dv] in
+ * `dtype`. The forward is recomputed. With W_i = [dout_i, -(dout_i . out_i)] / (Phi_Q z)_i:
  *   dPhi_Q,i = [S_i z_i] W_i,  R_j = sum_{i>=j} Phi_Q,i W_i^T,  dPhi_K,j = R_j [v_j 1],
  *   dv_j = R_j^T Phi_K,j (value columns),  then through the feature map as favor_bidir_backward.
  * dq, dk [B,H,L,d] and dv_grad [B,H,L,dv] are written in `dtype`, or fp32 when grad_f32 != 0.

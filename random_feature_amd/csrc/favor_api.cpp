@@ -179,7 +179,7 @@ favor_status favor_causal_backward(const void* q, const void* k, const void* v, 
   for (const void* p : {q, k, v, (const void*)omega, dout, (const void*)dq, (const void*)dk, (const void*)dv_,
                         (const void*)ws})
     if (!aligned16(p)) return FAVOR_ERR_INVALID_ARG;
-  if (kind != FAVOR_PRF) return FAVOR_ERR_UNSUPPORTED;
+  if (kind != FAVOR_PRF && kind != FAVOR_RELU) return FAVOR_ERR_UNSUPPORTED;
   if (!favor::bwd_shape_built(d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_causal_backward(s, dtype).total) return FAVOR_ERR_WORKSPACE;
   return hip_status(favor::launch_causal_backward(q, k, v, omega, dout, s, dtype, kind, eps, grad_f32 ? 1 : 0, dq, dk, dv_,

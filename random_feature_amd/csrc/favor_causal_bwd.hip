@@ -17,6 +17,9 @@
 //   R''_j = sum_{i>=j} phi~_i [g_i, -gamma_i]^T 2^(M_p - M_p(i))        (segment p of key j)
 //   phi_K * dPhi_K = phi'_K,j * (R''_j [v_j 1]),   dv_j = R''_j^T phi'_K,j
 // which are the true gradients: the 1/sqrt(m) factors and the scales of both sides cancel.
+// KIND = kRelu (the ReLU map of appendix A.4, phi = max(a, 0)/sqrt(m) + eps) has no stabiliser: the
+// keys' features are phi_K itself, l_i = log2 D_i, phi~_i = phi_Q,i 2^-l_i, and the derivative factors
+// phi' of P become the masks 1[a > 0]/sqrt(m) (times 2^-l_i on the query side), with no norm term.
 // Kernels, in launch order (after the forward's Omega fragments, segment reduction and scan):
 //   omegaT_pair_kernel  Omega'^T as hi + lo fragments for the back-projections
 //   cbwd_fwd_kernel     per segment, forwards: the forward output of every chunk (carried term and
@@ -67,6 +70,29 @@ __device__ __forceinline__ void mma_split(f32x4& acc, const V& ah, const V& al, 
     mma16(acc, ah, bl);
     mma16(acc, al, bh);
   }
+}
+
+// Feature of a key from its projection accumulator: PRF 2^a (the bias -(n'_k + M) is already in a);
+// ReLU max(a, 0)/sqrt(m) + eps (the accumulator starts at zero).
+template <int KIND>
+__device__ __forceinline__ float key_feature(float a, float inv_sqrt_m, float eps) {
+  if constexpr (KIND == kPrf) return fast_exp2(a);
+  return fmaxf(a, 0.f) * inv_sqrt_m + eps;
+}
+
+// phi~ of a query (its feature over its denominator) from its projection accumulator: PRF 2^a (the
+// accumulator starts at -l); ReLU (max(a, 0)/sqrt(m) + eps) 2^-l (it starts at zero). l = +inf (queries
+// outside the segment) gives 0 either way.
+template <int KIND>
+__device__ __forceinline__ float query_feature(float a, float l, float inv_sqrt_m, float eps) {
+  if constexpr (KIND == kPrf) return fast_exp2(a);
+  return (fmaxf(a, 0.f) * inv_sqrt_m + eps) * fast_exp2(-l);
+}
+
+// Accumulator start of a projection: the PRF bias, zero for ReLU.
+template <int KIND>
+__device__ __forceinline__ float proj_start(float prf_bias) {
+  return KIND == kPrf ? prf_bias : 0.f;
 }
 
 // Operand of 8 paired slots from a [k][n] array in LDS (row stride `stride`): lane (c, g) gets
@@ -168,13 +194,14 @@ __global__ void omegaT_pair_kernel(const float* __restrict__ omega, int H, int m
 //       o^T = S'^T Phi'_Q^T (A = Sc) + [V 1]^T masked (Phi'_K Phi'_Q^T), the wave's partial to its
 //       LDS buffer (fp32 inputs: LDS atomics into one sum, for want of LDS); Sc takes the chunk
 //   Y   per query: D' = o_z, out = o / D', gamma = g . out; l = b + log2 D' and gamma to HBM
-template <typename T, int D, int DV, int M>
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo,
                 const float* __restrict__ cpart, const float* __restrict__ cz, const float* __restrict__ cmax, int H,
-                int L, int seg_len, int nseg, float nscale, float* __restrict__ lg, float* __restrict__ gam) {
+                int L, int seg_len, int nseg, float nscale, float* __restrict__ lg, float* __restrict__ gam,
+                float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -269,8 +296,8 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       f32x4 kbias;
       const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kbias[i] = -(n4[i] + mk);
-      const float b = qn[buf][tb * 16 + c] * omax;
+      for (int i = 0; i < 4; ++i) kbias[i] = proj_start<KIND>(-(n4[i] + mk));
+      const float b = KIND == kPrf ? qn[buf][tb * 16 + c] * omax : 0.f;
       exact |= b > kQueryBoundLimit;
       vec8<P> kf[DC], qf[DC];
 #pragma unroll
@@ -315,7 +342,7 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     }
     if (w == 0 && g == 0)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) qbias[tb * 16 + c] = qn[buf][tb * 16 + c] * omax + qsh[tb];
+      for (int tb = 0; tb < 2; ++tb) qbias[tb * 16 + c] = KIND == kPrf ? qn[buf][tb * 16 + c] * omax + qsh[tb] : 0.f;
 
     // ---- features: Phi'_K^T (A [feature][key], paired key slots), Phi'_Q (B [feature][query],
     // paired feature slots), each as hi + lo
@@ -323,11 +350,11 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split2(fast_exp2(pk[j >> 2][fb][j & 3]), afh[fb], afl[fb], j);
+      for (int j = 0; j < 8; ++j) split2(key_feature<KIND>(pk[j >> 2][fb][j & 3], inv_sqrt_m, eps), afh[fb], afl[fb], j);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split2(fast_exp2(pq[tb][j >> 2][j & 3]), bqh[tb], bql[tb], j);
+      for (int j = 0; j < 8; ++j) split2(key_feature<KIND>(pq[tb][j >> 2][j & 3], inv_sqrt_m, eps), bqh[tb], bql[tb], j);
 
     // ---- forward, carried term: o^T[col][q] = S'^T (A: Sc, paired feature slots) x Phi'_Q
     f32x4 o[NB][2];
@@ -477,7 +504,9 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 //       P = phi~ * dPhi~ = phi_Q * dPhi_Q as rows [query][feature] (hi + lo); St takes the chunk
 //   P   dq^T blocks = Omega'^T P / log2(e), every wave its share over all features (the head's
 //       Omega'^T hi/lo fragments staged in LDS once per workgroup)
-template <typename T, int D, int DV, int M>
+// KIND = kRelu: pq holds the derivative factor 1[a > 0] 2^-l / sqrt(m) in place of phi~, and dq takes no
+// 1/log2(e).
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
               const typename Ops<T>::P* __restrict__ omf,
@@ -485,7 +514,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
               const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ cpart,
               const float* __restrict__ cz, const float* __restrict__ cmax, const float* __restrict__ lg,
               const float* __restrict__ gam, int H, int L, int seg_len, int nseg, float nscale, int grad_f32,
-              void* __restrict__ dq) {
+              void* __restrict__ dq, float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -594,8 +623,9 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       f32x4 kbias;
       const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[buf][tb * 16 + 4 * g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kbias[i] = -(n4[i] + mk);
-      const float qb = -rl[buf][tb * 16 + c];
+      for (int i = 0; i < 4; ++i) kbias[i] = proj_start<KIND>(-(n4[i] + mk));
+      const float ql = rl[buf][tb * 16 + c];
+      const float qb = proj_start<KIND>(-ql);
       vec8<P> kf[DC], qf[DC];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -614,8 +644,11 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          split2(fast_exp2(pk[i]), afh[fb], afl[fb], 4 * tb + i);
-          pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+          split2(key_feature<KIND>(pk[i], inv_sqrt_m, eps), afh[fb], afl[fb], 4 * tb + i);
+          if constexpr (KIND == kPrf)
+            pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+          else
+            pq[tb][fb][i] = pq[tb][fb][i] > 0.f ? inv_sqrt_m * fast_exp2(-ql) : 0.f;
         }
       }
     }
@@ -746,7 +779,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       const int tok = tok0 + qr;
       if (tok < tend) {
         const size_t off = (rowbase + tok) * D + db * 16 + 4 * g;
-        a = a * (1.f / kLog2e);
+        if constexpr (KIND == kPrf) a = a * (1.f / kLog2e);
         if (grad_f32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = a;
         } else {
@@ -776,12 +809,12 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 //   T[f][col] += phi~^T (A, paired query slots, hi + lo) x [g, -gamma] (B: value fragments of the
 //   g rows, exact; the gamma block built in registers, hi + lo)
 // The total goes to trow[pc] as fp32 rows [feature][NB*16].
-template <typename T, int D, int DV, int M>
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo,
               const float* __restrict__ lg, const float* __restrict__ gam, int H, int L, int seg_len, int nseg,
-              float* __restrict__ trow) {
+              float* __restrict__ trow, float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -849,12 +882,14 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
       fetch(tok0 + 32);
     }
     f32x4 pq[2][FB];
+    f32x4 lq[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x4 bias;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][qb * 16 + 4 * g]);
+      lq[qb] = l4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bias[i] = -l4[i];
+      for (int i = 0; i < 4; ++i) bias[i] = proj_start<KIND>(-l4[i]);
       vec8<P> qf[DC];
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -872,7 +907,8 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) split2(fast_exp2(pq[j >> 2][fb][j & 3]), ah[fb], al[fb], j);
+      for (int j = 0; j < 8; ++j)
+        split2(query_feature<KIND>(pq[j >> 2][fb][j & 3], lq[j >> 2][j & 3], inv_sqrt_m, eps), ah[fb], al[fb], j);
     vec8<C> wv[NB];
     value_frags<T, D, DV, NT>(ring[buf], wv, c, g);
     vec8<C> zh, zl;  // the -gamma column (c == 0 of the last block)
@@ -937,14 +973,17 @@ cbwd_rscan_kernel(float* __restrict__ trow, const float* __restrict__ cmax, int 
 //       features; Rc takes the chunk's queries
 //   B1  dk^T blocks = Omega'^T P / log2(e) - d^-1/2 k rho over all features (Omega'^T staged in
 //       LDS once per workgroup)
-template <typename T, int D, int DV, int M>
+// KIND = kRelu: pk holds the key's derivative factor 1[a > 0]/sqrt(m) in place of phi'_K; dk has no
+// 1/log2(e) and no norm term.
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
               const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo, const typename Ops<T>::C* __restrict__ omTh,
               const typename Ops<T>::C* __restrict__ omTl, const float* __restrict__ rcar,
               const float* __restrict__ cmax, const float* __restrict__ lg, const float* __restrict__ gam, int H,
-              int L, int seg_len, int nseg, float nscale, float s2, int grad_f32, void* __restrict__ dk) {
+              int L, int seg_len, int nseg, float nscale, float s2, int grad_f32, void* __restrict__ dk,
+              float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -1046,8 +1085,8 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][tb * 16 + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kbias[i] = -(n4[i] + mk);
-        qbias[i] = -l4[i];
+        kbias[i] = proj_start<KIND>(-(n4[i] + mk));
+        qbias[i] = proj_start<KIND>(-l4[i]);
       }
       vec8<P> kf[DC], qf[DC];
 #pragma unroll
@@ -1067,8 +1106,11 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pk[tb][fb][i] = fast_exp2(pk[tb][fb][i]);
-          pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+          if constexpr (KIND == kPrf)
+            pk[tb][fb][i] = fast_exp2(pk[tb][fb][i]);
+          else
+            pk[tb][fb][i] = pk[tb][fb][i] > 0.f ? inv_sqrt_m : 0.f;  // the derivative factor
+          pq[tb][fb][i] = query_feature<KIND>(pq[tb][fb][i], l4[i], inv_sqrt_m, eps);
         }
       }
     }
@@ -1225,8 +1267,10 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         const int d0 = db * 16 + 4 * g;
         const vec4<P> k4 = *reinterpret_cast<const vec4<P>*>(sl + Rg::x_off(1, key, d0 / Rg::EPC) +
                                                              (d0 % Rg::EPC) * (int)sizeof(P));
+        if constexpr (KIND == kPrf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = a[i] * (1.f / kLog2e) - s2 * to_f(k4[i]) * rs;
+          for (int i = 0; i < 4; ++i) a[i] = a[i] * (1.f / kLog2e) - s2 * to_f(k4[i]) * rs;
+        }
         const size_t off = (rowbase + tok) * D + d0;
         if (grad_f32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dk) + off) = a;
@@ -1260,13 +1304,13 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 //                  + g^T (A: value fragments of the g rows) x masked (phi~ phi'_K^T, q >= key) (B),
 //       written over the wave's rows once they are read; Rt takes the chunk's queries
 //   B1  the waves' partials summed, dv stored
-template <typename T, int D, int DV, int M>
+template <typename T, int D, int DV, int M, int KIND>
 __global__ void __launch_bounds__(64 * BwdSplit<M>::NW, 1)
 cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dOut,
               const typename Ops<T>::P* __restrict__ omf,
     const typename Ops<T>::P* __restrict__ omf_lo, const float* __restrict__ rcar,
               const float* __restrict__ cmax, const float* __restrict__ lg, int H, int L, int seg_len, int nseg,
-              float nscale, int grad_f32, void* __restrict__ dv) {
+              float nscale, int grad_f32, void* __restrict__ dv, float inv_sqrt_m, float eps) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = BwdSplit<M>::NW, FB = BwdSplit<M>::FB;
@@ -1358,8 +1402,8 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&rl[buf][tb * 16 + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kbias[i] = -(n4[i] + mk);
-        qbias[i] = -l4[i];
+        kbias[i] = proj_start<KIND>(-(n4[i] + mk));
+        qbias[i] = proj_start<KIND>(-l4[i]);
       }
       vec8<P> kf[DC], qf[DC];
 #pragma unroll
@@ -1379,8 +1423,8 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pk[tb][fb][i] = fast_exp2(pk[tb][fb][i]);
-          pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
+          pk[tb][fb][i] = key_feature<KIND>(pk[tb][fb][i], inv_sqrt_m, eps);
+          pq[tb][fb][i] = query_feature<KIND>(pq[tb][fb][i], l4[i], inv_sqrt_m, eps);
         }
       }
     }
@@ -1536,9 +1580,9 @@ CausalBackwardPlan plan_causal_backward(const Shape& s, int dtype) {
   return p;
 }
 
-template <typename T, int D, int DV, int M>
+template <typename T, int D, int DV, int M, int KIND>
 static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const float* omega, const T* dout,
-                                      const Shape& s, int grad_f32, void* dq, void* dk, void* dv, void* ws,
+                                      const Shape& s, float eps, int grad_f32, void* dq, void* dk, void* dv, void* ws,
                                       hipStream_t st) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
@@ -1563,7 +1607,7 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
   float* gam = reinterpret_cast<float*>(base + p.off_gam);
   float* trow = reinterpret_cast<float*>(base + p.off_trow);
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = sc * kLog2e;
+  const float wscale = KIND == kPrf ? sc * kLog2e : sc;
   const float nscale = sc * sc * kLog2e * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)M);
   const float log2_sqrt_m = 0.5f * std::log2((float)M);
@@ -1579,57 +1623,66 @@ static hipError_t run_causal_backward(const T* q, const T* k, const T* v, const 
         omega, s.H, M, D, wscale, omth, omtl);
   }
   {
-    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, kPrf, true, true>, f.G, 64 * NWR, 0, st, k, v, omf,
+    launch("reduce", kv_reduce_kernel<T, D, DV, M, 4, KIND, true, true>, f.G, 64 * NWR, 0, st, k, v, omf,
         omlo, s.H,
-        s.L, f.tpb, f.T_all, f.G, 0.f, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg, s.m, DV, DV);
+        s.L, f.tpb, f.T_all, f.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, f.seg_len / 32, f.nseg, s.m, DV, DV);
   }
   {
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
     launch("scan", scan_kernel<D, DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, f.nseg * sizeof(float), st, part,
-        zpart, pmax, f.nseg, kPrf, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr, s.m, DV, DV);
+        zpart, pmax, f.nseg, KIND, log2_sqrt_m, cpart, cz, cmax, nullptr, nullptr, s.m, DV, DV);
   }
   {
-    launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, cpart, cz, cmax, s.H,
-        s.L, f.seg_len, f.nseg, nscale, lg, gam);
+    launch("cbwd_fwd", cbwd_fwd_kernel<T, D, DV, M, KIND>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, cpart, cz, cmax,
+        s.H, s.L, f.seg_len, f.nseg, nscale, lg, gam, inv_sqrt_m, eps);
   }
   {
-    launch("cbwd_q", cbwd_q_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, cpart, cz,
-        cmax, lg, gam, s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq);
+    launch("cbwd_q", cbwd_q_kernel<T, D, DV, M, KIND>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, cpart,
+        cz, cmax, lg, gam, s.H, s.L, f.seg_len, f.nseg, nscale, grad_f32, dq, inv_sqrt_m, eps);
   }
   {
-    launch("cbwd_t", cbwd_t_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, dout, omf, omlo, lg, gam, s.H, s.L, f.seg_len,
-        f.nseg, trow);
+    launch("cbwd_t", cbwd_t_kernel<T, D, DV, M, KIND>, f.G, 64 * NWB, 0, st, q, dout, omf, omlo, lg, gam, s.H, s.L,
+        f.seg_len, f.nseg, trow, inv_sqrt_m, eps);
   }
   {
     const int per = M * NBC, nblk = (per + 255) / 256;
     launch("rscan", cbwd_rscan_kernel, (unsigned)(s.bh() * nblk), 256, 0, st, trow, cmax, f.nseg, per, nblk);
   }
   {
-    launch("cbwd_k", cbwd_k_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, trow, cmax, lg,
-        gam, s.H, s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk);
+    launch("cbwd_k", cbwd_k_kernel<T, D, DV, M, KIND>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, omth, omtl, trow,
+        cmax, lg, gam, s.H, s.L, f.seg_len, f.nseg, nscale, sc * sc, grad_f32, dk, inv_sqrt_m, eps);
   }
   {
-    launch("cbwd_v", cbwd_v_kernel<T, D, DV, M>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, trow, cmax, lg, s.H, s.L,
-        f.seg_len, f.nseg, nscale, grad_f32, dv);
+    launch("cbwd_v", cbwd_v_kernel<T, D, DV, M, KIND>, f.G, 64 * NWB, 0, st, q, k, v, dout, omf, omlo, trow, cmax, lg, s.H,
+        s.L, f.seg_len, f.nseg, nscale, grad_f32, dv, inv_sqrt_m, eps);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D, int DV, int M>
+static hipError_t run_causal_backward_kind(const void* q, const void* k, const void* v, const float* omega,
+                                           const void* dout, const Shape& s, int kind, float eps, int grad_f32,
+                                           void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+  const T* q_ = static_cast<const T*>(q);
+  const T* k_ = static_cast<const T*>(k);
+  const T* v_ = static_cast<const T*>(v);
+  const T* o_ = static_cast<const T*>(dout);
+  if (kind == kPrf)
+    return run_causal_backward<T, D, DV, M, kPrf>(q_, k_, v_, omega, o_, s, eps, grad_f32, dq, dk, dv, ws, st);
+  if (kind == kRelu)
+    return run_causal_backward<T, D, DV, M, kRelu>(q_, k_, v_, omega, o_, s, eps, grad_f32, dq, dk, dv, ws, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_causal_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
                                   const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk,
                                   void* dv, void* ws, hipStream_t st) {
-  (void)eps;
-  if (kind != kPrf) return hipErrorInvalidValue;  // positive features only
-#define X(D_, DV_, M_)                                                                                          \
-  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                  \
-    if (dtype == 0)                                                                                             \
-      return run_causal_backward<float, D_, DV_, M_>(                                                           \
-          static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), omega,      \
-          static_cast<const float*>(dout), s, grad_f32, dq, dk, dv, ws, st);                                    \
-    return run_causal_backward<bf16, D_, DV_, M_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),    \
-                                                  static_cast<const bf16*>(v), omega,                           \
-                                                  static_cast<const bf16*>(dout), s, grad_f32, dq, dk, dv, ws,  \
-                                                  st);                                                          \
+#define X(D_, DV_, M_)                                                                                           \
+  if (s.d == D_ && s.dv == DV_ && s.m == M_) {                                                                   \
+    if (dtype == 0) return run_causal_backward_kind<float, D_, DV_, M_>(q, k, v, omega, dout, s, kind, eps,       \
+                                                                        grad_f32, dq, dk, dv, ws, st);            \
+    return run_causal_backward_kind<bf16, D_, DV_, M_>(q, k, v, omega, dout, s, kind, eps, grad_f32, dq, dk, dv,  \
+                                                       ws, st);                                                   \
   }
   FAVOR_BWD_SHAPES(X)
 #undef X

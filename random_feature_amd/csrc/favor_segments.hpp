@@ -192,7 +192,7 @@ struct SweepRing {
       s2 = lanes_sum<CPR_X>(s2);  // the CPR_X chunks of a row sit on consecutive lanes
       if (has) {
         if (x == 0)
-          qn[row] = __builtin_sqrtf(s2) * kQueryMargin;
+          qn[row] = __builtin_amdgcn_sqrtf(s2) * kQueryMargin;  // hardware square root (1 ulp, inside the margin)
         else
           kn[row] = row < nvalid ? s2 * nscale : INFINITY;
       }

@@ -128,8 +128,6 @@ def test_backward_argument_checks(fn, wsfn):
                            FAKE, FAKE, FAKE, ctypes.c_size_t(wsb), None)
     assert call(q=None) == INVALID
     assert call(kind=1, eps=-1.0) == INVALID
-    if fn == "favor_causal_backward":
-        assert call(kind=1) == UNSUPPORTED      # ReLU: bidirectional backward only
     assert call(kind=2) == UNSUPPORTED          # the trigonometric features have no backward kernels
     assert call(d=16, dv=16, m=256) == UNSUPPORTED
     assert call(wsb=8) == WORKSPACE

@@ -749,6 +749,37 @@ def test_causal_backward(dtype, shape, L):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape,L,BH", [((16, 16, 32), 300, 2), ((32, 32, 64), 33, 2), ((64, 64, 128), 300, 2),
+                                        ((64, 64, 256), 300, 2), ((64, 64, 256), 1100, 1)])
+@pytest.mark.parametrize("eps", [1e-3, 0.0])
+def test_causal_backward_relu(dtype, shape, L, BH, eps):
+    """Causal gradients through the ReLU map (appendix A.4) against the oracle's: dv on every row, dq and dk on
+    the rows whose mask 1[w.xs > 0] is decided (dq's row 0 is zero: query 0 sees only key 0). L = 300 runs as
+    two segments, L = 1100 as five."""
+    d, dv, m = shape
+    q, k, v = _inputs(BH, BH, L, d, dv, dtype, 2700 + m + L)
+    g = workloads.make_tensor((BH, BH, L, dv), 2777 + L, 1.0, dtype)
+    om_dev, om = _omega(49, BH, m, d)
+    ref = oracle.causal_backward(q, k, v, om, g, kind="relu", eps=eps)
+    got = rf.causal_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), kind="relu", eps=eps,
+                             grad_f32=True)
+    torch.cuda.synchronize()
+    dq = got[0].cpu().double().numpy()
+    assert float(np.abs(dq[..., 0, :]).max()) <= 1e-3 * float(np.abs(ref[0]).max()), "dq row 0"
+    errs = {"dv": rel_err(got[2], ref[2])}
+    for name, a, r, x in (("dq", got[0], ref[0], q), ("dk", got[1], ref[1], k)):
+        ok = _relu_decided_rows(x, om)
+        assert ok.mean() > 0.98, (name, ok.mean())
+        if name == "dq":
+            ok[..., 0] = False
+        errs[name] = rel_err(a.cpu()[torch.from_numpy(ok)], np.asarray(r)[ok])
+    print(f"causal relu backward {dtype} {shape} L={L} eps={eps}: " +
+          " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e < TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_causal_backward_many_segments(dtype):
     """A single (b,h) of 1100 tokens runs as five segments (the suffix carries cross four boundaries, the
     last segment is ragged); bf16 output gradients as the training step would store them."""
