@@ -14,6 +14,11 @@ seeded inputs already resident in device memory:
   trig_bf16   favor_bidir with trigonometric features (FAVOR_TRIG) at bidir_bf16's shape
   features_bf16 favor_features alone on bidir_bf16's queries (phi written as fp32: 402 MB per step)
   bidir_fp32 / bidir_small  the fp32 parity workloads
+For bidir and causal workloads the timed step reads Omega's fragments prepared once before
+timing (favor_omega_prepare, then favor_bidir_prepared / favor_causal_prepared: Omega is a
+fixed parameter between redraws); the same steps with Omega converted on every call
+(favor_bidir / favor_causal) are timed too and reported as *_omega_per_call
+(--omega-per-call makes those the timed step).
 The step first runs untimed for --settle-ms (200 ms) so the GPU reaches its working
 clock, then W warm-up steps, then K timed steps. Prints one JSON line with
 whole-job throughput (tokens/s = B*H*L per second; for decode, head-tokens/s), the
@@ -226,6 +231,7 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
     fkind = w.feature
     om = rf.make_omega(w.seed, w.H, w.m, w.d, "trig_pairs" if fkind == "trig" else omega_mode, device=dev)
 
+    prepared = False  # the timed step reads prepared Omega fragments (bidir and causal)
     if w.kind in ("decode", "decode_gated"):
         S = torch.empty((w.B, w.H, w.m, w.dv), dtype=torch.float32, device=dev)
         z = torch.empty((w.B, w.H, w.m), dtype=torch.float32, device=dev)
@@ -283,10 +289,19 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
             ws = rf.workspace(w.kind == "causal", k, v, om)
             out = torch.empty((w.B, w.H, w.Lq_eff, w.dv), dtype=dt, device=dev)
             fn = {"bidir": rf.bidir, "cross": rf.bidir_cross, "causal": rf.causal}[w.kind]
+            # Omega's fragments prepared once (favor_omega_prepare; the timed calls read them), unless
+            # --omega-per-call; the per-call figure is timed as well below
+            if w.kind in ("bidir", "causal"):
+                prep = rf.prepare_omega(om, w.dv, dt, fkind)
+                torch.cuda.synchronize()
+                prepared = not a.omega_per_call
 
             def step():
                 qq, kk, vv = sets[cur[0]]
-                fn(qq, kk, vv, om, kind=fkind, ws=ws, out=out)
+                if prepared:
+                    fn(qq, kk, vv, om, kind=fkind, ws=ws, out=out, prep=prep)
+                else:
+                    fn(qq, kk, vv, om, kind=fkind, ws=ws, out=out)
         tokens_per_step = w.B * w.H * w.Lq_eff   # output (query) tokens
         unit = "tokens/s"
         out_bytes = 2 if dt == torch.bfloat16 else 4
@@ -328,6 +343,19 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
+    # the same rotating steps with Omega converted on every call (favor_bidir / favor_causal)
+    per_call_ms = None
+    if prepared:
+        prepared = False
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            rotate(i)
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call_ms = e0.elapsed_time(e1)
+        prepared = True
     # the same steps on one input set only (it stays resident in the last-level cache): the warm figure
     warm_ms = None
     if sets is not None and len(sets) > 1:
@@ -409,11 +437,16 @@ def measure(a, wname: str, omega_mode: str = "ortho_chi") -> dict:
         "config": {"workload": w.name, "kind": w.kind, "B": w.B, "H": w.H, "L": w.L, "Lq": w.Lq_eff, "d": w.d,
                    "dv": w.dv, "m": w.m, "feature_map": fkind if omega_mode != "hyperbolic" else "prf_hyperbolic",
                    "omega": "trig_pairs" if fkind == "trig" else omega_mode,
-                   "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype},
+                   "out_dtype": "fp32" if w.kind.startswith("decode") else w.dtype,
+                   "omega_fragments": ("prepared once (favor_omega_prepare), read by every timed call" if prepared
+                                       else "converted on every call")},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
         "roofline": roofline,
         "whole_step": whole,
     }
+    if per_call_ms is not None:
+        res["value_omega_per_call"] = tokens_per_step * steps / (per_call_ms * 1e-3)
+        res["ms_per_step_omega_per_call"] = per_call_ms / steps
     if sets is not None:
         res["inputs"] = (f"{len(sets)} input sets in rotation, one per step"
                          if len(sets) > 1 else "one input set, reused every step")
@@ -439,6 +472,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bidir_bf16", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--omega-per-call", action="store_true",
+                    help="bidir/causal: time the calls that convert Omega on every call (favor_bidir, favor_causal) "
+                         "instead of the prepared-Omega calls")
     ap.add_argument("--no-companions", action="store_true",
                     help="headline workload only (without the causal and decode figures)")
     ap.add_argument("--omega-mode", default="ortho_chi", choices=["ortho_chi", "iid", "ortho_sqrtd", "hyperbolic"],
@@ -465,7 +501,8 @@ def main():
             c = measure(a2, cname)
             res[cname] = {k: c[k] for k in ("metric", "value", "unit", "steps", "ms_per_step",
                                             "ms_per_step_p10_p50_p90", "config", "kernels_us", "roofline",
-                                            "whole_step", "inputs")}
+                                            "whole_step", "inputs", "value_omega_per_call",
+                                            "ms_per_step_omega_per_call") if k in c}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(workloads.WORKLOADS[a.workload], omega_mode=a.omega_mode)
     print(json.dumps(res), flush=True)

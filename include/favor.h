@@ -179,6 +179,31 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
                           void* out, float* S_final, float* z_final,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Prepared random features. Omega stays fixed over many calls (the Performer paper redraws it
+ * only periodically, section 4.2 with Figure 5, appendix B.2), while favor_bidir and favor_causal convert it into
+ * the kernels' scaled MFMA fragments on every call. favor_omega_prepare does that conversion
+ * once into a caller buffer `prep` of at least favor_omega_prepared_size(H, d, dv, m, dtype)
+ * bytes (0 for invalid or unbuilt sizes; the fragments depend on the compiled kernel, hence dv);
+ * favor_bidir_prepared and favor_causal_prepared then read `prep` in place of omega and are
+ * otherwise favor_bidir and favor_causal (same workspace, checks, errors and bit-identical
+ * outputs). `prep` must come from favor_omega_prepare with the same H, d, dv, m, dtype and kind
+ * (the library cannot check this; another one gives wrong outputs, not an error); it is only read,
+ * so any number of calls may share it, and it stays valid until omega changes. Stream-ordered:
+ * prepare on the stream of the calls, or synchronise first. prep_bytes too small:
+ * FAVOR_ERR_WORKSPACE; FAVOR_TRIG as favor_bidir (exact shapes only). */
+size_t favor_omega_prepared_size(int H, int d, int dv, int m, favor_dtype dtype);
+favor_status favor_omega_prepare(const float* omega, int H, int d, int dv, int m, favor_dtype dtype,
+                                 favor_kind kind, void* prep, size_t prep_bytes, hipStream_t stream);
+favor_status favor_bidir_prepared(const void* q, const void* k, const void* v, const void* prep,
+                                  int B, int H, int L, int d, int dv, int m,
+                                  favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                                  void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+favor_status favor_causal_prepared(const void* q, const void* k, const void* v, const void* prep,
+                                   int B, int H, int L, int d, int dv, int m,
+                                   favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                                   void* out, float* S_final, float* z_final,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* favor_decode — one recurrent step for N sequences x H heads (the causal sums
  * advanced by one token; token t's output reads the state that includes t).
  * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical

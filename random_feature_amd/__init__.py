@@ -48,6 +48,11 @@ _lib.favor_causal.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i
 _lib.favor_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_decode_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp]
 _lib.favor_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+_lib.favor_omega_prepared_size.argtypes = [_i, _i, _i, _i, _i]
+_lib.favor_omega_prepared_size.restype = _sz
+_lib.favor_omega_prepare.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.favor_bidir_prepared.argtypes = _lib.favor_bidir.argtypes
+_lib.favor_causal_prepared.argtypes = _lib.favor_causal.argtypes
 _lib.favor_bidir_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                       _vp, _vp, _sz, _vp]
 _lib.favor_backward_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i]
@@ -64,7 +69,8 @@ _lib.favor_status_string.argtypes = [_i]
 _lib.favor_status_string.restype = ctypes.c_char_p
 for _fn in ("favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_noalloc",
             "favor_bidir_cross",
-            "favor_bidir_backward", "favor_causal", "favor_causal_backward", "favor_decode", "favor_decode_gated"):
+            "favor_bidir_backward", "favor_causal", "favor_causal_backward", "favor_decode", "favor_decode_gated",
+            "favor_omega_prepare", "favor_bidir_prepared", "favor_causal_prepared"):
     getattr(_lib, _fn).restype = _i
 
 EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favor_bidir", "favor_bidir_noalloc",
@@ -72,7 +78,8 @@ EXPORTED = ["favor_make_omega", "favor_make_omega_host", "favor_features", "favo
             "favor_bidir_backward", "favor_backward_workspace_size", "favor_causal", "favor_causal_backward",
             "favor_causal_backward_workspace_size",
             "favor_decode", "favor_decode_gated", "favor_workspace_size", "favor_timing_enable", "favor_timing_read",
-            "favor_status_string"]
+            "favor_status_string", "favor_omega_prepared_size", "favor_omega_prepare", "favor_bidir_prepared",
+            "favor_causal_prepared"]
 
 
 class FavorError(RuntimeError):
@@ -239,11 +246,45 @@ def features(x: torch.Tensor, omega: torch.Tensor, kind="prf", eps: float = 0.0)
     return phi, ls
 
 
-def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, ws=None, out=None):
-    """Bidirectional FAVOR+ (Performer equation 4). Returns out [B,H,L,dv]."""
+class PreparedOmega:
+    """Omega' fragments written by favor_omega_prepare for one omega [H,m,d] and (dv, dtype, kind): pass as
+    `prep=` to bidir() or causal() with that omega, value width, input dtype and kind (checked here: the library
+    itself cannot tell). Valid until omega changes."""
+
+    def __init__(self, buf, H, d, dv, m, dtype, kind):
+        self.buf, self.key = buf, (H, d, dv, m, dtype, _kind(kind))
+
+    def check(self, H, d, dv, m, dtype, kind):
+        if self.key != (H, d, dv, m, dtype, _kind(kind)):
+            raise ValueError(f"prepared omega is for (H, d, dv, m, dtype, kind) = {self.key}, "
+                             f"not {(H, d, dv, m, dtype, _kind(kind))}")
+
+
+def prepare_omega(omega, dv: int, dtype=torch.bfloat16, kind="prf") -> PreparedOmega:
+    """favor_omega_prepare: omega [H,m,d] fp32 on the device into the kernels' fragments for value width dv and
+    inputs of `dtype`, on the current stream."""
+    _need(omega, "omega", 3, dtype=torch.float32)
+    _resident(omega=omega)
+    H, m, d = omega.shape
+    code = {torch.float32: 0, torch.bfloat16: 1}.get(dtype)
+    if code is None:
+        raise ValueError(f"dtype {dtype}: float32 or bfloat16")
+    n = int(_lib.favor_omega_prepared_size(H, d, dv, m, code))
+    if n == 0:
+        raise FavorError("favor_omega_prepared_size", 2)
+    buf = torch.empty(n, dtype=torch.uint8, device=omega.device)
+    _check("favor_omega_prepare",
+           _lib.favor_omega_prepare(_ptr(omega), H, d, dv, m, code, _kind(kind), _ptr(buf), n,
+                                    ctypes.c_void_p(_stream(omega.device))))
+    return PreparedOmega(buf, H, d, dv, m, dtype, kind)
+
+
+def bidir(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, ws=None, out=None, prep=None):
+    """Bidirectional FAVOR+ (Performer equation 4). Returns out [B,H,L,dv]. prep: a PreparedOmega of this omega
+    (favor_bidir_prepared: no per-call conversion of omega)."""
     _check_seq(q, k, v, omega)
     return bidir_cross(q, k, v, omega, kind=kind, eps=eps, renormalize=True, out_f32=out_f32, ws=ws, out=out,
-                       _fn="favor_bidir")
+                       _fn="favor_bidir", _prep=prep)
 
 
 NOALLOC_MAX_BYTES = 64 << 20  # FAVOR_BIDIR_NOALLOC_MAX_BYTES
@@ -265,7 +306,7 @@ def bidir_noalloc(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = 
 
 
 def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool = True, out_f32: bool = False,
-                ws=None, out=None, _fn="favor_bidir_cross"):
+                ws=None, out=None, _fn="favor_bidir_cross", _prep=None):
     """Bidirectional FAVOR+ between q [B,H,Lq,d] and k [B,H,Lk,d], v [B,H,Lk,dv]; without renormalisation the
     output is phi(q).S in canonical feature scale. Returns out [B,H,Lq,dv]."""
     B, H, Lq, Lk, d, dv, m = _check_seq(q, k, v, omega, cross=True)
@@ -278,7 +319,13 @@ def bidir_cross(q, k, v, omega, kind="prf", eps: float = 0.0, renormalize: bool 
         out = torch.empty((B, H, Lq, dv), dtype=odt, device=q.device)
     _check_out(out, "out", (B, H, Lq, dv), odt, q.device)
     st = ctypes.c_void_p(_stream(q.device))
-    if _fn == "favor_bidir":
+    if _prep is not None:
+        _prep.check(H, d, dv, m, q.dtype, kind)
+        _fn = "favor_bidir_prepared"
+        r = _lib.favor_bidir_prepared(_ptr(q), _ptr(k), _ptr(v), _ptr(_prep.buf), B, H, Lq, d, dv, m,
+                                      _dtype_code(q), _kind(kind), float(eps), 1 if out_f32 else 0, _ptr(out),
+                                      _ptr(ws), ws_bytes, st)
+    elif _fn == "favor_bidir":
         r = _lib.favor_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, Lq, d, dv, m, _dtype_code(q),
                              _kind(kind), float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(ws), ws_bytes, st)
     else:
@@ -328,8 +375,9 @@ def causal_backward(q, k, v, omega, dout, kind="prf", eps: float = 0.0, grad_f32
 
 
 def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, return_state: bool = False,
-           ws=None, out=None):
-    """Causal FAVOR+ (Performer appendix B.1). Returns out, or (out, S_final, z_final) in canonical scale."""
+           ws=None, out=None, prep=None):
+    """Causal FAVOR+ (Performer appendix B.1). Returns out, or (out, S_final, z_final) in canonical scale.
+    prep: a PreparedOmega of this omega (favor_causal_prepared)."""
     B, H, L, _, d, dv, m = _check_seq(q, k, v, omega)
     need = workspace_size(True, B, H, L, d, dv, m, q.dtype)
     if ws is None:
@@ -343,10 +391,13 @@ def causal(q, k, v, omega, kind="prf", eps: float = 0.0, out_f32: bool = False, 
     if return_state:
         S = torch.empty((B, H, m, dv), dtype=torch.float32, device=q.device)
         z = torch.empty((B, H, m), dtype=torch.float32, device=q.device)
-    _check("favor_causal",
-           _lib.favor_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(omega), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
-                             float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(S), _ptr(z), _ptr(ws), ws_bytes,
-                             ctypes.c_void_p(_stream(q.device))))
+    fn, om = "favor_causal", omega
+    if prep is not None:
+        prep.check(H, d, dv, m, q.dtype, kind)
+        fn, om = "favor_causal_prepared", prep.buf
+    _check(fn, getattr(_lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(om), B, H, L, d, dv, m, _dtype_code(q), _kind(kind),
+                                 float(eps), 1 if out_f32 else 0, _ptr(out), _ptr(S), _ptr(z), _ptr(ws), ws_bytes,
+                                 ctypes.c_void_p(_stream(q.device))))
     return (out, S, z) if return_state else out
 
 

@@ -138,6 +138,38 @@ favor_status favor_bidir(const void* q, const void* k, const void* v, const floa
                            stream);
 }
 
+size_t favor_omega_prepared_size(int H, int d, int dv, int m, favor_dtype dtype) {
+  const favor::Shape s{1, H, 1, d, dv, m};
+  if (check_seq(s, dtype, FAVOR_PRF, 0.0f) != FAVOR_OK) return 0;
+  return favor::omega_prepared_bytes(s, dtype);
+}
+
+favor_status favor_omega_prepare(const float* omega, int H, int d, int dv, int m, favor_dtype dtype, favor_kind kind,
+                                 void* prep, size_t prep_bytes, hipStream_t stream) {
+  const favor::Shape s{1, H, 1, d, dv, m};
+  favor_status st = check_seq(s, dtype, kind, 0.0f);
+  if (st != FAVOR_OK) return st;
+  if (!omega || !prep || !aligned16(omega) || !aligned16(prep)) return FAVOR_ERR_INVALID_ARG;
+  const favor::KShape ks = favor::kernel_shape(dtype, d, dv, m);
+  if (!ks.ok) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
+  if (kind == FAVOR_TRIG && !ks.exact) return FAVOR_ERR_UNSUPPORTED;
+  if (prep_bytes < favor::omega_prepared_bytes(s, dtype)) return FAVOR_ERR_WORKSPACE;
+  return hip_status(favor::launch_prepare_omega(omega, s, dtype, kind, prep, stream));
+}
+
+favor_status favor_bidir_prepared(const void* q, const void* k, const void* v, const void* prep, int B, int H, int L,
+                                  int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                                  void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const favor::Shape s{B, H, L, d, dv, m};
+  favor_status st = check_bidir(q, k, v, static_cast<const float*>(prep), s, L, dtype, kind, eps, 1, out);
+  if (st != FAVOR_OK) return st;
+  if (!ws || !aligned16(ws)) return FAVOR_ERR_INVALID_ARG;
+  if (ws_bytes < favor::plan_bidir(s, dtype).total) return FAVOR_ERR_WORKSPACE;
+  return hip_status(favor::launch_bidir(q, k, v, nullptr, s, L, 1, dtype, kind, eps, out_f32 ? 1 : 0, out, ws, stream,
+                                        prep));
+}
+
 size_t favor_backward_workspace_size(int B, int H, int L, int d, int dv, int m, favor_dtype dtype) {
   const favor::Shape s{B, H, L, d, dv, m};
   if (check_seq(s, dtype, FAVOR_PRF, 0.f) != FAVOR_OK) return 0;
@@ -186,9 +218,12 @@ favor_status favor_causal_backward(const void* q, const void* k, const void* v, 
                                                   ws, stream));
 }
 
-favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
-                          int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
-                          float* S_final, float* z_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+// favor_causal (omega) and favor_causal_prepared (prep): exactly one of the two is non-null.
+static favor_status causal_common(const void* q, const void* k, const void* v, const float* omega, const void* prep,
+                                  int B, int H, int L, int d, int dv, int m, favor_dtype dtype, favor_kind kind,
+                                  float eps, int out_f32, void* out, float* S_final, float* z_final, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  if (!omega) omega = static_cast<const float*>(prep);  // checked like omega
   const favor::Shape s{B, H, L, d, dv, m};
   favor_status st = check_seq(s, dtype, kind, eps);
   if (st != FAVOR_OK) return st;
@@ -201,8 +236,25 @@ favor_status favor_causal(const void* q, const void* k, const void* v, const flo
   if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
   if (S_final && (kind != FAVOR_PRF || d > 64)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_causal(s, dtype).total) return FAVOR_ERR_WORKSPACE;
-  return hip_status(
-      favor::launch_causal(q, k, v, omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out, S_final, z_final, ws, stream));
+  return hip_status(favor::launch_causal(q, k, v, prep ? nullptr : omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out,
+                                         S_final, z_final, ws, stream, prep));
+}
+
+favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega, int B, int H, int L, int d,
+                          int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32, void* out,
+                          float* S_final, float* z_final, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!omega) return FAVOR_ERR_INVALID_ARG;
+  return causal_common(q, k, v, omega, nullptr, B, H, L, d, dv, m, dtype, kind, eps, out_f32, out, S_final, z_final,
+                       ws, ws_bytes, stream);
+}
+
+favor_status favor_causal_prepared(const void* q, const void* k, const void* v, const void* prep, int B, int H, int L,
+                                   int d, int dv, int m, favor_dtype dtype, favor_kind kind, float eps, int out_f32,
+                                   void* out, float* S_final, float* z_final, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  if (!prep) return FAVOR_ERR_INVALID_ARG;
+  return causal_common(q, k, v, nullptr, prep, B, H, L, d, dv, m, dtype, kind, eps, out_f32, out, S_final, z_final,
+                       ws, ws_bytes, stream);
 }
 
 static favor_status decode_common(const void* q, const void* k, const void* v, const float* omega, float* S,

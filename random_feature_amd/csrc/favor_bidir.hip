@@ -614,7 +614,8 @@ BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
 // feature count and column groups); otherwise the exact ones, which also have the trigonometric map.
 template <typename T, int D, int DV, int M, bool GEN>
 static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int Lq,
-                            int renorm, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st) {
+                            int renorm, int kind, float eps, int out_f32, void* out, void* ws, hipStream_t st,
+                            const void* prep) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
   constexpr int NW = FeatSplit<M, D>::NW;
@@ -622,7 +623,7 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   constexpr int DC = (D + 31) / 32;
   const BidirPlan p = plan_bidir(s, sizeof(T) == 4 ? 0 : 1, Lq);
   char* base = static_cast<char*>(ws);
-  P* omf = reinterpret_cast<P*>(base + p.off_omf);
+  P* omf = prep ? static_cast<P*>(const_cast<void*>(prep)) : reinterpret_cast<P*>(base + p.off_omf);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
@@ -635,8 +636,9 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
-  launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-      omega, s.H, s.m, M, D, wscale, omf, 0);
+  if (!prep)
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
+        omega, s.H, s.m, M, D, wscale, omf, 0);
   for (int c0 = 0; c0 < s.dv; c0 += DV) {
     const int vcols = std::min(DV, s.dv - c0);
     const T* vg = v + c0;
@@ -670,7 +672,7 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
 
 hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s, int Lq,
                         int renorm, int dtype, int kind, float eps, int out_f32, void* out, void* ws,
-                        hipStream_t st) {
+                        hipStream_t st, const void* prep) {
   const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
   if (!ks.ok || (!ks.exact && kind == kTrig)) return hipErrorInvalidValue;
 #define X(D_, DV_, M_, GEN_)                                                                                   \
@@ -679,12 +681,12 @@ hipError_t launch_bidir(const void* q, const void* k, const void* v, const float
       if constexpr (fp32_built(GEN_, D_, M_))                                                                  \
         return run_bidir<float, D_, DV_, M_, GEN_>(static_cast<const float*>(q), static_cast<const float*>(k), \
                                                    static_cast<const float*>(v), omega, s, Lq, renorm, kind,   \
-                                                   eps, out_f32, out, ws, st);                                  \
+                                                   eps, out_f32, out, ws, st, prep);                            \
       return hipErrorInvalidValue;                                                                             \
     }                                                                                                          \
     return run_bidir<bf16, D_, DV_, M_, GEN_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),        \
                                               static_cast<const bf16*>(v), omega, s, Lq, renorm, kind, eps,     \
-                                              out_f32, out, ws, st);                                            \
+                                              out_f32, out, ws, st, prep);                                      \
   }
 #define XE(D_, DV_, M_) X(D_, DV_, M_, false)
 #define XG(D_, DV_, M_) X(D_, DV_, M_, true)
@@ -694,6 +696,27 @@ hipError_t launch_bidir(const void* q, const void* k, const void* v, const float
 #undef XE
 #undef X
   return hipErrorInvalidValue;
+}
+
+size_t omega_prepared_bytes(const Shape& s, int dtype) {
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
+  if (!ks.ok) return 0;
+  return align256((size_t)s.H * (ks.mk / 16) * ((s.d + 31) / 32) * 512 * elt(dtype));
+}
+
+hipError_t launch_prepare_omega(const float* omega, const Shape& s, int dtype, int kind, void* prep, hipStream_t st) {
+  const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
+  if (!ks.ok) return hipErrorInvalidValue;
+  const float wscale = omega_scale(kind, std::pow((float)ks.dk, -0.25f));
+  const long long nfrag = (long long)s.H * (ks.mk / 16) * ((ks.dk + 31) / 32) * 64;
+  const unsigned grid = (unsigned)std::min<long long>((nfrag + 255) / 256, 4096);
+  if (dtype == 0)
+    launch("omega_frag", omega_frag_kernel<float>, grid, 256, 0, st, omega, s.H, s.m, ks.mk, ks.dk, wscale,
+        static_cast<float*>(prep), 0);
+  else
+    launch("omega_frag", omega_frag_kernel<f16>, grid, 256, 0, st, omega, s.H, s.m, ks.mk, ks.dk, wscale,
+        static_cast<f16*>(prep), 0);
+  return hipGetLastError();
 }
 
 }  // namespace favor

@@ -412,13 +412,13 @@ CausalPlan plan_causal(const Shape& s, int dtype) {
 template <typename T, int D, int DV, int M, bool GEN>
 static hipError_t run_causal(const T* q, const T* k, const T* v, const float* omega, const Shape& s, int kind,
                              float eps, int out_f32, void* out, float* S_final, float* z_final, void* ws,
-                             hipStream_t st) {
+                             hipStream_t st, const void* prep) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
   constexpr int NWR = RedSplit<M, D>::NW;
   const CausalPlan p = plan_causal(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
-  P* omf = reinterpret_cast<P*>(base + p.off_omf);
+  P* omf = prep ? static_cast<P*>(const_cast<void*>(prep)) : reinterpret_cast<P*>(base + p.off_omf);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
@@ -432,8 +432,9 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   const float log2_sqrt_m = 0.5f * std::log2((float)s.m);
 
   const long long nfrag = (long long)s.H * (M / 16) * DC * 64;
-  launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
-      omega, s.H, s.m, M, D, wscale, omf, 0);
+  if (!prep)
+    launch("omega_frag", omega_frag_kernel<P>, (unsigned)std::min<long long>((nfrag + 255) / 256, 4096), 256, 0, st,
+        omega, s.H, s.m, M, D, wscale, omf, 0);
   const int seg_tiles = p.seg_len / 32;
   for (int c0 = 0; c0 < s.dv; c0 += DV) {
     const int vcols = std::min(DV, s.dv - c0);
@@ -463,7 +464,7 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
 
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
-                         void* ws, hipStream_t st) {
+                         void* ws, hipStream_t st, const void* prep) {
   const KShape ks = kernel_shape(dtype, s.d, s.dv, s.m);
   if (!ks.ok) return hipErrorInvalidValue;
 #define X(D_, DV_, M_, GEN_)                                                                                    \
@@ -472,12 +473,12 @@ hipError_t launch_causal(const void* q, const void* k, const void* v, const floa
       if constexpr (fp32_built(GEN_, D_, M_))                                                                   \
         return run_causal<float, D_, DV_, M_, GEN_>(static_cast<const float*>(q), static_cast<const float*>(k), \
                                                     static_cast<const float*>(v), omega, s, kind, eps, out_f32,  \
-                                                    out, S_final, z_final, ws, st);                             \
+                                                    out, S_final, z_final, ws, st, prep);                       \
       return hipErrorInvalidValue;                                                                              \
     }                                                                                                           \
     return run_causal<bf16, D_, DV_, M_, GEN_>(static_cast<const bf16*>(q), static_cast<const bf16*>(k),        \
                                                static_cast<const bf16*>(v), omega, s, kind, eps, out_f32, out,  \
-                                               S_final, z_final, ws, st);                                       \
+                                               S_final, z_final, ws, st, prep);                                 \
   }
 #define XE(D_, DV_, M_) X(D_, DV_, M_, false)
 #define XG(D_, DV_, M_) X(D_, DV_, M_, true)

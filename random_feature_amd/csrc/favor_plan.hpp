@@ -133,12 +133,18 @@ CausalBackwardPlan plan_causal_backward(const Shape& s, int dtype);
 
 hipError_t launch_features(const void* x, const float* omega, const Shape& s, int dtype, int kind, float eps,
                            float* phi, float* logscale, hipStream_t st);
+// prep: Omega' fragments written by launch_prepare_omega for the same (H, d, dv, m, dtype, kind), read in place
+// of converting omega on the call (omega is then unused); null: convert omega into the workspace.
 hipError_t launch_bidir(const void* q, const void* k, const void* v, const float* omega, const Shape& s, int Lq,
                         int renorm, int dtype, int kind, float eps, int out_f32, void* out, void* ws,
-                        hipStream_t st);
+                        hipStream_t st, const void* prep = nullptr);
 hipError_t launch_causal(const void* q, const void* k, const void* v, const float* omega, const Shape& s,
                          int dtype, int kind, float eps, int out_f32, void* out, float* S_final, float* z_final,
-                         void* ws, hipStream_t st);
+                         void* ws, hipStream_t st, const void* prep = nullptr);
+// Bytes of the Omega' fragments of the compiled kernels for (H, d, dv, m) (Shape's B and L unused), the same
+// area both plans reserve at offset 0 of their workspace; and their conversion from omega.
+size_t omega_prepared_bytes(const Shape& s, int dtype);
+hipError_t launch_prepare_omega(const float* omega, const Shape& s, int dtype, int kind, void* prep, hipStream_t st);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* omega, const void* dout,
                            const Shape& s, int dtype, int kind, float eps, int grad_f32, void* dq, void* dk, void* dv,
                            void* ws, hipStream_t st);

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 21
     lib = ctypes.CDLL(rf.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -176,6 +176,33 @@ def test_host_omega_head_rows_independent_of_H():
     a = rf.make_omega_host(9, 2, 64, 16)
     b = rf.make_omega_host(9, 5, 64, 16)
     assert np.array_equal(a, b[:2])
+
+
+def test_prepared_omega_checks():
+    """favor_omega_prepare and the prepared calls check their arguments before any launch: the prepared size is
+    the workspace's fragment area; a short buffer is FAVOR_ERR_WORKSPACE; the prepared calls check `prep` as
+    favor_bidir and favor_causal check omega."""
+    n = rf._lib.favor_omega_prepared_size(12, 64, 64, 256, 1)
+    assert n == 12 * 16 * 2 * 512 * 2  # H * (m/16) * (d/32) * 512 fragments' 2-byte elements
+    assert rf._lib.favor_omega_prepared_size(12, 48, 64, 256, 1) == 0   # d outside the built set
+    assert rf._lib.favor_omega_prepared_size(0, 64, 64, 256, 1) == 0
+
+    def prep_call(om=FAKE, prep=FAKE, nbytes=n, kind=0, d=64, m=256):
+        return rf.raw_call("favor_omega_prepare", om, 12, d, 64, m, 1, kind, prep, ctypes.c_size_t(nbytes), None)
+    assert prep_call(om=None) == INVALID
+    assert prep_call(prep=MISALIGNED) == INVALID
+    assert prep_call(nbytes=n - 1) == WORKSPACE
+    assert prep_call(d=48) == UNSUPPORTED
+    assert prep_call(kind=2, m=160) == UNSUPPORTED  # trigonometric features: exact shapes only
+
+    def call(fn, prep=FAKE, ws=FAKE, wsb=1 << 30):
+        extra = (FAKE, FAKE) if fn == "favor_causal_prepared" else ()
+        return rf.raw_call(fn, FAKE, FAKE, FAKE, prep, 1, 12, 64, 64, 64, 256, 1, 0, ctypes.c_float(0.0), 0, FAKE,
+                           *extra, ws, ctypes.c_size_t(wsb), None)
+    for fn in ("favor_bidir_prepared", "favor_causal_prepared"):
+        assert call(fn, prep=None) == INVALID
+        assert call(fn, prep=MISALIGNED) == INVALID
+        assert call(fn, wsb=8) == WORKSPACE
 
 
 def test_bidir_noalloc_checks_before_any_device_call():

@@ -101,3 +101,14 @@ def test_unsupported_dtype():
     q, k, v, om = seq(dtype=torch.float16)
     with pytest.raises(TypeError, match="unsupported dtype"):
         rf.bidir(q, k, v, om)
+
+
+def test_prepared_omega_must_match_the_call():
+    """A PreparedOmega is tied to (H, d, dv, m, dtype, kind); the binding refuses another combination before any
+    library call."""
+    prep = rf.PreparedOmega(None, 12, 64, 64, 256, torch.bfloat16, "prf")
+    prep.check(12, 64, 64, 256, torch.bfloat16, "prf")
+    for args in ((12, 64, 32, 256, torch.bfloat16, "prf"), (12, 64, 64, 256, torch.float32, "prf"),
+                 (12, 64, 64, 256, torch.bfloat16, "relu"), (8, 64, 64, 256, torch.bfloat16, "prf")):
+        with pytest.raises(ValueError):
+            prep.check(*args)

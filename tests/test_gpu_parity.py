@@ -885,3 +885,38 @@ def test_bidir_backward_workload_sampled():
             worst = max(worst, rel_err(a[sl], r))
     print(f"bidir_bf16 backward sampled rel err {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- prepared Omega
+
+@pytest.mark.parametrize("path", ["bidir", "causal"])
+@pytest.mark.parametrize("dtype,shape,kind", [
+    (torch.bfloat16, (64, 64, 256), "prf"), (torch.bfloat16, (64, 64, 256), "relu"),
+    (torch.float32, (16, 16, 32), "prf"), (torch.bfloat16, (16, 256, 32), "prf"),
+    (torch.bfloat16, (64, 208, 240), "prf"), (torch.float32, (32, 48, 48), "relu"),
+    (torch.bfloat16, (64, 64, 256), "trig")])
+def test_prepared_omega_bit_identical(path, dtype, shape, kind):
+    """favor_bidir_prepared / favor_causal_prepared on fragments from favor_omega_prepare give the very bits of
+    favor_bidir / favor_causal (the same fragments, converted once instead of on the call), on exact and general
+    shapes and every feature kind the path has; two calls in a row share one prepared buffer. The outputs are
+    also held to the oracle."""
+    if path == "causal" and kind == "trig":
+        pytest.skip("the causal path has no trigonometric features")
+    d, dv, m = shape
+    B, H, L = 2, 3, 300
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 3100 + m + dv, scale=0.4 if kind == "trig" else 0.5)
+    om_dev, om = _omega(51, H, m, d, "trig_pairs" if kind == "trig" else "ortho_chi")
+    eps = 1e-3 if kind == "relu" else 0.0
+    fn = rf.bidir if path == "bidir" else rf.causal
+    prep = rf.prepare_omega(om_dev, dv, dtype, kind)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ref_dev = fn(qd, kd, vd, om_dev, kind=kind, eps=eps, out_f32=True)
+    got1 = fn(qd, kd, vd, om_dev, kind=kind, eps=eps, out_f32=True, prep=prep)
+    got2 = fn(qd, kd, vd, om_dev, kind=kind, eps=eps, out_f32=True, prep=prep)
+    torch.cuda.synchronize()
+    assert torch.equal(got1, ref_dev) and torch.equal(got2, ref_dev)
+    if kind == "trig":
+        ref = oracle.bidir(q, k, v, oracle.make_omega(51, H, m // 2, d, "ortho_chi"), "trig")
+    else:
+        ref = (oracle.bidir if path == "bidir" else oracle.causal)(q, k, v, om, kind, eps)
+    assert rel_err(got1, ref) < TOL[dtype]
