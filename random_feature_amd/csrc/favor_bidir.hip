@@ -408,11 +408,19 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 // entry 1/sqrt(m)) and the per-row log scale. The m features are taken in groups of MG (the
 // Omega' fragments of one group are built in LDS from the fp32 matrix by the workgroup); with
 // more than one group the positive map first finds every row's maximum over all groups.
+// Workgroup = 4 waves over FeatIters * 64 tokens of one (b,h), wave w taking the 16-token blocks
+// w, w + 4, ...: every wave loads all its token rows (converted, with their norms) before its
+// first store, so no later wait on the memory counter (which counts stores as well) holds the
+// stream of phi rows up.
+template <typename T, int D>
+constexpr int FeatIters = (sizeof(T) == 2 && D <= 64) ? 8 : 4;
+
 template <typename T, int D, int MG>
 __global__ void __launch_bounds__(256)
 features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H, int L, int m, int kind, float eps,
                 float inv_sqrt_m, float wscale, float nscale_ln, float* __restrict__ phi,
                 float* __restrict__ logscale, int tok_per_wg, int n_tiles) {
+  constexpr int IT = FeatIters<T, D>;
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
   constexpr int NFB = MG / 16;
@@ -424,6 +432,7 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int ng = (m + MG - 1) / MG;
+  const float half_log2_m = -__log2f(inv_sqrt_m);
   const T* Xb = X + (size_t)bh * L * D;
   const int tstart = tile * tok_per_wg, tstop = min(L, tstart + tok_per_wg);
 
@@ -444,53 +453,68 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
     }
     __syncthreads();
   };
-  // projection of the 16 tokens from t0 against the group in LDS: pacc[fb][i] is feature fb*16 + 4g + i of
-  // token t0 + c; s2 gets |x|^2
-  auto project = [&](int t0, f32x4 (&pacc)[NFB], float& s2) {
-    const int tok = t0 + c;
-    vec8<P> xf[DC];
-    s2 = 0.f;
+  // the wave's token rows, converted to the projection type (block it: tokens tstart + (w + 4 it) * 16 + c),
+  // and their squared norms |x|^2; rows past L are zero
+  vec8<P> xq[IT][DC];
+  float xs2[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int tok = tstart + (w + 4 * it) * 16 + c;
+    float s2 = 0.f;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       const int col = dc * 32 + 8 * g;
-      const vec8<T> raw = (tok < L && col < D) ? ld8<T>(Xb + (size_t)tok * D + col) : zero8<T>();
+      const vec8<T> raw = (tok < tstop && col < D) ? ld8<T>(Xb + (size_t)tok * D + col) : zero8<T>();
       float c2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = to_f(raw[j]);
         c2 += v * v;
-        xf[dc][j] = to_t<P>(v);
+        xq[it][dc][j] = to_t<P>(v);
       }
       if constexpr (sizeof(P) == 2 && sizeof(T) == 2)
-        if (c2 >= kF16MaxSq) clamp_to_f16<P>(raw, xf[dc]);
+        if (c2 >= kF16MaxSq) clamp_to_f16<P>(raw, xq[it][dc]);
       s2 += c2;
     }
-    s2 = group_sum(s2);
+    xs2[it] = group_sum(s2);
+  }
+  // projection of the wave's token block it against the group in LDS: pacc[fb][i] is feature fb*16 + 4g + i
+  // of token tstart + (w + 4 it) * 16 + c
+  auto project = [&](int it, f32x4 (&pacc)[NFB]) {
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb) {
       pacc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) mma16(pacc[fb], ld8<P>(oms + ((fb * DC + dc) * 64 + lane) * 8), xf[dc]);
+      for (int dc = 0; dc < DC; ++dc) mma16(pacc[fb], ld8<P>(oms + ((fb * DC + dc) * 64 + lane) * 8), xq[it][dc]);
     }
   };
-  // largest valid exponent of the row among this group's features
+  // largest valid exponent of the row among this group's features (a whole group needs no mask: a per-element
+  // mask turns the chain of three-input maxima into selects)
   auto row_max = [&](int gi, const f32x4 (&pacc)[NFB]) {
     float mx = -INFINITY;
+    if (gi * MG + MG <= m) {
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb)
+      for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (gi * MG + fb * 16 + 4 * g + i < m) mx = fmaxf(mx, pacc[fb][i]);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, pacc[fb][i]);
+    } else {
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, gi * MG + fb * 16 + 4 * g + i < m ? pacc[fb][i] : -INFINITY);
+    }
     return group_max(mx);
   };
 
   if (kind == kPrf && ng > 1) {
     for (int gi = 0; gi < ng; ++gi) {
       build(gi);
-      for (int t0 = tstart + w * 16; t0 < tstop; t0 += 64) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int t0 = tstart + (w + 4 * it) * 16;
+        if (t0 >= tstop) break;
         f32x4 pacc[NFB];
-        float s2;
-        project(t0, pacc, s2);
+        project(it, pacc);
         const float mx = row_max(gi, pacc);
         if (g == 0 && t0 + c < tstop) rmax[t0 + c - tstart] = gi == 0 ? mx : fmaxf(rmax[t0 + c - tstart], mx);
       }
@@ -498,18 +522,22 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
   }
   for (int gi = 0; gi < ng; ++gi) {
     build(gi);
-    for (int t0 = tstart + w * 16; t0 < tstop; t0 += 64) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t0 = tstart + (w + 4 * it) * 16;
+      if (t0 >= tstop) break;
       const int tok = t0 + c;
+      const float s2 = xs2[it];
       f32x4 pacc[NFB];
-      float s2;
-      project(t0, pacc, s2);
+      project(it, pacc);
       float ls = 0.f;
       if (kind == kPrf) {
         const float mx = ng > 1 ? rmax[min(tok, tstop - 1) - tstart] : row_max(gi, pacc);
+        const float sh = mx + half_log2_m;  // the row's largest entry becomes 2^-log2(sqrt m) = 1/sqrt(m)
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - mx) * inv_sqrt_m;
+          for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - sh);
         ls = mx * kLn2 - s2 * nscale_ln;
       } else if (kind == kTrig) {
         // m/2 vectors: the scale 1/sqrt(m/2); exp(|x|^2/2) goes to the log scale
@@ -758,7 +786,7 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
   const float wscale = omega_scale(kind, sc);
   const float nscale_ln = sc * sc * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
-  const int tpw = 256;
+  const int tpw = 64 * FeatIters<T, D>;  // tokens per workgroup: 4 waves x FeatIters blocks of 16
   const int n_tiles = (s.L + tpw - 1) / tpw;
   const size_t lds = (size_t)(MG / 16) * DC * 512 * sizeof(P) + tpw * sizeof(float);
   // once per instantiation (a function-local static is initialised exactly once, also under concurrent
