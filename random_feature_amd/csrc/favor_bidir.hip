@@ -415,9 +415,9 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
 template <typename T, int D>
 constexpr int FeatIters = (sizeof(T) == 2 && D <= 64) ? 8 : 4;
 
-template <typename T, int D, int MG>
-__global__ void __launch_bounds__(256)
-features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H, int L, int m, int kind, float eps,
+template <typename T, int D, int MG, int KIND>
+__global__ void __launch_bounds__(256, 2)
+features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H, int L, int m, float eps,
                 float inv_sqrt_m, float wscale, float nscale_ln, float* __restrict__ phi,
                 float* __restrict__ logscale, int tok_per_wg, int n_tiles) {
   constexpr int IT = FeatIters<T, D>;
@@ -506,7 +506,7 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
     return group_max(mx);
   };
 
-  if (kind == kPrf && ng > 1) {
+  if (KIND == kPrf && ng > 1) {
     for (int gi = 0; gi < ng; ++gi) {
       build(gi);
 #pragma unroll
@@ -531,7 +531,7 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
       f32x4 pacc[NFB];
       project(it, pacc);
       float ls = 0.f;
-      if (kind == kPrf) {
+      if constexpr (KIND == kPrf) {
         const float mx = ng > 1 ? rmax[min(tok, tstop - 1) - tstart] : row_max(gi, pacc);
         const float sh = mx + half_log2_m;  // the row's largest entry becomes 2^-log2(sqrt m) = 1/sqrt(m)
 #pragma unroll
@@ -539,7 +539,7 @@ features_kernel(const T* __restrict__ X, const float* __restrict__ omega, int H,
 #pragma unroll
           for (int i = 0; i < 4; ++i) pacc[fb][i] = fast_exp2(pacc[fb][i] - sh);
         ls = mx * kLn2 - s2 * nscale_ln;
-      } else if (kind == kTrig) {
+      } else if constexpr (KIND == kTrig) {
         // m/2 vectors: the scale 1/sqrt(m/2); exp(|x|^2/2) goes to the log scale
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
@@ -777,13 +777,13 @@ hipError_t noalloc_scratch(int dev, void** ptr) {
 }
 
 // The feature map on groups of MG features (every m up to MG; 512 as two groups of 256).
-template <typename T, int D, int MG>
-static hipError_t run_features(const T* x, const float* omega, const Shape& s, int kind, float eps, float* phi,
+template <typename T, int D, int MG, int KIND>
+static hipError_t run_features(const T* x, const float* omega, const Shape& s, float eps, float* phi,
                                float* logscale, hipStream_t st) {
   using P = typename Ops<T>::P;
   constexpr int DC = (D + 31) / 32;
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = omega_scale(kind, sc);
+  const float wscale = omega_scale(KIND, sc);
   const float nscale_ln = sc * sc * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
   const int tpw = 64 * FeatIters<T, D>;  // tokens per workgroup: 4 waves x FeatIters blocks of 16
@@ -791,11 +791,12 @@ static hipError_t run_features(const T* x, const float* omega, const Shape& s, i
   const size_t lds = (size_t)(MG / 16) * DC * 512 * sizeof(P) + tpw * sizeof(float);
   // once per instantiation (a function-local static is initialised exactly once, also under concurrent
   // first calls)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&features_kernel<T, D, MG>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&features_kernel<T, D, MG, KIND>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
   if (attr != hipSuccess) return attr;
-  launch("features", features_kernel<T, D, MG>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H, s.L, s.m,
-      kind, eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
+  launch("features", features_kernel<T, D, MG, KIND>, (unsigned)(s.bh() * n_tiles), 256, lds, st, x, omega, s.H,
+      s.L, s.m, eps, inv_sqrt_m, wscale, nscale_ln, phi, logscale, tpw, n_tiles);
   return hipGetLastError();
 }
 
@@ -806,17 +807,25 @@ hipError_t launch_features(const void* x, const float* omega, const Shape& s, in
   const int mg_max = (dtype == 0 ? s.d >= 64 : s.d > 64) ? 128 : 256;
   int mg = 16;
   while (mg < s.m && mg < mg_max) mg *= 2;
-#define X(D_, MG_)                                                                                                \
-  if (s.d == D_ && mg == MG_) {                                                                                  \
+#define XK(D_, MG_, K_)                                                                                          \
+  if (kind == K_) {                                                                                              \
     if (dtype == 0)                                                                                              \
-      return run_features<float, D_, MG_>(static_cast<const float*>(x), omega, s, kind, eps, phi, logscale, st); \
-    return run_features<bf16, D_, MG_>(static_cast<const bf16*>(x), omega, s, kind, eps, phi, logscale, st);     \
+      return run_features<float, D_, MG_, K_>(static_cast<const float*>(x), omega, s, eps, phi, logscale, st);   \
+    return run_features<bf16, D_, MG_, K_>(static_cast<const bf16*>(x), omega, s, eps, phi, logscale, st);       \
+  }
+#define X(D_, MG_)                  \
+  if (s.d == D_ && mg == MG_) {     \
+    XK(D_, MG_, kPrf)               \
+    XK(D_, MG_, kRelu)              \
+    XK(D_, MG_, kTrig)              \
+    return hipErrorInvalidValue;    \
   }
 #define XD(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
   XD(16) XD(32) XD(64) XD(128)
   X(16, 256) X(32, 256) X(64, 256)
 #undef XD
 #undef X
+#undef XK
   return hipErrorInvalidValue;
 }
 
