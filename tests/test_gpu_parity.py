@@ -697,6 +697,29 @@ def test_bidir_backward_relu(dtype, shape, L, eps):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("path", ["bidir", "causal"])
+@pytest.mark.parametrize("mode", ["hyperbolic", "iid", "ortho_sqrtd"])
+def test_backward_omega_modes(dtype, path, mode):
+    """The gradients on the other random-feature modes: the hyperbolic features of Lemma 1 (the positive map over
+    [W; -W], which the oracle pins equal to the hyperbolic map), iid rows and SMREG's sqrt(d) lengths, against the
+    oracle's positive-map gradients on the same Omega."""
+    d, dv, m = 64, 64, 256
+    B, H, L = 2, 2, 300
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 4100 + L)
+    g = workloads.make_tensor((B, H, L, dv), 4177, 1.0, dtype)
+    om_dev, om = _omega(53, H, m, d, mode)
+    fb = rf.bidir_backward if path == "bidir" else rf.causal_backward
+    ref = (oracle.bidir_backward if path == "bidir" else oracle.causal_backward)(q, k, v, om, g)
+    got = fb(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    errs = _causal_grad_errs(got, ref) if path == "causal" else {
+        n: rel_err(a, r) for n, a, r in zip(("dq", "dk", "dv"), got, ref)}
+    print(f"backward {path} {mode} {dtype}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e < TOL[dtype], (name, e)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_bidir_backward_single_token(dtype):
     """The degenerate sequence L = 1: the output is v itself, so dv = dout exactly and dq, dk vanish; the
     kernels' dq and dk are the rounding residue of the cancelling terms, far below the scale of the
