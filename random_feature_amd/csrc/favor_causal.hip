@@ -135,11 +135,15 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
   auto store_chunk = [&](int tc) {
     constexpr int C8 = DV / 8;
     const int tok0 = t0 + 32 * tc;
+    // item e: query row (e >> 4 ... ) taken 16 rows at a time, so the 16 threads of a quarter-wave read one column
+    // chunk of 16 rows: 16 different 4-bank groups of the partial outputs (row-major items put a row's 8 chunks,
+    // all in the same banks, on consecutive threads)
     for (int e = threadIdx.x; e < 32 * C8; e += NT) {
-      const int qrow = e / C8, c8 = e % C8;
+      const int cq = e & 15, rest = e >> 4;
+      const int tb = rest / C8, c8 = rest % C8;
+      const int qrow = tb * 16 + cq;
       const int tok = tok0 + qrow;
       if (tok >= tend || c8 * 8 >= vcols) continue;
-      const int tb = qrow >> 4, cq = qrow & 15;
       const int cb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
       f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
       float den = 0.f;
