@@ -204,8 +204,12 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   constexpr int NDBW = (BPW + 1) / 2;  // dimension blocks per wave
   constexpr int RC = Rows<DV>::RC, KC = Rows<DV>::KC;
   constexpr int KROW = D + 8;
+  // row strides (elements) of the LDS rows: the transposing reads of W take 8 rows of 32 bytes per half wave,
+  // which land in 8 different bank groups when the stride is an odd multiple of 8 dwords; the g rows keep a
+  // stride whose 16 rows per quarter wave fall into distinct 4-bank groups for their row reads
   constexpr int EROW = FB * 16 + 8;
   constexpr int WROW = RC + 8;
+  constexpr int WBROW = RC + 16;
   constexpr int PROW = NFC * 32 + 8;
   constexpr int CPR = DV / 8;                     // 8-column chunks of a g row
   constexpr int IPT = (32 * CPR + NT - 1) / NT;  // (query, chunk) items per thread
@@ -215,12 +219,13 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   constexpr int NSPL = sizeof(XB) == 2 ? 2 : 1;  // bf16 operands of dS_aug as a sum of two (hi + lo)
   __shared__ __attribute__((aligned(16))) XB erow[NSPL][NW][32 * EROW];
   __shared__ __attribute__((aligned(16))) XS gsr[32 * WROW];
-  __shared__ __attribute__((aligned(16))) XB wbr[NSPL][32 * WROW];
+  __shared__ __attribute__((aligned(16))) XB wbr[NSPL][32 * WBROW];
   __shared__ __attribute__((aligned(16))) XS prow[32 * PROW];
-  // per-wave partials across the waves, [query][wave] so a lane reads a query's NW at once
-  __shared__ __attribute__((aligned(16))) float qmx[32][NW];
-  __shared__ __attribute__((aligned(16))) float dsum[32][NW];
-  __shared__ __attribute__((aligned(16))) float asum[32][NW];
+  // per-wave partials across the waves, [query][wave], a lane reading its query's NW (one padding column: the
+  // rows of a quarter wave then fall into distinct banks)
+  __shared__ __attribute__((aligned(16))) float qmx[32][NW + 1];
+  __shared__ __attribute__((aligned(16))) float dsum[32][NW + 1];
+  __shared__ __attribute__((aligned(16))) float asum[32][NW + 1];
   __shared__ __attribute__((aligned(16))) float gex[32], rsc[32];
   __shared__ float xch[NW];
 
@@ -510,16 +515,16 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
           wb[j] = to_t<XB>(x);
           wl[j] = to_t<XB>(x - to_f(wb[j]));
         }
-        *reinterpret_cast<vec8<XB>*>(&wbr[0][row * WROW + c8 * 8]) = wb;
-        if constexpr (NSPL == 2) *reinterpret_cast<vec8<XB>*>(&wbr[NSPL - 1][row * WROW + c8 * 8]) = wl;
+        *reinterpret_cast<vec8<XB>*>(&wbr[0][row * WBROW + c8 * 8]) = wb;
+        if constexpr (NSPL == 2) *reinterpret_cast<vec8<XB>*>(&wbr[NSPL - 1][row * WBROW + c8 * 8]) = wl;
         if (c8 == 0) {
           const int e = (int)gex[row] + eS;
           const float gam = ldexpf(aa, e) * rd;  // g . out
           for (int col = DV; col < RC; ++col) {
             const float x = col == DV ? -gam * rd : 0.f;
             const XB xh = to_t<XB>(x);
-            wbr[0][row * WROW + col] = xh;
-            if constexpr (NSPL == 2) wbr[NSPL - 1][row * WROW + col] = to_t<XB>(x - to_f(xh));
+            wbr[0][row * WBROW + col] = xh;
+            if constexpr (NSPL == 2) wbr[NSPL - 1][row * WBROW + col] = to_t<XB>(x - to_f(xh));
           }
           rsc[row] = ldexpf(rd * (KIND == kPrf ? 1.f / kLog2e : inv_sqrt_m), e);
         }
@@ -562,7 +567,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
 #pragma unroll
       for (int sp = 0; sp < NSPL; ++sp)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wt[sp][nb] = tr8(wbr[sp], WROW, nb * 16);
+        for (int nb = 0; nb < NB; ++nb) wt[sp][nb] = tr8(wbr[sp], WBROW, nb * 16);
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         const vec8<XB> ea = tr8(&erow[0][w][0], EROW, fb * 16);
@@ -634,8 +639,8 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
   __shared__ __attribute__((aligned(16))) XS vsr[32 * WROW];
   __shared__ __attribute__((aligned(16))) XS prow[32 * PROW];
   __shared__ __attribute__((aligned(16))) XB frow[32 * PROW];
-  __shared__ __attribute__((aligned(16))) float qmx[32][NW];  // [key][wave]
-  __shared__ __attribute__((aligned(16))) float rho[32][NW];
+  __shared__ __attribute__((aligned(16))) float qmx[32][NW + 1];  // [key][wave], one padding column
+  __shared__ __attribute__((aligned(16))) float rho[32][NW + 1];
   __shared__ __attribute__((aligned(16))) float vex[32];
   __shared__ float xch[NW];
 
