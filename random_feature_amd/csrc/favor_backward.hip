@@ -357,6 +357,9 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
           for (int j = 0; j < 8; ++j) sa[fb][kc][j] = to_t<XS>(ldexpf(sf[fb][kc][j], -eS));
+      // every operand has landed here, so no wait for them falls to their first uses in the tile,
+      // where it would also hold up the next tile's copies on every tile
+      wait_vmcnt<0>();
       cur_bh = bh;
     }
     // ---- g rows scaled per query (rows past L: zero)
@@ -752,6 +755,7 @@ bwd_k_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Op
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
           for (int j = 0; j < 8; ++j) da[fb][kc][j] = to_t<XS>(ldexpf(sf[fb][kc][j], -(int)eD));
+      wait_vmcnt<0>();  // every operand has landed (as in bwd_q_kernel)
       cur_bh = bh;
     }
     lds_barrier();  // ks, kn of this tile; every thread's copies landed

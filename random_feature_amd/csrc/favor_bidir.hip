@@ -212,11 +212,10 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
       }
       cur_bh = bh;
       if constexpr (KIND == kPrf) gm = renorm ? 0.f : gmx[bh];
-      if constexpr (KIND == kPrf) {
-        omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
-      } else {
-        wait_vmcnt<0>();
-      }
+      if constexpr (KIND == kPrf) omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
+      // the fragments have landed: no wait for them is left to the first uses in the tile loop,
+      // where it would also drain the copies and stores in flight on every tile
+      wait_vmcnt<0>();
     }
 
     // ---- phase 1: this wave's features of the tile

@@ -219,6 +219,31 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, uint32_t lds_base) {
   // an LDS DMA reading M0 right after an SALU write of M0 needs one wait state
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(base) : "memory");
 }
+// The same copy through a buffer resource: lane data = rsrc.base + voff, 16 bytes, and zero where the 16 bytes lie
+// at or past rsrc's byte count (the hardware's range check), so the address arithmetic per copy is one offset that
+// can stay fixed while the resource moves. rsrc must be the same across the wave's active lanes: the copy takes
+// the first active lane's.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 raw_buffer(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu);  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);                                     // range in bytes
+  r[3] = 0x00020000u;  // raw (unformatted) 32-bit data, no swizzle: the gfx9-family encoding
+  return r;
+}
+__device__ __forceinline__ void lds_dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(rsrc[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(rsrc[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(rsrc[2]);
+  r[3] = __builtin_amdgcn_readfirstlane(rsrc[3]);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
+               "s"(base)
+               : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }

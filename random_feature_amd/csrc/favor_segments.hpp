@@ -125,6 +125,7 @@ struct SweepRing {
   static constexpr int VC = 32 * CPR_V;
   static constexpr int NCH = 2 * XC + (WITH_G ? 2 : 1) * VC;  // Q, K, V (and G) chunks
   static constexpr int CPT = (NCH + NT - 1) / NT;
+  static_assert(XC % 64 == 0 && VC % 64 == 0 && NT % 64 == 0, "each wave's copies come from one tensor");
   static constexpr int SLOT = CPT * NT * 16;
   static constexpr bool SWZ_V = sizeof(T) == 2;
   static_assert((CPR_X & (CPR_X - 1)) == 0 && CPR_X <= 64, "rows of whole, power-of-two chunk counts");
@@ -136,25 +137,37 @@ struct SweepRing {
   // G (WITH_G): rows of a fourth [.., DV] array (the upstream gradient), laid out like V after it. V rows
   // are ldv elements apart with vcols valid columns (chunks past them are copied from the row's start
   // and masked by the consumer).
+  // Rows arrive through buffer resources that end at the chunk's last row inside L: rows past L land as zeros,
+  // and each thread's byte offsets stay the same from chunk to chunk.
   static __device__ __forceinline__ void issue(const T* Q, const T* K, const T* V, int L, size_t rowbase, int tok0,
                                                uint32_t slot, const T* G = nullptr, int ldv = DV, int vcols = DV) {
     const int tid = threadIdx.x, w = tid >> 6;
+    const size_t row0 = rowbase + tok0;
+    const uint32_t nrows = (uint32_t)max(0, min(32, L - tok0));
+    const u32x4 rq = raw_buffer(Q + row0 * D, nrows * (uint32_t)(D * sizeof(T)));
+    const u32x4 rk = raw_buffer(K + row0 * D, nrows * (uint32_t)(D * sizeof(T)));
+    const u32x4 rv = raw_buffer(V + row0 * ldv, nrows * (uint32_t)ldv * (uint32_t)sizeof(T));
+    u32x4 rg = rv;
+    if constexpr (WITH_G) rg = raw_buffer(G + row0 * DV, nrows * (uint32_t)(DV * sizeof(T)));
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int q = u * NT + tid;
-      const void* src = Q + rowbase * D;  // filler for positions past the tile: a valid row
+      const uint32_t lds = slot + (uint32_t)(u * NT + w * 64) * 16u;
       if (q < 2 * XC) {
         const int x = q / XC, p = q % XC, row = p / CPR_X;
         const int cc = (p % CPR_X) ^ (row & (CPR_X - 1));
-        src = (x == 0 ? Q : K) + (rowbase + min(tok0 + row, L - 1)) * D + cc * EPC;
+        lds_dma16_buf(x == 0 ? rq : rk, (uint32_t)((row * D + cc * EPC) * sizeof(T)), lds);
       } else if (q < NCH) {
         const bool isg = WITH_G && q >= 2 * XC + VC;
         const int p = q - 2 * XC - (isg ? VC : 0), row = p / CPR_V, pc = p % CPR_V;
         const int cc = SWZ_V ? (pc ^ (row & (CPR_V - 1))) : pc;
-        src = isg ? G + (rowbase + min(tok0 + row, L - 1)) * DV + cc * EPC
-                  : V + (rowbase + min(tok0 + row, L - 1)) * ldv + (cc * EPC < vcols ? cc * EPC : 0);
+        if (isg)
+          lds_dma16_buf(rg, (uint32_t)((row * DV + cc * EPC) * sizeof(T)), lds);
+        else
+          lds_dma16_buf(rv, (uint32_t)((row * ldv + (cc * EPC < vcols ? cc * EPC : 0)) * sizeof(T)), lds);
+      } else {
+        lds_dma16_buf(rq, 0xfffffff0u, lds);  // past every resource: zeros
       }
-      lds_dma16(src, slot + (uint32_t)(u * NT + w * 64) * 16u);
     }
   }
 

@@ -44,7 +44,7 @@ template <int M> struct BwdSplit {
   static constexpr int FB = M / (16 * NW);
 };
 
-constexpr int kNormNone = 0, kNormSq = 1, kNormAbs = 2;
+constexpr int kNormNone = 0, kNormSq = 1, kNormAbs = 2, kNormNegSq = 3;
 
 // ---------------------------------------------------------------- tile ring
 // 32-token tiles of X (keys or queries) and V arrive in an R-slot LDS ring through
@@ -65,29 +65,35 @@ struct Ring {
   static constexpr int XC = 32 * CPR_X;
   static constexpr int VC = WITH_V ? 32 * CPR_V : 0;
   static constexpr int CPT = (XC + VC + NT - 1) / NT;
+  static_assert(XC % 64 == 0 && VC % 64 == 0 && NT % 64 == 0, "each wave's copies come from one tensor");
   static constexpr int SLOT = CPT * NT * 16;
   static constexpr bool SWZ = sizeof(T) == 2 && WITH_V;
 
-  // copies of the tile at (bh, tok0) into the slot at LDS byte address `slot`; !live: filler
+  // copies of the tile at (bh, tok0) into the slot at LDS byte address `slot`; !live: filler. The tile's rows
+  // come through buffer resources that end at the tile's last row inside L, so rows past L (and every row of a
+  // filler) land as zeros, and each thread's byte offset stays the same from tile to tile.
   static __device__ __forceinline__ void issue(const T* X, const T* V, int L, int bh, int tok0, bool live,
                                                uint32_t slot, int ldv = DV, int vcols = DV) {
     const int tid = threadIdx.x, w = tid >> 6;
-    const size_t rowbase = (size_t)bh * L;
+    const size_t row0 = (size_t)bh * L + (live ? tok0 : 0);
+    const uint32_t nrows = live ? (uint32_t)min(32, L - tok0) : 0u;
+    const u32x4 rx = raw_buffer(X + row0 * D, nrows * (uint32_t)(D * sizeof(T)));
+    u32x4 rv = rx;
+    if constexpr (WITH_V) rv = raw_buffer(V + row0 * ldv, nrows * (uint32_t)ldv * (uint32_t)sizeof(T));
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int q = u * NT + tid;
-      const void* src = X;
-      if (live) {
-        if ((XC % NT == 0) ? (u * NT < XC) : (q < XC)) {
-          const int row = q / CPR_X, cc = q % CPR_X;
-          src = X + (rowbase + min(tok0 + row, L - 1)) * D + cc * EPC;
-        } else if (WITH_V && q < XC + VC) {
-          const int p = q - XC, row = p / CPR_V, pc = p % CPR_V;
-          const int cc = SWZ ? (pc ^ (row & (CPR_V - 1))) : pc;
-          src = V + (rowbase + min(tok0 + row, L - 1)) * ldv + (cc * EPC < vcols ? cc * EPC : 0);
-        }
+      const uint32_t lds = slot + (uint32_t)(u * NT + w * 64) * 16u;
+      if ((XC % NT == 0) ? (u * NT < XC) : (q < XC)) {
+        const int row = q / CPR_X, cc = q % CPR_X;
+        lds_dma16_buf(rx, (uint32_t)((row * D + cc * EPC) * sizeof(T)), lds);
+      } else if (WITH_V && q < XC + VC) {
+        const int p = q - XC, row = p / CPR_V, pc = p % CPR_V;
+        const int cc = SWZ ? (pc ^ (row & (CPR_V - 1))) : pc;
+        lds_dma16_buf(rv, (uint32_t)((row * ldv + (cc * EPC < vcols ? cc * EPC : 0)) * sizeof(T)), lds);
+      } else {
+        lds_dma16_buf(rx, 0xfffffff0u, lds);  // past every resource: zeros
       }
-      lds_dma16(src, slot + (uint32_t)(u * NT + w * 64) * 16u);
     }
   }
 
@@ -100,7 +106,7 @@ struct Ring {
 
   // this thread's X chunks of a landed slot -> projection type in `conv` (row stride KROW),
   // and per row into `nrm`: NORM == kNormSq: |x|^2 * nscale (+inf for rows at or past
-  // nvalid); NORM == kNormAbs: |x| * nscale
+  // nvalid); kNormNegSq: its negation; NORM == kNormAbs: |x| * nscale
   template <typename P, int KROW, int NORM>
   static __device__ __forceinline__ void convert(const unsigned char* slot, P* conv, float* nrm, float nscale,
                                                  int nvalid) {
@@ -140,6 +146,8 @@ struct Ring {
         if (has) {  // every lane of the row holds the sum and stores the same value
           if constexpr (NORM == kNormSq)
             nrm[row] = row < nvalid ? s2 * nscale : INFINITY;
+          else if constexpr (NORM == kNormNegSq)
+            nrm[row] = row < nvalid ? s2 * -nscale : -INFINITY;
           else
             nrm[row] = __builtin_amdgcn_sqrtf(s2) * nscale;  // hardware square root (1 ulp; the bound's margin covers it)
         }
@@ -256,6 +264,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   constexpr int KROW = D + 8;
   static_assert(R >= 4, "ring: the tile contracted, one converted ahead, one being converted, one in flight");
   using Rg = Ring<T, D, DV, NT, true>;
+  // key norms as stored: negated for the positive map, whose exponents start from -(n'_t + M)
+  constexpr int KN = KIND == kPrf ? kNormNegSq : kNormSq;
   // at the wait of iteration t the copies issued so far reach tile t+R-2 (each iteration
   // issues at its end): R-4 tiles are newer than tile t+2
   constexpr int WAIT_NEXT = Rg::CPT * (R - 4);
@@ -337,7 +347,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       if constexpr (KIND == kPrf) {
         const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[kb][tb * 16 + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bias[i] = -(n4[i] + rm);
+        for (int i = 0; i < 4; ++i) bias[i] = n4[i] - rm;  // n4 = -n'_t
       }
       vec8<P> kf[DC];
 #pragma unroll
@@ -367,10 +377,10 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   }
   // tiles 0 and 1 converted up front; iteration t converts tile t+2
   wait_vmcnt<Rg::CPT * (R - 2)>();
-  Rg::template convert<P, KROW, kNormSq>(ring[0], ks[0], kn[0], nscale, L - cv.tok0());
+  Rg::template convert<P, KROW, KN>(ring[0], ks[0], kn[0], nscale, L - cv.tok0());
   cv.next();
   wait_vmcnt<Rg::CPT * (R - 3)>();
-  Rg::template convert<P, KROW, kNormSq>(ring[1], ks[1], kn[1], nscale, L - cv.tok0());
+  Rg::template convert<P, KROW, KN>(ring[1], ks[1], kn[1], nscale, L - cv.tok0());
   cv.next();
   int cur_bh = cur.bh;
   load_om(cur_bh);
@@ -514,7 +524,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         mma16(sacc[fb][nb], af[fb], vf[nb]);
         if constexpr (LO) mma16(sacc[fb][nb], al[fb], vf[nb]);
       }
-    Rg::template convert<P, KROW, kNormSq>(ring[s_cv], ks[buf], kn[buf], nscale, L - cv.tok0());
+    Rg::template convert<P, KROW, KN>(ring[s_cv], ks[buf], kn[buf], nscale, L - cv.tok0());
     cv.next();
     {
       const bool live = it + R - 1 < n_tiles;
