@@ -461,9 +461,8 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
           pq[tb][fb][i] = ph;
           dz += ph * zv[fb][i];
           da += ph * uq[tb][fb][i];
-          e4[i] = to_t<XB>(ph);
-          e4lo[i] = to_t<XB>(ph - to_f(e4[i]));
         }
+        split_all<4>(e4, e4lo, [&](int i) { return pq[tb][fb][i]; });
         *reinterpret_cast<vec4<XB>*>(&erow[0][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4;
         if constexpr (NSPL == 2) *reinterpret_cast<vec4<XB>*>(&erow[NSPL - 1][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4lo;
       }
@@ -485,7 +484,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         den += dsum[tb * 16 + c][ww];
         aa += asum[tb * 16 + c][ww];
       }
-      const float ad = aa / den;
+      const float ad = aa * __builtin_amdgcn_rcpf(den);  // hardware reciprocal (1 ulp)
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         vec4<XS> p4;
@@ -510,14 +509,9 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
           aa += asum[row][ww];
         }
         // rows past L: W = 0 (their denominators are not used; a ReLU row of zero features has D' = 0)
-        const float rd = tok0 + row < L ? 1.f / den : 0.f;
+        const float rd = tok0 + row < L ? __builtin_amdgcn_rcpf(den) : 0.f;  // hardware reciprocal (1 ulp)
         vec8<XB> wb, wl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = gv[u][j] * rd;
-          wb[j] = to_t<XB>(x);
-          wl[j] = to_t<XB>(x - to_f(wb[j]));
-        }
+        split_all<8>(wb, wl, [&](int j) { return gv[u][j] * rd; });
         *reinterpret_cast<vec8<XB>*>(&wbr[0][row * WBROW + c8 * 8]) = wb;
         if constexpr (NSPL == 2) *reinterpret_cast<vec8<XB>*>(&wbr[NSPL - 1][row * WBROW + c8 * 8]) = wl;
         if (c8 == 0) {

@@ -349,23 +349,17 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     vec8<C> afh[FB], afl[FB], bqh[2], bql[2];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) split2(key_feature<KIND>(pk[j >> 2][fb][j & 3], inv_sqrt_m, eps), afh[fb], afl[fb], j);
+      split_all<8>(afh[fb], afl[fb], [&](int j) { return key_feature<KIND>(pk[j >> 2][fb][j & 3], inv_sqrt_m, eps); });
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) split2(key_feature<KIND>(pq[tb][j >> 2][j & 3], inv_sqrt_m, eps), bqh[tb], bql[tb], j);
+      split_all<8>(bqh[tb], bql[tb], [&](int j) { return key_feature<KIND>(pq[tb][j >> 2][j & 3], inv_sqrt_m, eps); });
 
     // ---- forward, carried term: o^T[col][q] = S'^T (A: Sc, paired feature slots) x Phi'_Q
     f32x4 o[NB][2];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       vec8<C> sh, slo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        split2(Sc[0][cb][j], sh, slo, j);
-        split2(Sc[1][cb][j], sh, slo, j + 4);
-      }
+      split_all<8>(sh, slo, [&](int j) { return Sc[j >> 2][cb][j & 3]; });
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         o[cb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -407,12 +401,11 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       vec8<C> sbh, sbl;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+      split_all<8>(sbh, sbl, [&](int jj) {
         const int kb = jj >> 2, i = jj & 3;
         const int key = kb * 16 + 4 * g + i, qry = tb * 16 + c;
-        split2(key <= qry ? sc[kb][tb][i] : 0.f, sbh, sbl, jj);
-      }
+        return key <= qry ? sc[kb][tb][i] : 0.f;
+      });
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         mma16(o[cb][tb], vf[cb], sbh);
@@ -475,7 +468,7 @@ cbwd_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
       for (int j = 0; j < 4; ++j) ga += to_f(g8[j]) * o0[j] + to_f(g8[j + 4]) * o1[j];
       ga = lanes_sum<CPR>(ga);
       if (c8 == 0) {
-        const float gm = ga / den;
+        const float gm = ga * __builtin_amdgcn_rcpf(den);  // hardware reciprocal (1 ulp)
         const int tok = tok0 + row;
         if (tok < tend) {
           lg[rowbase + tok] = qbias[row] + log2f(den);
@@ -643,8 +636,11 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
           mma16_split_a<PSO>(pq[tb][fb], om[fb][dc], oml[PSO ? fb : 0][PSO ? dc : 0], qf[dc]);
         }
 #pragma unroll
+        for (int i = 0; i < 4; i += 2)
+          split_pair(key_feature<KIND>(pk[i], inv_sqrt_m, eps), key_feature<KIND>(pk[i + 1], inv_sqrt_m, eps), afh[fb],
+                     afl[fb], 4 * tb + i);
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
-          split2(key_feature<KIND>(pk[i], inv_sqrt_m, eps), afh[fb], afl[fb], 4 * tb + i);
           if constexpr (KIND == kPrf)
             pq[tb][fb][i] = fast_exp2(pq[tb][fb][i]);
           else
@@ -662,11 +658,10 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       vec8<C> sth[FB], stl[FB];
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        split_all<8>(sth[fb], stl[fb], [&](int j) {
           const int nb = 2 * kc + (j >> 2);
-          split2(nb < NB ? St[nb][fb][j & 3] : 0.f, sth[fb], stl[fb], j);
-        }
+          return nb < NB ? St[nb][fb][j & 3] : 0.f;
+        });
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int qr = tb * 16 + c;
@@ -683,7 +678,9 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) split2(col0 + i == DV ? -rgm[buf][qr] : 0.f, gh, gl, 4 * hf + i);
+            for (int i = 0; i < 4; i += 2)
+              split_pair(col0 + i == DV ? -rgm[buf][qr] : 0.f, col0 + i + 1 == DV ? -rgm[buf][qr] : 0.f, gh, gl,
+                         4 * hf + i);
           }
         }
 #pragma unroll
@@ -723,12 +720,11 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
         const int qr = tb * 16 + c;
         const float gq = rgm[buf][qr];
         vec8<C> bh, bl;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        split_all<8>(bh, bl, [&](int jj) {
           const int kb = jj >> 2, i = jj & 3;
           const int key = kb * 16 + 4 * g + i;
-          split2(key <= qr ? bs[kb][tb][i] - gq : 0.f, bh, bl, jj);
-        }
+          return key <= qr ? bs[kb][tb][i] - gq : 0.f;
+        });
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb) mma_split<NSPL>(dph[fb][tb], afh[fb], afl[fb], bh, bl);
       }
@@ -739,8 +735,7 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         vec4<C> h4, l4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split2(pq[tb][fb][i] * dph[fb][tb][i], h4, l4, i);
+        split_all<4>(h4, l4, [&](int i) { return pq[tb][fb][i] * dph[fb][tb][i]; });
         const int off = (tb * 16 + c) * PROW + w * 32 + fb * 16 + 4 * g;
         *reinterpret_cast<vec4<C>*>(&prow[0][off]) = h4;
         if constexpr (NSPL == 2) *reinterpret_cast<vec4<C>*>(&prow[NSPL - 1][off]) = l4;
@@ -906,17 +901,15 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
     vec8<C> ah[FB], al[FB];  // phi~^T: A [feature][query], paired query slots
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        split2(query_feature<KIND>(pq[j >> 2][fb][j & 3], lq[j >> 2][j & 3], inv_sqrt_m, eps), ah[fb], al[fb], j);
+      split_all<8>(ah[fb], al[fb],
+                   [&](int j) { return query_feature<KIND>(pq[j >> 2][fb][j & 3], lq[j >> 2][j & 3], inv_sqrt_m, eps); });
     vec8<C> wv[NB];
     value_frags<T, D, DV, NT>(ring[buf], wv, c, g);
     vec8<C> zh, zl;  // the -gamma column (c == 0 of the last block)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    split_all<8>(zh, zl, [&](int j) {
       const int q = 16 * (j >> 2) + 4 * g + (j & 3);
-      split2(c == 0 ? -rgm[buf][q] : 0.f, zh, zl, j);
-    }
+      return c == 0 ? -rgm[buf][q] : 0.f;
+    });
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
@@ -1117,9 +1110,7 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     // phi~ as B [query][feature] (paired query slots), hi + lo
     vec8<C> qbh[FB], qbl[FB];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) split2(pq[j >> 2][fb][j & 3], qbh[fb], qbl[fb], j);
+    for (int fb = 0; fb < FB; ++fb) split_all<8>(qbh[fb], qbl[fb], [&](int j) { return pq[j >> 2][fb][j & 3]; });
     // ---- scores Bt[q][key] = g_q . v_key; A operand [key][query] of B = Bt - gamma_q, q >= key
     vec8<C> bah[2], bal[2];
     {
@@ -1144,12 +1135,11 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        split_all<8>(bah[kb], bal[kb], [&](int jj) {
           const int qb = jj >> 2, i = jj & 3;
           const int q = qb * 16 + 4 * g + i, key = kb * 16 + c;
-          split2(q >= key ? bt[qb][kb][i] - rgm[buf][q] : 0.f, bah[kb], bal[kb], jj);
-        }
+          return q >= key ? bt[qb][kb][i] - rgm[buf][q] : 0.f;
+        });
     }
     // ---- dPhi''_K[key][f]: [V 1] (A, paired column slots) x Rc (B, hi + lo), + B x phi~
     f32x4 dpk[2][FB];
@@ -1160,11 +1150,10 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       vec8<C> rh[FB], rlo[FB];
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        split_all<8>(rh[fb], rlo[fb], [&](int j) {
           const int nb = 2 * kc + (j >> 2);
-          split2(nb < NB ? Rc[nb][fb][j & 3] : 0.f, rh[fb], rlo[fb], j);
-        }
+          return nb < NB ? Rc[nb][fb][j & 3] : 0.f;
+        });
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 16 + c;
@@ -1213,8 +1202,7 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         vec4<C> h4, l4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split2(dpk[kb][fb][i], h4, l4, i);
+        split_all<4>(h4, l4, [&](int i) { return dpk[kb][fb][i]; });
         const int off = (w * 32 + fb * 16 + c) * FROW + kb * 16 + 4 * g;
         *reinterpret_cast<vec4<C>*>(&ft[0][off]) = h4;
         if constexpr (NSPL == 2) *reinterpret_cast<vec4<C>*>(&ft[NSPL - 1][off]) = l4;
@@ -1225,11 +1213,10 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     value_frags<T, D, DV, NT>(gbase, gv, c, g);
     {
       vec8<C> zh, zl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      split_all<8>(zh, zl, [&](int j) {
         const int q = 16 * (j >> 2) + 4 * g + (j & 3);
-        split2(c == 0 ? -rgm[buf][q] : 0.f, zh, zl, j);
-      }
+        return c == 0 ? -rgm[buf][q] : 0.f;
+      });
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
 #pragma unroll
@@ -1431,19 +1418,14 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     // phi~ as B [query][feature] (paired query slots), hi + lo; phi'_K and phi~ rows [feature][token]
     vec8<C> qbh[FB], qbl[FB];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) split2(pq[j >> 2][fb][j & 3], qbh[fb], qbl[fb], j);
+    for (int fb = 0; fb < FB; ++fb) split_all<8>(qbh[fb], qbl[fb], [&](int j) { return pq[j >> 2][fb][j & 3]; });
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
         vec4<C> kh4, kl4, qh4, ql4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          split2(pk[tb][fb][i], kh4, kl4, i);
-          split2(pq[tb][fb][i], qh4, ql4, i);
-        }
+        split_all<4>(kh4, kl4, [&](int i) { return pk[tb][fb][i]; });
+        split_all<4>(qh4, ql4, [&](int i) { return pq[tb][fb][i]; });
         const int off = (fb * 16 + c) * FROW + tb * 16 + 4 * g;
         *reinterpret_cast<vec4<C>*>(fth + off) = kh4;
         *reinterpret_cast<vec4<C>*>(qth + off) = qh4;
@@ -1468,8 +1450,7 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
       for (int nb = 0; nb < NVB; ++nb) {
         vec8<C> rth, rtl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) split2(Rt[j >> 2][nb][j & 3], rth, rtl, j);
+        split_all<8>(rth, rtl, [&](int j) { return Rt[j >> 2][nb][j & 3]; });
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) mma_split<NSPL>(dvt[nb][kb], rth, rtl, fah[kb], fal[kb]);
       }
@@ -1488,12 +1469,11 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         vec8<C> aah, aal;  // B [query][key], paired query slots, q >= key
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        split_all<8>(aah, aal, [&](int jj) {
           const int qb = jj >> 2, i = jj & 3;
           const int q = qb * 16 + 4 * g + i, key = kb * 16 + c;
-          split2(q >= key ? at[qb][kb][i] : 0.f, aah, aal, jj);
-        }
+          return q >= key ? at[qb][kb][i] : 0.f;
+        });
 #pragma unroll
         for (int nb = 0; nb < NVB; ++nb) {
           mma16(dvt[nb][kb], gv[nb], aah);

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace favor {
 
 typedef __bf16 bf16;
@@ -75,6 +77,37 @@ template <> __device__ __forceinline__ f16 to_t<f16>(float x) { return static_ca
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ float to_f(f16 x) { return static_cast<float>(x); }
+
+// x as a value of the 16-bit type C and its remainder (x - that value, also rounded to C), for slots j and
+// j + 1 of two operands at once: the pair is rounded in one packed conversion and widened back with a shift
+// and a mask, which the per-element form cannot share. Same results as rounding each x on its own.
+template <typename V>
+__device__ __forceinline__ void split_pair(float x0, float x1, V& h, V& l, int j) {
+  using C = std::remove_cv_t<std::remove_reference_t<decltype(h[0])>>;
+  if constexpr (std::is_same_v<C, bf16>) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 hp = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+    const float h0 = __builtin_bit_cast(float, hb << 16), h1 = __builtin_bit_cast(float, hb & 0xffff0000u);
+    const bf16x2 lp = __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2);
+    h[j] = hp[0];
+    h[j + 1] = hp[1];
+    l[j] = lp[0];
+    l[j + 1] = lp[1];
+  } else {
+    const C h0 = to_t<C>(x0), h1 = to_t<C>(x1);
+    h[j] = h0;
+    h[j + 1] = h1;
+    l[j] = to_t<C>(x0 - to_f(h0));
+    l[j + 1] = to_t<C>(x1 - to_f(h1));
+  }
+}
+// every slot of h and l from f(slot), in pairs
+template <int N, typename V, typename F>
+__device__ __forceinline__ void split_all(V& h, V& l, F&& f) {
+#pragma unroll
+  for (int j = 0; j < N; j += 2) split_pair(f(j), f(j + 1), h, l, j);
+}
 
 // Inputs of a 16-bit projection: a chunk whose sum of squares reaches 65504^2 may hold a value beyond fp16's
 // range; its fp16 copy is taken clamped to +-65504 (rarely taken; the norm keeps the true value, so a key of

@@ -496,7 +496,8 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
     constexpr bool LO = SPLIT && sizeof(C) == 2;
     vec8<C> af[FB], al[LO ? FB : 1];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+    for (int fb = 0; fb < FB; ++fb) {
+      float fv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float a = pcur[j >> 2][fb][j & 3];
@@ -509,9 +510,15 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
           const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L && (w * FB + fb) * 16 + c < m_valid;
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
-        af[fb][j] = to_t<C>(f);
-        if constexpr (LO) al[fb][j] = to_t<C>(f - to_f(af[fb][j]));
+        fv[j] = f;
       }
+      if constexpr (LO) {
+        split_all<8>(af[fb], al[fb], [&](int j) { return fv[j]; });
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) af[fb][j] = to_t<C>(fv[j]);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
     // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
     // the piece: a filler slot into an unused buffer) and the next copies
