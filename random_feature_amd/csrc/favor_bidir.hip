@@ -44,9 +44,10 @@ inline float omega_scale(int kind, float sc) {
 // 2^(M_piece,wave - M_max) and summed, give the A fragments of S_aug^T:
 // sfr[bh][fc][nb][lane][j] = S_aug[fc*32 + 16(j>>2) + 4g + (j&3)][nb*16 + c]; in the last
 // block only row c == 0 (the z column) is nonzero.
-template <typename C, int D, int DV, int M>
+// PT: the type of the stored partials (fp32; bf16 for 16-bit inputs, whose S_aug fragments are bf16 as well).
+template <typename C, int D, int DV, int M, typename PT>
 __global__ void __launch_bounds__(1024)
-combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
+combine_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const float* __restrict__ pmax,
                int tpb, long long T_all, int G, int kind, C* __restrict__ sfr, float* __restrict__ gmx) {
   constexpr int NW = RedSplit<M, D>::NW, FB = RedSplit<M, D>::FB;
   constexpr int NB = DV / 16 + 1;
@@ -81,10 +82,9 @@ combine_kernel(const float* __restrict__ part, const float* __restrict__ zpart, 
           const int k = k0 + j < np ? k0 + j : np - 1;
           const size_t slot = (size_t)(i_lo + k) + bh;
           sc[j] = k0 + j < np ? (scaled ? fast_exp2(pmax[slot * NW + wv] - gmax) : 1.f) : 0.f;
-          const float* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
-                                           : zpart + ((slot * NFC + fc) * 4 + g) * 8;
-          pl[j] = reinterpret_cast<const f32x4*>(src)[0];
-          ph[j] = reinterpret_cast<const f32x4*>(src)[1];
+          const PT* src = (nb < NB - 1) ? part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8
+                                        : zpart + ((slot * NFC + fc) * 4 + g) * 8;
+          ld8_f32(src, pl[j], ph[j]);
         }
 #pragma unroll
         for (int j = 0; j < KP; ++j) {
@@ -651,8 +651,11 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
   const BidirPlan p = plan_bidir(s, sizeof(T) == 4 ? 0 : 1, Lq);
   char* base = static_cast<char*>(ws);
   P* omf = prep ? static_cast<P*>(const_cast<void*>(prep)) : reinterpret_cast<P*>(base + p.off_omf);
-  float* part = reinterpret_cast<float*>(base + p.off_part);
-  float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
+  // partials in the contraction type: bf16 for 16-bit inputs (S_aug is rounded to bf16 for the output
+  // contraction in any case), fp32 for fp32 inputs
+  using PT = C;
+  PT* part = reinterpret_cast<PT*>(base + p.off_part);
+  PT* zpart = reinterpret_cast<PT*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   C* sfr = reinterpret_cast<C*>(base + p.off_sfr);
   float* gmx = reinterpret_cast<float*>(base + p.off_gmax);
@@ -671,18 +674,18 @@ static hipError_t run_bidir(const T* q, const T* k, const T* v, const float* ome
     const T* vg = v + c0;
     void* og = out_f32 ? static_cast<void*>(static_cast<float*>(out) + c0) : static_cast<void*>(static_cast<T*>(out) + c0);
     if (kind == kPrf)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
           s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv, vcols);
     else if (!GEN && kind == kTrig)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, GEN ? kPrf : kTrig, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg,
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, GEN ? kPrf : kTrig, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k, vg,
           omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv,
           vcols);
     else
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
+      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
           s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, 0, 0, s.m, s.dv, vcols);
     // one thread per (value block, lane): every partial is requested in a single round
     constexpr int NBC = DV / 16 + 1;
-    launch("combine", combine_kernel<C, D, DV, M>, (unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0,
+    launch("combine", combine_kernel<C, D, DV, M, PT>, (unsigned)(s.bh() * ((M + 31) / 32)), 64 * (NBC < 16 ? NBC : 16), 0,
         st, part, zpart, pmax, p.tpb, p.T_all, p.G, kind, sfr, gmx);
     if (kind == kPrf)
       launch("output", q_output_kernel<T, D, DV, M, kPrf, GEN>, p.G_q, 64 * NW, 0, st, q, omf, sfr, s.H, Lq, p.tpb_q,

@@ -56,11 +56,12 @@ namespace favor {
 // Shapes as kv_reduce_kernel (GEN): m_valid <= M features (the query features past it are zero, which
 // keeps the rest of those features out of every output), a column group of vcols <= DV columns of V
 // and out whose rows are ld elements apart.
-template <typename T, int D, int DV, int M, int KIND, bool GEN>
+// CT: the type of the stored carries (see scan_kernel).
+template <typename T, int D, int DV, int M, int KIND, bool GEN, typename CT>
 __global__ void __launch_bounds__(64 * (RedSplit<M, D>::NW), (RedSplit<M, D>::WPE))
 sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-             const typename Ops<T>::P* __restrict__ omf, const float* __restrict__ cpart,
-             const float* __restrict__ cz, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
+             const typename Ops<T>::P* __restrict__ omf, const CT* __restrict__ cpart,
+             const CT* __restrict__ cz, const float* __restrict__ cmax, int H, int L, int seg_len, int nseg,
              float eps, float inv_sqrt_m, float nscale, int out_f32, void* __restrict__ out, int m_valid_, int ld_,
              int vcols_) {
   using P = typename Ops<T>::P;
@@ -112,15 +113,10 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f}, hi = lo;
-      if (nb < NB - 1) {
-        const float* src = cpart + ((((size_t)pc * NFC + fc) * NVB + nb) * 64 + lane) * 8;
-        lo = reinterpret_cast<const f32x4*>(src)[0];
-        hi = reinterpret_cast<const f32x4*>(src)[1];
-      } else if (c == 0) {
-        const float* src = cz + (((size_t)pc * NFC + fc) * 4 + g) * 8;
-        lo = reinterpret_cast<const f32x4*>(src)[0];
-        hi = reinterpret_cast<const f32x4*>(src)[1];
-      }
+      if (nb < NB - 1)
+        ld8_f32(cpart + ((((size_t)pc * NFC + fc) * NVB + nb) * 64 + lane) * 8, lo, hi);
+      else if (c == 0)
+        ld8_f32(cz + (((size_t)pc * NFC + fc) * 4 + g) * 8, lo, hi);
       sacc[2 * p][nb] = lo;
       if (2 * p + 1 < FB) sacc[2 * p + 1][nb] = hi;
     }
@@ -426,8 +422,11 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   float* part = reinterpret_cast<float*>(base + p.off_part);
   float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
-  float* cpart = reinterpret_cast<float*>(base + p.off_cpart);
-  float* cz = reinterpret_cast<float*>(base + p.off_cz);
+  // carries in the contraction type: bf16 for 16-bit inputs (the sweep rounds its state to bf16 for the carried
+  // term in any case), fp32 for fp32 inputs
+  using CT = typename Ops<T>::C;
+  CT* cpart = reinterpret_cast<CT*>(base + p.off_cpart);
+  CT* cz = reinterpret_cast<CT*>(base + p.off_cz);
   float* cmax = reinterpret_cast<float*>(base + p.off_cmax);
   const float sc = std::pow((float)D, -0.25f);
   const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
@@ -453,14 +452,14 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
           s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg, s.m, s.dv,
           vcols);
     constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    launch("scan", scan_kernel<D, DV, M>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st,
+    launch("scan", scan_kernel<D, DV, M, CT>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st,
         part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final ? S_final + c0 : nullptr,
         c0 == 0 ? z_final : nullptr, s.m, s.dv, vcols);
     if (kind == kPrf)
-      launch("sweep", sweep_kernel<T, D, DV, M, kPrf, GEN>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
+      launch("sweep", sweep_kernel<T, D, DV, M, kPrf, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
           s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
     else
-      launch("sweep", sweep_kernel<T, D, DV, M, kRelu, GEN>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
+      launch("sweep", sweep_kernel<T, D, DV, M, kRelu, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
           s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
   }
   return hipGetLastError();

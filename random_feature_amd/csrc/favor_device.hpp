@@ -160,6 +160,55 @@ template <typename T> __device__ __forceinline__ void st8(T* p, const vec8<T>& x
   }
 }
 
+// Eight stored sums (fp32, or bf16 where a partial sum is kept in half the bytes) as two fp32 quads, and back:
+// element j of the eight is lo[j] for j < 4, hi[j - 4] otherwise. Stores round to nearest even.
+template <typename S> __device__ __forceinline__ void ld8_f32(const S* p, f32x4& lo, f32x4& hi) {
+  if constexpr (sizeof(S) == 4) {
+    lo = reinterpret_cast<const f32x4*>(p)[0];
+    hi = reinterpret_cast<const f32x4*>(p)[1];
+  } else {
+    const vec8<S> x = *reinterpret_cast<const vec8<S>*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = to_f(x[i]);
+      hi[i] = to_f(x[i + 4]);
+    }
+  }
+}
+template <typename S> __device__ __forceinline__ void st8_f32(S* p, const f32x4& lo, const f32x4& hi) {
+  if constexpr (sizeof(S) == 4) {
+    reinterpret_cast<f32x4*>(p)[0] = lo;
+    reinterpret_cast<f32x4*>(p)[1] = hi;
+  } else {
+    vec8<S> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = to_t<S>(lo[i]);
+      x[i + 4] = to_t<S>(hi[i]);
+    }
+    *reinterpret_cast<vec8<S>*>(p) = x;
+  }
+}
+// Four stored sums as one fp32 quad, and back.
+template <typename S> __device__ __forceinline__ f32x4 ld4_f32(const S* p) {
+  if constexpr (sizeof(S) == 4) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    const vec4<S> x = *reinterpret_cast<const vec4<S>*>(p);
+    return f32x4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
+  }
+}
+template <typename S> __device__ __forceinline__ void st4_f32(S* p, const f32x4& v) {
+  if constexpr (sizeof(S) == 4) {
+    *reinterpret_cast<f32x4*>(p) = v;
+  } else {
+    vec4<S> x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = to_t<S>(v[i]);
+    *reinterpret_cast<vec4<S>*>(p) = x;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Cross-lane exchanges on the VALU (no LDS round trip).

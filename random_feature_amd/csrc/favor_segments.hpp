@@ -18,10 +18,12 @@ namespace favor {
 // the four elements of a thread share fc and g and differ in j & 3.
 // The final state (S_final, z_final: nullable) goes out in canonical scale for the m_valid real features,
 // S_final rows ldS apart (a column group writes its vcols columns; z_final only when non-null).
-template <int D, int DV, int M>
+// CT: the type the carries are stored in (fp32; bf16 where the sweep rounds the carried state to bf16 for its
+// contractions anyway). The sums themselves and the final state are fp32.
+template <int D, int DV, int M, typename CT = float>
 __global__ void __launch_bounds__(256)
 scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
-            int nseg, int kind, float log2_sqrt_m, float* __restrict__ cpart, float* __restrict__ cz,
+            int nseg, int kind, float log2_sqrt_m, CT* __restrict__ cpart, CT* __restrict__ cz,
             float* __restrict__ cmax, float* __restrict__ S_final, float* __restrict__ z_final, int m_valid,
             int ldS, int vcols) {
   constexpr int NWR = RedSplit<M, D>::NW, FBR = RedSplit<M, D>::FB;
@@ -69,8 +71,9 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
   const int r0 = fc * 32 + 16 * (j0 >> 2) + 4 * g;  // features r0..r0+3 (rows of S_aug)
   const int wv = (fc * 32) / (FBR * 16);           // the reducing wave that owned them
   const f32x4* src = reinterpret_cast<const f32x4*>(isz ? zpart + (e - NP) : part + e);
-  f32x4* dst = reinterpret_cast<f32x4*>(isz ? cz + (e - NP) : cpart + e);
+  CT* dst = isz ? cz + (e - NP) : cpart + e;  // four carries at dst[slot * NE]
   const size_t stride = (isz ? NZ : NP) / 4;
+  const size_t NE = stride * 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float prev = 0.f;
   for (int p0 = 0; p0 < nseg; p0 += KB) {
@@ -90,7 +93,7 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
         const size_t slot = (size_t)bh * nseg + p;
         const float mp = pre[p];
         if (p > 0) acc *= fast_exp2(prev - mp);
-        dst[slot * stride] = acc;
+        st4_f32(dst + slot * NE, acc);
         acc += x[u] * ((kind == kPrf) ? fast_exp2(sc[u] - mp) : 1.f);
         prev = mp;
       }

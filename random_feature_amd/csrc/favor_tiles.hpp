@@ -245,12 +245,14 @@ constexpr float kKeyMargin = 8.f;
 // multiple of 16: the features past it are masked to zero and their wave maxima written as -inf)
 // and a column group of a wider V (rows ldv apart, vcols <= DV valid columns); without GEN those
 // arguments are ignored (m_valid = M, ldv = vcols = DV).
-template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false, bool PSPLIT = false, bool GEN = false>
+// PT: the type the partial sums are stored in (fp32, or bf16 where the reader rounds them to bf16 anyway).
+template <typename T, int D, int DV, int M, int R, int KIND, bool SPLIT = false, bool PSPLIT = false, bool GEN = false,
+          typename PT = float>
 __global__ void __launch_bounds__(64 * (RedSplit<M, D>::NW), (RedSplit<M, D>::WPE))
 kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typename Ops<T>::P* __restrict__ omf,
                  const typename Ops<T>::P* __restrict__ omf_lo,
                  int H, int L, int tpb, long long T_all, int G, float eps, float inv_sqrt_m, float nscale,
-                 float* __restrict__ part, float* __restrict__ zpart, float* __restrict__ pmax, int seg_tiles,
+                 PT* __restrict__ part, PT* __restrict__ zpart, float* __restrict__ pmax, int seg_tiles,
                  int nseg, int m_valid_, int ldv_, int vcols_) {
   using P = typename Ops<T>::P;
   using C = typename Ops<T>::C;
@@ -296,7 +298,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   bool first = true;
   vec8<P> om[FB][DC];
 
-  // one (b,h)'s sums of this piece, as fp32 A fragments of S^T (the layout of sfr):
+  // one (b,h)'s sums of this piece, as A fragments of S^T (the layout of sfr) in PT:
   // part[slot][fc][nb][lane][j], the z column compacted to zpart[slot][fc][g][j] (lanes c = 0)
   auto flush = [&](int fbh, float fmax) {
     const size_t slot = (size_t)pc + (seg_tiles > 0 ? 0 : fbh);
@@ -307,15 +309,12 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 lo = sacc[2 * p][nb], hi = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FB % 2 == 0) hi = sacc[2 * p + 1][nb];
-        float* dst;
+        PT* dst;
         if (nb < NB - 1)
           dst = part + (((slot * NFC + fc) * (NB - 1) + nb) * 64 + lane) * 8;
         else
           dst = zpart + ((slot * NFC + fc) * 4 + g) * 8;
-        if (nb < NB - 1 || c == 0) {
-          reinterpret_cast<f32x4*>(dst)[0] = lo;
-          reinterpret_cast<f32x4*>(dst)[1] = hi;
-        }
+        if (nb < NB - 1 || c == 0) st8_f32(dst, lo, hi);
       }
     }
     if (lane == 0) pmax[slot * NW + w] = w * FB * 16 < m_valid ? fmax : -INFINITY;  // -inf: no valid feature
