@@ -367,6 +367,8 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
 }
 
 // ---------------------------------------------------------------- host side
+template <typename X> struct TypeTag { using type = X; };
+
 static void segmenting(const Shape& s, int& nseg, int& seg_len) {
   // enough segments for ~512 workgroups, but at least 256 tokens each
   const long long bh = s.bh();
@@ -419,8 +421,6 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   const CausalPlan p = plan_causal(s, sizeof(T) == 4 ? 0 : 1);
   char* base = static_cast<char*>(ws);
   P* omf = prep ? static_cast<P*>(const_cast<void*>(prep)) : reinterpret_cast<P*>(base + p.off_omf);
-  float* part = reinterpret_cast<float*>(base + p.off_part);
-  float* zpart = reinterpret_cast<float*>(base + p.off_zpart);
   float* pmax = reinterpret_cast<float*>(base + p.off_pmax);
   // carries in the contraction type: bf16 for 16-bit inputs (the sweep rounds its state to bf16 for the carried
   // term in any case), fp32 for fp32 inputs
@@ -443,18 +443,34 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
     const int vcols = std::min(DV, s.dv - c0);
     const T* vg = v + c0;
     void* og = out_f32 ? static_cast<void*>(static_cast<float*>(out) + c0) : static_cast<void*>(static_cast<T*>(out) + c0);
-    if (kind == kPrf)
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
-          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg, s.m, s.dv,
-          vcols);
-    else
-      launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN>, p.G, 64 * NWR, 0, st, k, vg, omf, nullptr,
-          s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg, s.m, s.dv,
-          vcols);
-    constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
-    launch("scan", scan_kernel<D, DV, M, CT>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256, p.nseg * sizeof(float), st,
-        part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax, S_final ? S_final + c0 : nullptr,
-        c0 == 0 ? z_final : nullptr, s.m, s.dv, vcols);
+    // segment sums and their scan, with the partials stored as PT
+    auto reduce_scan = [&](auto tag) {
+      using PT = typename decltype(tag)::type;
+      PT* part = reinterpret_cast<PT*>(base + p.off_part);
+      PT* zpart = reinterpret_cast<PT*>(base + p.off_zpart);
+      if (kind == kPrf)
+        launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k, vg,
+            omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg,
+            s.m, s.dv, vcols);
+      else
+        launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k,
+            vg, omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles,
+            p.nseg, s.m, s.dv, vcols);
+      constexpr int NQ = ((M + 31) / 32) * ((DV / 16) * 512 + 32) / 4;
+      launch("scan", scan_kernel<D, DV, M, CT, PT>, (unsigned)(s.bh() * ((NQ + 255) / 256)), 256,
+          p.nseg * sizeof(float), st, part, zpart, pmax, p.nseg, kind, log2_sqrt_m, cpart, cz, cmax,
+          S_final ? S_final + c0 : nullptr, c0 == 0 ? z_final : nullptr, s.m, s.dv, vcols);
+    };
+    // partials in bf16 for 16-bit inputs when no final state is asked for (the carries they feed are bf16), else
+    // fp32 (the final state is summed from them)
+    if constexpr (sizeof(T) == 2) {
+      if (!S_final && !z_final)
+        reduce_scan(TypeTag<bf16>{});
+      else
+        reduce_scan(TypeTag<float>{});
+    } else {
+      reduce_scan(TypeTag<float>{});
+    }
     if (kind == kPrf)
       launch("sweep", sweep_kernel<T, D, DV, M, kPrf, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
           s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);

@@ -19,10 +19,11 @@ namespace favor {
 // The final state (S_final, z_final: nullable) goes out in canonical scale for the m_valid real features,
 // S_final rows ldS apart (a column group writes its vcols columns; z_final only when non-null).
 // CT: the type the carries are stored in (fp32; bf16 where the sweep rounds the carried state to bf16 for its
-// contractions anyway). The sums themselves and the final state are fp32.
-template <int D, int DV, int M, typename CT = float>
+// contractions anyway); PT: the type of the segment partials (fp32; bf16 when no final state is asked for). The
+// sums themselves and the final state are fp32.
+template <int D, int DV, int M, typename CT = float, typename PT = float>
 __global__ void __launch_bounds__(256)
-scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, const float* __restrict__ pmax,
+scan_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const float* __restrict__ pmax,
             int nseg, int kind, float log2_sqrt_m, CT* __restrict__ cpart, CT* __restrict__ cz,
             float* __restrict__ cmax, float* __restrict__ S_final, float* __restrict__ z_final, int m_valid,
             int ldS, int vcols) {
@@ -70,7 +71,7 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
   }
   const int r0 = fc * 32 + 16 * (j0 >> 2) + 4 * g;  // features r0..r0+3 (rows of S_aug)
   const int wv = (fc * 32) / (FBR * 16);           // the reducing wave that owned them
-  const f32x4* src = reinterpret_cast<const f32x4*>(isz ? zpart + (e - NP) : part + e);
+  const PT* src = isz ? zpart + (e - NP) : part + e;  // four partials at src[slot * NE]
   CT* dst = isz ? cz + (e - NP) : cpart + e;  // four carries at dst[slot * NE]
   const size_t stride = (isz ? NZ : NP) / 4;
   const size_t NE = stride * 4;
@@ -83,7 +84,7 @@ scan_kernel(const float* __restrict__ part, const float* __restrict__ zpart, con
     for (int u = 0; u < KB; ++u) {  // a segment past the last is read as the last, weight 0
       const int p = p0 + u < nseg ? p0 + u : nseg - 1;
       const size_t slot = (size_t)bh * nseg + p;
-      x[u] = src[slot * stride];
+      x[u] = ld4_f32(src + slot * NE);
       sc[u] = (kind == kPrf) ? pmax[slot * NWR + wv] : 0.f;
     }
 #pragma unroll
