@@ -171,8 +171,9 @@ favor_status favor_bidir_cross(const void* q, const void* k, const void* v, cons
  * z_final [B,H,m] (fp32, both or neither) are non-NULL, the state after the last
  * token is written in canonical (unstabilised) scale: exactly what
  * favor_decode continues from. Canonical state needs PRF with d <= 64
- * (exp(omega.x - |x|^2/2) <= exp(|omega|^2/2) stays inside fp32). FAVOR_TRIG:
- * FAVOR_ERR_UNSUPPORTED. */
+ * (exp(omega.x - |x|^2/2) <= exp(|omega|^2/2) stays inside fp32). FAVOR_TRIG
+ * (equation 5's sin/cos features over a FAVOR_TRIG_PAIRS Omega) as favor_bidir: m even,
+ * exact shapes only, and no final state (FAVOR_ERR_UNSUPPORTED with S_final). */
 favor_status favor_causal(const void* q, const void* k, const void* v, const float* omega,
                           int B, int H, int L, int d, int dv, int m,
                           favor_dtype dtype, favor_kind kind, float eps, int out_f32,
@@ -209,7 +210,9 @@ favor_status favor_causal_prepared(const void* q, const void* k, const void* v, 
  * q, k [N,H,d], v [N,H,dv] in `dtype`; S [N,H,m,dv] and z [N,H,m] fp32 in canonical
  * scale, updated in place; out [N,H,dv] fp32.
  * Requires d in {16, 32, 64}, dv a multiple of 16 in [16, 256], m a multiple of 16
- * with m <= 1024 (other values, and FAVOR_TRIG: FAVOR_ERR_UNSUPPORTED). */
+ * with m <= 1024 (other values: FAVOR_ERR_UNSUPPORTED). FAVOR_TRIG (over a
+ * FAVOR_TRIG_PAIRS Omega): the state holds the canonical features sin/cos(omega.k)
+ * exp(|k|^2/2)/sqrt(m/2) (k scaled by d^-1/4), finite while |k|^2 d^-1/2 < 176. */
 favor_status favor_decode(const void* q, const void* k, const void* v, const float* omega,
                           float* S, float* z, int N, int H, int d, int dv, int m,
                           favor_dtype dtype, favor_kind kind, float eps,

@@ -233,7 +233,8 @@ static favor_status causal_common(const void* q, const void* k, const void* v, c
     return FAVOR_ERR_INVALID_ARG;
   if (S_final && (!aligned16(S_final) || !aligned16(z_final))) return FAVOR_ERR_INVALID_ARG;
   if (!favor::shape_built(dtype, d, dv, m)) return FAVOR_ERR_UNSUPPORTED;
-  if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
+  if (kind == FAVOR_TRIG && m % 2 != 0) return FAVOR_ERR_INVALID_ARG;
+  if (kind == FAVOR_TRIG && !favor::kernel_shape(dtype, d, dv, m).exact) return FAVOR_ERR_UNSUPPORTED;
   if (S_final && (kind != FAVOR_PRF || d > 64)) return FAVOR_ERR_UNSUPPORTED;
   if (ws_bytes < favor::plan_causal(s, dtype).total) return FAVOR_ERR_WORKSPACE;
   return hip_status(favor::launch_causal(q, k, v, prep ? nullptr : omega, s, dtype, kind, eps, out_f32 ? 1 : 0, out,
@@ -270,7 +271,6 @@ static favor_status decode_common(const void* q, const void* k, const void* v, c
   if (!(d == 16 || d == 32 || d == 64)) return FAVOR_ERR_UNSUPPORTED;
   if (dv % 16 != 0 || dv < 16 || dv > 256) return FAVOR_ERR_UNSUPPORTED;
   if (m % 16 != 0 || m > 1024) return FAVOR_ERR_UNSUPPORTED;
-  if (kind == FAVOR_TRIG) return FAVOR_ERR_UNSUPPORTED;
   return hip_status(
       favor::launch_decode(q, k, v, omega, S, z, N, H, d, dv, m, dtype, kind, eps, gate, inw, out, stream));
 }

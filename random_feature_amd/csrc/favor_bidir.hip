@@ -32,12 +32,6 @@
 
 namespace favor {
 
-// Scale folded into the Omega' fragments: d^-1/4, times log2(e) for the exponential map (the
-// hardware exp2) or 1/(2 pi) for the trigonometric map (the hardware cosine takes revolutions).
-inline float omega_scale(int kind, float sc) {
-  return kind == kPrf ? sc * kLog2e : (kind == kTrig ? sc * 0.15915494309189535f : sc);
-}
-
 // ---------------------------------------------------------------- combine
 // One workgroup per (b*h, 32-feature chunk), one thread per (value block, lane): the
 // partials of the pieces of that (b,h), already in fragment layout, scaled by

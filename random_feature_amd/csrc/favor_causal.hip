@@ -121,7 +121,9 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
       if (2 * p + 1 < FB) sacc[2 * p + 1][nb] = hi;
     }
   }
-  const float mk = (KIND == kPrf) ? cmax[pc] : 0.f;
+  // the keys' fixed maximum of the segment: of their exponents (exponential map) or of their norms n'
+  // (trigonometric map, whose keys carry the scale 2^(n'_k))
+  const float mk = (KIND != kRelu) ? cmax[pc] : 0.f;
   float omax = 0.f;
   if constexpr (KIND == kPrf) omax = omega_norm_max<NW>(om, &qmx[0][0], 32);
   wait_vmcnt<0>();
@@ -180,6 +182,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
     // ---- projections
     f32x4 pk[2][FB], pq[2][FB];
     bool exact = false;
+    float tw[2][4];  // trigonometric map: the keys' scale 2^(n'_k - M*) (0 past the segment)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       f32x4 kbias = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -187,6 +190,10 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[s_cur][tb * 16 + 4 * g]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) kbias[i] = -(n4[i] + mk);
+      } else if constexpr (KIND == kTrig) {
+        const f32x4 n4 = *reinterpret_cast<const f32x4*>(&kn[s_cur][tb * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tw[tb][i] = n4[i] < INFINITY ? fast_exp2(n4[i] - mk) : 0.f;
       }
       const float b = (KIND == kPrf) ? qn[s_cur][tb * 16 + c] * omax : 0.f;
       if constexpr (KIND == kPrf) exact |= b > kQueryBoundLimit;
@@ -245,6 +252,8 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
         float f;
         if constexpr (KIND == kPrf) {
           f = fast_exp2(a);  // rows past the segment carry an infinite norm: exp2(-inf) = 0
+        } else if constexpr (KIND == kTrig) {
+          f = trig_feature(a, (w * FB + fb) * 16 + c, M) * tw[j >> 2][j & 3];
         } else {
           const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < tend;
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
@@ -263,7 +272,12 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
           // keys' features there are not masked) never reach an output
           if (fb < FB && (w * FB + fb) * 16 + 4 * g + (j & 3) < m_valid) {
             const float a = pq[tb][fb][j & 3];
-            f = (KIND == kPrf) ? fast_exp2(a) : fmaxf(a, 0.f) * inv_sqrt_m + eps;
+            if constexpr (KIND == kPrf)
+              f = fast_exp2(a);
+            else if constexpr (KIND == kTrig)
+              f = trig_feature(a, (w * FB + fb) * 16 + 4 * g + (j & 3), M);  // the query's scale cancels
+            else
+              f = fmaxf(a, 0.f) * inv_sqrt_m + eps;
           }
           bq[tb][fcw][j] = to_t<C>(f);
         }
@@ -429,7 +443,7 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
   CT* cz = reinterpret_cast<CT*>(base + p.off_cz);
   float* cmax = reinterpret_cast<float*>(base + p.off_cmax);
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = (kind == kPrf) ? sc * kLog2e : sc;
+  const float wscale = omega_scale(kind, sc);
   const float nscale = sc * sc * kLog2e * 0.5f;
   const float inv_sqrt_m = 1.0f / std::sqrt((float)s.m);
   const float log2_sqrt_m = 0.5f * std::log2((float)s.m);
@@ -452,6 +466,10 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
         launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kPrf, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k, vg,
             omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles, p.nseg,
             s.m, s.dv, vcols);
+      else if (!GEN && kind == kTrig)  // the trigonometric map on the exact shapes only
+        launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, GEN ? kPrf : kTrig, false, false, GEN, PT>, p.G,
+            64 * NWR, 0, st, k, vg, omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart,
+            pmax, seg_tiles, p.nseg, s.m, s.dv, vcols);
       else
         launch("reduce", kv_reduce_kernel<T, D, DV, M, kReduceRing, kRelu, false, false, GEN, PT>, p.G, 64 * NWR, 0, st, k,
             vg, omf, nullptr, s.H, s.L, p.tpb, p.T_all, p.G, eps, inv_sqrt_m, nscale, part, zpart, pmax, seg_tiles,
@@ -474,6 +492,9 @@ static hipError_t run_causal(const T* q, const T* k, const T* v, const float* om
     if (kind == kPrf)
       launch("sweep", sweep_kernel<T, D, DV, M, kPrf, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
           s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
+    else if (!GEN && kind == kTrig)
+      launch("sweep", sweep_kernel<T, D, DV, M, GEN ? kPrf : kTrig, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart,
+          cz, cmax, s.H, s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);
     else
       launch("sweep", sweep_kernel<T, D, DV, M, kRelu, GEN, CT>, p.G, 64 * NWR, 0, st, q, k, vg, omf, cpart, cz, cmax, s.H,
           s.L, p.seg_len, p.nseg, eps, inv_sqrt_m, nscale, out_f32, og, s.m, s.dv, vcols);

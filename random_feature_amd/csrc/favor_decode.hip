@@ -17,6 +17,7 @@
 //   and the workgroup reduces the shares through LDS.
 #include "favor_device.hpp"
 #include "favor_plan.hpp"
+#include "favor_reduce.hpp"
 #include "favor_timing.hpp"
 
 #include <algorithm>
@@ -193,7 +194,9 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
     float k2 = 0.f;
     for (int dd = lane; dd < D; dd += 64) k2 += xs[(wv * 2 + 1) * D + dd] * xs[(wv * 2 + 1) * D + dd];
     k2 = wave_sum(k2);
-    if (lane == 0) wred[wv][1][0] = k2 * nscale + log2_sqrt_m;  // log2 of the key's normaliser
+    // log2 of the key's normaliser exp(|k'|^2/2) sqrt(m) (exponential map: divides), or of its scale
+    // exp(|k'|^2/2) / sqrt(m/2) (trigonometric map, log2_sqrt_m then taken of m/2: multiplies)
+    if (lane == 0) wred[wv][1][0] = kind == kTrig ? k2 * nscale - log2_sqrt_m : k2 * nscale + log2_sqrt_m;
   }
   // feature r's projection from this thread's half of omega_r (w), completed across the
   // lane pair by DPP; every thread runs the same iterations
@@ -255,6 +258,10 @@ decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restr
       if (kind == 0) {
         fq[g * m + r] = fast_exp2(fq[g * m + r] - mx);
         fk[g * m + r] = fast_exp2(fk[g * m + r] - kbg);
+      } else if (kind == kTrig) {
+        // the m/2 sines, then the m/2 cosines; the query's scale cancels in the ratio
+        fq[g * m + r] = trig_feature(fq[g * m + r], r, m);
+        fk[g * m + r] = trig_feature(fk[g * m + r], r, m) * fast_exp2(kbg);
       } else {
         fq[g * m + r] = fmaxf(fq[g * m + r], 0.f) * inv_sqrt_m + eps;
         fk[g * m + r] = fmaxf(fk[g * m + r], 0.f) * inv_sqrt_m + eps;
@@ -327,9 +334,10 @@ static hipError_t run_decode(const T* q, const T* k, const T* v, const float* om
                              int dv, int m, int kind, float eps, const float* gate, const float* inw, float* out,
                              hipStream_t st) {
   const float sc = std::pow((float)D, -0.25f);
-  const float wscale = (kind == 0) ? sc * kLog2e : sc;
+  const float wscale = omega_scale(kind, sc);
   const float nscale = sc * sc * kLog2e * 0.5f;
-  const float log2_sqrt_m = 0.5f * std::log2((float)m);
+  // the features' normaliser: sqrt(m), or sqrt(m/2) for the trigonometric map (m/2 vectors, two features each)
+  const float log2_sqrt_m = 0.5f * std::log2((float)(kind == kTrig ? m / 2 : m));
   const float inv_sqrt_m = 1.0f / std::sqrt((float)m);
   const size_t lds =
       (size_t)(2 * kDecodeSeqs * m + kDecodeSeqs * 2 * D + kDecodeSeqs * kDecodeThreads * 4) * sizeof(float);

@@ -17,6 +17,12 @@ __device__ __forceinline__ float trig_feature(float a, int feature, int m) {
   return __builtin_amdgcn_cosf(a - (feature < (m >> 1) ? 0.25f : 0.f));
 }
 
+// Scale folded into the Omega' fragments: d^-1/4, times log2(e) for the exponential map (the
+// hardware exp2) or 1/(2 pi) for the trigonometric map (the hardware cosine takes revolutions).
+inline float omega_scale(int kind, float sc) {
+  return kind == kPrf ? sc * kLog2e : (kind == kTrig ? sc * 0.15915494309189535f : sc);
+}
+
 // ---------------------------------------------------------------- omega fragments
 // frag[h][fb][dc][lane][j] = scale * omega[h][fb*16 + c][dc*32 + 8g + j] (0 beyond d),
 // which is both the B operand (k = d, n = feature) of the key projection and the

@@ -34,6 +34,9 @@ scan_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const flo
   constexpr int NBLK = (NQ + 255) / 256;
   constexpr int KB = 8;  // segments loaded per batch
   extern __shared__ float pre[];  // [nseg] prefix maxima over segments and waves
+  // the keys carry a stabiliser (a running maximum of their exponents, or of their norms for the
+  // trigonometric map) except under ReLU
+  const bool scaled = kind != kRelu;
   const int bh = blockIdx.x / NBLK, blk = blockIdx.x % NBLK;
   for (int p = threadIdx.x; p < nseg; p += blockDim.x) {  // the segments' own maxima
     const size_t slot = (size_t)bh * nseg + p;
@@ -46,7 +49,7 @@ scan_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const flo
     float run = -INFINITY;
     for (int p = 0; p < nseg; ++p) {
       run = fmaxf(run, pre[p]);
-      pre[p] = (kind == kPrf) ? run : 0.f;
+      pre[p] = scaled ? run : 0.f;
       if (blk == 0) cmax[(size_t)bh * nseg + p] = pre[p];
     }
   }
@@ -85,7 +88,7 @@ scan_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const flo
       const int p = p0 + u < nseg ? p0 + u : nseg - 1;
       const size_t slot = (size_t)bh * nseg + p;
       x[u] = ld4_f32(src + slot * NE);
-      sc[u] = (kind == kPrf) ? pmax[slot * NWR + wv] : 0.f;
+      sc[u] = scaled ? pmax[slot * NWR + wv] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
@@ -95,7 +98,7 @@ scan_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const flo
         const float mp = pre[p];
         if (p > 0) acc *= fast_exp2(prev - mp);
         st4_f32(dst + slot * NE, acc);
-        acc += x[u] * ((kind == kPrf) ? fast_exp2(sc[u] - mp) : 1.f);
+        acc += x[u] * (scaled ? fast_exp2(sc[u] - mp) : 1.f);
         prev = mp;
       }
     }

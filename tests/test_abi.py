@@ -81,7 +81,8 @@ def test_causal_argument_checks():
     assert call(S=FAKE, z=None) == INVALID          # both or neither
     assert call(wsb=8) == WORKSPACE
     assert call(d=48) == UNSUPPORTED
-    assert call(kind=2) == UNSUPPORTED          # trigonometric features: bidirectional and features only
+    assert call(kind=2, wsb=8) == WORKSPACE    # trigonometric features: accepted up to the workspace check
+    assert call(kind=2, S=FAKE, z=FAKE) == UNSUPPORTED  # but no canonical final state for them
 
 
 def test_trig_argument_checks():
@@ -90,9 +91,6 @@ def test_trig_argument_checks():
                            ctypes.c_float(0.0), renorm, 0, FAKE, FAKE, ctypes.c_size_t(8), None)
     assert cross() == WORKSPACE                 # accepted up to the workspace check
     assert cross(renorm=0) == UNSUPPORTED       # no canonical scale for the trigonometric map
-    dec = rf.raw_call("favor_decode", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 64, 64, 256, 1, 2,
-                      ctypes.c_float(0.0), FAKE, None)
-    assert dec == UNSUPPORTED
     assert rf.raw_call("favor_make_omega_host", ctypes.c_uint64(0), 1, 33, 16, 4, FAKE) == INVALID
 
 
@@ -247,4 +245,10 @@ def test_shape_set(d, dv, m, dt, status):
 def test_trig_only_on_exact_shapes():
     assert _bidir(d=64, dv=64, m=256, kind=2, wsb=16) == WORKSPACE
     assert _bidir(d=64, dv=128, m=256, kind=2, wsb=16) == UNSUPPORTED
+
+    def causal(dv, m):
+        return rf.raw_call("favor_causal", FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, dv, m, 1, 2, ctypes.c_float(0.0), 0,
+                           FAKE, None, None, FAKE, ctypes.c_size_t(16), None)
+    assert causal(64, 256) == WORKSPACE
+    assert causal(128, 256) == UNSUPPORTED
 

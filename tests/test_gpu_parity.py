@@ -310,6 +310,41 @@ def test_decode_steps(dtype, d, dv, m):
     assert rel_err(z, z_ref) < 1e-5
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d,dv,m", [(16, 16, 32), (64, 64, 256)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_trig_steps(dtype, d, dv, m, gated):
+    """Decode steps with trigonometric features (the trig_pairs Omega under FAVOR_TRIG): the state in canonical
+    scale, sin/cos(w.k) exp(|k|^2/2)/sqrt(m/2), against the oracle's recurrence on features_trig of the m/2
+    vectors; plain and gated."""
+    N, H, T, P = 5, 3, 20, 40
+    om_dev = rf.make_omega(24, H, m, d, "trig_pairs")
+    om = oracle.make_omega(24, H, m // 2, d, "ortho_chi")
+    kp = workloads.make_tensor((N, H, P, d), 31, 0.4, dtype)
+    vp = workloads.make_tensor((N, H, P, dv), 32, 1.0, dtype)
+    S0, z0 = oracle.state_from_prior(kp, vp, om, kind="trig")
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    qs = workloads.make_tensor((T, N, H, d), 33, 0.4, dtype)
+    ks = workloads.make_tensor((T, N, H, d), 34, 0.4, dtype)
+    vs = workloads.make_tensor((T, N, H, dv), 35, 1.0, dtype)
+    S = torch.from_numpy(S0).to(DEV)
+    z = torch.from_numpy(z0).to(DEV)
+    qd, kd, vd = qs.to(DEV), ks.to(DEV), vs.to(DEV)
+    if gated:
+        gates = workloads.make_gates((T, N, H), 36, lo=0.5)
+        S_ref, z_ref, outs_ref = oracle.decode_gated_run(S0, z0, qs, ks, vs, om, gates.numpy(), None, kind="trig")
+        gd = gates.to(DEV)
+        outs = torch.stack([rf.decode_gated(qd[t], kd[t], vd[t], om_dev, S, z, gd[t], kind="trig") for t in range(T)])
+    else:
+        S_ref, z_ref, outs_ref = oracle.decode_run(S0, z0, qs, ks, vs, om, kind="trig")
+        outs = torch.stack([rf.decode(qd[t], kd[t], vd[t], om_dev, S, z, kind="trig") for t in range(T)])
+    torch.cuda.synchronize()
+    assert rel_err(outs, outs_ref) < TOL[dtype]
+    assert np.max(np.abs(S.cpu().double().numpy() - S_ref)) / np.max(np.abs(S_ref)) < 1e-5
+    assert rel_err(z, z_ref) < 1e-5
+
+
 def test_decode_continues_causal_state():
     """Checkpoint/resume: the causal pass's final state (canonical scale) continued by decode equals the
     oracle's causal output over the concatenated sequence."""
@@ -563,6 +598,25 @@ def test_trig_features_bidir(dtype, shape, L):
     om_half = oracle.make_omega(43, H, m // 2, d, "ortho_chi")
     ref = oracle.bidir(q, k, v, om_half, kind="trig")
     out = rf.bidir(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind="trig", out_f32=True)
+    torch.cuda.synchronize()
+    e = rel_err(out, ref)
+    assert e < TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(16, 16, 32), (32, 32, 64), (64, 64, 128), (64, 64, 256)])
+@pytest.mark.parametrize("L", [1100, 33, 1])
+def test_trig_features_causal(dtype, shape, L):
+    """Causal attention with trigonometric features: the keys' scale exp(|k|^2/2) rides on each segment's
+    stabiliser and the scan's prefix maxima (L = 1100 spans five segments), the queries' cancels; against the
+    oracle's prefix sums on features_trig of the m/2 vectors."""
+    d, dv, m = shape
+    B, H = 2, 2
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 900 + m + L, scale=0.4)
+    om_dev = rf.make_omega(46, H, m, d, "trig_pairs")
+    om_half = oracle.make_omega(46, H, m // 2, d, "ortho_chi")
+    ref = oracle.causal(q, k, v, om_half, kind="trig")
+    out = rf.causal(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, kind="trig", out_f32=True)
     torch.cuda.synchronize()
     e = rel_err(out, ref)
     assert e < TOL[dtype], e
