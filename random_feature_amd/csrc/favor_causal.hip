@@ -270,7 +270,7 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
           float f = 0.f;
           // features past m_valid: zero query features, so the state rows and scores they would feed (the
           // keys' features there are not masked) never reach an output
-          if (fb < FB && (w * FB + fb) * 16 + 4 * g + (j & 3) < m_valid) {
+          if (fb < FB && (!GEN || (w * FB + fb) * 16 + 4 * g + (j & 3) < m_valid)) {  // exact shapes: all valid
             const float a = pq[tb][fb][j & 3];
             if constexpr (KIND == kPrf)
               f = fast_exp2(a);

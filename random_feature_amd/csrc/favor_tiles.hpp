@@ -506,7 +506,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
         } else if constexpr (KIND == kTrig) {
           f = trig_feature(a, (w * FB + fb) * 16 + c, M) * tw[j >> 2][j & 3];
         } else {
-          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L && (w * FB + fb) * 16 + c < m_valid;
+          const bool ok = tok0 + 16 * (j >> 2) + 4 * g + (j & 3) < L && (!GEN || (w * FB + fb) * 16 + c < m_valid);
           f = ok ? fmaxf(a, 0.f) * inv_sqrt_m + eps : 0.f;
         }
         fv[j] = f;
