@@ -143,14 +143,14 @@ sweep_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restri
       const int tok = tok0 + qrow;
       if (tok >= tend || c8 * 8 >= vcols) continue;
       const int cb = (c8 * 8) >> 4, g0 = ((c8 * 8) & 15) >> 2;
-      const int off = ((tb * NVB + cb) * 64 + cq + 16 * g0) * 4, doff = 2 * NVB * 256 + tb * 16 + cq;
-      f32x4 lo = *reinterpret_cast<const f32x4*>(&xo[0][off]);
-      f32x4 hi = *reinterpret_cast<const f32x4*>(&xo[0][off + 64]);
+      const int xoff = ((tb * NVB + cb) * 64 + cq + 16 * g0) * 4, doff = 2 * NVB * 256 + tb * 16 + cq;
+      f32x4 lo = *reinterpret_cast<const f32x4*>(&xo[0][xoff]);
+      f32x4 hi = *reinterpret_cast<const f32x4*>(&xo[0][xoff + 64]);
       float den = xo[0][doff];
 #pragma unroll
       for (int ww = 1; ww < NW; ++ww) {
-        lo += *reinterpret_cast<const f32x4*>(&xo[ww][off]);
-        hi += *reinterpret_cast<const f32x4*>(&xo[ww][off + 64]);
+        lo += *reinterpret_cast<const f32x4*>(&xo[ww][xoff]);
+        hi += *reinterpret_cast<const f32x4*>(&xo[ww][xoff + 64]);
         den += xo[ww][doff];
       }
       const float rden = __builtin_amdgcn_rcpf(den);  // hardware reciprocal (1 ulp)
