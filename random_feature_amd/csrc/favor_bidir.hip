@@ -124,7 +124,7 @@ combine_kernel(const PT* __restrict__ part, const PT* __restrict__ zpart, const 
 // S_aug are zero, and their exponents are -inf so that the exact-maximum fallback ignores them);
 // out rows are ldo elements apart and the call writes its vcols <= DV columns of them.
 template <typename T, int D, int DV, int M, int KIND, bool GEN>
-__global__ void __launch_bounds__(64 * (FeatSplit<M, D>::NW), 2)
+__global__ void __launch_bounds__(64 * (FeatSplit<M, D>::NW), (kOutThree<T, M, D> ? 3 : 2))
 q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ omf,
                 const typename Ops<T>::C* __restrict__ sfr, int H, int L, int tpb, long long T_all, int G,
                 float eps, float inv_sqrt_m, int out_f32, int renorm, const float* __restrict__ gmx, float nscale,
@@ -139,10 +139,10 @@ q_output_kernel(const T* __restrict__ Q, const typename Ops<T>::P* __restrict__ 
   constexpr int NVB = DV / 16;              // value-column blocks
   // phase 2 split: with TBS wave w takes token half w & 1 and value blocks (w >> 1) + j*NW/2
   // (half the LDS reads of the features, twice the S fragments); else both halves and
-  // blocks w + j*NW
+  // blocks w + j*NW (three workgroups per CU: the registers for a third wave on every SIMD)
   constexpr int SF_REGS = sizeof(typename Ops<T>::C) == 2 ? 4 : 8;
   constexpr int NWH = NW / 2 > 0 ? NW / 2 : 1;
-  constexpr bool TBS = NW >= 2 && ((NVB + NWH - 1) / NWH) * ((M + 31) / 32) * SF_REGS <= 64;
+  constexpr bool TBS = !kOutThree<T, M, D> && NW >= 2 && ((NVB + NWH - 1) / NWH) * ((M + 31) / 32) * SF_REGS <= 64;
   constexpr int NW2 = TBS ? NWH : NW;
   constexpr int NCB = (NVB + NW2 - 1) / NW2;  // value-column blocks per wave
   constexpr int NTB = TBS ? 1 : 2;             // token halves per wave in phase 2
@@ -585,15 +585,16 @@ bool shape_built(int dtype, int d, int dv, int m) { return kernel_shape(dtype, d
 #define FAVOR_BIDIR_PIECES 512
 #endif
 constexpr int kMaxPieces = FAVOR_BIDIR_PIECES;  // two resident 4-wave workgroups on each of 256 CUs
+constexpr int kMaxPiecesThree = 3 * FAVOR_BIDIR_PIECES / 2;  // three (the output kernel where kOutThree holds)
 
-// Pieces of the flattened tile space: at most kMaxPieces, and a whole number per (b,h) when
+// Pieces of the flattened tile space: at most max_pieces, and a whole number per (b,h) when
 // that still gives at least 7/8 of them, so that no piece straddles two (b,h) (one set of
 // operands per workgroup, one partial per piece).
-static int pieces(long long bh, long long tpb) {
+static int pieces(long long bh, long long tpb, int max_pieces = kMaxPieces) {
   const long long total = bh * tpb;
-  long long g = std::min<long long>(total, kMaxPieces);
-  if (bh <= kMaxPieces) {
-    const long long per = std::min<long long>(tpb, kMaxPieces / bh);
+  long long g = std::min<long long>(total, max_pieces);
+  if (bh <= max_pieces) {
+    const long long per = std::min<long long>(tpb, max_pieces / bh);
     if (per * bh * 8 >= g * 7) g = per * bh;
   }
   return (int)g;
@@ -607,7 +608,8 @@ BidirPlan plan_bidir(const Shape& s, int dtype, int Lq) {
   p.G = pieces(s.bh(), p.tpb);
   p.tpb_q = ((Lq > 0 ? Lq : s.L) + 31) / 32;  // queries
   p.T_all_q = s.bh() * p.tpb_q;
-  p.G_q = pieces(s.bh(), p.tpb_q);
+  // the output kernel runs three workgroups per CU for 16-bit inputs on at most four waves (kOutThree)
+  p.G_q = pieces(s.bh(), p.tpb_q, dtype != 0 && output_waves(ks.mk, ks.dk) <= 4 ? kMaxPiecesThree : kMaxPieces);
   p.nw_reduce = reduce_waves(ks.mk, s.d);
   const int dc = (s.d + 31) / 32, nb = ks.dvk / 16 + 1;
   const size_t slots = (size_t)p.G + (size_t)s.bh();

@@ -70,6 +70,14 @@ inline int reduce_waves(int m, int d) {
   return m / base > fpw ? (m / fpw < 8 ? m / fpw : 8) : base;
 }
 
+// Waves of the query-side kernels for m features at projection width d (the device-side FeatSplit): up to
+// four waves of up to 64 features (32 at d = 128), then up to eight.
+inline int output_waves(int m, int d) {
+  const int base = (m / 16) < 4 ? (m / 16) : 4;
+  const int fpw = d > 64 ? 32 : 64;
+  return m / base > fpw ? (m / fpw < 8 ? m / fpw : 8) : base;
+}
+
 // Bidirectional path: omega fragments, per-segment partial (S, z) sums with their
 // stabiliser maxima, and the combined S fragments.
 // Both passes walk the B*H*ceil(L/32) token tiles split into G contiguous pieces (one

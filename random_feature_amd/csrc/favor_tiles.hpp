@@ -21,6 +21,10 @@ template <int M, int D> struct FeatSplit {
   static constexpr int NW = M / BASE > kFeatPerWave<D> ? (M / kFeatPerWave<D> < 8 ? M / kFeatPerWave<D> : 8) : BASE;
   static constexpr int FB = M / (16 * NW);
 };
+// Three output workgroups per CU (three waves per SIMD) where the registers allow it: 16-bit inputs with at most
+// four waves of up to 64 features. Their phase 2 then takes both token halves per wave, which holds the S fragments
+// of fewer value blocks (half the registers) for twice the LDS reads of the features.
+template <typename T, int M, int D> constexpr bool kOutThree = sizeof(T) == 2 && FeatSplit<M, D>::NW <= 4;
 // Waves of the key/value reduction (and of the causal sweep, which shares its split): up to
 // RW_MAX waves of 32 features or more, then up to eight when a wave would own more than
 // kFeatPerWave features. Up to four waves: two workgroups per CU (NW/2 waves per SIMD; the
