@@ -366,8 +366,8 @@ def test_decode_continues_causal_state():
 
 def test_decode_workload_sampled():
     """The decode workload (256 sequences x 16 heads, d64 m256, bf16, 1000 steps): the initial state of every
-    sequence comes from the oracle's 2048-token prefix of one of four prefix sequences; every step's output
-    of sampled (sequence, head) pairs is compared with the oracle's recurrence."""
+    sequence comes from the oracle's 2048-token prefix of one of four prefix sequences; every step's output of all
+    16 heads of four sequences (64 pairs), and their final states, are compared with the oracle's recurrence."""
     w = workloads.WORKLOADS["decode_bf16"]
     R = 4
     om_dev, om = _omega(w.seed, w.H, w.m, w.d)
@@ -379,24 +379,21 @@ def test_decode_workload_sampled():
     S = S0[idx].contiguous().to(DEV)
     z = z0[idx].contiguous().to(DEV)
     qs, ks, vs = workloads.make_decode_steps(w, DEV)
-    pairs = [(0, 0), (5, 3), (130, 7), (255, 15)]
-    steps = [t for t in range(w.steps) if t % 50 == 0 or t == w.steps - 1]
+    seqs = torch.tensor([0, 77, 130, 255])
+    seqs_dev = seqs.to(DEV)
     outs = []
     for t in range(w.steps):
         o = rf.decode(qs[t], ks[t], vs[t], om_dev, S, z)
-        if t in steps:
-            outs.append(torch.stack([o[s, h] for s, h in pairs]).cpu())
+        outs.append(o[seqs_dev])                   # [4, H, dv]
     torch.cuda.synchronize()
-    outs = torch.stack(outs)                       # [len(steps), len(pairs), dv]
-    worst = 0.0
-    for i, (s, h) in enumerate(pairs):
-        Sp, zp, ref = oracle.decode_run(S0[s % R, h][None, None].numpy(), z0[s % R, h][None, None].numpy(),
-                                        qs[:, s:s + 1, h:h + 1].cpu(), ks[:, s:s + 1, h:h + 1].cpu(),
-                                        vs[:, s:s + 1, h:h + 1].cpu(), om[h:h + 1])
-        worst = max(worst, rel_err(outs[:, i], ref[steps, 0, 0]))
-        assert np.max(np.abs(S[s, h].cpu().double().numpy() - Sp[0, 0])) / np.max(np.abs(Sp)) < 1e-4
-    print(f"decode_bf16 sampled rel err {worst:.3e}")
+    outs = torch.stack(outs).cpu()                 # [steps, 4, H, dv]
+    Sp, zp, ref = oracle.decode_run(S0[seqs % R].numpy(), z0[seqs % R].numpy(), qs[:, seqs_dev].cpu(),
+                                    ks[:, seqs_dev].cpu(), vs[:, seqs_dev].cpu(), om)
+    worst = rel_err(outs, ref)
+    print(f"decode_bf16 rel err over 64 pairs x {w.steps} steps {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+    assert np.max(np.abs(S[seqs_dev].cpu().double().numpy() - Sp)) / np.max(np.abs(Sp)) < 1e-4
+    assert rel_err(z[seqs_dev], zp) < 1e-4
 
 
 def _decode_workload_state(w, om, n_prior_seqs=4):
@@ -493,9 +490,10 @@ def test_decode_gated_unit_gate_is_decode():
 
 def test_decode_gated_workload_sampled():
     """The gated decode workload (256 sequences x 16 heads, d64 m256, bf16, gates U[0.9,1), input weight 1 - g):
-    200 steps, sampled pairs against the oracle's gated recurrence."""
+    1000 steps; every step's output of all 16 heads of four sequences (64 pairs), and their final states, against
+    the oracle's gated recurrence."""
     w = workloads.WORKLOADS["decode_gated_bf16"]
-    T, R = 200, 4
+    T, R = w.steps, 4
     om_dev, om = _omega(w.seed, w.H, w.m, w.d)
     kp, vp = workloads.make_decode_prior(w, n_seq=R)
     S0, z0 = oracle.state_from_prior(kp, vp, om)
@@ -507,22 +505,22 @@ def test_decode_gated_workload_sampled():
     qs, ks, vs = workloads.make_decode_steps(w, DEV, steps=T)
     gates = workloads.make_gates((T, w.B, w.H), w.seed, device=DEV)
     wts = 1.0 - gates
-    pairs = [(0, 0), (77, 9), (255, 15)]
+    seqs = torch.tensor([0, 77, 130, 255])
+    seqs_dev = seqs.to(DEV)
     outs = []
     for t in range(T):
         o = rf.decode_gated(qs[t], ks[t], vs[t], om_dev, S, z, gates[t], wts[t])
-        outs.append(torch.stack([o[s, h] for s, h in pairs]).cpu())
+        outs.append(o[seqs_dev])
     torch.cuda.synchronize()
-    outs = torch.stack(outs)
-    worst = 0.0
-    for i, (s, h) in enumerate(pairs):
-        sl = (slice(None), slice(s, s + 1), slice(h, h + 1))
-        _, _, ref = oracle.decode_gated_run(S0[s % R, h][None, None].numpy(), z0[s % R, h][None, None].numpy(),
-                                            qs[sl].cpu(), ks[sl].cpu(), vs[sl].cpu(), om[h:h + 1],
-                                            gates[sl].cpu().numpy(), wts[sl].cpu().numpy())
-        worst = max(worst, rel_err(outs[:, i], ref[:, 0, 0]))
-    print(f"decode_gated_bf16 sampled rel err {worst:.3e}")
+    outs = torch.stack(outs).cpu()                 # [T, 4, H, dv]
+    Sp, zp, ref = oracle.decode_gated_run(S0[seqs % R].numpy(), z0[seqs % R].numpy(), qs[:, seqs_dev].cpu(),
+                                          ks[:, seqs_dev].cpu(), vs[:, seqs_dev].cpu(), om,
+                                          gates[:, seqs_dev].cpu().numpy(), wts[:, seqs_dev].cpu().numpy())
+    worst = rel_err(outs, ref)
+    print(f"decode_gated_bf16 rel err over 64 pairs x {T} steps {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
+    assert np.max(np.abs(S[seqs_dev].cpu().double().numpy() - Sp)) / np.max(np.abs(Sp)) < 1e-4
+    assert rel_err(z[seqs_dev], zp) < 1e-4
 
 
 # ---------------------------------------------------------------- hyperbolic features
