@@ -671,18 +671,19 @@ def test_bidir_cross_equal_lengths_is_bidir():
     assert torch.equal(a, b)
 
 
-def test_cross_bf16_workload_sampled():
+def test_cross_bf16_workload_every_pair():
     """The cross-attention workload (B8 H12 Lq1024 Lk4096 d64 m256, bf16) in the benchmark's launch
-    configuration, sampled (b,h) pairs against the oracle."""
+    configuration, every (b,h) pair against the oracle."""
     w = workloads.WORKLOADS["cross_bf16"]
     q, k, v = workloads.make_qkv(w)
     om_dev, om = _omega(w.seed, w.H, w.m, w.d)
     out = rf.bidir_cross(q.to(DEV), k.to(DEV), v.to(DEV), om_dev).cpu()
     worst = 0.0
-    for b, h in _sample_pairs(w.B, w.H, 3, 2):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        worst = max(worst, rel_err(out[sl], oracle.bidir(q[sl], k[sl], v[sl], om[h:h + 1])))
-    print(f"cross_bf16 sampled rel err {worst:.3e}")
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            worst = max(worst, rel_err(out[sl], oracle.bidir(q[sl], k[sl], v[sl], om[h:h + 1])))
+    print(f"cross_bf16 rel err over every (b,h) {worst:.3e}")
     assert worst < TOL[torch.bfloat16]
 
 
@@ -946,20 +947,37 @@ def test_large_norm_inputs(dtype, path, scale):
 
 def test_bidir_backward_workload_sampled():
     """The backward at the headline workload's size (B8 H12 L4096 d64 m256, bf16) in the benchmark's launch
-    configuration, sampled (b,h) pairs against the oracle."""
+    configuration, 24 sampled (b,h) pairs against the oracle (about a second of oracle time each).
+
+    The products whose terms cancel take fp16 operands scaled per row or per (b,h), so each gradient's absolute
+    error is a few 2^-11 of its block's largest row (measured: at most 0.75 * 2^-11 for dk). Rows whose norm is a
+    few percent of their block's largest are formed by cancellation and miss row by row by up to 3e-2 (dk rows at
+    1.3 % of the block); they are judged block-normwise (every row's error against the block's largest row), the
+    other rows row by row, both at the bf16 bound. The worst error of any row on its own norm is printed."""
     w = workloads.WORKLOADS["bidir_bf16"]
     q, k, v = workloads.make_qkv(w)
     g = workloads.make_tensor((w.B, w.H, w.L, w.dv), 888, 1.0, torch.bfloat16)
     om_dev, om = _omega(w.seed, w.H, w.m, w.d)
     got = [t.cpu() for t in rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV))]
-    worst = 0.0
-    for b, h in _sample_pairs(w.B, w.H, 3, 3):
+    worst_block, worst_row, worst_any = 0.0, 0.0, 0.0
+    for b, h in _sample_pairs(w.B, w.H, 24, 3):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.bidir_backward(q[sl], k[sl], v[sl], om[h:h + 1], g[sl])
         for a, r in zip(got, ref):
-            worst = max(worst, rel_err(a[sl], r))
-    print(f"bidir_bf16 backward sampled rel err {worst:.3e}")
-    assert worst < TOL[torch.bfloat16]
+            a = a[sl].double().numpy()[0, 0]
+            r = np.asarray(r, np.float64)[0, 0]
+            assert np.all(np.isfinite(a))
+            num = np.max(np.abs(a - r), axis=-1)
+            den = np.max(np.abs(r), axis=-1)
+            top = np.max(den)
+            worst_block = max(worst_block, float(np.max(num) / top))
+            big = den >= 0.05 * top
+            worst_row = max(worst_row, float(np.max(num[big] / den[big])))
+            worst_any = max(worst_any, float(np.max(num / den)))
+    print(f"bidir_bf16 backward over 24 (b,h): block-normwise {worst_block:.3e}, rows >= 5 % of their block "
+          f"{worst_row:.3e}, any row on its own norm {worst_any:.3e}")
+    assert worst_block < TOL[torch.bfloat16]
+    assert worst_row < TOL[torch.bfloat16]
 
 
 # ---------------------------------------------------------------- prepared Omega
