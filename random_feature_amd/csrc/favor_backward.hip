@@ -247,10 +247,11 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   f32x4 sacc[FB][NB];
   int eS = 0;  // S rows were scaled by 2^-eS
   int cur_bh = -1;
-  // dq blocks of the previous tile, scaled: stored one tile late, after the next tile's first
-  // barriers, so the stores' latency is not waited for at the top of the next tile
+  // the contractions of a tile (dq and dS_aug) run one tile late, after the next tile's row maxima
+  // are exchanged, beside that tile's feature map; the tile's dq blocks are stored from there
   f32x4 pend[BPW];
   int pend_bh = -1, pend_tok0 = 0;
+  bool pending = false;
   auto store_pending = [&]() {
     if (pend_bh < 0) return;
 #pragma unroll
@@ -297,6 +298,67 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
     }
   };
 
+  // dq and dS_aug of the pending tile, from its rows in LDS (prow, wbr, the wave's own erow, rsc): between
+  // the next tile's row-maximum exchange and the exchange of its sums (which precedes every write of
+  // those rows), or before the sums of the pending tile's (b,h) are flushed
+  auto contract_pending = [&]() {
+    if (!pending) return;
+    pending = false;
+    // ---- dq: this wave's blocks of dq^T over all features, scaled and stored
+#pragma unroll
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = w * BPW + bi, tb = blk & 1;
+      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int fc = 0; fc < NFC; ++fc) mma16(a, omt[bi >> 1][fc], ld8<XS>(&prow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
+      pend[bi] = a * rsc[tb * 16 + c];
+    }
+    store_pending();
+
+    // ---- dS_aug += phi'^T W over the tile's queries: with bf16 operands as hi + lo pairs,
+    // hi*hi + hi*lo + lo*hi (the sums over the queries cancel, so 8-bit operands would not do)
+    {
+      auto tr8 = [&](const XB* base, int stride, int col0) {
+        vec8<XB> r;
+        if constexpr (sizeof(XB) == 2) {
+          const bf16x4 lo = lds_read_tr4(reinterpret_cast<const bf16*>(base + (4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
+          const bf16x4 hi = lds_read_tr4(reinterpret_cast<const bf16*>(base + (16 + 4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r[i] = lo[i];
+            r[i + 4] = hi[i];
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) r[jj] = base[(16 * (jj >> 2) + 4 * g + (jj & 3)) * stride + col0 + c];
+        }
+        return r;
+      };
+      // the phi' fragments of the wave's features once, then W one column block at a time (fewer live
+      // registers beside the next tile's projections)
+      vec8<XB> ea[FB], el[NSPL == 2 ? FB : 1];
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        ea[fb] = tr8(&erow[0][w][0], EROW, fb * 16);
+        if constexpr (NSPL == 2) el[fb] = tr8(&erow[NSPL - 1][w][0], EROW, fb * 16);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const vec8<XB> w0 = tr8(wbr[0], WBROW, nb * 16);
+        vec8<XB> w1 = w0;
+        if constexpr (NSPL == 2) w1 = tr8(wbr[NSPL - 1], WBROW, nb * 16);
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+          mma16(sacc[fb][nb], ea[fb], w0);
+          if constexpr (NSPL == 2) {
+            mma16(sacc[fb][nb], ea[fb], w1);
+            mma16(sacc[fb][nb], el[fb], w0);
+          }
+        }
+      }
+    }
+  };
+
   Rg::issue(Q, dOut, L, ahead.bh, ahead.tok0(), true, ring0);
   ahead.next();
   for (int it = 0; it < n_tiles; ++it) {
@@ -313,6 +375,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
     }
     // ---- a new (b,h): close the old one's sums, load this one's operands
     if (bh != cur_bh) {
+      contract_pending();  // the previous tile's rows are complete (top barrier); before Omega'^T is replaced
       if (cur_bh >= 0) flush(cur_bh);
       zero_sums();
       const int h = bh % H;
@@ -432,7 +495,7 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       }
     }
     lds_barrier();  // B1: row maxima
-    store_pending();
+    contract_pending();
 
     // ---- phi' = 2^(a' - max) (ReLU: the features); D' and A partials; phi' rows for the dS transposes
     unsigned pos = 0;  // ReLU: bit (tb*FB + fb)*4 + i set where a > 0
@@ -527,62 +590,15 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         }
       }
     }
-    lds_barrier();  // B3: dPhi_Q rows, W rows
-
-    // ---- dq: this wave's blocks of dq^T over all features, unscaled (stored later)
-#pragma unroll
-    for (int bi = 0; bi < BPW; ++bi) {
-      const int blk = w * BPW + bi, tb = blk & 1;
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int fc = 0; fc < NFC; ++fc) mma16(a, omt[bi >> 1][fc], ld8<XS>(&prow[(tb * 16 + c) * PROW + fc * 32 + 8 * g]));
-      pend[bi] = a * rsc[tb * 16 + c];
-    }
+    // the rows of this tile (dPhi_Q, W, phi', the dq scales) are read by its contractions, after the
+    // next tile's top barrier
+    pending = true;
     pend_bh = bh;
     pend_tok0 = tok0;
-
-    // ---- dS_aug += phi'^T W over the tile's queries: with bf16 operands as hi + lo pairs,
-    // hi*hi + hi*lo + lo*hi (the sums over the queries cancel, so 8-bit operands would not do)
-    {
-      auto tr8 = [&](const XB* base, int stride, int col0) {
-        vec8<XB> r;
-        if constexpr (sizeof(XB) == 2) {
-          const bf16x4 lo = lds_read_tr4(reinterpret_cast<const bf16*>(base + (4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
-          const bf16x4 hi = lds_read_tr4(reinterpret_cast<const bf16*>(base + (16 + 4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3)));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            r[i] = lo[i];
-            r[i + 4] = hi[i];
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) r[jj] = base[(16 * (jj >> 2) + 4 * g + (jj & 3)) * stride + col0 + c];
-        }
-        return r;
-      };
-      vec8<XB> wt[NSPL][NB];
-#pragma unroll
-      for (int sp = 0; sp < NSPL; ++sp)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wt[sp][nb] = tr8(wbr[sp], WBROW, nb * 16);
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb) {
-        const vec8<XB> ea = tr8(&erow[0][w][0], EROW, fb * 16);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) mma16(sacc[fb][nb], ea, wt[0][nb]);
-        if constexpr (NSPL == 2) {
-          const vec8<XB> el = tr8(&erow[NSPL - 1][w][0], EROW, fb * 16);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            mma16(sacc[fb][nb], ea, wt[NSPL - 1][nb]);
-            mma16(sacc[fb][nb], el, wt[0][nb]);
-          }
-        }
-      }
-    }
     cur.next();
   }
-  store_pending();
+  lds_barrier();  // the last tile's rows
+  contract_pending();
   flush(cur_bh);
 }
 
