@@ -711,6 +711,49 @@ def test_bidir_backward(dtype, shape, L):
         assert e < TOL[dtype], (name, e)
 
 
+def _grad_block_and_row_errs(got, ref):
+    """Worst errors of gradients [B,H,L,n] against the oracle's over every (b,h) block: block-normwise (each row's
+    largest error over the block's largest row), row by row for the rows of at least 5 % of their block, and
+    any row on its own norm (reported, not bounded: rows formed by cancellation miss by more, as described at
+    the headline workload)."""
+    worst = [0.0, 0.0, 0.0]
+    for a, r in zip(got, ref):
+        a = a.detach().float().cpu().double().numpy()
+        r = np.asarray(r, np.float64)
+        assert a.shape == r.shape and np.all(np.isfinite(a))
+        num = np.max(np.abs(a - r), axis=-1)
+        den = np.max(np.abs(r), axis=-1)
+        top = np.max(den, axis=-1, keepdims=True)
+        big = den >= 0.05 * top
+        worst[0] = max(worst[0], float(np.max(num / top)))
+        worst[1] = max(worst[1], float(np.max((num / den)[big])))
+        worst[2] = max(worst[2], float(np.max(num / den)))
+    return worst
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+def test_bidir_backward_pieces_of_several_tiles(dtype, shape):
+    """B2 H4 L4000: 1000 tiles of 32 queries (and of 32 keys) over the gradient kernels' 256 pieces, so every
+    piece walks several tiles and most cross a (b,h) boundary mid-piece. The query-side kernel runs the
+    contractions of a tile during the next tile of its piece, or, when that tile opens another (b,h), before the
+    sums of the old one are written. Against the oracle block-normwise and row by row on the rows of at least
+    5 % of their block."""
+    d, dv, m = shape
+    B, H, L = 2, 4, 4000
+    q, k, v = _inputs(B, H, L, d, dv, dtype, 5100 + m)
+    g = workloads.make_tensor((B, H, L, dv), 5177 + m, 1.0, dtype)
+    om_dev, om = _omega(57, H, m, d)
+    ref = oracle.bidir_backward(q, k, v, om, g)
+    got = rf.bidir_backward(q.to(DEV), k.to(DEV), v.to(DEV), om_dev, g.to(DEV), grad_f32=True)
+    torch.cuda.synchronize()
+    block, rows, any_row = _grad_block_and_row_errs(got, ref)
+    print(f"backward {dtype} {shape} B{B} H{H} L{L}: block-normwise {block:.2e}, rows >= 5 % {rows:.2e}, "
+          f"any row {any_row:.2e}")
+    assert block < TOL[dtype]
+    assert rows < TOL[dtype]
+
+
 def _relu_decided_rows(x, om, rel=2e-6):
     """Rows of x [B,H,L,d] whose every ReLU pre-activation w_r.xs (fp64) is farther than rel * max|w.xs| of the
     head from zero: there the mask 1[w.xs > 0] of the gradient is the same in any precision near fp32. At a
