@@ -272,9 +272,9 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
   using Rg = Ring<T, D, DV, NT, true>;
   // key norms as stored: negated for the positive map, whose exponents start from -(n'_t + M)
   constexpr int KN = KIND == kPrf ? kNormNegSq : kNormSq;
-  // at the wait of iteration t the copies issued so far reach tile t+R-2 (each iteration
-  // issues at its end): R-4 tiles are newer than tile t+2
-  constexpr int WAIT_NEXT = Rg::CPT * (R - 4);
+  // at the wait of iteration t the copies issued so far reach tile t+R-1 (each iteration issues
+  // at its start, into the slot its predecessor has just released): R-3 tiles are newer than tile t+2
+  constexpr int WAIT_NEXT = Rg::CPT * (R - 3);
   __shared__ __attribute__((aligned(16))) unsigned char ring[R][Rg::SLOT];
   __shared__ __attribute__((aligned(16))) P ks[2][32 * KROW];
   __shared__ __attribute__((aligned(16))) float kn[2][32];
@@ -410,6 +410,12 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       flush_bh = -1;
       wait_vmcnt<0>();  // no stores may stay in flight under the partial waits of the ring
     }
+    {
+      // the copies of tile t+R-1, into the slot of tile t-1 (its value rows were read before the last barrier)
+      const bool live = it + R - 1 < n_tiles;
+      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT, ldv, vcols);
+      if (live) ahead.next();
+    }
     // stabiliser of tile t (its projection is complete)
     // trigonometric features: the keys' own scale exp(|y|^2/2) = 2^(n'_t) rides on a running
     // maximum of n'_t in the same way (rows past L carry an infinite norm: weight 0)
@@ -524,7 +530,7 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
     }
     __builtin_amdgcn_s_setprio(0);
     // stretch 2: contraction of tile t beside the conversion of tile t+2 (past the end of
-    // the piece: a filler slot into an unused buffer) and the next copies
+    // the piece: a filler slot into an unused buffer)
     vec8<C> vf[NB];
     value_frags<T, D, DV, NT>(ring[s_cur], vf, c, g, vcols);
 #pragma unroll
@@ -536,11 +542,6 @@ kv_reduce_kernel(const T* __restrict__ K, const T* __restrict__ V, const typenam
       }
     Rg::template convert<P, KROW, KN>(ring[s_cv], ks[buf], kn[buf], nscale, L - cv.tok0());
     cv.next();
-    {
-      const bool live = it + R - 1 < n_tiles;
-      Rg::issue(K, V, L, ahead.bh, ahead.tok0(), live, ring0 + s_iss * Rg::SLOT, ldv, vcols);
-      if (live) ahead.next();
-    }
     lds_barrier();
 
     if (next_new) {
