@@ -254,19 +254,22 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
   bool pending = false;
   auto store_pending = [&]() {
     if (pend_bh < 0) return;
+    // the (b,h)'s rows from a base common to the wave and 32-bit offsets within them (one register per lane
+    // instead of a 64-bit address, which the tile loop otherwise keeps in scratch)
+    const size_t bh_off = (size_t)pend_bh * L * D;
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       const int blk = w * BPW + bi, db = blk >> 1, tb = blk & 1;
       const int tok = pend_tok0 + tb * 16 + c;
       if (tok < L) {
-        const size_t off = ((size_t)pend_bh * L + tok) * D + db * 16 + 4 * g;
+        const uint32_t off = (uint32_t)tok * D + db * 16 + 4 * g;
         if (grad_f32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = pend[bi];
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + bh_off + off) = pend[bi];
         } else {
           vec4<T> o4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) o4[i] = to_t<T>(pend[bi][i]);
-          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dq) + off) = o4;
+          *reinterpret_cast<vec4<T>*>(reinterpret_cast<T*>(dq) + bh_off + off) = o4;
         }
       }
     }

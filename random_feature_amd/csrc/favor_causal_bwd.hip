@@ -786,8 +786,10 @@ cbwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       }
     }
     // ---- chunk t+1 lands and is converted
+    // (the wait on every path: otherwise the compiler, which does not see the ring's copies, takes the next
+    // iteration's fetch() loads as possibly outstanding and waits for every copy right after issuing them)
+    wait_vmcnt<0>();
     if (t + 1 < n) {
-      wait_vmcnt<0>();
       Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - tok0 - 32);
       if (threadIdx.x < 32) {
         rl[buf ^ 1][threadIdx.x] = pl;
@@ -919,8 +921,8 @@ cbwd_t_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typenam
       }
       mma_split<NSPL>(Ta[fb][NVB], ah[fb], al[fb], zh, zl);
     }
+    wait_vmcnt<0>();  // on every path (see cbwd_q_kernel)
     if (t + 1 < n) {
-      wait_vmcnt<0>();
       Rg::template convert<P, KROW, kNormNone>(ring[buf ^ 1], qs[buf ^ 1], nullptr, 0.f, L);
       if (threadIdx.x < 32) {
         rl[buf ^ 1][threadIdx.x] = pl;
@@ -1270,8 +1272,8 @@ cbwd_k_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       }
     }
     // ---- chunk t-1 lands and is converted
+    wait_vmcnt<0>();  // on every path (see cbwd_q_kernel)
     if (t > 0) {
-      wait_vmcnt<0>();
       Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - (tok0 - 32));
       if (threadIdx.x < 32) {
         rl[buf ^ 1][threadIdx.x] = pl;
@@ -1529,8 +1531,8 @@ cbwd_v_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
       }
     }
     // ---- chunk t-1 lands and is converted
+    wait_vmcnt<0>();  // on every path (see cbwd_q_kernel)
     if (t > 0) {
-      wait_vmcnt<0>();
       Rg::template convert<P>(ring[buf ^ 1], qn[buf ^ 1], kn[buf ^ 1], nscale, tend - (tok0 - 32));
       if (threadIdx.x < 32) rl[buf ^ 1][threadIdx.x] = pl;
     }
