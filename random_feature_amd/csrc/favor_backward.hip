@@ -498,7 +498,12 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       }
     }
     lds_barrier();  // B1: row maxima
-    contract_pending();
+    // the two waves of a SIMD (w and w + NW/2) take the pending contractions and the feature map below in opposite
+    // orders, so that one's matrix work overlaps the other's vector work; the phi' rows that the contractions read
+    // are rewritten only after both
+    // (the ReLU map keeps one order: its mask bits leave no registers for the other)
+    const bool first_half = KIND != kPrf || __builtin_amdgcn_readfirstlane(w) < NW / 2;
+    if (first_half) contract_pending();
 
     // ---- phi' = 2^(a' - max) (ReLU: the features); D' and A partials; phi' rows for the dS transposes
     unsigned pos = 0;  // ReLU: bit (tb*FB + fb)*4 + i set where a > 0
@@ -513,7 +518,6 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
       float dz = 0.f, da = 0.f;
 #pragma unroll
       for (int fb = 0; fb < FB; ++fb) {
-        vec4<XB> e4, e4lo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float ph;
@@ -528,9 +532,6 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
           dz += ph * zv[fb][i];
           da += ph * uq[tb][fb][i];
         }
-        split_all<4>(e4, e4lo, [&](int i) { return pq[tb][fb][i]; });
-        *reinterpret_cast<vec4<XB>*>(&erow[0][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4;
-        if constexpr (NSPL == 2) *reinterpret_cast<vec4<XB>*>(&erow[NSPL - 1][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4lo;
       }
       dz = group_sum(dz);
       da = group_sum(da);
@@ -539,6 +540,16 @@ bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ dOut, const typename
         asum[tb * 16 + c][w] = da;
       }
     }
+    if (!first_half) contract_pending();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) {
+        vec4<XB> e4, e4lo;
+        split_all<4>(e4, e4lo, [&](int i) { return pq[tb][fb][i]; });
+        *reinterpret_cast<vec4<XB>*>(&erow[0][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4;
+        if constexpr (NSPL == 2) *reinterpret_cast<vec4<XB>*>(&erow[NSPL - 1][w][(tb * 16 + c) * EROW + fb * 16 + 4 * g]) = e4lo;
+      }
     lds_barrier();  // B2: D' and A partials, phi' rows
 
     // ---- phi' * dPhi_Q (scaled) as rows [query][feature]
