@@ -179,6 +179,9 @@ __device__ __forceinline__ int scale_exp(float x) {
 //                in LDS), B = W (transposing reads), both as sums of two bf16 parts;
 //                accumulated over the piece's tiles of one (b,h) and written as a partial in
 //                the reduction's fragment layout
+// The dq and dS_aug contractions of a tile run during the next tile, between its row-maximum and
+// sums exchanges, so a tile has three barriers: the rows they read are published by the next
+// tile's first barrier.
 // KIND = kRelu: phi' = max(a, 0)/sqrt(m) + eps (the features themselves, no row maximum), and the
 // rows of dPhi_Q carry the mask 1[a > 0] instead of the factor phi' (1/sqrt(m) goes into the scale).
 template <typename T, int D, int DV, int M, int KIND>
